@@ -1,0 +1,25 @@
+"""CPU oracle for the tree-verification step.  TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, obviously correct reference of what the verification step
+computes, in float64:
+  * ``mask``      - the ancestor-or-self tree mask and node depths;
+  * ``attention`` - tree attention over a paged prefix plus tree ancestors;
+  * ``sampling``  - softmax of target/draft logits, Philox4x64-10 uniforms and
+                    the root-down rejection-sampling walk (plain C, fp64);
+  * ``commit``    - the KV commit of the accepted path;
+  * ``step``      - the four composed.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import, call, link or execute anything in this package. The
+GPU library never does, and this package shares no code with it.
+
+Functions pinned only by properties that the pages do not fix are marked
+"parity unpinned" in their docstrings; at present there are none.
+"""
+
+from .mask import tree_mask, ancestor_matrix  # noqa: F401
+from .attention import tree_attention, bf16_bits_to_f64  # noqa: F401
+from .sampling import (softmax, philox4x64_10, node_uniforms,  # noqa: F401
+                       verify_walk, WalkResult)
+from .commit import kv_commit  # noqa: F401
+from .step import verify_step_ref  # noqa: F401
