@@ -1,0 +1,226 @@
+/*
+ * tav.h — tree-attention verification on AMD MI355X (gfx950).
+ *
+ * C ABI of the verification step of tree-based speculative decoding:
+ *   tree_mask_build     parent[] -> packed ancestor-or-self bitmasks
+ *   tree_attn_verify    tree attention over a paged KV prefix plus ancestors
+ *   spec_verify_sample  target/draft softmax and the rejection-sampling walk
+ *   kv_commit_path      copy the accepted path's K/V into the paged cache
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers unless stated otherwise. All tensors are
+ *     owned by the caller; the library keeps no pointer after a call returns
+ *     and holds no mutable global state. Buffers must stay alive until the
+ *     work queued on `stream` has finished.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call is asynchronous; the four calls chain on one stream with no
+ *     host synchronisation.
+ *   - The return value reports host-checkable argument errors only; nothing
+ *     is launched when it is not TAV_OK. Faults found in device data (a bad
+ *     tree, a bad block-table entry, non-finite logits) are OR-ed into
+ *     `*dev_flags` (a device uint32 the caller zeroes and reads when it
+ *     chooses; may be NULL to ignore them). Kernels never trap; outputs are
+ *     unspecified for a sequence whose data raised a flag.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Tree nodes are numbered topologically: node 0 is the root
+ *     (parent -1) and 0 <= parent[i] < i for i >= 1. 1 <= N <= 256.
+ *   - Paged KV: 16-token blocks. K cache [num_blocks][Hkv][16][D]
+ *     (token-major), V cache [num_blocks][Hkv][D][16] (feature-major).
+ *     block_table[b][j] is the physical block of logical block j of sequence b
+ *     (token position pos lives in block block_table[b][pos/16], slot pos%16).
+ */
+#ifndef TAV_H
+#define TAV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t tav_status;
+
+#define TAV_OK 0
+#define TAV_ERR_ARG 1          /* null or misaligned pointer, size out of range */
+#define TAV_ERR_UNSUPPORTED 2  /* valid but unsupported shape (D, block size, N, ...) */
+#define TAV_ERR_WORKSPACE 3    /* workspace missing or smaller than required */
+#define TAV_ERR_LAUNCH 4       /* the HIP runtime refused a launch */
+
+/* Bits OR-ed into *dev_flags by the kernels. */
+#define TAV_FLAG_BAD_PARENT 0x1u        /* parent[] is not a rooted topological tree */
+#define TAV_FLAG_BAD_BLOCK 0x2u         /* block-table entry outside [0, num_blocks) */
+#define TAV_FLAG_NONFINITE_LOGITS 0x4u  /* NaN logit, or a row with no finite logit */
+#define TAV_FLAG_CAPACITY 0x8u          /* prefix/commit beyond max_prefix_len or the table */
+#define TAV_FLAG_BAD_TOKEN 0x10u        /* token[b][i] outside [0, V) for i >= 1 */
+#define TAV_FLAG_SYNC_TIMEOUT 0x20u     /* a bounded inter-workgroup wait ran out */
+
+#define TAV_ABI_VERSION 1
+
+/* Version of this ABI (TAV_ABI_VERSION of the library that was built). */
+int32_t tav_abi_version(void);
+
+/* Static text naming a status code. */
+const char *tav_status_string(tav_status status);
+
+/*
+ * tree_mask_build — ancestor-or-self masks of a batch of candidate trees.
+ *
+ * Defined by the jisaku.com glossary ("tree-based speculative decoding",
+ * tree-attention section: M[i][j] = 1 exactly when node j is node i or one of
+ * its ancestors) with the 5-node instance printed in the radar-34b blog §3
+ * (Tree Attention Verification Matrix).
+ *
+ *   parent  int32 [B][N]        parent of each node (-1 for node 0)
+ *   mask    uint64 [B][N][W]    out, W = ceil(N/64); bit j%64 of word j/64 of
+ *                               row i is M[i][j]; unused bits are zero
+ *   depth   int32 [B][N]        out, nullable; number of proper ancestors
+ *   B >= 1, 1 <= N <= 256. mask must be 8-byte aligned.
+ *   Sets TAV_FLAG_BAD_PARENT for a tree that breaks the numbering rule.
+ */
+tav_status tree_mask_build(const int32_t *parent, int32_t B, int32_t N, uint64_t *mask,
+                           int32_t *depth, uint32_t *dev_flags, void *stream);
+
+/*
+ * tree_attn_workspace_bytes — device workspace tree_attn_verify needs for
+ * these sizes on the current device (may be 0). Returns 0 for sizes that
+ * tree_attn_verify would reject.
+ */
+size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                 int32_t max_prefix_len);
+
+/*
+ * tree_attn_verify — one attention layer of the verification forward pass.
+ *
+ * The target scores all candidates in one pass over the prefix with the
+ * candidates appended (LLM Primer ch. 9, §9.1); each candidate attends only
+ * along its root-to-node path (jisaku.com glossary, tree-attention section;
+ * radar-34b blog §3); the prefix is read from a paged cache through a block
+ * table (radar-34b blog §5; jisaku.com glossary, KV-cache section).
+ *
+ * For sequence b, query head h (KV head h / (Hq/Hkv)) and node i:
+ *   keys = prefix positions [0, prefix_len[b]) and tree nodes j with bit j of
+ *          mask[b][i] set;
+ *   out[b][i][h] = softmax(scale * q·k over keys) · v, in fp32.
+ *
+ *   q              bf16 [B][N][Hq][D]
+ *   k_tree,v_tree  bf16 [B][N][Hkv][D]    K/V of the tree nodes themselves
+ *   k_cache        bf16 [num_blocks][Hkv][16][D]
+ *   v_cache        bf16 [num_blocks][Hkv][D][16]
+ *   block_table    int32 [B][max_blocks]
+ *   prefix_len     int32 [B], each in [0, max_prefix_len]
+ *   mask           uint64 [B][N][ceil(N/64)] from tree_mask_build
+ *   out            fp32 [B][N][Hq][D]
+ *   workspace      device buffer of >= tree_attn_workspace_bytes(...) bytes
+ *                  (256-byte aligned; NULL allowed when that is 0)
+ *   Supported: D in {64, 128}, block_size == 16, Hq % Hkv == 0,
+ *   1 <= N <= 256, Hq/Hkv * N <= 4096. bf16 tensors 16-byte aligned.
+ *   Flags: TAV_FLAG_BAD_BLOCK for a needed block outside [0, num_blocks);
+ *   TAV_FLAG_CAPACITY for prefix_len beyond max_prefix_len or the table.
+ */
+tav_status tree_attn_verify(const uint16_t *q, const uint16_t *k_tree, const uint16_t *v_tree,
+                            const uint16_t *k_cache, const uint16_t *v_cache, int32_t num_blocks,
+                            const int32_t *block_table, int32_t max_blocks,
+                            const int32_t *prefix_len, int32_t max_prefix_len,
+                            const uint64_t *mask, int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                            int32_t D, int32_t block_size, float scale, float *out,
+                            void *workspace, size_t ws_bytes, uint32_t *dev_flags, void *stream);
+
+/*
+ * spec_verify_workspace_bytes — device workspace spec_verify_sample needs
+ * for these sizes on the current device. Returns 0 for unsupported sizes.
+ */
+size_t spec_verify_workspace_bytes(int32_t B, int32_t N, int32_t V);
+
+/*
+ * spec_verify_sample — lossless rejection-sampling verification of a batch of
+ * candidate trees, walked from the root down.
+ *
+ * Acceptance with probability min(1, p(x)/q(x)) and redraw from the
+ * normalised positive part of p - q on rejection: radar-34b blog §2
+ * (rejection-sampling acceptance condition). N+1 target distributions per
+ * pass, so a fully accepted path still emits a bonus token: LLM Primer ch. 9,
+ * §9.1. Root-down depth-first decisions: jisaku.com glossary, SpecInfer.
+ *
+ * For each sequence, starting at u = 0 (the root, never tested):
+ *   p_u = softmax(target_logits[b][u] / T), q_u = softmax(draft_logits[b][u] / T);
+ *   the children of u are tried in ascending node index: child c with token x
+ *   is accepted iff r_acc(b,c) * q_u(x) < p_res(x), where p_res starts at p_u
+ *   and, after each rejection, becomes max(0, p_res - q_u) / sum(...)
+ *   (unchanged if that sum is 0); an accepted child becomes u;
+ *   when u has no children, or all were rejected, one token is drawn from
+ *   p_res (p_u at a leaf): the smallest k with C(k) > r_res(b,u) * sum(p_res).
+ * Uniforms: Philox4x64-10 on counter (offset, b, i, 0), key (seed, 0); word 0
+ * gives r_acc(b,i), word 1 gives r_res(b,i), as (w >> 40) * 2^-24.
+ * All softmax, residual and CDF arithmetic is float64.
+ *
+ *   target_logits, draft_logits  fp32 [B][N][V]; draft row u is the
+ *                                distribution u's children were drawn from
+ *   parent, token                int32 [B][N]; token[b][0] is ignored
+ *   temperature                  > 0
+ *   path        int32 [B][N] out: accepted nodes from the root (path[b][0] = 0), -1 padded
+ *   n_accepted  int32 [B] out: accepted children (path length - 1)
+ *   out_tokens  int32 [B][N] out: emitted tokens, n_accepted[b] + 1 of them, -1 padded
+ *   workspace   device buffer of >= spec_verify_workspace_bytes(B, N, V) bytes,
+ *               256-byte aligned; its contents need no initialisation
+ *   Supported: 1 <= N <= 256, 1 <= V <= 2^24, fp32 logits 16-byte aligned.
+ *   Flags: TAV_FLAG_BAD_PARENT, TAV_FLAG_BAD_TOKEN, TAV_FLAG_NONFINITE_LOGITS,
+ *   TAV_FLAG_SYNC_TIMEOUT.
+ */
+tav_status spec_verify_sample(const float *target_logits, const float *draft_logits,
+                              const int32_t *parent, const int32_t *token, int32_t B, int32_t N,
+                              int32_t V, float temperature, uint64_t seed, uint64_t offset,
+                              int32_t *path, int32_t *n_accepted, int32_t *out_tokens,
+                              void *workspace, size_t ws_bytes, uint32_t *dev_flags,
+                              void *stream);
+
+/*
+ * kv_commit_path — keep the accepted path's K/V, discarding the rest.
+ *
+ * Only the accepted path survives verification; rejected branches are pruned
+ * and the cache rolls back to the accepted length, which paged blocks make
+ * cheap: radar-34b blog §5 (KV-cache management); jisaku.com glossary,
+ * KV-cache section.
+ *
+ * For t = 0..n_accepted[b], node path[b][t] is written at position
+ * prefix_len[b] + t of sequence b (block block_table[b][pos/16], slot pos%16);
+ * commit_slots[b][t] = block * 16 + pos % 16 (-1 beyond the path);
+ * new_prefix_len[b] = prefix_len[b] + n_accepted[b] + 1. Nothing else in the
+ * caches is written.
+ *
+ *   k_tree, v_tree   bf16 [B][N][Hkv][D]
+ *   path, n_accepted as written by spec_verify_sample (read on the device)
+ *   k_cache, v_cache the paged caches, updated in place
+ *   commit_slots     int32 [B][N] out;  new_prefix_len int32 [B] out
+ *   Supported: D in {64, 128}, block_size == 16, 1 <= N <= 256.
+ *   Flags: TAV_FLAG_BAD_BLOCK, TAV_FLAG_CAPACITY (table too short),
+ *   TAV_FLAG_BAD_PARENT (path entry outside [0, N) or n_accepted outside [0, N)).
+ */
+tav_status kv_commit_path(const uint16_t *k_tree, const uint16_t *v_tree, const int32_t *path,
+                          const int32_t *n_accepted, int32_t num_blocks,
+                          const int32_t *block_table, int32_t max_blocks,
+                          const int32_t *prefix_len, uint16_t *k_cache, uint16_t *v_cache,
+                          int32_t B, int32_t N, int32_t Hkv, int32_t D, int32_t block_size,
+                          int32_t *commit_slots, int32_t *new_prefix_len, uint32_t *dev_flags,
+                          void *stream);
+
+/*
+ * tav_philox_uniforms — the uniforms spec_verify_sample draws, for checking:
+ * u[b][i][0] = r_acc(b, i), u[b][i][1] = r_res(b, i) (fp32, exact).
+ */
+tav_status tav_philox_uniforms(uint64_t seed, uint64_t offset, int32_t B, int32_t N, float *u,
+                               void *stream);
+
+/*
+ * tav_target_probs — p = softmax(logits / T) per row in float64, with the
+ * device softmax spec_verify_sample uses (radar-34b blog §2 names p and q).
+ *   logits fp32 [rows][V] (16-byte aligned), p fp64 [rows][V].
+ */
+tav_status tav_target_probs(const float *logits, int64_t rows, int32_t V, float temperature,
+                            double *p, uint32_t *dev_flags, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TAV_H */

@@ -1,0 +1,107 @@
+"""The C-ABI library loads and exports every declared entry point, and its
+host-side argument checks reject bad calls before touching the GPU (CPU only).
+"""
+
+import ctypes
+
+import pytest
+
+import tree_attention_verification_ancestor_amd as tav
+
+
+def test_library_exports_every_declared_function():
+    names = tav.header_functions()
+    assert set(names) >= {"tree_mask_build", "tree_attn_verify", "spec_verify_sample",
+                          "kv_commit_path", "tree_attn_workspace_bytes",
+                          "spec_verify_workspace_bytes", "tav_philox_uniforms",
+                          "tav_target_probs", "tav_status_string", "tav_abi_version"}
+    lib = tav.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(tav._SIGNATURES)
+
+
+def test_abi_version_and_status_strings():
+    assert tav.abi_version() == 1
+    for code in range(5):
+        assert tav.status_string(code)
+    assert "unknown" in tav.status_string(99)
+
+
+P = ctypes.c_void_p
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every case fails its checks first
+
+
+def test_mask_build_rejects_bad_arguments():
+    lib = tav.lib()
+    assert lib.tree_mask_build(None, 1, 5, FAKE, None, None, None) == tav.ERR_ARG
+    assert lib.tree_mask_build(FAKE, 0, 5, FAKE, None, None, None) == tav.ERR_ARG
+    assert lib.tree_mask_build(FAKE, 1, 0, FAKE, None, None, None) == tav.ERR_ARG
+    assert lib.tree_mask_build(FAKE, 1, 257, FAKE, None, None, None) == tav.ERR_UNSUPPORTED
+    assert lib.tree_mask_build(FAKE, 1, 5, ctypes.c_void_p(0x10004), None, None, None) == tav.ERR_ARG
+
+
+def _attn(**kw):
+    args = dict(q=FAKE, k_tree=FAKE, v_tree=FAKE, k_cache=FAKE, v_cache=FAKE, num_blocks=10,
+                block_table=FAKE, max_blocks=4, prefix_len=FAKE, max_prefix_len=64, mask=FAKE,
+                B=1, N=5, Hq=8, Hkv=2, D=128, block_size=16, scale=0.088, out=FAKE,
+                workspace=None, ws_bytes=0, dev_flags=None, stream=None)
+    args.update(kw)
+    return tav.lib().tree_attn_verify(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), tav.ERR_ARG), (dict(out=None), tav.ERR_ARG), (dict(B=0), tav.ERR_ARG),
+    (dict(N=0), tav.ERR_ARG), (dict(scale=0.0), tav.ERR_ARG), (dict(scale=float("nan")), tav.ERR_ARG),
+    (dict(max_prefix_len=-1), tav.ERR_ARG), (dict(num_blocks=0), tav.ERR_ARG),
+    (dict(D=96), tav.ERR_UNSUPPORTED), (dict(Hq=7), tav.ERR_UNSUPPORTED),
+    (dict(block_size=32), tav.ERR_UNSUPPORTED), (dict(N=300), tav.ERR_UNSUPPORTED),
+    (dict(N=256, Hq=64, Hkv=2), tav.ERR_UNSUPPORTED),
+    (dict(q=ctypes.c_void_p(0x10008)), tav.ERR_ARG),
+])
+def test_attention_rejects_bad_arguments(kw, code):
+    assert _attn(**kw) == code
+
+
+def _sample(**kw):
+    args = dict(tl=FAKE, dl=FAKE, parent=FAKE, token=FAKE, B=2, N=5, V=1000, T=1.0, seed=0,
+                offset=0, path=FAKE, n_acc=FAKE, out_tok=FAKE, ws=FAKE, ws_bytes=1 << 20,
+                flags=None, stream=None)
+    args.update(kw)
+    return tav.lib().spec_verify_sample(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tl=None), tav.ERR_ARG), (dict(path=None), tav.ERR_ARG), (dict(B=0), tav.ERR_ARG),
+    (dict(V=0), tav.ERR_ARG), (dict(T=0.0), tav.ERR_ARG), (dict(T=-1.0), tav.ERR_ARG),
+    (dict(T=float("inf")), tav.ERR_ARG), (dict(N=257), tav.ERR_UNSUPPORTED),
+    (dict(V=(1 << 24) + 1), tav.ERR_UNSUPPORTED),
+])
+def test_sampler_rejects_bad_arguments(kw, code):
+    assert _sample(**kw) == code
+
+
+def _commit(**kw):
+    args = dict(k_tree=FAKE, v_tree=FAKE, path=FAKE, n_acc=FAKE, num_blocks=10,
+                block_table=FAKE, max_blocks=4, prefix_len=FAKE, k_cache=FAKE, v_cache=FAKE,
+                B=1, N=5, Hkv=2, D=128, block_size=16, slots=FAKE, new_len=FAKE, flags=None,
+                stream=None)
+    args.update(kw)
+    return tav.lib().kv_commit_path(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(path=None), tav.ERR_ARG), (dict(k_cache=None), tav.ERR_ARG), (dict(B=0), tav.ERR_ARG),
+    (dict(num_blocks=0), tav.ERR_ARG), (dict(D=80), tav.ERR_UNSUPPORTED),
+    (dict(block_size=8), tav.ERR_UNSUPPORTED), (dict(N=1000), tav.ERR_UNSUPPORTED),
+])
+def test_commit_rejects_bad_arguments(kw, code):
+    assert _commit(**kw) == code
+
+
+def test_helpers_reject_bad_arguments():
+    lib = tav.lib()
+    assert lib.tav_philox_uniforms(0, 0, 1, 1, None, None) == tav.ERR_ARG
+    assert lib.tav_philox_uniforms(0, 0, 0, 1, FAKE, None) == tav.ERR_ARG
+    assert lib.tav_target_probs(None, 1, 10, 1.0, FAKE, None, None) == tav.ERR_ARG
+    assert lib.tav_target_probs(FAKE, 1, 10, 0.0, FAKE, None, None) == tav.ERR_ARG

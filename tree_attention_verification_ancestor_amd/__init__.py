@@ -1,0 +1,294 @@
+"""Python binding of the tav C ABI (``include/tav.h``): tree-attention
+verification on AMD MI355X.
+
+Argument marshalling only: every function checks tensor placement, dtype and
+layout, allocates outputs and workspaces with torch when the caller passes
+none, and calls the C entry point of the same name on the current HIP stream.
+All arithmetic runs in the library's HIP kernels. If ``libtav.so`` has not
+been built, every call raises; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtav.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tav.h")
+
+OK = 0
+ERR_ARG = 1
+ERR_UNSUPPORTED = 2
+ERR_WORKSPACE = 3
+ERR_LAUNCH = 4
+
+FLAG_BAD_PARENT = 0x1
+FLAG_BAD_BLOCK = 0x2
+FLAG_NONFINITE_LOGITS = 0x4
+FLAG_CAPACITY = 0x8
+FLAG_BAD_TOKEN = 0x10
+FLAG_SYNC_TIMEOUT = 0x20
+
+BLOCK = 16
+
+
+class TavError(RuntimeError):
+    """A tav entry point returned a non-OK status."""
+
+    def __init__(self, name: str, status: int):
+        super().__init__(f"{name}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_U64 = ctypes.c_uint64
+_F32 = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "tav_abi_version": (_I32, []),
+    "tav_status_string": (ctypes.c_char_p, [_I32]),
+    "tree_mask_build": (_I32, [_P, _I32, _I32, _P, _P, _P, _P]),
+    "tree_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "tree_attn_verify": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _P, _I32, _I32,
+                                _I32, _I32, _I32, _I32, _F32, _P, _P, _SZ, _P, _P]),
+    "spec_verify_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "spec_verify_sample": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _F32, _U64, _U64, _P, _P,
+                                  _P, _P, _SZ, _P, _P]),
+    "kv_commit_path": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _P, _I32, _I32, _I32,
+                              _I32, _I32, _P, _P, _P, _P]),
+    "tav_philox_uniforms": (_I32, [_U64, _U64, _I32, _I32, _P, _P]),
+    "tav_target_probs": (_I32, [_P, _I64, _I32, _F32, _P, _P, _P]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ``libtav.so``; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def header_functions(path: str = HEADER_PATH):
+    """Names of the functions ``include/tav.h`` declares."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def abi_version() -> int:
+    return int(lib().tav_abi_version())
+
+
+def status_string(status: int) -> str:
+    return lib().tav_status_string(int(status)).decode()
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(name: str, status: int):
+    if status != OK:
+        raise TavError(name, status)
+
+
+def _need(t: torch.Tensor, name: str, dtypes, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_I32T = (torch.int32,)
+_U32T = (torch.int32, torch.uint32)
+_MASKT = (torch.int64, torch.uint64)
+
+
+def new_flags(device=None) -> torch.Tensor:
+    """A zeroed device word for ``dev_flags``."""
+    return torch.zeros(1, dtype=torch.int32, device=device or "cuda")
+
+
+# ---------------------------------------------------------------------------
+# entry points
+
+def tree_mask_build(parent: torch.Tensor, mask: Optional[torch.Tensor] = None,
+                    depth: Optional[torch.Tensor] = None, dev_flags: Optional[torch.Tensor] = None,
+                    stream=None, want_depth: bool = True):
+    """parent int32 [B, N] -> (mask int64 [B, N, ceil(N/64)], depth int32 [B, N] or None)."""
+    _need(parent, "parent", _I32T)
+    B, N = parent.shape
+    W = (N + 63) // 64
+    dev = parent.device
+    if mask is None:
+        mask = torch.empty((B, N, W), dtype=torch.int64, device=dev)
+    _need(mask, "mask", _MASKT, (B, N, W), dev)
+    if depth is None and want_depth:
+        depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if depth is not None:
+        _need(depth, "depth", _I32T, (B, N), dev)
+    _check("tree_mask_build", lib().tree_mask_build(_ptr(parent), B, N, _ptr(mask), _ptr(depth),
+                                                    _ptr(dev_flags), _stream(stream)))
+    return mask, depth
+
+
+def tree_attn_workspace_bytes(B, N, Hq, Hkv, D, max_prefix_len) -> int:
+    return int(lib().tree_attn_workspace_bytes(B, N, Hq, Hkv, D, max_prefix_len))
+
+
+def tree_attn_verify(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len,
+                     max_prefix_len: int, mask, scale: Optional[float] = None,
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     dev_flags: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Tree attention of one layer; returns out fp32 [B, N, Hq, D]."""
+    _need(q, "q", _BF16)
+    B, N, Hq, D = q.shape
+    dev = q.device
+    Hkv = k_tree.shape[2]
+    _need(k_tree, "k_tree", _BF16, (B, N, Hkv, D), dev)
+    _need(v_tree, "v_tree", _BF16, (B, N, Hkv, D), dev)
+    nblk = k_cache.shape[0]
+    _need(k_cache, "k_cache", _BF16, (nblk, Hkv, BLOCK, D), dev)
+    _need(v_cache, "v_cache", _BF16, (nblk, Hkv, D, BLOCK), dev)
+    _need(block_table, "block_table", _I32T, None, dev)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    _need(prefix_len, "prefix_len", _I32T, (B,), dev)
+    _need(mask, "mask", _MASKT, (B, N, (N + 63) // 64), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, N, Hq, D), dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,), (B, N, Hq, D), dev)
+    need = tree_attn_workspace_bytes(B, N, Hq, Hkv, D, max_prefix_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("tree_attn_verify", lib().tree_attn_verify(
+        _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), nblk,
+        _ptr(block_table), block_table.shape[1], _ptr(prefix_len), int(max_prefix_len),
+        _ptr(mask), B, N, Hq, Hkv, D, BLOCK, float(scale), _ptr(out), _ptr(workspace), ws_bytes,
+        _ptr(dev_flags), _stream(stream)))
+    return out
+
+
+def spec_verify_workspace_bytes(B, N, V) -> int:
+    return int(lib().spec_verify_workspace_bytes(B, N, V))
+
+
+def spec_verify_sample(target_logits, draft_logits, parent, token, temperature: float = 1.0,
+                       seed: int = 0, offset: int = 0, path=None, n_accepted=None,
+                       out_tokens=None, workspace=None, dev_flags=None, stream=None):
+    """Rejection-sampling walk; returns (path [B,N], n_accepted [B], out_tokens [B,N])."""
+    _need(target_logits, "target_logits", (torch.float32,))
+    B, N, V = target_logits.shape
+    dev = target_logits.device
+    _need(draft_logits, "draft_logits", (torch.float32,), (B, N, V), dev)
+    _need(parent, "parent", _I32T, (B, N), dev)
+    _need(token, "token", _I32T, (B, N), dev)
+    if path is None:
+        path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if n_accepted is None:
+        n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    _need(path, "path", _I32T, (B, N), dev)
+    _need(n_accepted, "n_accepted", _I32T, (B,), dev)
+    _need(out_tokens, "out_tokens", _I32T, (B, N), dev)
+    if workspace is None:
+        workspace = torch.empty(max(1, spec_verify_workspace_bytes(B, N, V)), dtype=torch.uint8,
+                                device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("spec_verify_sample", lib().spec_verify_sample(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(parent), _ptr(token), B, N, V,
+        float(temperature), int(seed), int(offset), _ptr(path), _ptr(n_accepted),
+        _ptr(out_tokens), _ptr(workspace), ws_bytes, _ptr(dev_flags), _stream(stream)))
+    return path, n_accepted, out_tokens
+
+
+def kv_commit_path(k_tree, v_tree, path, n_accepted, block_table, prefix_len, k_cache, v_cache,
+                   commit_slots=None, new_prefix_len=None, dev_flags=None, stream=None):
+    """Commit the accepted path in place; returns (commit_slots [B,N], new_prefix_len [B])."""
+    _need(k_tree, "k_tree", _BF16)
+    B, N, Hkv, D = k_tree.shape
+    dev = k_tree.device
+    _need(v_tree, "v_tree", _BF16, (B, N, Hkv, D), dev)
+    _need(path, "path", _I32T, (B, N), dev)
+    _need(n_accepted, "n_accepted", _I32T, (B,), dev)
+    _need(block_table, "block_table", _I32T, None, dev)
+    _need(prefix_len, "prefix_len", _I32T, (B,), dev)
+    nblk = k_cache.shape[0]
+    _need(k_cache, "k_cache", _BF16, (nblk, Hkv, BLOCK, D), dev)
+    _need(v_cache, "v_cache", _BF16, (nblk, Hkv, D, BLOCK), dev)
+    if commit_slots is None:
+        commit_slots = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if new_prefix_len is None:
+        new_prefix_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check("kv_commit_path", lib().kv_commit_path(
+        _ptr(k_tree), _ptr(v_tree), _ptr(path), _ptr(n_accepted), nblk, _ptr(block_table),
+        block_table.shape[1], _ptr(prefix_len), _ptr(k_cache), _ptr(v_cache), B, N, Hkv, D,
+        BLOCK, _ptr(commit_slots), _ptr(new_prefix_len), _ptr(dev_flags), _stream(stream)))
+    return commit_slots, new_prefix_len
+
+
+def philox_uniforms(seed: int, offset: int, B: int, N: int, out=None, device=None, stream=None):
+    """fp32 [B, N, 2]: (acceptance, resampling) uniform of every node."""
+    if out is None:
+        out = torch.empty((B, N, 2), dtype=torch.float32, device=device or "cuda")
+    _need(out, "out", (torch.float32,), (B, N, 2))
+    _check("tav_philox_uniforms", lib().tav_philox_uniforms(int(seed), int(offset), B, N,
+                                                            _ptr(out), _stream(stream)))
+    return out
+
+
+def target_probs(logits: torch.Tensor, temperature: float = 1.0, out=None, dev_flags=None,
+                 stream=None) -> torch.Tensor:
+    """fp64 softmax(logits / T) over the last axis, with the sampler's device softmax."""
+    _need(logits, "logits", (torch.float32,))
+    V = logits.shape[-1]
+    rows = logits.numel() // V
+    if out is None:
+        out = torch.empty(logits.shape, dtype=torch.float64, device=logits.device)
+    _need(out, "out", (torch.float64,), tuple(logits.shape), logits.device)
+    _check("tav_target_probs", lib().tav_target_probs(_ptr(logits), rows, V, float(temperature),
+                                                      _ptr(out), _ptr(dev_flags),
+                                                      _stream(stream)))
+    return out

@@ -1,0 +1,37 @@
+// Shared helpers of the tav HIP library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tav.h"
+
+namespace tav {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+constexpr int kBlock = 16;     // tokens per paged KV block
+constexpr int kMaxNodes = 256; // largest supported tree
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+__device__ inline void raise_flag(uint32_t *flags, uint32_t bit)
+{
+    if (flags)
+        atomicOr(flags, bit);
+}
+
+inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Compute units of the current device (0 if there is no usable device).
+int device_cu_count();
+
+} // namespace tav
