@@ -1,0 +1,256 @@
+"""Benchmark of the tree-verification step on one MI355X.
+
+A step is one pass of the whole path over one batch: tree_mask_build,
+tree_attn_verify (one attention layer), spec_verify_sample and kv_commit_path,
+chained on one stream with no host synchronisation. The workload is the
+Llama-3-70B-shaped layer: batch 8, 64-node trees (depth 6, width 4), 64 query
+/ 8 KV heads, head_dim 128, paged prefixes of 6144..8192 tokens, a 128256-entry
+vocabulary. Inputs are seeded synthetic data already resident in HBM; three
+copies of the paged caches rotate across steps so the 256 MB last-level cache
+cannot hold the step's KV working set.
+
+Prints one JSON line: verified tree nodes/s (B*N per step time), with the
+attention kernel's roofline and the CPU oracle's rate on this host.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config llama70b] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
+
+
+def workload_desc(w) -> str:
+    return (f"{w.name}: B={w.B}, N={w.N}-node trees, {w.Hq}/{w.Hkv} heads, D={w.D}, "
+            f"paged prefix {int(w.prefix_len.min())}..{int(w.prefix_len.max())} "
+            f"(block {w.block}), vocab {w.V}, T={w.temperature}")
+
+
+def attention_work(w, depth):
+    """Algorithmic bytes and FLOPs of one tree_attn_verify launch."""
+    L = int(w.prefix_len.sum())
+    kv = L * w.Hkv * w.D * 2 * 2                       # prefix K and V, bf16, read once
+    q = w.B * w.N * w.Hq * w.D * 2
+    tree = w.B * w.N * w.Hkv * w.D * 2 * 2
+    out = w.B * w.N * w.Hq * w.D * 4
+    small = w.B * w.N * ((w.N + 63) // 64) * 8 + w.block_table.size * 4
+    anc = int((depth + 1).sum())                        # sum over nodes of |ancestors or self|
+    flops = 4 * w.Hq * w.D * (w.N * L + anc)
+    return kv + q + tree + out + small, flops
+
+
+def sampler_bytes(w, path, n_acc):
+    """Target row of every visited node, plus the draft row of every visited
+    node that has children (the rows the walk must read at least once)."""
+    rows = 0
+    for b in range(w.B):
+        kids = set(int(x) for x in w.parent[b, 1:])
+        for t in range(int(n_acc[b]) + 1):
+            u = int(path[b, t])
+            rows += 1 + (1 if u in kids else 0)
+    return rows * w.V * 4 + w.B * w.N * 4 * 4
+
+
+def commit_bytes(w, n_acc):
+    return int((n_acc + 1).sum()) * w.Hkv * w.D * 2 * 2 * 2
+
+
+def run_gpu(args, w):
+    import torch
+
+    import tree_attention_verification_ancestor_amd as tav
+    from synth.device import to_numpy, upload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = upload(w, dev)
+    copies = [(d["k_cache"], d["v_cache"])]
+    for _ in range(args.cache_copies - 1):
+        copies.append((d["k_cache"].clone(), d["v_cache"].clone()))
+    B, N, V = w.B, w.N, w.V
+    flags = tav.new_flags(dev)
+    mask = torch.empty((B, N, (N + 63) // 64), dtype=torch.int64, device=dev)
+    depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+    out = torch.empty((B, N, w.Hq, w.D), dtype=torch.float32, device=dev)
+    ws_a = torch.empty(max(1, tav.tree_attn_workspace_bytes(B, N, w.Hq, w.Hkv, w.D,
+                                                            w.max_prefix_len)),
+                       dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(max(1, tav.spec_verify_workspace_bytes(B, N, V)), dtype=torch.uint8,
+                       device=dev)
+    path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    n_acc = torch.empty((B,), dtype=torch.int32, device=dev)
+    toks = torch.empty((B, N), dtype=torch.int32, device=dev)
+    slots = torch.empty((B, N), dtype=torch.int32, device=dev)
+    new_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    nblk, maxb = int(w.k_cache.shape[0]), int(w.block_table.shape[1])
+    ws_a_n = ws_a.numel()
+    ws_s_n = ws_s.numel()
+
+    # one checked call of each entry point, then pre-marshalled calls for the loop
+    tav.tree_mask_build(d["parent"], mask, depth, flags, stream)
+    tav.tree_attn_verify(d["q"], d["k_tree"], d["v_tree"], copies[0][0], copies[0][1],
+                         d["block_table"], d["prefix_len"], w.max_prefix_len, mask, w.scale, out,
+                         ws_a, flags, stream)
+    tav.spec_verify_sample(d["target_logits"], d["draft_logits"], d["parent"], d["token"],
+                           w.temperature, w.philox_seed, w.philox_offset, path, n_acc, toks, ws_s,
+                           flags, stream)
+    tav.kv_commit_path(d["k_tree"], d["v_tree"], path, n_acc, d["block_table"], d["prefix_len"],
+                       copies[0][0], copies[0][1], slots, new_len, flags, stream)
+    torch.cuda.synchronize()
+    calls = []
+    for kc, vc in copies:
+        calls.append((
+            tav.prepare("tree_mask_build", d["parent"], B, N, mask, depth, flags, stream),
+            tav.prepare("tree_attn_verify", d["q"], d["k_tree"], d["v_tree"], kc, vc, nblk,
+                        d["block_table"], maxb, d["prefix_len"], w.max_prefix_len, mask, B, N,
+                        w.Hq, w.Hkv, w.D, w.block, w.scale, out, ws_a, ws_a_n, flags, stream),
+            tav.prepare("spec_verify_sample", d["target_logits"], d["draft_logits"], d["parent"],
+                        d["token"], B, N, V, w.temperature, w.philox_seed, w.philox_offset, path,
+                        n_acc, toks, ws_s, ws_s_n, flags, stream),
+            tav.prepare("kv_commit_path", d["k_tree"], d["v_tree"], path, n_acc, nblk,
+                        d["block_table"], maxb, d["prefix_len"], kc, vc, B, N, w.Hkv, w.D,
+                        w.block, slots, new_len, flags, stream),
+        ))
+
+    def step(i, ev=None):
+        c = calls[i % len(calls)]
+        if ev:
+            ev[0].record(stream)
+        for k in range(4):
+            c[k]()
+            if ev:
+                ev[k + 1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # the timed region: exactly `steps` steps between two synchronised events
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+
+    # per-stage times with events on the launch stream (a second pass)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i, evs[i])
+    torch.cuda.synchronize()
+    stage = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in evs])
+    stage_ms = stage.mean(axis=0)
+    assert int(flags.item()) == 0, f"device flags {int(flags.item()):#x}"
+    return dict(ms_step=ms_step, stage_ms=stage_ms, depth=to_numpy(depth), path=to_numpy(path),
+                n_acc=to_numpy(n_acc))
+
+
+def cpu_baseline(w, min_seconds=10.0):
+    import threadpoolctl
+
+    import oracle
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.verify_step_ref(w)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    per_step = el / reps
+    info = threadpoolctl.threadpool_info()
+    blas = max([i.get("num_threads", 1) for i in info] or [1])
+    return {"value": w.B * w.N / per_step, "unit": "nodes/s", "cores": int(blas),
+            "kind": "oracle",
+            "sample": (f"the whole step ({w.B} sequences x {w.N} nodes) repeated {reps} times in "
+                       f"{el:.1f} s; fp64 numpy attention on {blas} BLAS threads, "
+                       f"single-threaded C walk; {len(os.sched_getaffinity(0))} cores visible")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama70b")
+    ap.add_argument("--cache-copies", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path is single-GPU; see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    from synth import make_workload
+    w = make_workload(args.config)
+    g = run_gpu(args, w)
+
+    attn_bytes, attn_flops = attention_work(w, g["depth"])
+    t_attn = g["stage_ms"][1] * 1e-3
+    tflops = attn_flops / t_attn / 1e12
+    gbs = attn_bytes / t_attn / 1e9
+    t_hbm = attn_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = attn_flops / (MFMA_PEAK_TFLOPS * 1e12)
+    bound = "mfma" if t_mfma >= t_hbm else "hbm"
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+
+    step_bytes = attn_bytes + sampler_bytes(w, g["path"], g["n_acc"]) + commit_bytes(w, g["n_acc"])
+    t_floor = max(step_bytes / (HBM_PEAK_GBS * 1e9), attn_flops / (MFMA_PEAK_TFLOPS * 1e12))
+    ms = g["ms_step"]
+    rec = {
+        "metric": "verified tree nodes/s",
+        "value": round(w.B * w.N / (ms * 1e-3), 1),
+        "unit": "nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload_desc(w), "global_batch": w.B, "tree_nodes": w.N,
+                   "prefix_tokens": int(w.prefix_len.sum()), "vocab": w.V,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "verify_step_us": round(ms * 1e3, 2),
+        "stages_us": {k: round(v * 1e3, 2) for k, v in
+                      zip(["tree_mask_build", "tree_attn_verify", "spec_verify_sample",
+                           "kv_commit_path"], g["stage_ms"])},
+        "tree_attn": {"hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                      "tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+                      "algorithmic_bytes": attn_bytes, "algorithmic_flops": attn_flops,
+                      "roofline_frac": round(max(t_hbm, t_mfma) / t_attn, 4)},
+        "step_roofline": {"algorithmic_bytes": step_bytes, "floor_us": round(t_floor * 1e6, 2),
+                          "frac": round(t_floor / (ms * 1e-3), 4)},
+        "accepted": g["n_acc"].tolist(),
+    }
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -54,6 +54,8 @@ typedef int32_t tav_status;
 #define TAV_FLAG_CAPACITY 0x8u          /* prefix/commit beyond max_prefix_len or the table */
 #define TAV_FLAG_BAD_TOKEN 0x10u        /* token[b][i] outside [0, V) for i >= 1 */
 #define TAV_FLAG_SYNC_TIMEOUT 0x20u     /* a bounded inter-workgroup wait ran out */
+#define TAV_FLAG_ATTN_RANGE 0x40u       /* an attention output is not finite (a V entry of
+                                           magnitude >= 65520, or a non-finite input) */
 
 #define TAV_ABI_VERSION 1
 
@@ -115,8 +117,12 @@ size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, 
  *                  (256-byte aligned; NULL allowed when that is 0)
  *   Supported: D in {64, 128}, block_size == 16, Hq % Hkv == 0,
  *   1 <= N <= 256, Hq/Hkv * N <= 4096. bf16 tensors 16-byte aligned.
+ *   Precision: Q·K runs as a bf16 MFMA with fp32 accumulation; the weights
+ *   and V enter the P·V MFMA as fp16 (V converts from bf16 exactly while
+ *   |v| < 65520), accumulating in fp32.
  *   Flags: TAV_FLAG_BAD_BLOCK for a needed block outside [0, num_blocks);
- *   TAV_FLAG_CAPACITY for prefix_len beyond max_prefix_len or the table.
+ *   TAV_FLAG_CAPACITY for prefix_len beyond max_prefix_len or the table;
+ *   TAV_FLAG_ATTN_RANGE for a non-finite output.
  */
 tav_status tree_attn_verify(const uint16_t *q, const uint16_t *k_tree, const uint16_t *v_tree,
                             const uint16_t *k_cache, const uint16_t *v_cache, int32_t num_blocks,
@@ -157,19 +163,19 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t N, int32_t V);
  *   target_logits, draft_logits  fp32 [B][N][V]; draft row u is the
  *                                distribution u's children were drawn from
  *   parent, token                int32 [B][N]; token[b][0] is ignored
- *   temperature                  > 0
+ *   temperature                  > 0 and finite (float64, used as given)
  *   path        int32 [B][N] out: accepted nodes from the root (path[b][0] = 0), -1 padded
  *   n_accepted  int32 [B] out: accepted children (path length - 1)
  *   out_tokens  int32 [B][N] out: emitted tokens, n_accepted[b] + 1 of them, -1 padded
  *   workspace   device buffer of >= spec_verify_workspace_bytes(B, N, V) bytes,
  *               256-byte aligned; its contents need no initialisation
- *   Supported: 1 <= N <= 256, 1 <= V <= 2^24, fp32 logits 16-byte aligned.
+ *   Supported: 1 <= N <= 256, 1 <= V <= 2^24, fp32 logits 4-byte aligned.
  *   Flags: TAV_FLAG_BAD_PARENT, TAV_FLAG_BAD_TOKEN, TAV_FLAG_NONFINITE_LOGITS,
  *   TAV_FLAG_SYNC_TIMEOUT.
  */
 tav_status spec_verify_sample(const float *target_logits, const float *draft_logits,
                               const int32_t *parent, const int32_t *token, int32_t B, int32_t N,
-                              int32_t V, float temperature, uint64_t seed, uint64_t offset,
+                              int32_t V, double temperature, uint64_t seed, uint64_t offset,
                               int32_t *path, int32_t *n_accepted, int32_t *out_tokens,
                               void *workspace, size_t ws_bytes, uint32_t *dev_flags,
                               void *stream);
@@ -216,7 +222,7 @@ tav_status tav_philox_uniforms(uint64_t seed, uint64_t offset, int32_t B, int32_
  * device softmax spec_verify_sample uses (radar-34b blog §2 names p and q).
  *   logits fp32 [rows][V] (16-byte aligned), p fp64 [rows][V].
  */
-tav_status tav_target_probs(const float *logits, int64_t rows, int32_t V, float temperature,
+tav_status tav_target_probs(const float *logits, int64_t rows, int32_t V, double temperature,
                             double *p, uint32_t *dev_flags, void *stream);
 
 #ifdef __cplusplus

@@ -34,6 +34,7 @@ FLAG_NONFINITE_LOGITS = 0x4
 FLAG_CAPACITY = 0x8
 FLAG_BAD_TOKEN = 0x10
 FLAG_SYNC_TIMEOUT = 0x20
+FLAG_ATTN_RANGE = 0x40
 
 BLOCK = 16
 
@@ -52,6 +53,7 @@ _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 _U64 = ctypes.c_uint64
 _F32 = ctypes.c_float
+_F64 = ctypes.c_double
 _SZ = ctypes.c_size_t
 
 _SIGNATURES = {
@@ -62,12 +64,12 @@ _SIGNATURES = {
     "tree_attn_verify": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _P, _I32, _I32,
                                 _I32, _I32, _I32, _I32, _F32, _P, _P, _SZ, _P, _P]),
     "spec_verify_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
-    "spec_verify_sample": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _F32, _U64, _U64, _P, _P,
+    "spec_verify_sample": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _F64, _U64, _U64, _P, _P,
                                   _P, _P, _SZ, _P, _P]),
     "kv_commit_path": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _P, _I32, _I32, _I32,
                               _I32, _I32, _P, _P, _P, _P]),
     "tav_philox_uniforms": (_I32, [_U64, _U64, _I32, _I32, _P, _P]),
-    "tav_target_probs": (_I32, [_P, _I64, _I32, _F32, _P, _P, _P]),
+    "tav_target_probs": (_I32, [_P, _I64, _I32, _F64, _P, _P, _P]),
 }
 
 
@@ -140,6 +142,27 @@ _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
 _I32T = (torch.int32,)
 _U32T = (torch.int32, torch.uint32)
 _MASKT = (torch.int64, torch.uint64)
+
+
+def prepare(name: str, *args):
+    """A zero-argument callable that calls C entry point ``name`` with
+    ``args`` converted once (tensors become their device pointers, streams
+    their handles). For tight loops over the same buffers; the caller keeps
+    the tensors alive and has checked them with the functions below."""
+    fn = getattr(lib(), name)
+    conv = []
+    for a in args:
+        if isinstance(a, torch.Tensor):
+            conv.append(ctypes.c_void_p(a.data_ptr()))
+        elif isinstance(a, torch.cuda.Stream):
+            conv.append(ctypes.c_void_p(a.cuda_stream))
+        else:
+            conv.append(a)
+    conv = tuple(conv)
+
+    def call():
+        _check(name, fn(*conv))
+    return call
 
 
 def new_flags(device=None) -> torch.Tensor:

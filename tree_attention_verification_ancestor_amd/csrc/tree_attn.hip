@@ -19,12 +19,18 @@
 //   softmax       online, per lane; the running max is only moved when a tile
 //                 exceeds it by more than 2^8 in probability, so the O rescale
 //                 is rare; exp2 with the scale folded into one FMA.
-//   O^T += V^T P^T  P^T is the S^T accumulator itself, rounded to bf16: the
-//                 key order inside each 32-key tile is permuted (rows 4..7 and
-//                 8..11 of the tile swapped, and so on) so that each lane's 16
-//                 accumulator values are exactly the 8+8 consecutive keys the
-//                 PV B operand needs. V^T comes from feature-major V blocks, so
-//                 its A operand is one 16-byte LDS read.
+//   O^T += V^T P^T  v_mfma_f32_32x32x16_f16. P^T is the S^T accumulator
+//                 itself: the key order inside each 32-key tile is permuted
+//                 (rows 4..7 and 8..11 of the tile swapped, and so on) so that
+//                 each lane's 16 accumulator values are exactly the 8+8
+//                 consecutive keys the PV B operand needs. V^T comes from
+//                 feature-major V blocks, so its A operand is one 16-byte LDS
+//                 read. This contraction runs in fp16, not bf16: bf16 V
+//                 converts to fp16 exactly (within fp16's range) while staging,
+//                 and fp16 keeps 11 significant bits of each weight where bf16
+//                 keeps 8, which the output tolerance needs when attention
+//                 falls on a few keys. Weights carry a 2^7 bias so small ones
+//                 stay clear of fp16 subnormals; the bias cancels in O/l.
 // Tiles are double-buffered in LDS; the next tile's global loads are issued
 // before the current tile's MFMAs. Splits of the prefix write unnormalised
 // partials (O, max, sum) that a combine kernel merges with log-sum-exp; the
@@ -38,7 +44,9 @@ namespace tav {
 namespace {
 
 constexpr int kKT = 64;              // keys per tile
+constexpr int kMaxSplitBlocks = 2048; // block-table entries one split stages in LDS
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kWeightBias = 7.0f;  // log2 of the bias on the fp16 weights
 
 template <int D, int NW>
 struct Cfg {
@@ -85,6 +93,14 @@ __device__ __forceinline__ int k_off(int k, int cc)
     return ((k & ~31) | perm32(k & 31)) * (D * 2 + 16) + (cc << 4);
 }
 
+// Two bf16 values (low, high half of w) to two fp16 values, round to nearest.
+// Exact while |v| < 65520; larger magnitudes become infinite.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w)
+{
+    const f32x2 f = {__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xFFFF0000u)};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+}
+
 // LDS byte offset of keys [8*hh, 8*hh+8) of feature d in 16-key block bi of a V tile.
 template <int D>
 __device__ __forceinline__ int v_off(int bi, int d, int hh)
@@ -97,6 +113,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
 {
     using C = Cfg<D, NW>;
     __shared__ __attribute__((aligned(16))) char lds[2 * C::kBufBytes];
+    __shared__ int32_t s_bt[kMaxSplitBlocks];   // this split's physical block ids
 
     // ---- which (sequence, kv head, split, row block) ------------------------
     const int bid = blockIdx.x;
@@ -129,7 +146,21 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     const int n_pre = t_end - t_begin;
     const int n_tree = (s == a.S - 1) ? (a.N + kKT - 1) / kKT : 0;
     const int n_tiles = n_pre + n_tree;
-    const int32_t *bt = a.block_table + (int64_t)b * a.max_blocks;
+    // The split's block-table slice, validated once: later tiles look block
+    // ids up in LDS instead of waiting on a dependent global load per tile.
+    {
+        const int32_t *bt = a.block_table + (int64_t)b * a.max_blocks;
+        const int nb = std::min(n_pre * (kKT / kBlock), (L + kBlock - 1) / kBlock - t_begin * (kKT / kBlock));
+        for (int i = tid; i < nb; i += C::kThreads) {
+            int32_t blk = bt[t_begin * (kKT / kBlock) + i];
+            if (blk < 0 || blk >= a.num_blocks) {
+                raise_flag(a.flags, TAV_FLAG_BAD_BLOCK);
+                blk = -1;
+            }
+            s_bt[i] = blk;
+        }
+    }
+    const int blk0 = t_begin * (kKT / kBlock);
 
     // ---- this lane's query row ---------------------------------------------
     const int row = rb * C::kRows + wave * 32 + col;
@@ -163,12 +194,10 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
                     const int pos = p0 + k;
                     u32x4 v = {0, 0, 0, 0};
                     if (pos < L) {
-                        const int blk = bt[pos >> 4];
-                        if (blk >= 0 && blk < a.num_blocks)
+                        const int blk = s_bt[(pos >> 4) - blk0];
+                        if (blk >= 0)
                             v = *reinterpret_cast<const u32x4 *>(
                                 a.k_cache + (((int64_t)blk * a.Hkv + kvh) * kBlock + (pos & 15)) * D + cc * 8);
-                        else
-                            raise_flag(a.flags, TAV_FLAG_BAD_BLOCK);
                     }
                     kreg[r] = v;
                 }
@@ -179,8 +208,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
                     const int pos0 = p0 + bi * 16 + h2 * 8;
                     u32x4 v = {0, 0, 0, 0};
                     if (pos0 < L) {
-                        const int blk = bt[pos0 >> 4];
-                        if (blk >= 0 && blk < a.num_blocks) {
+                        const int blk = s_bt[(pos0 >> 4) - blk0];
+                        if (blk >= 0) {
                             v = *reinterpret_cast<const u32x4 *>(
                                 a.v_cache + (((int64_t)blk * a.Hkv + kvh) * D + d) * kBlock + h2 * 8);
                             const int valid = L - pos0;   // keys past the prefix read as zero
@@ -192,8 +221,6 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
                                         w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
                                 v = u32x4{w[0], w[1], w[2], w[3]};
                             }
-                        } else {
-                            raise_flag(a.flags, TAV_FLAG_BAD_BLOCK);
                         }
                     }
                     vreg[r] = v;
@@ -227,18 +254,27 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
             const int ci = tid + r * C::kThreads;
             const int k = ci / C::kCpr, cc = ci % C::kCpr;
             *reinterpret_cast<u32x4 *>(kl + k_off<D>(k, cc)) = kreg[r];
+            const uint32_t w[4] = {vreg[r].x, vreg[r].y, vreg[r].z, vreg[r].w};
             if (!tree) {
                 const int bi = ci / (2 * D), rem = ci % (2 * D);
-                *reinterpret_cast<u32x4 *>(vl + v_off<D>(bi, rem >> 1, rem & 1)) = vreg[r];
+                u32x4 h;
+                h.x = bf16x2_to_f16x2(w[0]);
+                h.y = bf16x2_to_f16x2(w[1]);
+                h.z = bf16x2_to_f16x2(w[2]);
+                h.w = bf16x2_to_f16x2(w[3]);
+                *reinterpret_cast<u32x4 *>(vl + v_off<D>(bi, rem >> 1, rem & 1)) = h;
             } else {
                 // tree V rows are feature-contiguous: scatter 8 features of key k
-                const uint32_t w[4] = {vreg[r].x, vreg[r].y, vreg[r].z, vreg[r].w};
                 const int bi = k >> 4, kb = k & 15;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int d = cc * 8 + e;
-                    *reinterpret_cast<uint16_t *>(vl + v_off<D>(bi, d, kb >> 3) + (kb & 7) * 2) =
-                        (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+                for (int e = 0; e < 8; e += 2) {
+                    const uint32_t h = bf16x2_to_f16x2(w[e >> 1]);
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int d = cc * 8 + e + u;
+                        *reinterpret_cast<uint16_t *>(vl + v_off<D>(bi, d, kb >> 3) + (kb & 7) * 2) =
+                            (uint16_t)(h >> (u * 16));
+                    }
                 }
             }
         }
@@ -253,8 +289,9 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
             oacc[m][e] = 0.f;
     float m_used = -INFINITY;   // raw-score max the exponentials are taken against
     float lsum = 0.f;           // this lane's share of the softmax denominator
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
+    __syncthreads();   // s_bt ready
     if (n_tiles > 0) {
         load_tile(0);
         store_tile(0, 0);
@@ -348,9 +385,10 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
             lsum *= alpha;
             m_used = mnew;
         }
-        const float moff = (m_used == -INFINITY) ? 0.f : m_used * a.c;
+        // weights 2^(s*c - m*c + 7): at most 2^15 after the lazy threshold
+        const float moff = (m_used == -INFINITY) ? 0.f : m_used * a.c - kWeightBias;
 
-        bf16x8 pb[2][2];
+        f16x8 pb[2][2];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -360,10 +398,10 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
                     const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * h2 + e], a.c, -moff));
                     const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * h2 + e + 1], a.c, -moff));
                     const f32x2 pf = {p0, p1};
-                    const bf16x2 pk = __builtin_convertvector(pf, bf16x2);
+                    const f16x2 pk = __builtin_convertvector(pf, f16x2);
                     pb[t][h2][e] = pk[0];
                     pb[t][h2][e + 1] = pk[1];
-                    lsum = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, lsum, false);
+                    lsum = __builtin_amdgcn_fdot2(pk, ones, lsum, false);
                 }
             }
 
@@ -374,9 +412,9 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
             for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                 for (int m = 0; m < C::kDTiles; ++m) {
-                    const bf16x8 av =
-                        *reinterpret_cast<const bf16x8 *>(vl + v_off<D>(2 * t + h2, 32 * m + col, hh));
-                    oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[t][h2], oacc[m], 0, 0, 0);
+                    const f16x8 av =
+                        *reinterpret_cast<const f16x8 *>(vl + v_off<D>(2 * t + h2, 32 * m + col, hh));
+                    oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[t][h2], oacc[m], 0, 0, 0);
                 }
 
         if (it + 1 < n_tiles) {
@@ -394,14 +432,19 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     if (a.S == 1) {
         const float inv = 1.0f / ltot;
         float *orow = a.out + (((int64_t)b * a.N + node) * a.Hq + head) * D;
+        bool finite = true;
 #pragma unroll
         for (int m = 0; m < C::kDTiles; ++m)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const f32x4 v = {oacc[m][4 * i] * inv, oacc[m][4 * i + 1] * inv,
                                  oacc[m][4 * i + 2] * inv, oacc[m][4 * i + 3] * inv};
+                finite &= __builtin_isfinite(v.x) && __builtin_isfinite(v.y) &&
+                          __builtin_isfinite(v.z) && __builtin_isfinite(v.w);
                 *reinterpret_cast<f32x4 *>(orow + 32 * m + 8 * i + 4 * hh) = v;
             }
+        if (!finite)
+            raise_flag(a.flags, TAV_FLAG_ATTN_RANGE);
     } else {
         const int64_t P = ((int64_t)bh * a.RB + rb) * a.S + s;
         const int rloc = wave * 32 + col;
@@ -457,8 +500,11 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(AttnArgs a, int 
         o += w * v;
     }
     const float inv = 1.0f / lsum;
-    *reinterpret_cast<f32x4 *>(a.out + (((int64_t)b * a.N + node) * a.Hq + head) * D + dq * 4) =
-        o * inv;
+    const f32x4 r = o * inv;
+    if (!(__builtin_isfinite(r.x) && __builtin_isfinite(r.y) && __builtin_isfinite(r.z) &&
+          __builtin_isfinite(r.w)))
+        raise_flag(a.flags, TAV_FLAG_ATTN_RANGE);
+    *reinterpret_cast<f32x4 *>(a.out + (((int64_t)b * a.N + node) * a.Hq + head) * D + dq * 4) = r;
 }
 
 struct AttnPlan {
@@ -487,6 +533,9 @@ bool attn_plan(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D, int32_t
     const int64_t tiles = std::max<int64_t>(1, ceil_div(max_prefix_len, kKT));
     int64_t S = ceil_div(target, base);
     S = std::max<int64_t>(1, std::min<int64_t>(S, tiles));
+    // a split's block-table slice must fit its LDS copy
+    const int64_t max_tiles_per_split = kMaxSplitBlocks / (kKT / kBlock);
+    S = std::max<int64_t>(S, ceil_div(tiles, max_tiles_per_split));
     p.S = (int)S;
     p.KS = (int)((int64_t)B * Hkv * p.S);
     p.grid = ceil_div(p.KS, 8) * 8 * p.RB;

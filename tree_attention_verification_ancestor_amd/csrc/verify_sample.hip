@@ -79,6 +79,18 @@ __device__ __forceinline__ double wave_max(double v)
     return v;
 }
 
+// Sum over the wave in lane order (an inclusive scan's last value).
+__device__ __forceinline__ double wave_sum_ordered(double v)
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(v, o);
+        if ((threadIdx.x & 63) >= o)
+            v += y;
+    }
+    return __shfl(v, 63);
+}
+
 // Workgroup-wide reductions; every thread gets the result. `red` holds
 // kSvWaves doubles; waves combine in index order.
 __device__ double block_sum(double v, double *red)
@@ -112,21 +124,34 @@ __device__ double block_max(double v, double *red)
 }
 
 // Group barrier (sense by generation). Returns false if the wait expired.
+//
+// Everything workgroups exchange (the partial sums in `xch`, the arrival
+// count, the generation word) moves through agent-scope atomics, which the
+// hardware keeps coherent across XCDs at the memory side without flushing or
+// invalidating the L2. Ordering comes from completion waits instead of
+// release/acquire fences: thread 0, which also wrote this workgroup's
+// exchange slots, waits until those stores and its read of the generation
+// have completed before it counts itself in; the last arrival resets the
+// count and only then publishes the next generation. Waiters poll the
+// generation; the exchange slots they read afterwards were complete before
+// any arrival that let the generation move.
 __device__ bool group_barrier(uint32_t *cnt, uint32_t *gen, uint32_t members, uint32_t *flags,
                               int *s_ok)
 {
     __syncthreads();
     if (threadIdx.x == 0) {
         int ok = 1;
-        const uint32_t g0 = __hip_atomic_load(gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t g0 = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
         const uint32_t arrived =
-            __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (arrived == members - 1) {
             __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(gen, g0 + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_s_waitcnt(0);
+            __hip_atomic_store(gen, g0 + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
             uint32_t polls = 0;
-            while (__hip_atomic_load(gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == g0) {
+            while (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0) {
                 __builtin_amdgcn_s_sleep(1);
                 if (++polls > kSpinLimit) {
                     ok = 0;
@@ -164,6 +189,8 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
     __shared__ int s_bad;
     __shared__ int s_found;
     __shared__ int s_last_live;
+    __shared__ int s_hit;
+    __shared__ double s_slot[kSvEpt * kSvWaves];
 
     const int g = blockIdx.x % a.ngroups;
     const int rank = blockIdx.x / a.ngroups;
@@ -422,11 +449,43 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 break;
             }
             if (mass > 0.0 && before <= target && target < after) {
-                double offset_e = before;
-                double *wtot = s_red;   // per-wave totals
+                // element e of thread t is token base + e*256 + t, so token order
+                // is (e, wave, lane). Totals of every (e, wave) slot first, in
+                // that order; then the one wave holding the target scans its lanes.
+                const int lane = tid & 63, wave = tid >> 6;
+                double *slot_tot = s_slot;     // [kSvEpt][kSvWaves]
+#pragma unroll
                 for (int e = 0; e < kSvEpt; ++e) {
-                    const double v = pr[e];
-                    const int lane = tid & 63, wave = tid >> 6;
+                    const double t = wave_sum_ordered(pr[e]);
+                    if (lane == 0)
+                        slot_tot[e * kSvWaves + wave] = t;
+                }
+                __syncthreads();
+                if (tid == 0) {
+                    double run = before;
+                    int hit = -1;
+                    double hit_off = 0.0;
+                    for (int k2 = 0; k2 < kSvEpt * kSvWaves; ++k2) {
+                        const double nxt = run + slot_tot[k2];
+                        if (slot_tot[k2] > 0.0 && run <= target && target < nxt) {
+                            hit = k2;
+                            hit_off = run;
+                            break;
+                        }
+                        run = nxt;
+                    }
+                    s_hit = hit;
+                    s_stats[2] = hit_off;
+                }
+                __syncthreads();
+                const int hit = s_hit;
+                if (hit >= 0 && wave == hit % kSvWaves) {
+                    const int e_hit = hit / kSvWaves;
+                    double v = 0.0;
+#pragma unroll
+                    for (int e = 0; e < kSvEpt; ++e)
+                        if (e == e_hit)
+                            v = pr[e];
                     double incl = v;
 #pragma unroll
                     for (int o = 1; o < 64; o <<= 1) {
@@ -434,39 +493,31 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                         if (lane >= o)
                             incl += y;
                     }
-                    // exclusive value = the previous lane's inclusive value, so
-                    // each element's lower bound is its predecessor's upper bound
                     double excl = __shfl_up(incl, 1);
                     if (lane == 0)
                         excl = 0.0;
-                    __syncthreads();
-                    if (lane == 63)
-                        wtot[wave] = incl;
-                    __syncthreads();
-                    double wave_off = offset_e;
-                    double etotal = offset_e;
-                    for (int w = 0; w < kSvWaves; ++w) {
-                        if (w < wave)
-                            wave_off = wave_off + wtot[w];
-                        etotal = etotal + wtot[w];
-                    }
-                    const double cum_before = lane == 0 ? wave_off : wave_off + excl;
-                    const double cum_after = wave_off + incl;
-                    const int64_t idx = base + (int64_t)e * kSvThreads + tid;
+                    const double off = s_stats[2];
+                    const double lo = off + excl, hi = off + incl;
+                    const int64_t idx = base + (int64_t)e_hit * kSvThreads + tid;
                     if (v > 0.0) {
                         atomicMax(&s_last_live, (int)idx);
-                        if (cum_before <= target && target < cum_after)
-                            s_found = (int)idx;   // at most one element qualifies
+                        if (lo <= target && target < hi)
+                            s_found = (int)idx;   // at most one lane qualifies
                     }
-                    __syncthreads();
-                    if (s_found >= 0)
-                        break;
-                    offset_e = etotal;
                 }
-                if (tid == 0) {
-                    const int tok = s_found >= 0 ? s_found : s_last_live;
-                    a.out_tok[rowbase + nacc] = tok;
+                // rounding left the target past the last live token: take that token
+                if (hit < 0) {
+#pragma unroll
+                    for (int e = 0; e < kSvEpt; ++e)
+                        if (pr[e] > 0.0)
+                            atomicMax(&s_last_live, (int)(base + (int64_t)e * kSvThreads + tid));
                 }
+                __syncthreads();
+                // the lane intervals of the hit slot partition its total exactly
+                // (same scan), so s_found is set unless rounding put the target
+                // past the chunk's summed slots; then the last live token wins
+                if (tid == 0)
+                    a.out_tok[rowbase + nacc] = s_found >= 0 ? s_found : s_last_live;
             }
             break;
         }
@@ -584,7 +635,7 @@ extern "C" size_t spec_verify_workspace_bytes(int32_t B, int32_t N, int32_t V)
 
 extern "C" tav_status spec_verify_sample(const float *target_logits, const float *draft_logits,
                                          const int32_t *parent, const int32_t *token, int32_t B,
-                                         int32_t N, int32_t V, float temperature, uint64_t seed,
+                                         int32_t N, int32_t V, double temperature, uint64_t seed,
                                          uint64_t offset, int32_t *path, int32_t *n_accepted,
                                          int32_t *out_tokens, void *workspace, size_t ws_bytes,
                                          uint32_t *dev_flags, void *stream)
@@ -593,7 +644,7 @@ extern "C" tav_status spec_verify_sample(const float *target_logits, const float
     if (!target_logits || !draft_logits || !parent || !token || !path || !n_accepted ||
         !out_tokens)
         return TAV_ERR_ARG;
-    if (B < 1 || N < 1 || V < 1 || !(temperature > 0.0f) || !(temperature < INFINITY))
+    if (B < 1 || N < 1 || V < 1 || !(temperature > 0.0) || !(temperature < INFINITY))
         return TAV_ERR_ARG;
     if (N > kMaxNodes || V > (1 << 24))
         return TAV_ERR_UNSUPPORTED;
@@ -614,7 +665,7 @@ extern "C" tav_status spec_verify_sample(const float *target_logits, const float
     a.B = B;
     a.N = N;
     a.V = V;
-    a.T = (double)temperature;
+    a.T = temperature;
     a.seed = seed;
     a.offset = offset;
     a.path = path;
@@ -652,15 +703,15 @@ extern "C" tav_status tav_philox_uniforms(uint64_t seed, uint64_t offset, int32_
 }
 
 extern "C" tav_status tav_target_probs(const float *logits, int64_t rows, int32_t V,
-                                       float temperature, double *p, uint32_t *dev_flags,
+                                       double temperature, double *p, uint32_t *dev_flags,
                                        void *stream)
 {
     using namespace tav;
-    if (!logits || !p || rows < 1 || V < 1 || !(temperature > 0.0f))
+    if (!logits || !p || rows < 1 || V < 1 || !(temperature > 0.0) || !(temperature < INFINITY))
         return TAV_ERR_ARG;
     if (rows > (1ll << 31) - 1)
         return TAV_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(target_probs_kernel, dim3((unsigned)rows), dim3(kSvThreads), 0,
-                       as_stream(stream), logits, V, (double)temperature, p, dev_flags);
+                       as_stream(stream), logits, V, temperature, p, dev_flags);
     return hipGetLastError() == hipSuccess ? TAV_OK : TAV_ERR_LAUNCH;
 }
