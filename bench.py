@@ -88,8 +88,7 @@ def run_gpu(args, w):
     ws_a = torch.empty(max(1, tav.tree_attn_workspace_bytes(B, N, w.Hq, w.Hkv, w.D,
                                                             w.max_prefix_len)),
                        dtype=torch.uint8, device=dev)
-    ws_s = torch.empty(max(1, tav.spec_verify_workspace_bytes(B, N, V)), dtype=torch.uint8,
-                       device=dev)
+    ws_s = tav.new_sampler_workspace(B, N, V, dev)
     path = torch.empty((B, N), dtype=torch.int32, device=dev)
     n_acc = torch.empty((B,), dtype=torch.int32, device=dev)
     toks = torch.empty((B, N), dtype=torch.int32, device=dev)

@@ -168,8 +168,10 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t N, int32_t V);
  *   n_accepted  int32 [B] out: accepted children (path length - 1)
  *   out_tokens  int32 [B][N] out: emitted tokens, n_accepted[b] + 1 of them, -1 padded
  *   workspace   device buffer of >= spec_verify_workspace_bytes(B, N, V) bytes,
- *               256-byte aligned; its contents need no initialisation
- *   Supported: 1 <= N <= 256, 1 <= V <= 2^24, fp32 logits 4-byte aligned.
+ *               256-byte aligned, zero-filled before its first use; every call
+ *               leaves it zero-filled again. Calls that share a workspace must
+ *               not overlap in time (e.g. keep them on one stream).
+ *   Supported: 1 <= N <= 256, 1 <= V <= 2^21, fp32 logits 4-byte aligned.
  *   Flags: TAV_FLAG_BAD_PARENT, TAV_FLAG_BAD_TOKEN, TAV_FLAG_NONFINITE_LOGITS,
  *   TAV_FLAG_SYNC_TIMEOUT.
  */

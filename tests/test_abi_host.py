@@ -75,7 +75,7 @@ def _sample(**kw):
     (dict(tl=None), tav.ERR_ARG), (dict(path=None), tav.ERR_ARG), (dict(B=0), tav.ERR_ARG),
     (dict(V=0), tav.ERR_ARG), (dict(T=0.0), tav.ERR_ARG), (dict(T=-1.0), tav.ERR_ARG),
     (dict(T=float("inf")), tav.ERR_ARG), (dict(N=257), tav.ERR_UNSUPPORTED),
-    (dict(V=(1 << 24) + 1), tav.ERR_UNSUPPORTED),
+    (dict(V=(1 << 21) + 1), tav.ERR_UNSUPPORTED),
 ])
 def test_sampler_rejects_bad_arguments(kw, code):
     assert _sample(**kw) == code

@@ -237,6 +237,14 @@ def spec_verify_workspace_bytes(B, N, V) -> int:
     return int(lib().spec_verify_workspace_bytes(B, N, V))
 
 
+def new_sampler_workspace(B, N, V, device=None) -> torch.Tensor:
+    """A zero-filled workspace for ``spec_verify_sample`` (each call leaves it zeroed)."""
+    n = spec_verify_workspace_bytes(B, N, V)
+    if n == 0:
+        raise ValueError(f"spec_verify_sample does not support B={B}, N={N}, V={V}")
+    return torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
+
+
 def spec_verify_sample(target_logits, draft_logits, parent, token, temperature: float = 1.0,
                        seed: int = 0, offset: int = 0, path=None, n_accepted=None,
                        out_tokens=None, workspace=None, dev_flags=None, stream=None):
@@ -257,8 +265,7 @@ def spec_verify_sample(target_logits, draft_logits, parent, token, temperature: 
     _need(n_accepted, "n_accepted", _I32T, (B,), dev)
     _need(out_tokens, "out_tokens", _I32T, (B, N), dev)
     if workspace is None:
-        workspace = torch.empty(max(1, spec_verify_workspace_bytes(B, N, V)), dtype=torch.uint8,
-                                device=dev)
+        workspace = new_sampler_workspace(B, N, V, dev)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("spec_verify_sample", lib().spec_verify_sample(
         _ptr(target_logits), _ptr(draft_logits), _ptr(parent), _ptr(token), B, N, V,

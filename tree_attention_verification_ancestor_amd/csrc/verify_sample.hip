@@ -14,22 +14,36 @@
 // time; workgroup r of the group owns vocabulary entries
 // [r*chunk, (r+1)*chunk) and keeps them in registers (16 per thread), so
 // every pass over a row after the first is register-resident. The walk is
-// serial: for each visited node u the group
-//   1. loads its chunk of target row u (and draft row u if u has children),
-//      reduces a local (max, sum exp), publishes it and meets at a barrier;
-//      every workgroup merges the wpg pairs in the same order, so all hold
-//      bit-identical (max, normaliser) pairs;
-//   2. tests the children in order. The test values p(x), q(x) and the
-//      residual at x are recomputed from the logits at x by every workgroup
-//      with the same instructions, so every workgroup takes the same decision;
-//   3. after each rejection reduces sum(max(0, p_res - q)) (one barrier) and
-//      updates its register chunk;
-//   4. at the stopping node reduces the chunk masses (one barrier); the one
-//      workgroup whose prefix interval holds r * total scans its chunk.
-// Barriers are group-local (an arrival counter plus a generation word in the
-// workspace) and every wait is bounded: on expiry the kernel raises
-// TAV_FLAG_SYNC_TIMEOUT and the workgroup stops, so every wave exits. The
-// launch is cooperative, which guarantees all workgroups are resident.
+// serial; for each visited node u the group
+//   1. loads its chunk of target row u (and draft row u if u has children)
+//      and the logits of u's children's tokens, reduces a local
+//      (max, sum exp) per row and exchanges it (one group sync). Every
+//      workgroup merges the wpg pairs in the same order, so all hold
+//      bit-identical normalisers and per-chunk masses;
+//   2. tests the children in order. p(x), q(x) and the residual at x are
+//      recomputed from the logits at x with the same instructions in every
+//      workgroup, so every workgroup takes the same decision;
+//   3. after each rejection exchanges the chunk sums of max(0, p_res - q)
+//      (one group sync), which give the new normaliser and the new chunk
+//      masses, and updates its registers;
+//   4. if it stops at u, every workgroup already holds the chunk masses of
+//      the final distribution; the one workgroup whose prefix interval holds
+//      r * total scans its chunk, so the draw costs no further sync.
+//
+// Group sync. Each workgroup owns a 64-byte mailbox slot per parity: up to
+// eight 64-bit words, each carrying the sync's generation in its high half
+// and 32 bits of payload in its low half (fp32 maxima as they are, fp64 sums
+// split in two). Words are written and read with agent-scope 64-bit atomics,
+// which are single-copy atomic and stay coherent across XCDs at the memory
+// side, so no cache is flushed or invalidated and no write has to be
+// acknowledged before another: a reader polls a member's words (one lane per
+// member) until every one carries the current generation. Two parities
+// suffice: a member can only reuse a slot after every member has arrived at
+// the sync in between, i.e. after everyone has read it. Every wait is
+// bounded: on expiry the kernel raises TAV_FLAG_SYNC_TIMEOUT and the
+// workgroup stops, so every wave exits. The launch is cooperative, which
+// guarantees all workgroups are resident. The last workgroup to finish clears
+// every slot, so each call leaves the workspace as it found it (zero-filled).
 
 #include <algorithm>
 
@@ -43,8 +57,12 @@ constexpr int kSvThreads = 256;
 constexpr int kSvWaves = kSvThreads / 64;
 constexpr int kSvEpt = 16;                      // vocabulary entries per thread
 constexpr int kSvChunk = kSvThreads * kSvEpt;   // per workgroup
-constexpr uint32_t kSpinLimit = 1u << 21;       // polls before a wait gives up
-constexpr int kSyncStride = 32;                 // uint32 words per group (128 B)
+constexpr int kMaxWpg = 512;                    // workgroups per sequence
+constexpr int kSlotsPerThread = kMaxWpg / kSvThreads;
+constexpr int64_t kMaxVocab = (int64_t)kSvChunk * kMaxWpg;   // 2^21
+constexpr uint32_t kSpinLimit = 1u << 20;       // polls before a wait gives up
+constexpr int kSlotWords = 8;                   // 64-byte slot of tagged 64-bit words
+constexpr size_t kHeaderBytes = 256;            // exit counter
 
 struct SvArgs {
     const float *tl;
@@ -57,8 +75,8 @@ struct SvArgs {
     int32_t *path;
     int32_t *n_acc;
     int32_t *out_tok;
-    double *xch;      // [ngroups][2][wpg][4]
-    uint32_t *sync;   // [ngroups][kSyncStride]: [0] arrivals, [16] generation
+    uint32_t *done;   // exit counter
+    uint64_t *box;    // [ngroups][2][wpg][kSlotWords]
     uint32_t *flags;
     int32_t wpg, ngroups, chunk;
 };
@@ -91,90 +109,122 @@ __device__ __forceinline__ double wave_sum_ordered(double v)
     return __shfl(v, 63);
 }
 
-// Workgroup-wide reductions; every thread gets the result. `red` holds
-// kSvWaves doubles; waves combine in index order.
-__device__ double block_sum(double v, double *red)
+// Workgroup-wide reductions of two values at once; every thread gets the
+// results. Waves combine in index order, so the result depends only on the
+// inputs, never on timing. `red` holds 2 * kSvWaves doubles.
+__device__ void block_sum2(double &a, double &b, double *red)
 {
-    v = wave_sum(v);
+    a = wave_sum(a);
+    b = wave_sum(b);
     const int wave = threadIdx.x >> 6;
     __syncthreads();
-    if ((threadIdx.x & 63) == 0)
-        red[wave] = v;
+    if ((threadIdx.x & 63) == 0) {
+        red[wave] = a;
+        red[kSvWaves + wave] = b;
+    }
     __syncthreads();
-    double s = 0.0;
+    a = 0.0;
+    b = 0.0;
 #pragma unroll
-    for (int w = 0; w < kSvWaves; ++w)
-        s += red[w];
-    return s;
+    for (int w = 0; w < kSvWaves; ++w) {
+        a += red[w];
+        b += red[kSvWaves + w];
+    }
 }
 
-__device__ double block_max(double v, double *red)
+__device__ void block_max2(double &a, double &b, double *red)
 {
-    v = wave_max(v);
+    a = wave_max(a);
+    b = wave_max(b);
     const int wave = threadIdx.x >> 6;
     __syncthreads();
-    if ((threadIdx.x & 63) == 0)
-        red[wave] = v;
+    if ((threadIdx.x & 63) == 0) {
+        red[wave] = a;
+        red[kSvWaves + wave] = b;
+    }
     __syncthreads();
-    double m = -INFINITY;
+    a = -INFINITY;
+    b = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kSvWaves; ++w)
-        m = fmax(m, red[w]);
-    return m;
+    for (int w = 0; w < kSvWaves; ++w) {
+        a = fmax(a, red[w]);
+        b = fmax(b, red[kSvWaves + w]);
+    }
 }
 
-// Group barrier (sense by generation). Returns false if the wait expired.
-//
-// Everything workgroups exchange (the partial sums in `xch`, the arrival
-// count, the generation word) moves through agent-scope atomics, which the
-// hardware keeps coherent across XCDs at the memory side without flushing or
-// invalidating the L2. Ordering comes from completion waits instead of
-// release/acquire fences: thread 0, which also wrote this workgroup's
-// exchange slots, waits until those stores and its read of the generation
-// have completed before it counts itself in; the last arrival resets the
-// count and only then publishes the next generation. Waiters poll the
-// generation; the exchange slots they read afterwards were complete before
-// any arrival that let the generation move.
-__device__ bool group_barrier(uint32_t *cnt, uint32_t *gen, uint32_t members, uint32_t *flags,
-                              int *s_ok)
+__device__ __forceinline__ uint64_t tag_word(uint32_t gen, uint32_t payload)
 {
+    return ((uint64_t)gen << 32) | payload;
+}
+
+// One group sync. Threads 0..NW-1 publish word i = mine[i] (32 payload bits)
+// in this workgroup's slot for generation `gen`; on return (true) thread t
+// holds the payloads of member t + k*kSvThreads in got[k][0..NW). Returns
+// false on a timeout.
+template <int NW>
+__device__ bool group_sync(uint64_t *box, int wpg, int rank, uint32_t gen,
+                           const uint32_t (&mine)[NW], uint32_t (&got)[kSlotsPerThread][NW],
+                           uint32_t *flags)
+{
+    uint64_t *base = box + (size_t)(gen & 1u) * wpg * kSlotWords;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int ok = 1;
-        const uint32_t g0 = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0);
-        const uint32_t arrived =
-            __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (arrived == members - 1) {
-            __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __builtin_amdgcn_s_waitcnt(0);
-            __hip_atomic_store(gen, g0 + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
+    if (threadIdx.x < NW) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+            if ((int)threadIdx.x == i)
+                v = mine[i];
+        __hip_atomic_store(base + (size_t)rank * kSlotWords + threadIdx.x, tag_word(gen, v),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    bool ok = true;
+#pragma unroll
+    for (int k = 0; k < kSlotsPerThread; ++k) {
+        const int w = threadIdx.x + k * kSvThreads;
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+            got[k][i] = 0u;
+        if (w < wpg && ok) {
+            uint64_t *slot = base + (size_t)w * kSlotWords;
             uint32_t polls = 0;
-            while (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0) {
+            for (;;) {
+                uint64_t word[NW];
+#pragma unroll
+                for (int i = 0; i < NW; ++i)
+                    word[i] = __hip_atomic_load(slot + i, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+                bool all = true;
+#pragma unroll
+                for (int i = 0; i < NW; ++i) {
+                    all &= (uint32_t)(word[i] >> 32) == gen;
+                    got[k][i] = (uint32_t)word[i];
+                }
+                if (all)
+                    break;
                 __builtin_amdgcn_s_sleep(1);
                 if (++polls > kSpinLimit) {
-                    ok = 0;
-                    raise_flag(flags, TAV_FLAG_SYNC_TIMEOUT);
+                    ok = false;
                     break;
                 }
             }
         }
-        *s_ok = ok;
     }
-    __syncthreads();
-    return *s_ok != 0;
+    ok = __syncthreads_and(ok);
+    if (!ok && threadIdx.x == 0)
+        raise_flag(flags, TAV_FLAG_SYNC_TIMEOUT);
+    return ok;
 }
 
-__device__ __forceinline__ void xch_put(double *slot, double v)
+__device__ __forceinline__ uint32_t f32_bits(float v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ float bits_f32(uint32_t v) { return __builtin_bit_cast(float, v); }
+__device__ __forceinline__ uint32_t f64_hi(double v)
 {
-    __hip_atomic_store(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return (uint32_t)(__builtin_bit_cast(uint64_t, v) >> 32);
 }
-
-__device__ __forceinline__ double xch_get(const double *slot)
+__device__ __forceinline__ uint32_t f64_lo(double v) { return (uint32_t)__builtin_bit_cast(uint64_t, v); }
+__device__ __forceinline__ double bits_f64(uint32_t hi, uint32_t lo)
 {
-    return __hip_atomic_load(const_cast<double *>(slot), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
 __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
@@ -182,27 +232,30 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
     __shared__ int32_t s_par[kMaxNodes];
     __shared__ int32_t s_first[kMaxNodes];
     __shared__ int32_t s_next[kMaxNodes];
-    __shared__ double s_red[kSvWaves];
-    __shared__ double s_zhist[kMaxNodes];
-    __shared__ double s_stats[4];
-    __shared__ int s_ok;
+    __shared__ int32_t s_tok[kMaxNodes];
+    __shared__ float s_tx[kMaxNodes];     // target logit of child c's token in its parent's row
+    __shared__ float s_dx[kMaxNodes];     // draft logit of the same
+    __shared__ double s_red[2 * kSvWaves];
+    __shared__ double s_mass[kMaxWpg];    // mass of every member's chunk in the current distribution
+    __shared__ double s_zhist[kMaxNodes]; // residual normalisers after each rejection at u
+    __shared__ double s_slot[kSvEpt * kSvWaves];
+    __shared__ double s_hit_off;
     __shared__ int s_bad;
     __shared__ int s_found;
     __shared__ int s_last_live;
     __shared__ int s_hit;
-    __shared__ double s_slot[kSvEpt * kSvWaves];
+    __shared__ int s_is_last;
 
     const int g = blockIdx.x % a.ngroups;
     const int rank = blockIdx.x / a.ngroups;
     const int tid = threadIdx.x;
     const int N = a.N;
+    const int wpg = a.wpg;
     const int64_t base = (int64_t)rank * a.chunk;
     const int64_t lim = std::min<int64_t>((int64_t)a.V, base + a.chunk);
-    uint32_t *cnt = a.sync + (int64_t)g * kSyncStride;
-    uint32_t *gen = cnt + 16;
-    double *xch = a.xch + (int64_t)g * 2 * a.wpg * 4;
-    const uint32_t members = (uint32_t)a.wpg;
-    int parity = 0;
+    uint64_t *box = a.box + (size_t)g * 2 * wpg * kSlotWords;
+    const double invT = 1.0 / a.T;
+    uint32_t gen = 0;
     bool alive = true;
 
     for (int b = g; b < a.B && alive; b += a.ngroups) {
@@ -213,6 +266,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             s_bad = 0;
         for (int i = tid; i < N; i += kSvThreads) {
             s_par[i] = a.parent[rowbase + i];
+            s_tok[i] = a.token[rowbase + i];
             s_first[i] = N;
             s_next[i] = -1;
         }
@@ -222,7 +276,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             if (i == 0 ? p != -1 : (p < 0 || p >= i))
                 atomicOr(&s_bad, 1);
             if (i > 0) {
-                const int x = a.token[rowbase + i];
+                const int x = s_tok[i];
                 if (x < 0 || x >= a.V)
                     atomicOr(&s_bad, 2);
             }
@@ -258,71 +312,89 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             const bool has_kids = s_first[u] >= 0;
 
             // ---- 1. local (max, sum exp) of target and draft rows ------------
-            double pr[kSvEpt], qv[kSvEpt];
-            bool nan_seen = false;
-            double mt = -INFINITY, mq = -INFINITY;
+            // chunk loads first, then the logits of u's children's tokens, so
+            // all of them are in flight together
+            float tf[kSvEpt], df[kSvEpt];
 #pragma unroll
             for (int e = 0; e < kSvEpt; ++e) {
                 const int64_t idx = base + (int64_t)e * kSvThreads + tid;
-                pr[e] = -INFINITY;
-                qv[e] = -INFINITY;
+                tf[e] = -INFINITY;
+                df[e] = -INFINITY;
                 if (idx < lim) {
-                    pr[e] = (double)trow[idx] / a.T;
+                    tf[e] = trow[idx];
                     if (has_kids)
-                        qv[e] = (double)drow[idx] / a.T;
+                        df[e] = drow[idx];
                 }
-                nan_seen |= __builtin_isnan(pr[e]) || __builtin_isnan(qv[e]);
-                mt = fmax(mt, pr[e]);
-                mq = fmax(mq, qv[e]);
             }
-            mt = block_max(mt, s_red);
-            mq = block_max(mq, s_red);
+            for (int c = u + 1 + tid; c < N; c += kSvThreads)
+                if (s_par[c] == u) {
+                    const int x = s_tok[c];
+                    s_tx[c] = trow[x];
+                    s_dx[c] = drow[x];
+                }
+            // maxima of the raw fp32 logits (exact); x -> x/T is monotone
+            bool nan_seen = false;
+            double mt_d = -INFINITY, mq_d = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < kSvEpt; ++e) {
+                nan_seen |= __builtin_isnan(tf[e]) || __builtin_isnan(df[e]);
+                mt_d = fmax(mt_d, (double)tf[e]);
+                mq_d = fmax(mq_d, (double)df[e]);
+            }
+            block_max2(mt_d, mq_d, s_red);
+            const float mt_raw = (float)mt_d, mq_raw = (float)mq_d;
+            const double mts = (double)mt_raw * invT, mqs = (double)mq_raw * invT;
+            double pr[kSvEpt], qv[kSvEpt];
             double zt = 0.0, zq = 0.0;
 #pragma unroll
             for (int e = 0; e < kSvEpt; ++e) {
-                pr[e] = (mt == -INFINITY) ? 0.0 : exp(pr[e] - mt);
-                qv[e] = (mq == -INFINITY) ? 0.0 : exp(qv[e] - mq);
+                pr[e] = (mt_raw == -INFINITY) ? 0.0 : exp((double)tf[e] * invT - mts);
+                qv[e] = (mq_raw == -INFINITY) ? 0.0 : exp((double)df[e] * invT - mqs);
                 zt += pr[e];
                 zq += qv[e];
             }
-            zt = block_sum(zt, s_red);
-            zq = block_sum(zq, s_red);
+            block_sum2(zt, zq, s_red);
             if (__syncthreads_or(nan_seen))
                 zt = NAN;
-            double *mine = xch + ((int64_t)parity * a.wpg + rank) * 4;
-            if (tid == 0) {
-                xch_put(mine + 0, mt);
-                xch_put(mine + 1, zt);
-                xch_put(mine + 2, mq);
-                xch_put(mine + 3, zq);
-            }
-            if (!group_barrier(cnt, gen, members, a.flags, &s_ok)) {
-                alive = false;
-                break;
-            }
-            // every workgroup merges the wpg pairs in rank order
-            if (tid == 0) {
-                const double *all = xch + (int64_t)parity * a.wpg * 4;
-                double Mp = -INFINITY, Mq = -INFINITY;
-                for (int w = 0; w < a.wpg; ++w) {
-                    Mp = fmax(Mp, xch_get(all + w * 4 + 0));
-                    Mq = fmax(Mq, xch_get(all + w * 4 + 2));
+
+            double got[kSlotsPerThread][4];
+            {
+                const uint32_t mine[6] = {f32_bits(mt_raw), f64_hi(zt), f64_lo(zt),
+                                          f32_bits(mq_raw), f64_hi(zq), f64_lo(zq)};
+                uint32_t words[kSlotsPerThread][6];
+                if (!group_sync<6>(box, wpg, rank, ++gen, mine, words, a.flags)) {
+                    alive = false;
+                    break;
                 }
-                double Zp = 0.0, Zq = 0.0;
-                for (int w = 0; w < a.wpg; ++w) {
-                    const double m1 = xch_get(all + w * 4 + 0), z1 = xch_get(all + w * 4 + 1);
-                    const double m2 = xch_get(all + w * 4 + 2), z2 = xch_get(all + w * 4 + 3);
+#pragma unroll
+                for (int k = 0; k < kSlotsPerThread; ++k) {
+                    got[k][0] = (double)bits_f32(words[k][0]) * invT;
+                    got[k][1] = bits_f64(words[k][1], words[k][2]);
+                    got[k][2] = (double)bits_f32(words[k][3]) * invT;
+                    got[k][3] = bits_f64(words[k][4], words[k][5]);
+                }
+            }
+            // merge the members' (max, sum) pairs: per thread over its slots,
+            // then across the workgroup, in a fixed order
+            double Mp = -INFINITY, Mq = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < kSlotsPerThread; ++k)
+                if (tid + k * kSvThreads < wpg) {
+                    Mp = fmax(Mp, got[k][0]);
+                    Mq = fmax(Mq, got[k][2]);
+                }
+            block_max2(Mp, Mq, s_red);
+            double Zp = 0.0, Zq = 0.0;
+#pragma unroll
+            for (int k = 0; k < kSlotsPerThread; ++k)
+                if (tid + k * kSvThreads < wpg) {
+                    const double m1 = got[k][0], z1 = got[k][1];
+                    const double m2 = got[k][2], z2 = got[k][3];
+                    // a NaN sum travels through; an empty chunk adds nothing
                     Zp += (m1 == -INFINITY) ? (z1 != z1 ? z1 : 0.0) : z1 * exp(m1 - Mp);
                     Zq += (m2 == -INFINITY) ? 0.0 : z2 * exp(m2 - Mq);
                 }
-                s_stats[0] = Mp;
-                s_stats[1] = Zp;
-                s_stats[2] = Mq;
-                s_stats[3] = Zq;
-            }
-            parity ^= 1;
-            __syncthreads();
-            const double Mp = s_stats[0], Zp = s_stats[1], Mq = s_stats[2], Zq = s_stats[3];
+            block_sum2(Zp, Zq, s_red);
             const bool bad_p = !(Zp > 0.0) || Mp == -INFINITY || __builtin_isinf(Mp) ||
                                __builtin_isnan(Zp) || __builtin_isinf(Zp);
             const bool bad_q = has_kids && (!(Zq > 0.0) || Mq == -INFINITY ||
@@ -333,24 +405,31 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 failed = true;
                 break;
             }
-            // registers now hold p and q of this chunk
+            // chunk masses of p, and p and q of this chunk in registers
+#pragma unroll
+            for (int k = 0; k < kSlotsPerThread; ++k) {
+                const int w = tid + k * kSvThreads;
+                if (w < wpg)
+                    s_mass[w] = (got[k][0] == -INFINITY) ? 0.0 : got[k][1] * exp(got[k][0] - Mp) / Zp;
+            }
             {
-                const double sp = (mt == -INFINITY) ? 0.0 : exp(mt - Mp) / Zp;
-                const double sq = (mq == -INFINITY) ? 0.0 : exp(mq - Mq) / Zq;
+                const double sp = (mt_raw == -INFINITY) ? 0.0 : exp(mts - Mp) / Zp;
+                const double sq = (mq_raw == -INFINITY) ? 0.0 : exp(mqs - Mq) / Zq;
 #pragma unroll
                 for (int e = 0; e < kSvEpt; ++e) {
                     pr[e] *= sp;
                     qv[e] *= sq;
                 }
             }
+            __syncthreads();   // s_mass, s_tx, s_dx visible
 
             // ---- 2./3. children in ascending order against the running residual
             int k = 0;
             bool accepted = false;
             for (int c = s_first[u]; c >= 0; c = s_next[c]) {
-                const int x = a.token[rowbase + c];
-                const double px = exp((double)trow[x] / a.T - Mp) / Zp;
-                const double qx = exp((double)drow[x] / a.T - Mq) / Zq;
+                const int x = s_tok[c];
+                const double px = exp((double)s_tx[c] * invT - Mp) / Zp;
+                const double qx = exp((double)s_dx[c] * invT - Mq) / Zq;
                 double prx = px;
                 for (int j = 0; j < k; ++j) {
                     const double zj = s_zhist[j];
@@ -370,39 +449,48 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     accepted = true;
                     break;
                 }
-                // rejected: residual normaliser over the whole vocabulary
-                double s = 0.0;
+                // rejected: chunk sums of the residual, exchanged
+                double s = 0.0, unused = 0.0;
 #pragma unroll
                 for (int e = 0; e < kSvEpt; ++e) {
                     const double d = pr[e] - qv[e];
                     s += d > 0.0 ? d : 0.0;
                 }
-                s = block_sum(s, s_red);
-                double *slot = xch + ((int64_t)parity * a.wpg + rank) * 4;
-                if (tid == 0)
-                    xch_put(slot, s);
-                if (!group_barrier(cnt, gen, members, a.flags, &s_ok)) {
-                    alive = false;
-                    break;
+                block_sum2(s, unused, s_red);
+                double rs[kSlotsPerThread][1];
+                {
+                    const uint32_t mine[2] = {f64_hi(s), f64_lo(s)};
+                    uint32_t words[kSlotsPerThread][2];
+                    if (!group_sync<2>(box, wpg, rank, ++gen, mine, words, a.flags)) {
+                        alive = false;
+                        break;
+                    }
+#pragma unroll
+                    for (int kk = 0; kk < kSlotsPerThread; ++kk)
+                        rs[kk][0] = bits_f64(words[kk][0], words[kk][1]);
                 }
-                if (tid == 0) {
-                    const double *all = xch + (int64_t)parity * a.wpg * 4;
-                    double Z = 0.0;
-                    for (int w = 0; w < a.wpg; ++w)
-                        Z += xch_get(all + w * 4);
-                    s_zhist[k] = Z;
-                }
-                parity ^= 1;
-                __syncthreads();
-                const double Z = s_zhist[k];
-                ++k;
+                double Z = 0.0, unused2 = 0.0;
+#pragma unroll
+                for (int kk = 0; kk < kSlotsPerThread; ++kk)
+                    Z += rs[kk][0];
+                block_sum2(Z, unused2, s_red);
                 if (Z > 0.0) {
+#pragma unroll
+                    for (int kk = 0; kk < kSlotsPerThread; ++kk) {
+                        const int w = tid + kk * kSvThreads;
+                        if (w < wpg)
+                            s_mass[w] = rs[kk][0] / Z;
+                    }
 #pragma unroll
                     for (int e = 0; e < kSvEpt; ++e) {
                         const double d = pr[e] - qv[e];
                         pr[e] = (d > 0.0 ? d : 0.0) / Z;
                     }
                 }
+                if (tid == 0)
+                    s_zhist[k] = Z;
+                ++k;
+                __syncthreads();   // s_zhist, s_mass visible
             }
             if (!alive)
                 break;
@@ -410,72 +498,55 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 continue;
 
             // ---- 4. inverse-CDF draw from the final distribution at u ---------
-            double mass = 0.0;
-#pragma unroll
-            for (int e = 0; e < kSvEpt; ++e)
-                mass += pr[e];
-            mass = block_sum(mass, s_red);
-            double *slot = xch + ((int64_t)parity * a.wpg + rank) * 4;
-            if (tid == 0)
-                xch_put(slot, mass);
-            if (!group_barrier(cnt, gen, members, a.flags, &s_ok)) {
-                alive = false;
-                break;
-            }
+            // Member w's interval is [before_w, before_w + mass_w) with the
+            // masses summed in member order, identically in every workgroup.
             if (tid == 0) {
-                const double *all = xch + (int64_t)parity * a.wpg * 4;
-                double before = 0.0, run = 0.0;
-                for (int w = 0; w < a.wpg; ++w) {
+                double run = 0.0, before = 0.0;
+                for (int w = 0; w < wpg; ++w) {
                     if (w == rank)
                         before = run;
-                    run += xch_get(all + w * 4);
+                    run += s_mass[w];
                 }
-                s_stats[0] = before;
-                s_stats[1] = run;   // total mass
+                s_red[0] = before;
+                s_red[1] = run;
                 s_found = -1;
                 s_last_live = -1;
+                s_hit = -1;
             }
-            parity ^= 1;
             __syncthreads();
-            const double before = s_stats[0], total = s_stats[1];
+            const double before = s_red[0], total = s_red[1];
+            const double mass = s_mass[rank];
             const double target = node_uniforms(a.seed, a.offset, b, u).res * total;
-            // this workgroup's interval is [before, before + mass) in the same
-            // summation order the total used
-            const double after = before + mass;
+            __syncthreads();
             if (!(total > 0.0)) {
                 if (lead)
                     raise_flag(a.flags, TAV_FLAG_NONFINITE_LOGITS);
                 failed = true;
                 break;
             }
-            if (mass > 0.0 && before <= target && target < after) {
+            if (mass > 0.0 && before <= target && target < before + mass) {
                 // element e of thread t is token base + e*256 + t, so token order
                 // is (e, wave, lane). Totals of every (e, wave) slot first, in
                 // that order; then the one wave holding the target scans its lanes.
                 const int lane = tid & 63, wave = tid >> 6;
-                double *slot_tot = s_slot;     // [kSvEpt][kSvWaves]
 #pragma unroll
                 for (int e = 0; e < kSvEpt; ++e) {
                     const double t = wave_sum_ordered(pr[e]);
                     if (lane == 0)
-                        slot_tot[e * kSvWaves + wave] = t;
+                        s_slot[e * kSvWaves + wave] = t;
                 }
                 __syncthreads();
                 if (tid == 0) {
                     double run = before;
-                    int hit = -1;
-                    double hit_off = 0.0;
                     for (int k2 = 0; k2 < kSvEpt * kSvWaves; ++k2) {
-                        const double nxt = run + slot_tot[k2];
-                        if (slot_tot[k2] > 0.0 && run <= target && target < nxt) {
-                            hit = k2;
-                            hit_off = run;
+                        const double nxt = run + s_slot[k2];
+                        if (s_slot[k2] > 0.0 && run <= target && target < nxt) {
+                            s_hit = k2;
+                            s_hit_off = run;
                             break;
                         }
                         run = nxt;
                     }
-                    s_hit = hit;
-                    s_stats[2] = hit_off;
                 }
                 __syncthreads();
                 const int hit = s_hit;
@@ -496,8 +567,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     double excl = __shfl_up(incl, 1);
                     if (lane == 0)
                         excl = 0.0;
-                    const double off = s_stats[2];
-                    const double lo = off + excl, hi = off + incl;
+                    const double lo = s_hit_off + excl, hi = s_hit_off + incl;
                     const int64_t idx = base + (int64_t)e_hit * kSvThreads + tid;
                     if (v > 0.0) {
                         atomicMax(&s_last_live, (int)idx);
@@ -505,7 +575,8 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                             s_found = (int)idx;   // at most one lane qualifies
                     }
                 }
-                // rounding left the target past the last live token: take that token
+                // rounding left the target past the chunk's summed slots: the
+                // chunk's last live token takes it
                 if (hit < 0) {
 #pragma unroll
                     for (int e = 0; e < kSvEpt; ++e)
@@ -513,9 +584,6 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                             atomicMax(&s_last_live, (int)(base + (int64_t)e * kSvThreads + tid));
                 }
                 __syncthreads();
-                // the lane intervals of the hit slot partition its total exactly
-                // (same scan), so s_found is set unless rounding put the target
-                // past the chunk's summed slots; then the last live token wins
                 if (tid == 0)
                     a.out_tok[rowbase + nacc] = s_found >= 0 ? s_found : s_last_live;
             }
@@ -540,18 +608,29 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             }
         }
     }
-}
 
-__global__ void zero_words_kernel(uint32_t *p, int64_t n)
-{
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = 0u;
+    // ---- exit: the last workgroup out clears every generation word ----------
+    // Each workgroup counts itself out only after its last poll, so the last
+    // one knows no slot is still being read.
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t out =
+            __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_is_last = out == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (s_is_last) {
+        const int64_t words = (int64_t)a.ngroups * 2 * wpg * kSlotWords;
+        for (int64_t i = tid; i < words; i += kSvThreads)
+            __hip_atomic_store(a.box + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0)
+            __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 struct SvPlan {
     int wpg, ngroups, chunk;
-    size_t xch_bytes, sync_bytes;
+    size_t box_bytes;
 };
 
 bool sv_plan(int32_t B, int32_t V, SvPlan &p)
@@ -566,16 +645,13 @@ bool sv_plan(int32_t B, int32_t V, SvPlan &p)
         return false;
     const int64_t resident = (int64_t)per_cu * cus;
     p.wpg = (int)ceil_div(V, kSvChunk);
-    if (p.wpg > resident)
+    if (p.wpg > resident || p.wpg > kMaxWpg)
         return false;
     p.chunk = (int)ceil_div(V, p.wpg);
     p.ngroups = (int)std::min<int64_t>(B, resident / p.wpg);
-    p.xch_bytes = (size_t)p.ngroups * 2 * p.wpg * 4 * sizeof(double);
-    p.sync_bytes = (size_t)p.ngroups * kSyncStride * sizeof(uint32_t);
+    p.box_bytes = (size_t)p.ngroups * 2 * p.wpg * kSlotWords * sizeof(uint64_t);
     return true;
 }
-
-size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ---------------------------------------------------------------------------
 // Diagnostics: the uniforms and the device softmax, exposed for checking.
@@ -595,21 +671,21 @@ __global__ __launch_bounds__(kSvThreads) void target_probs_kernel(const float *l
                                                                   int32_t V, double T,
                                                                   double *p, uint32_t *flags)
 {
-    __shared__ double red[kSvWaves];
+    __shared__ double red[2 * kSvWaves];
     const float *row = logits + (int64_t)blockIdx.x * V;
     double *out = p + (int64_t)blockIdx.x * V;
-    double m = -INFINITY;
+    double m = -INFINITY, unused = -INFINITY;
     bool nan_seen = false;
     for (int x = threadIdx.x; x < V; x += kSvThreads) {
         const double v = (double)row[x] / T;
         nan_seen |= __builtin_isnan(v);
         m = fmax(m, v);
     }
-    m = block_max(m, red);
-    double z = 0.0;
+    block_max2(m, unused, red);
+    double z = 0.0, unused2 = 0.0;
     for (int x = threadIdx.x; x < V; x += kSvThreads)
         z += exp((double)row[x] / T - m);
-    z = block_sum(z, red);
+    block_sum2(z, unused2, red);
     if (__syncthreads_or(nan_seen) || m == -INFINITY || __builtin_isinf(m)) {
         if (threadIdx.x == 0)
             raise_flag(flags, TAV_FLAG_NONFINITE_LOGITS);
@@ -625,12 +701,12 @@ __global__ __launch_bounds__(kSvThreads) void target_probs_kernel(const float *l
 extern "C" size_t spec_verify_workspace_bytes(int32_t B, int32_t N, int32_t V)
 {
     using namespace tav;
-    if (B < 1 || N < 1 || N > kMaxNodes || V < 1 || V > (1 << 24))
+    if (B < 1 || N < 1 || N > kMaxNodes || V < 1 || V > kMaxVocab)
         return 0;
     SvPlan p;
     if (!sv_plan(B, V, p))
         return 0;
-    return round_up(p.xch_bytes, 256) + round_up(p.sync_bytes, 256);
+    return kHeaderBytes + p.box_bytes;
 }
 
 extern "C" tav_status spec_verify_sample(const float *target_logits, const float *draft_logits,
@@ -646,14 +722,14 @@ extern "C" tav_status spec_verify_sample(const float *target_logits, const float
         return TAV_ERR_ARG;
     if (B < 1 || N < 1 || V < 1 || !(temperature > 0.0) || !(temperature < INFINITY))
         return TAV_ERR_ARG;
-    if (N > kMaxNodes || V > (1 << 24))
+    if (N > kMaxNodes || V > kMaxVocab)
         return TAV_ERR_UNSUPPORTED;
     if (!aligned(target_logits, 4) || !aligned(draft_logits, 4))
         return TAV_ERR_ARG;
     SvPlan p;
     if (!sv_plan(B, V, p))
         return TAV_ERR_LAUNCH;
-    const size_t need = round_up(p.xch_bytes, 256) + round_up(p.sync_bytes, 256);
+    const size_t need = kHeaderBytes + p.box_bytes;
     if (!workspace || ws_bytes < need || !aligned(workspace, 256))
         return TAV_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);
@@ -671,22 +747,17 @@ extern "C" tav_status spec_verify_sample(const float *target_logits, const float
     a.path = path;
     a.n_acc = n_accepted;
     a.out_tok = out_tokens;
-    a.xch = reinterpret_cast<double *>(ws);
-    a.sync = reinterpret_cast<uint32_t *>(ws + round_up(p.xch_bytes, 256));
+    a.done = reinterpret_cast<uint32_t *>(ws);
+    a.box = reinterpret_cast<uint64_t *>(ws + kHeaderBytes);
     a.flags = dev_flags;
     a.wpg = p.wpg;
     a.ngroups = p.ngroups;
     a.chunk = p.chunk;
-    hipStream_t s = as_stream(stream);
-    const int64_t words = (int64_t)p.ngroups * kSyncStride;
-    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(words, 256), 64)),
-                       dim3(256), 0, s, a.sync, words);
-    if (hipGetLastError() != hipSuccess)
-        return TAV_ERR_LAUNCH;
     void *args[] = {&a};
     const hipError_t err =
         hipLaunchCooperativeKernel(reinterpret_cast<const void *>(spec_verify_kernel),
-                                   dim3(p.wpg * p.ngroups), dim3(kSvThreads), args, 0, s);
+                                   dim3(p.wpg * p.ngroups), dim3(kSvThreads), args, 0,
+                                   as_stream(stream));
     return err == hipSuccess ? TAV_OK : TAV_ERR_LAUNCH;
 }
 
