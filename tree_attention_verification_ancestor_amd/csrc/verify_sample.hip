@@ -12,17 +12,19 @@
 //
 // Layout of the work. A "group" of wpg workgroups owns one sequence at a
 // time; workgroup r of the group owns vocabulary entries
-// [r*chunk, (r+1)*chunk) and keeps them in registers (16 per thread), so
-// every pass over a row after the first is register-resident. The walk is
-// serial; for each visited node u the group
-//   1. loads its chunk of target row u (and draft row u if u has children)
+// [r*chunk, (r+1)*chunk) and keeps them in registers (8 per thread, 512
+// threads), so every pass over a row after the first is register-resident.
+// The walk is serial; for each visited node u the group
+//   1. takes its chunk of target row u (and draft row u if u has children)
 //      and the logits of u's children's tokens, reduces a local
 //      (max, sum exp) per row and exchanges it (one group sync). Every
 //      workgroup merges the wpg pairs in the same order, so all hold
 //      bit-identical normalisers and per-chunk masses;
 //   2. tests the children in order. p(x), q(x) and the residual at x are
 //      recomputed from the logits at x with the same instructions in every
-//      workgroup, so every workgroup takes the same decision;
+//      workgroup, so every workgroup takes the same decision. Meanwhile the
+//      rows of u's first child, the likeliest next node, are already being
+//      fetched, so a walk down first children never waits on memory;
 //   3. after each rejection exchanges the chunk sums of max(0, p_res - q)
 //      (one group sync), which give the new normaliser and the new chunk
 //      masses, and updates its registers;
@@ -39,11 +41,17 @@
 // acknowledged before another: a reader polls a member's words (one lane per
 // member) until every one carries the current generation. Two parities
 // suffice: a member can only reuse a slot after every member has arrived at
-// the sync in between, i.e. after everyone has read it. Every wait is
-// bounded: on expiry the kernel raises TAV_FLAG_SYNC_TIMEOUT and the
-// workgroup stops, so every wave exits. The launch is cooperative, which
-// guarantees all workgroups are resident. The last workgroup to finish clears
-// every slot, so each call leaves the workspace as it found it (zero-filled).
+// the sync in between, i.e. after everyone has read it. The grid never
+// exceeds what the device holds resident at once (from the occupancy query),
+// and every wait is bounded: on expiry the kernel raises
+// TAV_FLAG_SYNC_TIMEOUT and the workgroup stops, so every wave exits even on
+// a device shared with other work. The last workgroup to finish clears every
+// slot, so each call leaves the workspace as it found it (zero-filled).
+//
+// exp. Every exponential is exp_f64 below: a 64-entry table of 2^(j/64) and
+// a degree-6 polynomial on |r| <= ln2/128 (a few ulp), about a third of the
+// instructions of the general-purpose routine, which matters because the
+// stats pass takes one exp per vocabulary entry and row.
 
 #include <algorithm>
 
@@ -53,16 +61,17 @@
 namespace tav {
 namespace {
 
-constexpr int kSvThreads = 256;
+constexpr int kSvThreads = 512;
 constexpr int kSvWaves = kSvThreads / 64;
-constexpr int kSvEpt = 16;                      // vocabulary entries per thread
+constexpr int kSvEpt = 8;                       // vocabulary entries per thread
 constexpr int kSvChunk = kSvThreads * kSvEpt;   // per workgroup
-constexpr int kMaxWpg = 512;                    // workgroups per sequence
-constexpr int kSlotsPerThread = kMaxWpg / kSvThreads;
-constexpr int64_t kMaxVocab = (int64_t)kSvChunk * kMaxWpg;   // 2^21
+constexpr int kMaxWpg = kSvThreads;             // workgroups per sequence (one slot per thread)
+constexpr int64_t kMaxVocab = (int64_t)1 << 21;
 constexpr uint32_t kSpinLimit = 1u << 20;       // polls before a wait gives up
 constexpr int kSlotWords = 8;                   // 64-byte slot of tagged 64-bit words
 constexpr size_t kHeaderBytes = 256;            // exit counter
+
+static_assert(kMaxVocab <= (int64_t)kSvChunk * kMaxWpg, "vocabulary limit");
 
 struct SvArgs {
     const float *tl;
@@ -81,20 +90,87 @@ struct SvArgs {
     int32_t wpg, ngroups, chunk;
 };
 
+// ---------------------------------------------------------------------------
+// exp in float64: x = (n/64) ln2 + r, exp(x) = 2^(n>>6) * 2^((n&63)/64) * e^r.
+
+struct ExpTable {
+    double t[64];   // 2^(j/64)
+};
+
+__device__ __forceinline__ double exp_f64(double x, const ExpTable &T)
+{
+    if (x < -746.0)
+        return 0.0;   // below the smallest subnormal (also x = -inf); NaN falls through
+    constexpr double kScale = 0x1.71547652b82fep+6;        // 64 / ln 2
+    constexpr double kLn2Hi = 0x1.62e42fee00000p-1 / 64.0;  // ln 2 / 64, high part (exact n*hi)
+    constexpr double kLn2Lo = 0x1.a39ef35793c76p-33 / 64.0; // ln 2 / 64, low part
+    constexpr double kRound = 0x1.8p52;
+    x = fmin(x, 709.0);
+    const double nd = (x * kScale + kRound) - kRound;        // nearest integer to 64x/ln2
+    const int n = (int)nd;
+    double r = fma(-nd, kLn2Hi, x);
+    r = fma(-nd, kLn2Lo, r);
+    // e^r - 1 = r + r^2 (1/2 + r (1/6 + r (1/24 + r (1/120 + r/720))))
+    double p = fma(r, 1.0 / 720.0, 1.0 / 120.0);
+    p = fma(r, p, 1.0 / 24.0);
+    p = fma(r, p, 1.0 / 6.0);
+    p = fma(r, p, 0.5);
+    p = fma(r * r, p, r);
+    const double t = T.t[n & 63];
+    return ldexp(fma(t, p, t), n >> 6);
+}
+
+__device__ void exp_table_init(ExpTable &T)
+{
+    if (threadIdx.x < 64)
+        T.t[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+}
+
+// ---------------------------------------------------------------------------
+// Reductions. Within a wave: DPP butterflies inside each 16-lane row, then
+// the four row totals read out and combined in a fixed order, so every lane
+// holds the same bits. Across the workgroup: the waves' totals in index order.
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF,
+                                                              false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL,
+                                                              0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double lane_f64(double v, int lane)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+constexpr int kQuadSwap1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
 __device__ __forceinline__ double wave_sum(double v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v += __shfl_xor(v, o);
-    return v;
+    v += dpp_f64<kQuadSwap1>(v);
+    v += dpp_f64<kQuadSwap2>(v);
+    v += dpp_f64<kRowHalfMirror>(v);
+    v += dpp_f64<kRowMirror>(v);
+    return (lane_f64(v, 0) + lane_f64(v, 16)) + (lane_f64(v, 32) + lane_f64(v, 48));
 }
 
 __device__ __forceinline__ double wave_max(double v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v = fmax(v, __shfl_xor(v, o));
-    return v;
+    v = fmax(v, dpp_f64<kQuadSwap1>(v));
+    v = fmax(v, dpp_f64<kQuadSwap2>(v));
+    v = fmax(v, dpp_f64<kRowHalfMirror>(v));
+    v = fmax(v, dpp_f64<kRowMirror>(v));
+    return fmax(fmax(lane_f64(v, 0), lane_f64(v, 16)), fmax(lane_f64(v, 32), lane_f64(v, 48)));
 }
 
 // Sum over the wave in lane order (an inclusive scan's last value).
@@ -110,8 +186,7 @@ __device__ __forceinline__ double wave_sum_ordered(double v)
 }
 
 // Workgroup-wide reductions of two values at once; every thread gets the
-// results. Waves combine in index order, so the result depends only on the
-// inputs, never on timing. `red` holds 2 * kSvWaves doubles.
+// results. `red` holds 2 * kSvWaves doubles.
 __device__ void block_sum2(double &a, double &b, double *red)
 {
     a = wave_sum(a);
@@ -152,20 +227,28 @@ __device__ void block_max2(double &a, double &b, double *red)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Group sync.
+
 __device__ __forceinline__ uint64_t tag_word(uint32_t gen, uint32_t payload)
 {
     return ((uint64_t)gen << 32) | payload;
 }
 
-// One group sync. Threads 0..NW-1 publish word i = mine[i] (32 payload bits)
-// in this workgroup's slot for generation `gen`; on return (true) thread t
-// holds the payloads of member t + k*kSvThreads in got[k][0..NW). Returns
-// false on a timeout.
+// Threads 0..NW-1 publish word i = mine[i] (32 payload bits) in this
+// workgroup's slot for generation `gen`; on return (true) thread t < wpg holds
+// member t's payloads in got[0..NW). A group of one workgroup exchanges
+// nothing. Returns false on a timeout.
 template <int NW>
 __device__ bool group_sync(uint64_t *box, int wpg, int rank, uint32_t gen,
-                           const uint32_t (&mine)[NW], uint32_t (&got)[kSlotsPerThread][NW],
-                           uint32_t *flags)
+                           const uint32_t (&mine)[NW], uint32_t (&got)[NW], uint32_t *flags)
 {
+    if (wpg == 1) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+            got[i] = mine[i];
+        return true;
+    }
     uint64_t *base = box + (size_t)(gen & 1u) * wpg * kSlotWords;
     __syncthreads();
     if (threadIdx.x < NW) {
@@ -179,33 +262,28 @@ __device__ bool group_sync(uint64_t *box, int wpg, int rank, uint32_t gen,
     }
     bool ok = true;
 #pragma unroll
-    for (int k = 0; k < kSlotsPerThread; ++k) {
-        const int w = threadIdx.x + k * kSvThreads;
+    for (int i = 0; i < NW; ++i)
+        got[i] = 0u;
+    if ((int)threadIdx.x < wpg) {
+        uint64_t *slot = base + (size_t)threadIdx.x * kSlotWords;
+        uint32_t polls = 0;
+        for (;;) {
+            uint64_t word[NW];
 #pragma unroll
-        for (int i = 0; i < NW; ++i)
-            got[k][i] = 0u;
-        if (w < wpg && ok) {
-            uint64_t *slot = base + (size_t)w * kSlotWords;
-            uint32_t polls = 0;
-            for (;;) {
-                uint64_t word[NW];
+            for (int i = 0; i < NW; ++i)
+                word[i] = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            bool all = true;
 #pragma unroll
-                for (int i = 0; i < NW; ++i)
-                    word[i] = __hip_atomic_load(slot + i, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-                bool all = true;
-#pragma unroll
-                for (int i = 0; i < NW; ++i) {
-                    all &= (uint32_t)(word[i] >> 32) == gen;
-                    got[k][i] = (uint32_t)word[i];
-                }
-                if (all)
-                    break;
-                __builtin_amdgcn_s_sleep(1);
-                if (++polls > kSpinLimit) {
-                    ok = false;
-                    break;
-                }
+            for (int i = 0; i < NW; ++i) {
+                all &= (uint32_t)(word[i] >> 32) == gen;
+                got[i] = (uint32_t)word[i];
+            }
+            if (all)
+                break;
+            __builtin_amdgcn_s_sleep(1);
+            if (++polls > kSpinLimit) {
+                ok = false;
+                break;
             }
         }
     }
@@ -227,8 +305,11 @@ __device__ __forceinline__ double bits_f64(uint32_t hi, uint32_t lo)
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
+// ---------------------------------------------------------------------------
+
 __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
 {
+    __shared__ ExpTable s_exp;
     __shared__ int32_t s_par[kMaxNodes];
     __shared__ int32_t s_first[kMaxNodes];
     __shared__ int32_t s_next[kMaxNodes];
@@ -257,6 +338,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
     const double invT = 1.0 / a.T;
     uint32_t gen = 0;
     bool alive = true;
+    exp_table_init(s_exp);
 
     for (int b = g; b < a.B && alive; b += a.ngroups) {
         const int64_t rowbase = (int64_t)b * N;
@@ -264,38 +346,32 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
         __syncthreads();
         if (tid == 0)
             s_bad = 0;
-        for (int i = tid; i < N; i += kSvThreads) {
-            s_par[i] = a.parent[rowbase + i];
-            s_tok[i] = a.token[rowbase + i];
-            s_first[i] = N;
-            s_next[i] = -1;
+        if (tid < N) {
+            s_par[tid] = a.parent[rowbase + tid];
+            s_tok[tid] = a.token[rowbase + tid];
+            s_first[tid] = N;
+            s_next[tid] = -1;
         }
         __syncthreads();
-        for (int i = tid; i < N; i += kSvThreads) {
-            const int p = s_par[i];
-            if (i == 0 ? p != -1 : (p < 0 || p >= i))
+        if (tid < N) {
+            const int p = s_par[tid];
+            if (tid == 0 ? p != -1 : (p < 0 || p >= tid))
                 atomicOr(&s_bad, 1);
-            if (i > 0) {
-                const int x = s_tok[i];
-                if (x < 0 || x >= a.V)
-                    atomicOr(&s_bad, 2);
-            }
+            if (tid > 0 && (s_tok[tid] < 0 || s_tok[tid] >= a.V))
+                atomicOr(&s_bad, 2);
         }
         __syncthreads();
-        if (s_bad == 0) {
-            for (int c = 1 + tid; c < N; c += kSvThreads) {
-                atomicMin(&s_first[s_par[c]], c);
-                for (int c2 = c + 1; c2 < N; ++c2)
-                    if (s_par[c2] == s_par[c]) {
-                        s_next[c] = c2;
-                        break;
-                    }
-            }
+        if (s_bad == 0 && tid >= 1 && tid < N) {
+            atomicMin(&s_first[s_par[tid]], tid);
+            for (int c2 = tid + 1; c2 < N; ++c2)
+                if (s_par[c2] == s_par[tid]) {
+                    s_next[tid] = c2;
+                    break;
+                }
         }
         __syncthreads();
-        for (int i = tid; i < N; i += kSvThreads)
-            if (s_first[i] == N)
-                s_first[i] = -1;
+        if (tid < N && s_first[tid] == N)
+            s_first[tid] = -1;
         __syncthreads();
 
         const bool lead = rank == 0 && tid == 0;
@@ -305,6 +381,11 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             raise_flag(a.flags, (s_bad & 1 ? TAV_FLAG_BAD_PARENT : 0u) |
                                     (s_bad & 2 ? TAV_FLAG_BAD_TOKEN : 0u));
 
+        // rows of the likeliest next node, fetched a level ahead
+        int pf_node = -1;
+        float pf_t[kSvEpt], pf_d[kSvEpt];
+        float pf_tx = 0.f, pf_dx = 0.f;   // logits of child `tid` of pf_node, if any
+
         int u = 0;
         while (!failed) {
             const float *trow = a.tl + (rowbase + u) * a.V;
@@ -312,26 +393,35 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             const bool has_kids = s_first[u] >= 0;
 
             // ---- 1. local (max, sum exp) of target and draft rows ------------
-            // chunk loads first, then the logits of u's children's tokens, so
-            // all of them are in flight together
             float tf[kSvEpt], df[kSvEpt];
+            if (pf_node == u) {
 #pragma unroll
-            for (int e = 0; e < kSvEpt; ++e) {
-                const int64_t idx = base + (int64_t)e * kSvThreads + tid;
-                tf[e] = -INFINITY;
-                df[e] = -INFINITY;
-                if (idx < lim) {
-                    tf[e] = trow[idx];
-                    if (has_kids)
-                        df[e] = drow[idx];
+                for (int e = 0; e < kSvEpt; ++e) {
+                    tf[e] = pf_t[e];
+                    df[e] = has_kids ? pf_d[e] : -INFINITY;
+                }
+                if (tid < N && s_par[tid] == u) {
+                    s_tx[tid] = pf_tx;
+                    s_dx[tid] = pf_dx;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < kSvEpt; ++e) {
+                    const int64_t idx = base + (int64_t)e * kSvThreads + tid;
+                    tf[e] = -INFINITY;
+                    df[e] = -INFINITY;
+                    if (idx < lim) {
+                        tf[e] = trow[idx];
+                        if (has_kids)
+                            df[e] = drow[idx];
+                    }
+                }
+                if (tid < N && s_par[tid] == u) {
+                    const int x = s_tok[tid];
+                    s_tx[tid] = trow[x];
+                    s_dx[tid] = drow[x];
                 }
             }
-            for (int c = u + 1 + tid; c < N; c += kSvThreads)
-                if (s_par[c] == u) {
-                    const int x = s_tok[c];
-                    s_tx[c] = trow[x];
-                    s_dx[c] = drow[x];
-                }
             // maxima of the raw fp32 logits (exact); x -> x/T is monotone
             bool nan_seen = false;
             double mt_d = -INFINITY, mq_d = -INFINITY;
@@ -348,8 +438,8 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             double zt = 0.0, zq = 0.0;
 #pragma unroll
             for (int e = 0; e < kSvEpt; ++e) {
-                pr[e] = (mt_raw == -INFINITY) ? 0.0 : exp((double)tf[e] * invT - mts);
-                qv[e] = (mq_raw == -INFINITY) ? 0.0 : exp((double)df[e] * invT - mqs);
+                pr[e] = (mt_raw == -INFINITY) ? 0.0 : exp_f64((double)tf[e] * invT - mts, s_exp);
+                qv[e] = (mq_raw == -INFINITY) ? 0.0 : exp_f64((double)df[e] * invT - mqs, s_exp);
                 zt += pr[e];
                 zq += qv[e];
             }
@@ -357,43 +447,57 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             if (__syncthreads_or(nan_seen))
                 zt = NAN;
 
-            double got[kSlotsPerThread][4];
+            // the first child's rows and its children's logits, for the next level
+            if (has_kids) {
+                const int c1 = s_first[u];
+                pf_node = c1;
+                const float *t1 = a.tl + (rowbase + c1) * a.V;
+                const float *d1 = a.dl + (rowbase + c1) * a.V;
+                const bool c1_kids = s_first[c1] >= 0;
+#pragma unroll
+                for (int e = 0; e < kSvEpt; ++e) {
+                    const int64_t idx = base + (int64_t)e * kSvThreads + tid;
+                    pf_t[e] = -INFINITY;
+                    pf_d[e] = -INFINITY;
+                    if (idx < lim) {
+                        pf_t[e] = t1[idx];
+                        if (c1_kids)
+                            pf_d[e] = d1[idx];
+                    }
+                }
+                if (tid < N && s_par[tid] == c1) {
+                    const int x = s_tok[tid];
+                    pf_tx = t1[x];
+                    pf_dx = d1[x];
+                }
+            }
+
+            double m_got = -INFINITY, z_got = 0.0, mq_got = -INFINITY, zq_got = 0.0;
             {
                 const uint32_t mine[6] = {f32_bits(mt_raw), f64_hi(zt), f64_lo(zt),
                                           f32_bits(mq_raw), f64_hi(zq), f64_lo(zq)};
-                uint32_t words[kSlotsPerThread][6];
+                uint32_t words[6];
                 if (!group_sync<6>(box, wpg, rank, ++gen, mine, words, a.flags)) {
                     alive = false;
                     break;
                 }
-#pragma unroll
-                for (int k = 0; k < kSlotsPerThread; ++k) {
-                    got[k][0] = (double)bits_f32(words[k][0]) * invT;
-                    got[k][1] = bits_f64(words[k][1], words[k][2]);
-                    got[k][2] = (double)bits_f32(words[k][3]) * invT;
-                    got[k][3] = bits_f64(words[k][4], words[k][5]);
+                if (tid < wpg) {
+                    m_got = (double)bits_f32(words[0]) * invT;
+                    z_got = bits_f64(words[1], words[2]);
+                    mq_got = (double)bits_f32(words[3]) * invT;
+                    zq_got = bits_f64(words[4], words[5]);
                 }
             }
-            // merge the members' (max, sum) pairs: per thread over its slots,
-            // then across the workgroup, in a fixed order
-            double Mp = -INFINITY, Mq = -INFINITY;
-#pragma unroll
-            for (int k = 0; k < kSlotsPerThread; ++k)
-                if (tid + k * kSvThreads < wpg) {
-                    Mp = fmax(Mp, got[k][0]);
-                    Mq = fmax(Mq, got[k][2]);
-                }
+            // merge the members' (max, sum) pairs in a fixed order
+            double Mp = m_got, Mq = mq_got;
             block_max2(Mp, Mq, s_red);
-            double Zp = 0.0, Zq = 0.0;
-#pragma unroll
-            for (int k = 0; k < kSlotsPerThread; ++k)
-                if (tid + k * kSvThreads < wpg) {
-                    const double m1 = got[k][0], z1 = got[k][1];
-                    const double m2 = got[k][2], z2 = got[k][3];
-                    // a NaN sum travels through; an empty chunk adds nothing
-                    Zp += (m1 == -INFINITY) ? (z1 != z1 ? z1 : 0.0) : z1 * exp(m1 - Mp);
-                    Zq += (m2 == -INFINITY) ? 0.0 : z2 * exp(m2 - Mq);
-                }
+            double em = 0.0, Zp = 0.0, Zq = 0.0;
+            if (tid < wpg) {
+                em = (m_got == -INFINITY) ? 0.0 : exp_f64(m_got - Mp, s_exp);
+                // a NaN sum travels through; an empty chunk adds nothing
+                Zp = (m_got == -INFINITY) ? (z_got != z_got ? z_got : 0.0) : z_got * em;
+                Zq = (mq_got == -INFINITY) ? 0.0 : zq_got * exp_f64(mq_got - Mq, s_exp);
+            }
             block_sum2(Zp, Zq, s_red);
             const bool bad_p = !(Zp > 0.0) || Mp == -INFINITY || __builtin_isinf(Mp) ||
                                __builtin_isnan(Zp) || __builtin_isinf(Zp);
@@ -406,15 +510,11 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 break;
             }
             // chunk masses of p, and p and q of this chunk in registers
-#pragma unroll
-            for (int k = 0; k < kSlotsPerThread; ++k) {
-                const int w = tid + k * kSvThreads;
-                if (w < wpg)
-                    s_mass[w] = (got[k][0] == -INFINITY) ? 0.0 : got[k][1] * exp(got[k][0] - Mp) / Zp;
-            }
+            if (tid < wpg)
+                s_mass[tid] = z_got * em / Zp;
             {
-                const double sp = (mt_raw == -INFINITY) ? 0.0 : exp(mts - Mp) / Zp;
-                const double sq = (mq_raw == -INFINITY) ? 0.0 : exp(mqs - Mq) / Zq;
+                const double sp = (mt_raw == -INFINITY) ? 0.0 : exp_f64(mts - Mp, s_exp) / Zp;
+                const double sq = (mq_raw == -INFINITY) ? 0.0 : exp_f64(mqs - Mq, s_exp) / Zq;
 #pragma unroll
                 for (int e = 0; e < kSvEpt; ++e) {
                     pr[e] *= sp;
@@ -428,8 +528,8 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             bool accepted = false;
             for (int c = s_first[u]; c >= 0; c = s_next[c]) {
                 const int x = s_tok[c];
-                const double px = exp((double)s_tx[c] * invT - Mp) / Zp;
-                const double qx = exp((double)s_dx[c] * invT - Mq) / Zq;
+                const double px = exp_f64((double)s_tx[c] * invT - Mp, s_exp) / Zp;
+                const double qx = exp_f64((double)s_dx[c] * invT - Mq, s_exp) / Zq;
                 double prx = px;
                 for (int j = 0; j < k; ++j) {
                     const double zj = s_zhist[j];
@@ -457,34 +557,27 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     s += d > 0.0 ? d : 0.0;
                 }
                 block_sum2(s, unused, s_red);
-                double rs[kSlotsPerThread][1];
+                double rs = 0.0;
                 {
                     const uint32_t mine[2] = {f64_hi(s), f64_lo(s)};
-                    uint32_t words[kSlotsPerThread][2];
+                    uint32_t words[2];
                     if (!group_sync<2>(box, wpg, rank, ++gen, mine, words, a.flags)) {
                         alive = false;
                         break;
                     }
-#pragma unroll
-                    for (int kk = 0; kk < kSlotsPerThread; ++kk)
-                        rs[kk][0] = bits_f64(words[kk][0], words[kk][1]);
+                    if (tid < wpg)
+                        rs = bits_f64(words[0], words[1]);
                 }
-                double Z = 0.0, unused2 = 0.0;
-#pragma unroll
-                for (int kk = 0; kk < kSlotsPerThread; ++kk)
-                    Z += rs[kk][0];
+                double Z = rs, unused2 = 0.0;
                 block_sum2(Z, unused2, s_red);
                 if (Z > 0.0) {
-#pragma unroll
-                    for (int kk = 0; kk < kSlotsPerThread; ++kk) {
-                        const int w = tid + kk * kSvThreads;
-                        if (w < wpg)
-                            s_mass[w] = rs[kk][0] / Z;
-                    }
+                    if (tid < wpg)
+                        s_mass[tid] = rs / Z;
+                    const double inv = 1.0 / Z;
 #pragma unroll
                     for (int e = 0; e < kSvEpt; ++e) {
                         const double d = pr[e] - qv[e];
-                        pr[e] = (d > 0.0 ? d : 0.0) / Z;
+                        pr[e] = (d > 0.0 ? d : 0.0) * inv;
                     }
                 }
                 if (tid == 0)
@@ -525,9 +618,10 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 break;
             }
             if (mass > 0.0 && before <= target && target < before + mass) {
-                // element e of thread t is token base + e*256 + t, so token order
-                // is (e, wave, lane). Totals of every (e, wave) slot first, in
-                // that order; then the one wave holding the target scans its lanes.
+                // element e of thread t is token base + e*512 + t, so token
+                // order is (e, wave, lane). Totals of every (e, wave) slot
+                // first, in that order; then the one wave holding the target
+                // scans its lanes.
                 const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
                 for (int e = 0; e < kSvEpt; ++e) {
@@ -609,7 +703,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
         }
     }
 
-    // ---- exit: the last workgroup out clears every generation word ----------
+    // ---- exit: the last workgroup out clears every mailbox word -------------
     // Each workgroup counts itself out only after its last poll, so the last
     // one knows no slot is still being read.
     __syncthreads();
@@ -667,24 +761,28 @@ __global__ void philox_uniforms_kernel(uint64_t seed, uint64_t offset, int32_t B
     u[2 * i + 1] = (float)r.res;
 }
 
+// One row per workgroup, with the sampler's scaling, maximum and exp.
 __global__ __launch_bounds__(kSvThreads) void target_probs_kernel(const float *logits,
                                                                   int32_t V, double T,
                                                                   double *p, uint32_t *flags)
 {
+    __shared__ ExpTable s_exp;
     __shared__ double red[2 * kSvWaves];
+    exp_table_init(s_exp);
     const float *row = logits + (int64_t)blockIdx.x * V;
     double *out = p + (int64_t)blockIdx.x * V;
+    const double invT = 1.0 / T;
     double m = -INFINITY, unused = -INFINITY;
     bool nan_seen = false;
     for (int x = threadIdx.x; x < V; x += kSvThreads) {
-        const double v = (double)row[x] / T;
-        nan_seen |= __builtin_isnan(v);
-        m = fmax(m, v);
+        nan_seen |= __builtin_isnan(row[x]);
+        m = fmax(m, (double)row[x]);
     }
     block_max2(m, unused, red);
+    const double ms = (double)(float)m * invT;
     double z = 0.0, unused2 = 0.0;
     for (int x = threadIdx.x; x < V; x += kSvThreads)
-        z += exp((double)row[x] / T - m);
+        z += exp_f64((double)row[x] * invT - ms, s_exp);
     block_sum2(z, unused2, red);
     if (__syncthreads_or(nan_seen) || m == -INFINITY || __builtin_isinf(m)) {
         if (threadIdx.x == 0)
@@ -692,7 +790,7 @@ __global__ __launch_bounds__(kSvThreads) void target_probs_kernel(const float *l
         return;
     }
     for (int x = threadIdx.x; x < V; x += kSvThreads)
-        out[x] = exp((double)row[x] / T - m) / z;
+        out[x] = exp_f64((double)row[x] * invT - ms, s_exp) / z;
 }
 
 } // namespace
@@ -753,12 +851,9 @@ extern "C" tav_status spec_verify_sample(const float *target_logits, const float
     a.wpg = p.wpg;
     a.ngroups = p.ngroups;
     a.chunk = p.chunk;
-    void *args[] = {&a};
-    const hipError_t err =
-        hipLaunchCooperativeKernel(reinterpret_cast<const void *>(spec_verify_kernel),
-                                   dim3(p.wpg * p.ngroups), dim3(kSvThreads), args, 0,
-                                   as_stream(stream));
-    return err == hipSuccess ? TAV_OK : TAV_ERR_LAUNCH;
+    hipLaunchKernelGGL(spec_verify_kernel, dim3(p.wpg * p.ngroups), dim3(kSvThreads), 0,
+                       as_stream(stream), a);
+    return hipGetLastError() == hipSuccess ? TAV_OK : TAV_ERR_LAUNCH;
 }
 
 extern "C" tav_status tav_philox_uniforms(uint64_t seed, uint64_t offset, int32_t B, int32_t N,
