@@ -28,6 +28,8 @@ CASES = [
     dict(N=256, B=1, Hq=2, Hkv=1, D=128, L=(3000, 3000), tree="random"),   # 4 tree tiles, split-K
     dict(N=16, B=4, Hq=32, Hkv=8, D=128, L=(2047, 2049), tree="random"),
     dict(N=6, B=3, Hq=32, Hkv=8, D=128, L=(2048, 2048), tree="chain"),
+    dict(N=20, B=2, Hq=8, Hkv=2, D=128, L=(1000, 1100), tree="random"),    # 80 rows: 4 waves x 32
+    dict(N=48, B=1, Hq=64, Hkv=8, D=64, L=(513, 700), tree="random"),      # 384 rows, D=64, 2 row blocks
 ]
 
 

@@ -31,10 +31,14 @@
 //                 keeps 8, which the output tolerance needs when attention
 //                 falls on a few keys. Weights carry a 2^7 bias so small ones
 //                 stay clear of fp16 subnormals; the bias cancels in O/l.
-// Tiles are double-buffered in LDS; the next tile's global loads are issued
-// before the current tile's MFMAs. Splits of the prefix write unnormalised
-// partials (O, max, sum) that a combine kernel merges with log-sum-exp; the
-// last split also takes the tree tiles (keys masked by the ancestor bitmask).
+// Tiles are double-buffered in LDS. Prefix tiles move from HBM straight into
+// LDS (global_load_lds_dwordx4: 16 bytes per lane, no staging registers), a
+// whole tile ahead of the MFMAs that use them; one pass per tile then turns the
+// tile's V from bf16 into fp16 in place and zeroes keys past the prefix. The
+// few tree tiles go through registers (their V rows need a transpose). Splits
+// of the prefix write unnormalised partials (O, max, sum) that a combine
+// kernel merges with log-sum-exp; the last split also takes the tree tiles
+// (keys masked by the ancestor bitmask).
 
 #include <algorithm>
 
@@ -48,23 +52,23 @@ constexpr int kMaxSplitBlocks = 2048; // block-table entries one split stages in
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kWeightBias = 7.0f;  // log2 of the bias on the fp16 weights
 
-template <int D, int NW>
+template <int D, int NW, int CT>
 struct Cfg {
     static constexpr int kThreads = NW * 64;
-    static constexpr int kRows = NW * 32;
+    static constexpr int kWaveRows = CT * 32;            // query rows per wave
+    static constexpr int kRows = NW * kWaveRows;         // query rows per workgroup
     static constexpr int kKSteps = D / 16;
     static constexpr int kDTiles = D / 32;
     static constexpr int kCpr = D / 8;                   // 16-byte chunks per row
-    static constexpr int kKRow = D * 2 + 16;             // padded K row in LDS
+    static constexpr int kKRow = D * 2;                  // K row in LDS (16-byte chunks swizzled)
     static constexpr int kKTileBytes = kKT * kKRow;
     static constexpr int kVTileBytes = kKT * D * 2;
     static constexpr int kBufBytes = kKTileBytes + kVTileBytes;
-    static constexpr int kChunks = kKT * kCpr;           // 16-byte chunks per tile
+    static constexpr int kChunks = kKT * kCpr;           // 16-byte chunks per K (or V) tile
+    static constexpr int kLoadsPerWave = kChunks / 64 / NW;   // direct loads per wave per K (or V) tile
     static constexpr int kChPerThread = kChunks / kThreads;
-    // Below this many chunks per thread the next tile is prefetched into
-    // registers during the current tile's MFMAs; above it, staged directly.
-    static constexpr bool kPrefetch = kChPerThread <= 4;
     static_assert(kChunks % kThreads == 0, "tile chunks must split evenly");
+    static_assert(kLoadsPerWave * 64 * NW == kChunks, "direct loads must split evenly");
 };
 
 struct AttnArgs {
@@ -83,14 +87,56 @@ struct AttnArgs {
 // Row r of a 32-row MFMA tile holds key perm(r): bits 2 and 3 of r swapped.
 __device__ __forceinline__ int perm32(int r) { return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// LDS byte offset of chunk cc (8 features) of key k in a K tile. Keys are
-// stored in MFMA-row order (row 32t + r holds key 32t + perm32(r)), so lane r
-// of a wave reads row r, and rows are padded by 16 bytes so the 8 lanes of a
-// 128-byte LDS access hit 8 different bank groups.
+// LDS byte offset of chunk cc (8 features) of MFMA row `row` of a K tile.
+// Row 32t + r holds key 32t + perm32(r), so lane r of a wave reads row r. The
+// chunk position within a row is XOR-swizzled by k_swz(row) so the lanes that
+// one LDS cycle serves (8 or 16 for a 16-byte read) hit distinct bank groups:
+// 256-byte rows (D = 128) use the row's low four bits; 128-byte rows (D = 64)
+// pair up (rows r and r+2 share banks), so bit 3 breaks the tie of rows 8
+// apart.
+template <int D>
+__device__ __forceinline__ int k_swz(int row)
+{
+    return D == 128 ? (row & 15) : ((row & 7) ^ ((row >> 3) & 1));
+}
+
+template <int D>
+__device__ __forceinline__ int k_off_row(int row, int cc)
+{
+    return row * (D * 2) + ((cc ^ k_swz<D>(row)) << 4);
+}
+
+// The same for key k of the tile.
 template <int D>
 __device__ __forceinline__ int k_off(int k, int cc)
 {
-    return ((k & ~31) | perm32(k & 31)) * (D * 2 + 16) + (cc << 4);
+    return k_off_row<D>((k & ~31) | perm32(k & 31), cc);
+}
+
+// One direct HBM -> LDS load: lane l's 16 bytes at base + off land at LDS
+// byte address lds_addr + 16 l (lds_addr is the same for the whole wave).
+// Issued as inline assembly: the compiler then neither makes later LDS reads
+// of the other tile buffer wait for it nor reasons about what it writes; the
+// code that reads the destination waits for it explicitly with
+// lds_loads_landed().
+__device__ __forceinline__ void load_lds16(const void *base, uint32_t off, uint32_t lds_addr)
+{
+    const char *src = static_cast<const char *>(base) + off;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ object (folded at compile time).
+#define TAV_LDS_ADDR(obj) ((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)(obj))
+
+// Every direct load this workgroup issued has landed in LDS and is visible to
+// all its waves.
+__device__ __forceinline__ void lds_loads_landed()
+{
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 }
 
 // Two bf16 values (low, high half of w) to two fp16 values, round to nearest.
@@ -101,19 +147,29 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
 }
 
-// LDS byte offset of keys [8*hh, 8*hh+8) of feature d in 16-key block bi of a V tile.
+// LDS byte offset of keys [8*hh, 8*hh+8) of feature d in 16-key block bi of a
+// V tile. A feature's two halves share 32 bytes; which half comes first
+// flips with bits 2 and 3 of d, so the 8 or 16 consecutive features one LDS
+// cycle serves land in distinct bank groups.
+__device__ __forceinline__ int v_slot(int d, int hh) { return hh ^ ((d >> 2) & 1) ^ ((d >> 3) & 1); }
+
 template <int D>
 __device__ __forceinline__ int v_off(int bi, int d, int hh)
 {
-    return bi * (D * 32) + d * 32 + ((hh ^ ((d >> 2) & 1)) << 4);
+    return bi * (D * 32) + d * 32 + (v_slot(d, hh) << 4);
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
+template <int D, int NW, int CT>
+__global__ __launch_bounds__(NW * 64, 2) void tree_attn_kernel(AttnArgs a)
 {
-    using C = Cfg<D, NW>;
-    __shared__ __attribute__((aligned(16))) char lds[2 * C::kBufBytes];
-    __shared__ int32_t s_bt[kMaxSplitBlocks];   // this split's physical block ids
+    using C = Cfg<D, NW, CT>;
+    // Two tile buffers as separate objects: with the loop unrolled by two,
+    // every access names its buffer statically, so the compiler can tell the
+    // next tile's direct loads from the current tile's LDS reads and does not
+    // make the reads wait for those loads.
+    __shared__ __attribute__((aligned(16))) char lds_a[C::kBufBytes];
+    __shared__ __attribute__((aligned(16))) char lds_b[C::kBufBytes];
+    __shared__ __attribute__((aligned(16))) int32_t s_bt[kMaxSplitBlocks];   // this split's physical block ids
 
     // ---- which (sequence, kv head, split, row block) ------------------------
     const int bid = blockIdx.x;
@@ -130,8 +186,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int col = lane & 31;      // query column of this lane
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: SGPR arithmetic
+    const int col = lane & 31;      // query column of this lane within a 32-row tile
     const int hh = lane >> 5;       // which half of the K dimension this lane feeds
 
     int L = a.prefix_len[b];
@@ -162,166 +218,203 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     }
     const int blk0 = t_begin * (kKT / kBlock);
 
-    // ---- this lane's query row ---------------------------------------------
-    const int row = rb * C::kRows + wave * 32 + col;
-    const bool row_ok = row < a.NG;
-    const int node = row_ok ? row / a.G : 0;
-    const int head = kvh * a.G + (row_ok ? row % a.G : 0);
-    bf16x8 qf[C::kKSteps];
-    {
-        const uint16_t *qrow = a.q + (((int64_t)b * a.N + node) * a.Hq + head) * D;
+    // ---- this lane's query rows: one per 32-row column tile --------------------
+    int node[CT], head[CT];
+    bool row_ok[CT];
+    bf16x8 qf[CT][C::kKSteps];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        const int row = rb * C::kRows + wave * C::kWaveRows + 32 * c + col;
+        row_ok[c] = row < a.NG;
+        node[c] = row_ok[c] ? row / a.G : 0;
+        head[c] = kvh * a.G + (row_ok[c] ? row % a.G : 0);
+        const uint16_t *qrow = a.q + (((int64_t)b * a.N + node[c]) * a.Hq + head[c]) * D;
 #pragma unroll
         for (int k = 0; k < C::kKSteps; ++k) {
             u32x4 v = {0, 0, 0, 0};
-            if (row_ok)
+            if (row_ok[c])
                 v = *reinterpret_cast<const u32x4 *>(qrow + 16 * k + 8 * hh);
-            qf[k] = __builtin_bit_cast(bf16x8, v);
+            qf[c][k] = __builtin_bit_cast(bf16x8, v);
         }
     }
 
-    // ---- staging of one tile into registers, then LDS ------------------------
-    u32x4 kreg[C::kChPerThread], vreg[C::kChPerThread];
-
-    auto load_tile = [&](int it) {
-        if (it < n_pre) {
-            const int p0 = (t_begin + it) * kKT;
+    // ---- staging -----------------------------------------------------------
+    // Prefix tile: each wave issues kLoadsPerWave direct loads for K and as
+    // many for V; load j fills LDS chunks [64j, 64j+64) of the tile in lane
+    // order. The chunks of one load always come from a single 16-key paged
+    // block (4 or 8 whole MFMA rows of K, whose keys differ only in their low
+    // bits; or 64 feature halves of one V block), so the block's address is a
+    // wave-uniform base and each lane adds a byte offset below 4 KB. A block
+    // past the prefix or a bad block reads the cache's first block instead;
+    // those keys' scores are masked and their V entries zeroed later.
+    auto issue_prefix_tile = [&](int it, uint32_t kl) __attribute__((always_inline)) {
+        const uint32_t vl = kl + C::kKTileBytes;
+        const int p0 = (t_begin + it) * kKT;
+        // the tile's four block ids in one 16-byte LDS read (tiles start on a
+        // multiple of four blocks); entries past the prefix are never used
+        const u32x4 ids = *reinterpret_cast<const u32x4 *>(&s_bt[it * (kKT / kBlock)]);
+        const uint32_t idv[4] = {ids.x, ids.y, ids.z, ids.w};
+        uint64_t kb[4], vb[4];   // uniform block base addresses
 #pragma unroll
-            for (int r = 0; r < C::kChPerThread; ++r) {
-                const int ci = tid + r * C::kThreads;
-                // K: key k, chunk cc
-                {
-                    const int k = ci / C::kCpr, cc = ci % C::kCpr;
-                    const int pos = p0 + k;
-                    u32x4 v = {0, 0, 0, 0};
-                    if (pos < L) {
-                        const int blk = s_bt[(pos >> 4) - blk0];
-                        if (blk >= 0)
-                            v = *reinterpret_cast<const u32x4 *>(
-                                a.k_cache + (((int64_t)blk * a.Hkv + kvh) * kBlock + (pos & 15)) * D + cc * 8);
-                    }
-                    kreg[r] = v;
-                }
-                // V: block bi, feature d, key half h2
-                {
-                    const int bi = ci / (2 * D), rem = ci % (2 * D);
-                    const int d = rem >> 1, h2 = rem & 1;
-                    const int pos0 = p0 + bi * 16 + h2 * 8;
-                    u32x4 v = {0, 0, 0, 0};
-                    if (pos0 < L) {
-                        const int blk = s_bt[(pos0 >> 4) - blk0];
-                        if (blk >= 0) {
-                            v = *reinterpret_cast<const u32x4 *>(
-                                a.v_cache + (((int64_t)blk * a.Hkv + kvh) * D + d) * kBlock + h2 * 8);
-                            const int valid = L - pos0;   // keys past the prefix read as zero
-                            if (valid < 8) {
-                                uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        for (int bb = 0; bb < 4; ++bb) {
+            const int blk = (int)__builtin_amdgcn_readfirstlane(idv[bb]);
+            const bool ok = p0 + bb * kBlock < L && blk >= 0;
+            const int64_t e = ok ? ((int64_t)blk * a.Hkv + kvh) * (kBlock * D) : 0;
+            kb[bb] = (uint64_t)(uintptr_t)(a.k_cache + e);
+            vb[bb] = (uint64_t)(uintptr_t)(a.v_cache + e);
+        }
+        auto pick = [&](const uint64_t (&t)[4], int bb) __attribute__((always_inline)) -> const void * {
+            return (const void *)(uintptr_t)(bb == 0 ? t[0] : bb == 1 ? t[1] : bb == 2 ? t[2] : t[3]);
+        };
 #pragma unroll
-                                for (int e = 0; e < 8; ++e)
-                                    if (e >= valid)
-                                        w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-                                v = u32x4{w[0], w[1], w[2], w[3]};
-                            }
-                        }
-                    }
-                    vreg[r] = v;
-                }
-            }
-        } else {
-            const int j0 = (it - n_pre) * kKT;
+        for (int i = 0; i < C::kLoadsPerWave; ++i) {
+            const int j = wave + i * NW;
+            const int row0 = j * 64 / C::kCpr;                   // first MFMA row of this load
+            const int bb = ((row0 & ~31) | perm32(row0 & 31)) >> 4;
+            const int q = j * 64 + lane;
+            const int row = q / C::kCpr, pos = q % C::kCpr;
+            const int cc = pos ^ k_swz<D>(row);
+            const int key = (row & ~31) | perm32(row & 31);
+            const uint32_t off = (uint32_t)(((key & 15) * D + cc * 8) * 2);
+            load_lds16(pick(kb, bb), off, kl + j * 1024u);
+        }
 #pragma unroll
-            for (int r = 0; r < C::kChPerThread; ++r) {
-                const int ci = tid + r * C::kThreads;
-                const int k = ci / C::kCpr, cc = ci % C::kCpr;
-                const int j = j0 + k;
-                u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-                if (j < a.N) {
-                    const int64_t src = (((int64_t)b * a.N + j) * a.Hkv + kvh) * D + cc * 8;
-                    kv = *reinterpret_cast<const u32x4 *>(a.k_tree + src);
-                    vv = *reinterpret_cast<const u32x4 *>(a.v_tree + src);
-                }
-                kreg[r] = kv;
-                vreg[r] = vv;
-            }
+        for (int i = 0; i < C::kLoadsPerWave; ++i) {
+            const int j = wave + i * NW;
+            const int bb = j * 64 / (2 * D);
+            const int q = j * 64 + lane;
+            const int rem = q % (2 * D);
+            const int d = rem >> 1, pos = rem & 1;
+            const int h2 = v_slot(d, pos);   // v_slot is its own inverse in hh
+            const uint32_t off = (uint32_t)((d * kBlock + h2 * 8) * 2);
+            load_lds16(pick(vb, bb), off, vl + j * 1024u);
         }
     };
 
-    auto store_tile = [&](int it, int buf) {
-        char *kl = lds + buf * C::kBufBytes;
-        char *vl = kl + C::kKTileBytes;
-        const bool tree = it >= n_pre;
+    // bf16 -> fp16 of a landed prefix tile's V, in place; keys past the prefix
+    // become zero (unused cache slots may hold anything).
+    auto convert_prefix_v = [&](int it, char *buf) __attribute__((always_inline)) {
+        char *vl = buf + C::kKTileBytes;
+        const int p0 = (t_begin + it) * kKT;
 #pragma unroll
+        for (int r = 0; r < C::kChPerThread; ++r) {
+            const int q = tid + r * C::kThreads;
+            u32x4 *pv = reinterpret_cast<u32x4 *>(vl + q * 16);
+            const u32x4 v = *pv;
+            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            const int bi = q / (2 * D), rem = q % (2 * D);
+            const int d = rem >> 1, pos = rem & 1;
+            const int h2 = v_slot(d, pos);   // v_slot is its own inverse in hh
+            const int valid = L - (p0 + bi * 16 + h2 * 8);
+            if (valid < 8) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (e >= valid)
+                        w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+            }
+            u32x4 h;
+            h.x = bf16x2_to_f16x2(w[0]);
+            h.y = bf16x2_to_f16x2(w[1]);
+            h.z = bf16x2_to_f16x2(w[2]);
+            h.w = bf16x2_to_f16x2(w[3]);
+            *pv = h;
+        }
+    };
+
+    // Tree tile: through registers. K rows go to their MFMA rows; V rows are
+    // feature-contiguous, so 8 features of a key are scattered (as fp16).
+    auto stage_tree_tile = [&](int it, char *kl) __attribute__((always_inline)) {
+        char *vl = kl + C::kKTileBytes;
+        const int j0 = (it - n_pre) * kKT;
+#pragma unroll 1   // keeps one chunk's registers live
         for (int r = 0; r < C::kChPerThread; ++r) {
             const int ci = tid + r * C::kThreads;
             const int k = ci / C::kCpr, cc = ci % C::kCpr;
-            *reinterpret_cast<u32x4 *>(kl + k_off<D>(k, cc)) = kreg[r];
-            const uint32_t w[4] = {vreg[r].x, vreg[r].y, vreg[r].z, vreg[r].w};
-            if (!tree) {
-                const int bi = ci / (2 * D), rem = ci % (2 * D);
-                u32x4 h;
-                h.x = bf16x2_to_f16x2(w[0]);
-                h.y = bf16x2_to_f16x2(w[1]);
-                h.z = bf16x2_to_f16x2(w[2]);
-                h.w = bf16x2_to_f16x2(w[3]);
-                *reinterpret_cast<u32x4 *>(vl + v_off<D>(bi, rem >> 1, rem & 1)) = h;
-            } else {
-                // tree V rows are feature-contiguous: scatter 8 features of key k
-                const int bi = k >> 4, kb = k & 15;
+            const int j = j0 + k;
+            u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+            if (j < a.N) {
+                const int64_t src = (((int64_t)b * a.N + j) * a.Hkv + kvh) * D + cc * 8;
+                kv = *reinterpret_cast<const u32x4 *>(a.k_tree + src);
+                vv = *reinterpret_cast<const u32x4 *>(a.v_tree + src);
+            }
+            *reinterpret_cast<u32x4 *>(kl + k_off<D>(k, cc)) = kv;
+            const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+            const int bi = k >> 4, kb = k & 15;
 #pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const uint32_t h = bf16x2_to_f16x2(w[e >> 1]);
+            for (int e = 0; e < 8; e += 2) {
+                const uint32_t h = bf16x2_to_f16x2(w[e >> 1]);
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int d = cc * 8 + e + u;
-                        *reinterpret_cast<uint16_t *>(vl + v_off<D>(bi, d, kb >> 3) + (kb & 7) * 2) =
-                            (uint16_t)(h >> (u * 16));
-                    }
+                for (int u = 0; u < 2; ++u) {
+                    const int d = cc * 8 + e + u;
+                    *reinterpret_cast<uint16_t *>(vl + v_off<D>(bi, d, kb >> 3) + (kb & 7) * 2) =
+                        (uint16_t)(h >> (u * 16));
                 }
             }
         }
     };
 
     // ---- accumulators --------------------------------------------------------
-    f32x16 oacc[C::kDTiles];
+    f32x16 oacc[C::kDTiles][CT];
 #pragma unroll
     for (int m = 0; m < C::kDTiles; ++m)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            oacc[m][e] = 0.f;
-    float m_used = -INFINITY;   // raw-score max the exponentials are taken against
-    float lsum = 0.f;           // this lane's share of the softmax denominator
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                oacc[m][c][e] = 0.f;
+    float m_used[CT];   // raw-score max the exponentials are taken against
+    float lsum[CT];     // this lane's share of the softmax denominator
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        m_used[c] = -INFINITY;
+        lsum[c] = 0.f;
+    }
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
     __syncthreads();   // s_bt ready
     if (n_tiles > 0) {
-        load_tile(0);
-        store_tile(0, 0);
+        if (n_pre > 0)
+            issue_prefix_tile(0, TAV_LDS_ADDR(lds_a));
+        else
+            stage_tree_tile(0, lds_a);
     }
-    __syncthreads();
+    lds_loads_landed();
+    if (n_pre > 0) {
+        convert_prefix_v(0, lds_a);
+        __syncthreads();
+    }
 
-    for (int it = 0; it < n_tiles; ++it) {
-        const int buf = it & 1;
-        if (C::kPrefetch && it + 1 < n_tiles)
-            load_tile(it + 1);
+    // One tile: compute on `cur` while the next tile streams into `nxt`.
+    auto tile_step = [&](int it, char *cur, char *nxt, uint32_t nxt_addr) __attribute__((always_inline)) {
+        if (it + 1 < n_pre)
+            issue_prefix_tile(it + 1, nxt_addr);
 
-        const char *kl = lds + buf * C::kBufBytes;
+        const char *kl = cur;
         const char *vl = kl + C::kKTileBytes;
 
-        // S^T = K Q^T for two 32-key tiles
-        f32x16 sacc[2];
+        // S^T = K Q^T for two 32-key tiles and every column tile; each K
+        // fragment read from LDS feeds CT MFMAs
+        f32x16 sacc[2][CT];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                sacc[t][e] = 0.f;
-        const char *krd = kl + col * C::kKRow + hh * 16;   // this lane's MFMA row
+            for (int c = 0; c < CT; ++c)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    sacc[t][c][e] = 0.f;
 #pragma unroll
         for (int k = 0; k < C::kKSteps; ++k) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const bf16x8 av =
-                    *reinterpret_cast<const bf16x8 *>(krd + t * 32 * C::kKRow + k * 32);
-                sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[k], sacc[t], 0, 0, 0);
+                    *reinterpret_cast<const bf16x8 *>(kl + k_off_row<D>(32 * t + col, 2 * k + hh));
+#pragma unroll
+                for (int c = 0; c < CT; ++c)
+                    sacc[t][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[c][k], sacc[t][c], 0, 0, 0);
             }
+            // keep at most two k-steps of K fragments in flight (registers)
+            if (k & 1)
+                __builtin_amdgcn_sched_barrier(0);
         }
 
         // masks: ragged prefix tail, or ancestor bits of the tree tile
@@ -329,83 +422,90 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
         // the lane-dependent 8hh is taken out once so the rest are constants.
         if (it >= n_pre) {
             const int tt = it - n_pre;
-            uint64_t mw = 1;
-            if (row_ok)
-                mw = a.mask[((int64_t)b * a.N + node) * a.W + tt];
-            mw >>= 8 * hh;
-            const uint32_t mlo = (uint32_t)mw, mhi = (uint32_t)(mw >> 32);
             const int nlim = a.N - tt * kKT - 8 * hh;   // keys at or past it are not nodes
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int kr = 16 * (i >> 1) + 4 * (i & 1) + j;   // < 32
-                        const uint32_t word = t ? mhi : mlo;
-                        const bool ok = (32 * t + kr < nlim) && ((word >> kr) & 1u);
-                        if (!ok)
-                            sacc[t][4 * i + j] = -INFINITY;
-                    }
-        } else {
-            const int p0 = (t_begin + it) * kKT;
-            if (p0 + kKT > L) {
-                const int plim = L - p0 - 8 * hh;
+            for (int c = 0; c < CT; ++c) {
+                uint64_t mw = 1;
+                if (row_ok[c])
+                    mw = a.mask[((int64_t)b * a.N + node[c]) * a.W + tt];
+                mw >>= 8 * hh;
+                const uint32_t mlo = (uint32_t)mw, mhi = (uint32_t)(mw >> 32);
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            const int kr = 32 * t + 16 * (i >> 1) + 4 * (i & 1) + j;
-                            if (kr >= plim)
-                                sacc[t][4 * i + j] = -INFINITY;
+                            const int kr = 16 * (i >> 1) + 4 * (i & 1) + j;   // < 32
+                            const uint32_t word = t ? mhi : mlo;
+                            const bool ok = (32 * t + kr < nlim) && ((word >> kr) & 1u);
+                            if (!ok)
+                                sacc[t][c][4 * i + j] = -INFINITY;
                         }
             }
+        } else {
+            const int p0 = (t_begin + it) * kKT;
+            if (p0 + kKT > L) {
+                const int plim = L - p0 - 8 * hh;
+#pragma unroll
+                for (int c = 0; c < CT; ++c)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const int kr = 32 * t + 16 * (i >> 1) + 4 * (i & 1) + j;
+                                if (kr >= plim)
+                                    sacc[t][c][4 * i + j] = -INFINITY;
+                            }
+            }
         }
 
-        // online softmax with lazy rescaling
-        float mt = -INFINITY;
+        // online softmax with lazy rescaling, per column tile
+        f16x8 pb[CT][2][2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int c = 0; c < CT; ++c) {
+            float mt = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                mt = fmaxf(mt, sacc[t][e]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const bool need = mt > m_used + a.th;
-        if (__any(need)) {
-            const float mnew = need ? mt : m_used;
-            const float alpha =
-                (m_used == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_used - mnew) * a.c);
-#pragma unroll
-            for (int m = 0; m < C::kDTiles; ++m)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
-                    oacc[m][e] *= alpha;
-            lsum *= alpha;
-            m_used = mnew;
-        }
-        // weights 2^(s*c - m*c + 7): at most 2^15 after the lazy threshold
-        const float moff = (m_used == -INFINITY) ? 0.f : m_used * a.c - kWeightBias;
-
-        f16x8 pb[2][2];
+                    mt = fmaxf(mt, sacc[t][c][e]);
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            const bool need = mt > m_used[c] + a.th;
+            if (__any(need)) {
+                const float mnew = need ? mt : m_used[c];
+                const float alpha =
+                    (m_used[c] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_used[c] - mnew) * a.c);
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+                for (int m = 0; m < C::kDTiles; ++m)
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * h2 + e], a.c, -moff));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * h2 + e + 1], a.c, -moff));
-                    const f32x2 pf = {p0, p1};
-                    const f16x2 pk = __builtin_convertvector(pf, f16x2);
-                    pb[t][h2][e] = pk[0];
-                    pb[t][h2][e + 1] = pk[1];
-                    lsum = __builtin_amdgcn_fdot2(pk, ones, lsum, false);
-                }
+                    for (int e = 0; e < 16; ++e)
+                        oacc[m][c][e] *= alpha;
+                lsum[c] *= alpha;
+                m_used[c] = mnew;
             }
+            // weights 2^(s*c - m*c + 7): at most 2^15 after the lazy threshold
+            const float moff = (m_used[c] == -INFINITY) ? 0.f : m_used[c] * a.c - kWeightBias;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2) {
+                        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[t][c][8 * h2 + e], a.c, -moff));
+                        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[t][c][8 * h2 + e + 1], a.c, -moff));
+                        const f32x2 pf = {p0, p1};
+                        const f16x2 pk = __builtin_convertvector(pf, f16x2);
+                        pb[c][t][h2][e] = pk[0];
+                        pb[c][t][h2][e + 1] = pk[1];
+                        lsum[c] = __builtin_amdgcn_fdot2(pk, ones, lsum[c], false);
+                    }
+                }
+        }
 
-        // O^T += V^T P^T
+        // O^T += V^T P^T; each V fragment read from LDS feeds CT MFMAs
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -414,53 +514,68 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
                 for (int m = 0; m < C::kDTiles; ++m) {
                     const f16x8 av =
                         *reinterpret_cast<const f16x8 *>(vl + v_off<D>(2 * t + h2, 32 * m + col, hh));
-                    oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[t][h2], oacc[m], 0, 0, 0);
+#pragma unroll
+                    for (int c = 0; c < CT; ++c)
+                        oacc[m][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[c][t][h2], oacc[m][c], 0, 0, 0);
+                    if (m & 1)
+                        __builtin_amdgcn_sched_barrier(0);
                 }
 
         if (it + 1 < n_tiles) {
-            if (!C::kPrefetch)
-                load_tile(it + 1);
-            store_tile(it + 1, buf ^ 1);
+            if (it + 1 >= n_pre)
+                stage_tree_tile(it + 1, nxt);
+            lds_loads_landed();
+            if (it + 1 < n_pre) {
+                convert_prefix_v(it + 1, nxt);
+                __syncthreads();
+            }
         }
-        __syncthreads();
+    };
+    for (int it = 0; it < n_tiles; it += 2) {
+        tile_step(it, lds_a, lds_b, TAV_LDS_ADDR(lds_b));
+        if (it + 1 < n_tiles)
+            tile_step(it + 1, lds_b, lds_a, TAV_LDS_ADDR(lds_a));
     }
 
     // ---- write the result or the split's partial ------------------------------
-    const float ltot = lsum + __shfl_xor(lsum, 32);
-    if (!row_ok)
-        return;
-    if (a.S == 1) {
-        const float inv = 1.0f / ltot;
-        float *orow = a.out + (((int64_t)b * a.N + node) * a.Hq + head) * D;
-        bool finite = true;
 #pragma unroll
-        for (int m = 0; m < C::kDTiles; ++m)
+    for (int c = 0; c < CT; ++c) {
+        const float ltot = lsum[c] + __shfl_xor(lsum[c], 32);
+        if (!row_ok[c])
+            continue;
+        if (a.S == 1) {
+            const float inv = 1.0f / ltot;
+            float *orow = a.out + (((int64_t)b * a.N + node[c]) * a.Hq + head[c]) * D;
+            bool finite = true;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x4 v = {oacc[m][4 * i] * inv, oacc[m][4 * i + 1] * inv,
-                                 oacc[m][4 * i + 2] * inv, oacc[m][4 * i + 3] * inv};
-                finite &= __builtin_isfinite(v.x) && __builtin_isfinite(v.y) &&
-                          __builtin_isfinite(v.z) && __builtin_isfinite(v.w);
-                *reinterpret_cast<f32x4 *>(orow + 32 * m + 8 * i + 4 * hh) = v;
+            for (int m = 0; m < C::kDTiles; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4 v = {oacc[m][c][4 * i] * inv, oacc[m][c][4 * i + 1] * inv,
+                                     oacc[m][c][4 * i + 2] * inv, oacc[m][c][4 * i + 3] * inv};
+                    finite &= __builtin_isfinite(v.x) && __builtin_isfinite(v.y) &&
+                              __builtin_isfinite(v.z) && __builtin_isfinite(v.w);
+                    *reinterpret_cast<f32x4 *>(orow + 32 * m + 8 * i + 4 * hh) = v;
+                }
+            if (!finite)
+                raise_flag(a.flags, TAV_FLAG_ATTN_RANGE);
+        } else {
+            const int64_t P = ((int64_t)bh * a.RB + rb) * a.S + s;
+            const int rloc = wave * C::kWaveRows + 32 * c + col;
+            float *po = a.part_o + (P * C::kRows + rloc) * D;
+#pragma unroll
+            for (int m = 0; m < C::kDTiles; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4 v = {oacc[m][c][4 * i], oacc[m][c][4 * i + 1], oacc[m][c][4 * i + 2],
+                                     oacc[m][c][4 * i + 3]};
+                    *reinterpret_cast<f32x4 *>(po + 32 * m + 8 * i + 4 * hh) = v;
+                }
+            if (hh == 0) {
+                float *pml = a.part_ml + (P * C::kRows + rloc) * 2;
+                pml[0] = (m_used[c] == -INFINITY) ? -INFINITY : m_used[c] * a.c;
+                pml[1] = ltot;
             }
-        if (!finite)
-            raise_flag(a.flags, TAV_FLAG_ATTN_RANGE);
-    } else {
-        const int64_t P = ((int64_t)bh * a.RB + rb) * a.S + s;
-        const int rloc = wave * 32 + col;
-        float *po = a.part_o + (P * C::kRows + rloc) * D;
-#pragma unroll
-        for (int m = 0; m < C::kDTiles; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x4 v = {oacc[m][4 * i], oacc[m][4 * i + 1], oacc[m][4 * i + 2],
-                                 oacc[m][4 * i + 3]};
-                *reinterpret_cast<f32x4 *>(po + 32 * m + 8 * i + 4 * hh) = v;
-            }
-        if (hh == 0) {
-            float *pml = a.part_ml + (P * C::kRows + rloc) * 2;
-            pml[0] = (m_used == -INFINITY) ? -INFINITY : m_used * a.c;
-            pml[1] = ltot;
         }
     }
 }
@@ -508,31 +623,58 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(AttnArgs a, int 
 }
 
 struct AttnPlan {
-    int NW, rows, RB, S, KS;
+    int NW, CT, rows, RB, S, KS;
     int64_t grid;
     size_t part_o_bytes, part_ml_bytes, ws_bytes;
 };
 
 size_t round_up(size_t v, size_t al) { return (v + al - 1) / al * al; }
 
+constexpr int kMinTilesPerSplit = 4;   // below this, partials cost more than the split gains
+
+template <int D>
+const void *kernel_for(int NW, int CT)
+{
+    (void)CT;
+    switch (NW) {
+    case 8:
+        return reinterpret_cast<const void *>(tree_attn_kernel<D, 8, 1>);
+    case 4:
+        return reinterpret_cast<const void *>(tree_attn_kernel<D, 4, 1>);
+    case 2:
+        return reinterpret_cast<const void *>(tree_attn_kernel<D, 2, 1>);
+    default:
+        return reinterpret_cast<const void *>(tree_attn_kernel<D, 1, 1>);
+    }
+}
+
+// Work decomposition for a shape: rows per wave (32*CT), waves per workgroup
+// (NW), row blocks (RB) and prefix splits (S), enough workgroups to fill the
+// device once.
 bool attn_plan(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_prefix_len,
                AttnPlan &p)
 {
-    (void)D;
     const int G = Hq / Hkv;
     const int NG = N * G;
+    // 32 query rows per wave, up to 4 waves per workgroup; two workgroups
+    // share a CU so one's softmax overlaps the other's MFMAs
+    p.CT = 1;
     p.NW = NG > 128 ? 8 : NG > 64 ? 4 : NG > 32 ? 2 : 1;
-    p.rows = 32 * p.NW;
+    p.rows = 32 * p.CT * p.NW;
     p.RB = (int)ceil_div(NG, p.rows);
     const int cus = device_cu_count();
     if (cus <= 0)
         return false;
+    int per_cu = 0;
+    const void *fn = D == 128 ? kernel_for<128>(p.NW, p.CT) : kernel_for<64>(p.NW, p.CT);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, p.NW * 64, 0) != hipSuccess ||
+        per_cu <= 0)
+        return false;
     const int64_t base = (int64_t)B * Hkv * p.RB;
-    const int64_t per_cu = std::max(1, 8 / p.NW);          // resident workgroups per CU
     const int64_t target = (int64_t)cus * per_cu;
     const int64_t tiles = std::max<int64_t>(1, ceil_div(max_prefix_len, kKT));
     int64_t S = ceil_div(target, base);
-    S = std::max<int64_t>(1, std::min<int64_t>(S, tiles));
+    S = std::max<int64_t>(1, std::min<int64_t>(S, tiles / kMinTilesPerSplit));
     // a split's block-table slice must fit its LDS copy
     const int64_t max_tiles_per_split = kMaxSplitBlocks / (kKT / kBlock);
     S = std::max<int64_t>(S, ceil_div(tiles, max_tiles_per_split));
@@ -556,10 +698,10 @@ bool attn_shape_ok(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
            (D == 64 || D == 128) && (int64_t)(Hq / Hkv) * N <= 4096 && max_prefix_len >= 0;
 }
 
-template <int D, int NW>
+template <int D, int NW, int CT>
 hipError_t launch_main(const AttnPlan &p, const AttnArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL((tree_attn_kernel<D, NW>), dim3((unsigned)p.grid), dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((tree_attn_kernel<D, NW, CT>), dim3((unsigned)p.grid), dim3(NW * 64), 0, s, a);
     return hipGetLastError();
 }
 
@@ -567,14 +709,14 @@ template <int D>
 hipError_t launch_main_d(const AttnPlan &p, const AttnArgs &a, hipStream_t s)
 {
     switch (p.NW) {
-    case 1:
-        return launch_main<D, 1>(p, a, s);
-    case 2:
-        return launch_main<D, 2>(p, a, s);
+    case 8:
+        return launch_main<D, 8, 1>(p, a, s);
     case 4:
-        return launch_main<D, 4>(p, a, s);
+        return launch_main<D, 4, 1>(p, a, s);
+    case 2:
+        return launch_main<D, 2, 1>(p, a, s);
     default:
-        return launch_main<D, 8>(p, a, s);
+        return launch_main<D, 1, 1>(p, a, s);
     }
 }
 
