@@ -31,16 +31,24 @@
 //                 keeps 8, which the output tolerance needs when attention
 //                 falls on a few keys. Weights carry a 2^7 bias so small ones
 //                 stay clear of fp16 subnormals; the bias cancels in O/l.
-// Tiles are double-buffered in LDS. Prefix tiles move from HBM straight into
-// LDS (global_load_lds_dwordx4: 16 bytes per lane, no staging registers), a
-// whole tile ahead of the MFMAs that use them; one pass per tile then turns the
-// tile's V from bf16 into fp16 in place and zeroes keys past the prefix. The
-// few tree tiles go through registers (their V rows need a transpose). Splits
-// of the prefix write unnormalised partials (O, max, sum) that a combine
-// kernel merges with log-sum-exp; the last split also takes the tree tiles
-// (keys masked by the ancestor bitmask).
+// Staging. K tiles sit in a ring of three LDS slots and V tiles in a ring of
+// five, filled two tiles ahead. Prefix tiles move from HBM straight into LDS
+// (global_load_lds_dwordx4: 16 bytes per lane, no staging registers), with
+// the block table resolved once per split into head-block indices in LDS;
+// each tile's V is then turned from bf16 into fp16 in place, keys past the
+// prefix zeroed, while the S MFMAs run. The few tree tiles go through
+// registers (their V rows need a transpose). One barrier per tile.
+// Overlap. A wave's work per tile is an MFMA phase (S) and a phase that is
+// mostly vector ALU work (the softmax, then P.V of the tile before). In an
+// 8-wave workgroup the two waves that share a SIMD run these in opposite
+// order, one a tile behind the other, so one's vector work runs under the
+// other's MFMAs.
+// Splits of the prefix write unnormalised partials (O, max, sum) that a
+// combine kernel merges with log-sum-exp; the last split also takes the tree
+// tiles (keys masked by the ancestor bitmask).
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -52,11 +60,10 @@ constexpr int kMaxSplitBlocks = 2048; // block-table entries one split stages in
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kWeightBias = 7.0f;  // log2 of the bias on the fp16 weights
 
-template <int D, int NW, int CT>
+template <int D, int NW>
 struct Cfg {
     static constexpr int kThreads = NW * 64;
-    static constexpr int kWaveRows = CT * 32;            // query rows per wave
-    static constexpr int kRows = NW * kWaveRows;         // query rows per workgroup
+    static constexpr int kRows = NW * 32;                // query rows per workgroup (32 per wave)
     static constexpr int kKSteps = D / 16;
     static constexpr int kDTiles = D / 32;
     static constexpr int kCpr = D / 8;                   // 16-byte chunks per row
@@ -113,30 +120,27 @@ __device__ __forceinline__ int k_off(int k, int cc)
     return k_off_row<D>((k & ~31) | perm32(k & 31), cc);
 }
 
-// One direct HBM -> LDS load: lane l's 16 bytes at base + off land at LDS
-// byte address lds_addr + 16 l (lds_addr is the same for the whole wave).
-// Issued as inline assembly: the compiler then neither makes later LDS reads
-// of the other tile buffer wait for it nor reasons about what it writes; the
-// code that reads the destination waits for it explicitly with
-// lds_loads_landed().
-__device__ __forceinline__ void load_lds16(const void *base, uint32_t off, uint32_t lds_addr)
+// One direct HBM -> LDS load: lane l's 16 bytes at base + voff land at LDS
+// byte address lds_addr + 16 l (base and lds_addr are the same for the whole
+// wave). Issued as inline assembly: the compiler then neither makes later LDS
+// reads wait for it nor reasons about what it writes; the code that reads
+// the destination waits for it explicitly (wait_vmem, then a barrier).
+__device__ __forceinline__ void load_lds16(const void *base, uint32_t voff, uint32_t lds_addr)
 {
-    const char *src = static_cast<const char *>(base) + off;
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 : "v"(voff), "s"(base), "s"(lds_addr)
                  : "memory", "m0");
 }
 
 // LDS byte address of a __shared__ object (folded at compile time).
 #define TAV_LDS_ADDR(obj) ((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)(obj))
 
-// Every direct load this workgroup issued has landed in LDS and is visible to
-// all its waves.
-__device__ __forceinline__ void lds_loads_landed()
+// An LDS location by byte address.
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(3))) T *lds_at(uint32_t addr)
 {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    return reinterpret_cast<__attribute__((address_space(3))) T *>((uintptr_t)addr);
 }
 
 // Two bf16 values (low, high half of w) to two fp16 values, round to nearest.
@@ -159,17 +163,33 @@ __device__ __forceinline__ int v_off(int bi, int d, int hh)
     return bi * (D * 32) + d * 32 + (v_slot(d, hh) << 4);
 }
 
-template <int D, int NW, int CT>
-__global__ __launch_bounds__(NW * 64, 2) void tree_attn_kernel(AttnArgs a)
+// s_waitcnt with only the vector-memory count set: wait until at most N of
+// this wave's vector memory operations are outstanding (they complete in
+// issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem()
 {
-    using C = Cfg<D, NW, CT>;
-    // Two tile buffers as separate objects: with the loop unrolled by two,
-    // every access names its buffer statically, so the compiler can tell the
-    // next tile's direct loads from the current tile's LDS reads and does not
-    // make the reads wait for those loads.
-    __shared__ __attribute__((aligned(16))) char lds_a[C::kBufBytes];
-    __shared__ __attribute__((aligned(16))) char lds_b[C::kBufBytes];
-    __shared__ __attribute__((aligned(16))) int32_t s_bt[kMaxSplitBlocks];   // this split's physical block ids
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// sched_group_barrier instruction classes
+constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100, kSgDsWrite = 0x200;
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
+{
+    using C = Cfg<D, NW>;
+    constexpr int LPW = C::kLoadsPerWave;
+    constexpr int KTB = C::kKTileBytes, VTB = C::kVTileBytes;
+    // K tiles live in a ring of 3 slots and V tiles in a ring of 5: tile t's
+    // K is read in step t only, its V in step t+1 or t+2 (P.V runs one or
+    // two tiles behind), and tile t+2 streams in during step t.
+    constexpr int kKSlots = 3, kVSlots = 5;
+    __shared__ __attribute__((aligned(16))) char s_k[kKSlots * KTB];
+    __shared__ __attribute__((aligned(16))) char s_v[kVSlots * VTB];
+    // this split's cache blocks as head-block indices (block * Hkv + kvh)
+    __shared__ __attribute__((aligned(16))) uint32_t s_bt[kMaxSplitBlocks];
 
     // ---- which (sequence, kv head, split, row block) ------------------------
     const int bid = blockIdx.x;
@@ -187,7 +207,7 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_kernel(AttnArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: SGPR arithmetic
-    const int col = lane & 31;      // query column of this lane within a 32-row tile
+    const int col = lane & 31;      // query column of this lane
     const int hh = lane >> 5;       // which half of the K dimension this lane feeds
 
     int L = a.prefix_len[b];
@@ -202,111 +222,120 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_kernel(AttnArgs a)
     const int n_pre = t_end - t_begin;
     const int n_tree = (s == a.S - 1) ? (a.N + kKT - 1) / kKT : 0;
     const int n_tiles = n_pre + n_tree;
-    // The split's block-table slice, validated once: later tiles look block
-    // ids up in LDS instead of waiting on a dependent global load per tile.
+    // The split's block-table slice, validated once. Entries past the prefix
+    // (and bad ones, which also raise a flag) name block 0 of this head, a
+    // valid address whose keys are masked and whose V entries are zeroed.
     {
         const int32_t *bt = a.block_table + (int64_t)b * a.max_blocks;
-        const int nb = std::min(n_pre * (kKT / kBlock), (L + kBlock - 1) / kBlock - t_begin * (kKT / kBlock));
-        for (int i = tid; i < nb; i += C::kThreads) {
-            int32_t blk = bt[t_begin * (kKT / kBlock) + i];
-            if (blk < 0 || blk >= a.num_blocks) {
-                raise_flag(a.flags, TAV_FLAG_BAD_BLOCK);
-                blk = -1;
+        const int nbt = n_pre * (kKT / kBlock);
+        const int nvalid = (L + kBlock - 1) / kBlock - t_begin * (kKT / kBlock);
+        for (int i = tid; i < nbt; i += C::kThreads) {
+            uint32_t hb = (uint32_t)kvh;
+            if (i < nvalid) {
+                const int32_t blk = bt[t_begin * (kKT / kBlock) + i];
+                if (blk < 0 || blk >= a.num_blocks)
+                    raise_flag(a.flags, TAV_FLAG_BAD_BLOCK);
+                else
+                    hb = (uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)kvh;
             }
-            s_bt[i] = blk;
+            s_bt[i] = hb;
         }
     }
-    const int blk0 = t_begin * (kKT / kBlock);
 
-    // ---- this lane's query rows: one per 32-row column tile --------------------
-    int node[CT], head[CT];
-    bool row_ok[CT];
-    bf16x8 qf[CT][C::kKSteps];
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-        const int row = rb * C::kRows + wave * C::kWaveRows + 32 * c + col;
-        row_ok[c] = row < a.NG;
-        node[c] = row_ok[c] ? row / a.G : 0;
-        head[c] = kvh * a.G + (row_ok[c] ? row % a.G : 0);
-        const uint16_t *qrow = a.q + (((int64_t)b * a.N + node[c]) * a.Hq + head[c]) * D;
+    // ---- this lane's query row, and the first word of its ancestor mask ------
+    const int row = rb * C::kRows + wave * 32 + col;
+    const bool row_ok = row < a.NG;
+    const int node = row_ok ? row / a.G : 0;
+    const int head = kvh * a.G + (row_ok ? row % a.G : 0);
+    bf16x8 qf[C::kKSteps];
+    {
+        const uint16_t *qrow = a.q + (((int64_t)b * a.N + node) * a.Hq + head) * D;
 #pragma unroll
         for (int k = 0; k < C::kKSteps; ++k) {
             u32x4 v = {0, 0, 0, 0};
-            if (row_ok[c])
+            if (row_ok)
                 v = *reinterpret_cast<const u32x4 *>(qrow + 16 * k + 8 * hh);
-            qf[c][k] = __builtin_bit_cast(bf16x8, v);
+            qf[k] = __builtin_bit_cast(bf16x8, v);
         }
     }
+    const uint64_t mrow0 = (n_tree > 0 && row_ok) ? a.mask[((int64_t)b * a.N + node) * a.W] : 1;
+
+    // ---- direct-load descriptors, fixed for the whole kernel ------------------
+    // Load j of a tile fills LDS chunks [64j, 64j+64) in lane order; this wave
+    // issues loads j = wave + i*NW. The chunks of one load always come from a
+    // single 16-key cache block (4 or 8 whole MFMA rows of K, whose keys differ
+    // only in their low bits; or 64 feature halves of one V block): the
+    // block's address is a wave-uniform base and each lane adds a byte offset
+    // below 4 KB.
+    int kbb[LPW], vbb[LPW];          // which of the tile's four blocks
+    uint32_t koff[LPW], voff[LPW];   // this lane's byte offset inside it
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int j = wave + i * NW;
+        const int row0 = j * 64 / C::kCpr;   // first MFMA row of this load
+        kbb[i] = ((row0 & ~31) | perm32(row0 & 31)) >> 4;
+        const int q = j * 64 + lane;
+        const int r = q / C::kCpr, pos = q % C::kCpr;
+        const int cc = pos ^ k_swz<D>(r);
+        const int key = (r & ~31) | perm32(r & 31);
+        koff[i] = (uint32_t)(((key & 15) * D + cc * 8) * 2);
+        vbb[i] = j * 64 / (2 * D);
+        const int rem = q % (2 * D);
+        const int d = rem >> 1, hpos = rem & 1;
+        const int h2 = v_slot(d, hpos);   // v_slot is its own inverse in hh
+        voff[i] = (uint32_t)((d * kBlock + h2 * 8) * 2);
+    }
+    const uint32_t k_lds = TAV_LDS_ADDR(s_k), v_lds = TAV_LDS_ADDR(s_v);
 
     // ---- staging -----------------------------------------------------------
-    // Prefix tile: each wave issues kLoadsPerWave direct loads for K and as
-    // many for V; load j fills LDS chunks [64j, 64j+64) of the tile in lane
-    // order. The chunks of one load always come from a single 16-key paged
-    // block (4 or 8 whole MFMA rows of K, whose keys differ only in their low
-    // bits; or 64 feature halves of one V block), so the block's address is a
-    // wave-uniform base and each lane adds a byte offset below 4 KB. A block
-    // past the prefix or a bad block reads the cache's first block instead;
-    // those keys' scores are masked and their V entries zeroed later.
-    auto issue_prefix_tile = [&](int it, uint32_t kl) __attribute__((always_inline)) {
-        const uint32_t vl = kl + C::kKTileBytes;
-        const int p0 = (t_begin + it) * kKT;
-        // the tile's four block ids in one 16-byte LDS read (tiles start on a
-        // multiple of four blocks); entries past the prefix are never used
-        const u32x4 ids = *reinterpret_cast<const u32x4 *>(&s_bt[it * (kKT / kBlock)]);
-        const uint32_t idv[4] = {ids.x, ids.y, ids.z, ids.w};
-        uint64_t kb[4], vb[4];   // uniform block base addresses
+    // The head-block indices a prefix tile's loads need, read from LDS ahead
+    // of the barrier that precedes the loads.
+    struct TileIds {
+        uint32_t k[LPW], v[LPW];
+    };
+    auto read_ids = [&](int it) __attribute__((always_inline)) {
+        TileIds ids;
+        const int e0 = it * (kKT / kBlock);
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            const int blk = (int)__builtin_amdgcn_readfirstlane(idv[bb]);
-            const bool ok = p0 + bb * kBlock < L && blk >= 0;
-            const int64_t e = ok ? ((int64_t)blk * a.Hkv + kvh) * (kBlock * D) : 0;
-            kb[bb] = (uint64_t)(uintptr_t)(a.k_cache + e);
-            vb[bb] = (uint64_t)(uintptr_t)(a.v_cache + e);
+        for (int i = 0; i < LPW; ++i) {
+            ids.k[i] = s_bt[e0 + kbb[i]];
+            ids.v[i] = s_bt[e0 + vbb[i]];
         }
-        auto pick = [&](const uint64_t (&t)[4], int bb) __attribute__((always_inline)) -> const void * {
-            return (const void *)(uintptr_t)(bb == 0 ? t[0] : bb == 1 ? t[1] : bb == 2 ? t[2] : t[3]);
-        };
+        return ids;
+    };
+    auto issue_prefix_tile = [&](const TileIds &ids, uint32_t kdst, uint32_t vdst) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < C::kLoadsPerWave; ++i) {
-            const int j = wave + i * NW;
-            const int row0 = j * 64 / C::kCpr;                   // first MFMA row of this load
-            const int bb = ((row0 & ~31) | perm32(row0 & 31)) >> 4;
-            const int q = j * 64 + lane;
-            const int row = q / C::kCpr, pos = q % C::kCpr;
-            const int cc = pos ^ k_swz<D>(row);
-            const int key = (row & ~31) | perm32(row & 31);
-            const uint32_t off = (uint32_t)(((key & 15) * D + cc * 8) * 2);
-            load_lds16(pick(kb, bb), off, kl + j * 1024u);
+        for (int i = 0; i < LPW; ++i) {
+            const uint32_t hb = __builtin_amdgcn_readfirstlane(ids.k[i]);
+            load_lds16(a.k_cache + (uint64_t)hb * (kBlock * D), koff[i], kdst + (wave + i * NW) * 1024u);
         }
 #pragma unroll
-        for (int i = 0; i < C::kLoadsPerWave; ++i) {
-            const int j = wave + i * NW;
-            const int bb = j * 64 / (2 * D);
-            const int q = j * 64 + lane;
-            const int rem = q % (2 * D);
-            const int d = rem >> 1, pos = rem & 1;
-            const int h2 = v_slot(d, pos);   // v_slot is its own inverse in hh
-            const uint32_t off = (uint32_t)((d * kBlock + h2 * 8) * 2);
-            load_lds16(pick(vb, bb), off, vl + j * 1024u);
+        for (int i = 0; i < LPW; ++i) {
+            const uint32_t hb = __builtin_amdgcn_readfirstlane(ids.v[i]);
+            load_lds16(a.v_cache + (uint64_t)hb * (kBlock * D), voff[i], vdst + (wave + i * NW) * 1024u);
         }
     };
 
-    // bf16 -> fp16 of a landed prefix tile's V, in place; keys past the prefix
-    // become zero (unused cache slots may hold anything).
-    auto convert_prefix_v = [&](int it, char *buf) __attribute__((always_inline)) {
-        char *vl = buf + C::kKTileBytes;
+    // bf16 -> fp16 of a landed prefix tile's V, in place, in two halves so
+    // the S MFMAs can run between them (the compiler cannot tell the V writes
+    // from the K reads apart). `masked`: the tile ends past the prefix, whose
+    // keys become zero (unused cache slots may hold anything).
+    auto convert_load = [&](uint32_t vaddr, u32x4 (&cv)[C::kChPerThread]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < C::kChPerThread; ++r)
+            cv[r] = *lds_at<u32x4>(vaddr + (tid + r * C::kThreads) * 16);
+    };
+    auto convert_store = [&](int it, uint32_t vaddr, u32x4 (&cv)[C::kChPerThread], bool masked)
+                             __attribute__((always_inline)) {
         const int p0 = (t_begin + it) * kKT;
 #pragma unroll
         for (int r = 0; r < C::kChPerThread; ++r) {
             const int q = tid + r * C::kThreads;
-            u32x4 *pv = reinterpret_cast<u32x4 *>(vl + q * 16);
-            const u32x4 v = *pv;
-            uint32_t w[4] = {v.x, v.y, v.z, v.w};
-            const int bi = q / (2 * D), rem = q % (2 * D);
-            const int d = rem >> 1, pos = rem & 1;
-            const int h2 = v_slot(d, pos);   // v_slot is its own inverse in hh
-            const int valid = L - (p0 + bi * 16 + h2 * 8);
-            if (valid < 8) {
+            uint32_t w[4] = {cv[r].x, cv[r].y, cv[r].z, cv[r].w};
+            if (masked) {
+                const int bi = q / (2 * D), rem = q % (2 * D);
+                const int d = rem >> 1, hpos = rem & 1;
+                const int valid = L - (p0 + bi * 16 + v_slot(d, hpos) * 8);
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     if (e >= valid)
@@ -317,14 +346,13 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_kernel(AttnArgs a)
             h.y = bf16x2_to_f16x2(w[1]);
             h.z = bf16x2_to_f16x2(w[2]);
             h.w = bf16x2_to_f16x2(w[3]);
-            *pv = h;
+            *lds_at<u32x4>(vaddr + q * 16) = h;
         }
     };
 
     // Tree tile: through registers. K rows go to their MFMA rows; V rows are
     // feature-contiguous, so 8 features of a key are scattered (as fp16).
-    auto stage_tree_tile = [&](int it, char *kl) __attribute__((always_inline)) {
-        char *vl = kl + C::kKTileBytes;
+    auto stage_tree_tile = [&](int it, char *kl, char *vl) __attribute__((always_inline)) {
         const int j0 = (it - n_pre) * kKT;
 #pragma unroll 1   // keeps one chunk's registers live
         for (int r = 0; r < C::kChPerThread; ++r) {
@@ -353,229 +381,321 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_kernel(AttnArgs a)
         }
     };
 
-    // ---- accumulators --------------------------------------------------------
-    f32x16 oacc[C::kDTiles][CT];
+    // S^T = K Q^T for the two 32-key halves of a tile (MFMA: A = K rows from
+    // LDS, B = this wave's Q^T in registers). K fragment k of row 32t + col
+    // sits at col*2D + ((2k ^ x) << 4) + t*64D with x = hh ^ k_swz(col): a
+    // per-lane offset for each k, and a constant for t.
+    uint32_t kfrag[C::kKSteps];
 #pragma unroll
-    for (int m = 0; m < C::kDTiles; ++m)
-#pragma unroll
-        for (int c = 0; c < CT; ++c)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                oacc[m][c][e] = 0.f;
-    float m_used[CT];   // raw-score max the exponentials are taken against
-    float lsum[CT];     // this lane's share of the softmax denominator
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-        m_used[c] = -INFINITY;
-        lsum[c] = 0.f;
-    }
-    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-
-    __syncthreads();   // s_bt ready
-    if (n_tiles > 0) {
-        if (n_pre > 0)
-            issue_prefix_tile(0, TAV_LDS_ADDR(lds_a));
-        else
-            stage_tree_tile(0, lds_a);
-    }
-    lds_loads_landed();
-    if (n_pre > 0) {
-        convert_prefix_v(0, lds_a);
-        __syncthreads();
-    }
-
-    // One tile: compute on `cur` while the next tile streams into `nxt`.
-    auto tile_step = [&](int it, char *cur, char *nxt, uint32_t nxt_addr) __attribute__((always_inline)) {
-        if (it + 1 < n_pre)
-            issue_prefix_tile(it + 1, nxt_addr);
-
-        const char *kl = cur;
-        const char *vl = kl + C::kKTileBytes;
-
-        // S^T = K Q^T for two 32-key tiles and every column tile; each K
-        // fragment read from LDS feeds CT MFMAs
-        f32x16 sacc[2][CT];
+    for (int k = 0; k < C::kKSteps; ++k)
+        kfrag[k] = (uint32_t)(col * (2 * D) + (((2 * k) ^ hh ^ k_swz<D>(col)) << 4));
+    auto qk = [&](uint32_t kaddr, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int c = 0; c < CT; ++c)
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    sacc[t][c][e] = 0.f;
+            for (int e = 0; e < 16; ++e)
+                sacc[t][e] = 0.f;
 #pragma unroll
         for (int k = 0; k < C::kKSteps; ++k) {
+            const uint32_t ka = kaddr + kfrag[k];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const bf16x8 av =
-                    *reinterpret_cast<const bf16x8 *>(kl + k_off_row<D>(32 * t + col, 2 * k + hh));
-#pragma unroll
-                for (int c = 0; c < CT; ++c)
-                    sacc[t][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[c][k], sacc[t][c], 0, 0, 0);
+                const bf16x8 av = *lds_at<bf16x8>(ka + t * (64 * D));
+                sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[k], sacc[t], 0, 0, 0);
             }
-            // keep at most two k-steps of K fragments in flight (registers)
-            if (k & 1)
-                __builtin_amdgcn_sched_barrier(0);
         }
+    };
 
-        // masks: ragged prefix tail, or ancestor bits of the tree tile
-        // Accumulator entry (t, 4i+j) is key 32t + 16(i>>1) + 8hh + 4(i&1) + j;
-        // the lane-dependent 8hh is taken out once so the rest are constants.
+    // ---- accumulators --------------------------------------------------------
+    f32x16 oacc[C::kDTiles];
+#pragma unroll
+    for (int m = 0; m < C::kDTiles; ++m)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            oacc[m][e] = 0.f;
+    float m_used = -INFINITY;   // raw-score max the exponentials are taken against
+    float lsum = 0.f;           // this lane's share of the softmax denominator
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+
+    // Keys a tile may not see get score -inf: keys past the prefix in the
+    // last prefix tile of a split, and in tree tiles the keys that are not
+    // ancestors of this lane's node (or are not nodes). Accumulator entry
+    // (t, 4i+j) is key 32t + 16(i>>1) + 8hh + 4(i&1) + j.
+    auto apply_mask = [&](int it, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
+        uint64_t mw;   // bit k: key k of the tile is visible
+        int lim;       // keys at or past it are not keys
         if (it >= n_pre) {
             const int tt = it - n_pre;
-            const int nlim = a.N - tt * kKT - 8 * hh;   // keys at or past it are not nodes
-#pragma unroll
-            for (int c = 0; c < CT; ++c) {
-                uint64_t mw = 1;
-                if (row_ok[c])
-                    mw = a.mask[((int64_t)b * a.N + node[c]) * a.W + tt];
-                mw >>= 8 * hh;
-                const uint32_t mlo = (uint32_t)mw, mhi = (uint32_t)(mw >> 32);
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int kr = 16 * (i >> 1) + 4 * (i & 1) + j;   // < 32
-                            const uint32_t word = t ? mhi : mlo;
-                            const bool ok = (32 * t + kr < nlim) && ((word >> kr) & 1u);
-                            if (!ok)
-                                sacc[t][c][4 * i + j] = -INFINITY;
-                        }
-            }
+            mw = 1;    // a padding row sees key 0 only
+            if (row_ok)
+                mw = tt == 0 ? mrow0 : a.mask[((int64_t)b * a.N + node) * a.W + tt];
+            lim = a.N - tt * kKT;
         } else {
-            const int p0 = (t_begin + it) * kKT;
-            if (p0 + kKT > L) {
-                const int plim = L - p0 - 8 * hh;
-#pragma unroll
-                for (int c = 0; c < CT; ++c)
-#pragma unroll
-                    for (int t = 0; t < 2; ++t)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                const int kr = 32 * t + 16 * (i >> 1) + 4 * (i & 1) + j;
-                                if (kr >= plim)
-                                    sacc[t][c][4 * i + j] = -INFINITY;
-                            }
-            }
+            mw = ~0ull;
+            lim = L - (t_begin + it) * kKT;
         }
-
-        // online softmax with lazy rescaling, per column tile
-        f16x8 pb[CT][2][2];
+        mw >>= 8 * hh;
+        lim -= 8 * hh;
+        const uint32_t mlo = (uint32_t)mw, mhi = (uint32_t)(mw >> 32);
 #pragma unroll
-        for (int c = 0; c < CT; ++c) {
-            float mt = -INFINITY;
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    mt = fmaxf(mt, sacc[t][c][e]);
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const bool need = mt > m_used[c] + a.th;
-            if (__any(need)) {
-                const float mnew = need ? mt : m_used[c];
-                const float alpha =
-                    (m_used[c] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_used[c] - mnew) * a.c);
-#pragma unroll
-                for (int m = 0; m < C::kDTiles; ++m)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        oacc[m][c][e] *= alpha;
-                lsum[c] *= alpha;
-                m_used[c] = mnew;
-            }
-            // weights 2^(s*c - m*c + 7): at most 2^15 after the lazy threshold
-            const float moff = (m_used[c] == -INFINITY) ? 0.f : m_used[c] * a.c - kWeightBias;
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2) {
-                        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[t][c][8 * h2 + e], a.c, -moff));
-                        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[t][c][8 * h2 + e + 1], a.c, -moff));
-                        const f32x2 pf = {p0, p1};
-                        const f16x2 pk = __builtin_convertvector(pf, f16x2);
-                        pb[c][t][h2][e] = pk[0];
-                        pb[c][t][h2][e + 1] = pk[1];
-                        lsum[c] = __builtin_amdgcn_fdot2(pk, ones, lsum[c], false);
-                    }
+                for (int j = 0; j < 4; ++j) {
+                    const int kr = 16 * (i >> 1) + 4 * (i & 1) + j;   // < 32
+                    const uint32_t word = t ? mhi : mlo;
+                    const bool ok = (32 * t + kr < lim) && ((word >> kr) & 1u);
+                    if (!ok)
+                        sacc[t][4 * i + j] = -INFINITY;
                 }
-        }
+    };
 
-        // O^T += V^T P^T; each V fragment read from LDS feeds CT MFMAs
+    // Online softmax of one tile's scores, without branches: the running max
+    // only moves when the tile exceeds it by more than 2^8 in probability
+    // (then alpha < 1 rescales what was accumulated before), and the weights
+    // 2^(s*c - m*c + 7), at most 2^15, go to pb as fp16.
+    auto softmax = [&](f32x16 (&sacc)[2], f16x8 (&pb)[2][2], float &alpha) __attribute__((always_inline)) {
+        // (NaN-propagating maximum: no canonicalising of the MFMA results; a
+        // NaN score leaves the max alone and surfaces in the output check)
+        float mt = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; e += 2)
+                mt = __builtin_elementwise_maximum(mt, __builtin_elementwise_maximum(sacc[t][e], sacc[t][e + 1]));
+        {   // the other half of the wave holds the same column's other keys
+            const uint32_t u = __builtin_bit_cast(uint32_t, mt);
+            const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+            const uint32_t u0 = sw[0];
+            const uint32_t u1 = sw[1];
+            mt = __builtin_elementwise_maximum(__builtin_bit_cast(float, u0), __builtin_bit_cast(float, u1));
+        }
+        const bool need = mt > m_used + a.th;
+        const float mnew = need ? mt : m_used;
+        // m_used = -inf gives exp2(-inf) = 0: nothing accumulated yet
+        alpha = need ? __builtin_amdgcn_exp2f((m_used - mnew) * a.c) : 1.0f;
+        m_used = mnew;
+        lsum *= alpha;
+        const float moff = (m_used == -INFINITY) ? 0.f : m_used * a.c - kWeightBias;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * h2 + e], a.c, -moff));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * h2 + e + 1], a.c, -moff));
+                    const f32x2 pf = {p0, p1};
+                    const f16x2 pk = __builtin_convertvector(pf, f16x2);
+                    pb[t][h2][e] = pk[0];
+                    pb[t][h2][e + 1] = pk[1];
+                    lsum = __builtin_amdgcn_fdot2(pk, ones, lsum, false);
+                }
+            }
+    };
+
+    // O^T += V^T P^T for one tile (MFMA: A = V^T from the fp16 V tile at LDS
+    // byte address vaddr, B = the weights). Feature d = 32m + col of block bi
+    // sits at v_off(bi, d, hh) = bi*32D + 1024m + v_off(0, col, hh): one
+    // per-lane base register and constant offsets that fit the LDS
+    // instruction's offset field.
+    auto pv = [&](const f16x8 (&pb)[2][2], uint32_t vaddr) __attribute__((always_inline)) {
+        uint32_t base = vaddr + (uint32_t)v_off<D>(0, col, hh);
+        asm("" : "+v"(base));   // keep the sum in one register
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                 for (int m = 0; m < C::kDTiles; ++m) {
-                    const f16x8 av =
-                        *reinterpret_cast<const f16x8 *>(vl + v_off<D>(2 * t + h2, 32 * m + col, hh));
-#pragma unroll
-                    for (int c = 0; c < CT; ++c)
-                        oacc[m][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[c][t][h2], oacc[m][c], 0, 0, 0);
-                    if (m & 1)
-                        __builtin_amdgcn_sched_barrier(0);
+                    const f16x8 av = *lds_at<f16x8>(base + (uint32_t)((2 * t + h2) * (D * 32) + m * 1024));
+                    oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[t][h2], oacc[m], 0, 0, 0);
                 }
+    };
 
-        if (it + 1 < n_tiles) {
-            if (it + 1 >= n_pre)
-                stage_tree_tile(it + 1, nxt);
-            lds_loads_landed();
-            if (it + 1 < n_pre) {
-                convert_prefix_v(it + 1, nxt);
-                __syncthreads();
+    // ---- the tile pipeline ---------------------------------------------------
+    // Tile t's K sits in K slot t % 3 and its V in V slot t % 5; both are
+    // filled two steps ahead, by direct loads (prefix tiles) or through
+    // registers (tree tiles). Every step starts by waiting for tile t (tile
+    // t+1's loads may stay in flight) and passing the step's only barrier,
+    // after which every wave is done with tile t-1's K and tile t-3's V; it
+    // then fills tile t+2 into those slots. Per tile a wave has an MFMA phase
+    //   Q(t): S = K Q^T (and tile t's V turned into fp16 meanwhile)
+    // and a phase that is mostly vector ALU work:
+    //   R(t): the softmax of tile t, with P.V of the tile before on the
+    //         matrix cores in between.
+    // The two waves that share a SIMD (waves w and w+4 of an 8-wave
+    // workgroup) run them in opposite order: one runs Q(t) R(t) in step t,
+    // the other R(t-1) Q(t), carrying S across the barrier. Each one's
+    // vector work then overlaps the other's MFMAs. A rescale of O (rare)
+    // waits for the P.V before it through the register dependency.
+    const bool lag = NW == 8 && wave >= NW / 2;
+    auto fill = [&](int t, const TileIds &ids) __attribute__((always_inline)) {
+        const int kslot = t % kKSlots, vslot = t % kVSlots;
+        if (t < n_pre)
+            issue_prefix_tile(ids, k_lds + kslot * KTB, v_lds + vslot * VTB);
+        else if (t < n_tiles)
+            stage_tree_tile(t, s_k + kslot * KTB, s_v + vslot * VTB);
+    };
+    // "tiles -2 and -1" (V slots 3 and 4) contribute nothing: zero weights
+    // times zero V
+    for (int q = tid; q < 2 * VTB / 16; q += C::kThreads)
+        *lds_at<u32x4>(v_lds + 3 * VTB + q * 16) = u32x4{0, 0, 0, 0};
+    __syncthreads();   // s_bt written by all threads before any wave reads it
+    fill(0, read_ids(0));
+    fill(1, read_ids(1));
+
+    f16x8 pb_prev[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                pb_prev[t][h2][e] = (_Float16)0.0f;
+    f32x16 sacc[2];   // the lagging wave's "tile -1" scores: all masked
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            sacc[t][e] = -INFINITY;
+
+    // Q(it): scores of tile it into sacc.
+    auto phase_q = [&](int it, uint32_t kcur, uint32_t vcur) __attribute__((always_inline)) {
+        if (it < n_pre && (t_begin + it + 1) * kKT <= L) {
+            // a whole prefix tile: its V conversion hides under the S MFMAs
+            u32x4 cv[C::kChPerThread];
+            convert_load(vcur, cv);
+            qk(kcur, sacc);
+            convert_store(it, vcur, cv, false);
+            // K fragment reads run four MFMAs ahead
+#pragma unroll
+            for (int i = 0; i < C::kChPerThread + 4; ++i)
+                __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 1);
+#pragma unroll
+            for (int i = 0; i < 2 * C::kKSteps; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 1);
+                if (i + 4 < 2 * C::kKSteps)
+                    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(kSgValu, 2, 1);
             }
+        } else {
+            if (it < n_pre) {
+                u32x4 cv[C::kChPerThread];
+                convert_load(vcur, cv);
+                convert_store(it, vcur, cv, true);
+            }
+            qk(kcur, sacc);
+            apply_mask(it, sacc);
         }
     };
-    for (int it = 0; it < n_tiles; it += 2) {
-        tile_step(it, lds_a, lds_b, TAV_LDS_ADDR(lds_b));
-        if (it + 1 < n_tiles)
-            tile_step(it + 1, lds_b, lds_a, TAV_LDS_ADDR(lds_a));
-    }
+    // R: P.V of the tile whose weights are in pb_prev (its fp16 V at vprev),
+    // then the softmax of sacc into pb_prev.
+    auto phase_r = [&](uint32_t vprev) __attribute__((always_inline)) {
+        f16x8 pb[2][2];
+        float alpha;
+        // The softmax first, as one stretch of vector work with no LDS waits
+        // in it (a wave issues in order: a wait would hold up everything
+        // behind it), then P.V of the tile before.
+        softmax(sacc, pb, alpha);
+        asm volatile("" ::"v"(pb[0][0]), "v"(pb[0][1]), "v"(pb[1][0]), "v"(pb[1][1]), "v"(lsum));
+        __builtin_amdgcn_sched_barrier(0);
+        pv(pb_prev, vprev);
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+            for (int m = 0; m < C::kDTiles; ++m)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    oacc[m][e] *= alpha;
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+                pb_prev[t][h2] = pb[t][h2];
+    };
+
+    // one loop per phase order, so each gets its own register allocation
+    // (every wave passes the same number of barriers)
+    auto run = [&](auto lag_c) __attribute__((always_inline)) {
+        constexpr bool kLag = decltype(lag_c)::value;
+        int kslot = 0, vslot = 0;   // tile it's slots
+        auto vslot_back = [&](int n) __attribute__((always_inline)) {
+            const int v = vslot - n;
+            return v < 0 ? v + kVSlots : v;
+        };
+        for (int it = 0; it < n_tiles; ++it) {
+            TileIds ids{};
+            if (it + 2 < n_pre)
+                ids = read_ids(it + 2);
+            if (it + 1 < n_pre)
+                wait_vmem<(2 * LPW < 64 ? 2 * LPW : 63)>();   // beyond the counter's range: waits longer
+            else
+                wait_vmem<0>();
+            __syncthreads();
+            fill(it + 2, ids);
+
+            const uint32_t kcur = k_lds + kslot * KTB;
+            const uint32_t vcur = v_lds + vslot * VTB;
+            if (!kLag) {
+                phase_q(it, kcur, vcur);
+                phase_r(v_lds + vslot_back(1) * VTB);
+            } else {
+                phase_r(v_lds + vslot_back(2) * VTB);
+                phase_q(it, kcur, vcur);
+            }
+            kslot = kslot == kKSlots - 1 ? 0 : kslot + 1;
+            vslot = vslot == kVSlots - 1 ? 0 : vslot + 1;
+        }
+        if (n_tiles > 0) {
+            if (kLag)
+                phase_r(v_lds + vslot_back(2) * VTB);   // softmax of the last tile
+            __syncthreads();             // the last tile's fp16 V is visible
+            pv(pb_prev, v_lds + vslot_back(1) * VTB);
+        }
+    };
+    if (lag)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
 
     // ---- write the result or the split's partial ------------------------------
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    if (!row_ok)
+        return;
+    if (a.S == 1) {
+        const float inv = 1.0f / ltot;
+        float *orow = a.out + (((int64_t)b * a.N + node) * a.Hq + head) * D;
+        bool finite = true;
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-        const float ltot = lsum[c] + __shfl_xor(lsum[c], 32);
-        if (!row_ok[c])
-            continue;
-        if (a.S == 1) {
-            const float inv = 1.0f / ltot;
-            float *orow = a.out + (((int64_t)b * a.N + node[c]) * a.Hq + head[c]) * D;
-            bool finite = true;
+        for (int m = 0; m < C::kDTiles; ++m)
 #pragma unroll
-            for (int m = 0; m < C::kDTiles; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const f32x4 v = {oacc[m][c][4 * i] * inv, oacc[m][c][4 * i + 1] * inv,
-                                     oacc[m][c][4 * i + 2] * inv, oacc[m][c][4 * i + 3] * inv};
-                    finite &= __builtin_isfinite(v.x) && __builtin_isfinite(v.y) &&
-                              __builtin_isfinite(v.z) && __builtin_isfinite(v.w);
-                    *reinterpret_cast<f32x4 *>(orow + 32 * m + 8 * i + 4 * hh) = v;
-                }
-            if (!finite)
-                raise_flag(a.flags, TAV_FLAG_ATTN_RANGE);
-        } else {
-            const int64_t P = ((int64_t)bh * a.RB + rb) * a.S + s;
-            const int rloc = wave * C::kWaveRows + 32 * c + col;
-            float *po = a.part_o + (P * C::kRows + rloc) * D;
-#pragma unroll
-            for (int m = 0; m < C::kDTiles; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const f32x4 v = {oacc[m][c][4 * i], oacc[m][c][4 * i + 1], oacc[m][c][4 * i + 2],
-                                     oacc[m][c][4 * i + 3]};
-                    *reinterpret_cast<f32x4 *>(po + 32 * m + 8 * i + 4 * hh) = v;
-                }
-            if (hh == 0) {
-                float *pml = a.part_ml + (P * C::kRows + rloc) * 2;
-                pml[0] = (m_used[c] == -INFINITY) ? -INFINITY : m_used[c] * a.c;
-                pml[1] = ltot;
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 v = {oacc[m][4 * i] * inv, oacc[m][4 * i + 1] * inv,
+                                 oacc[m][4 * i + 2] * inv, oacc[m][4 * i + 3] * inv};
+                finite &= __builtin_isfinite(v.x) && __builtin_isfinite(v.y) &&
+                          __builtin_isfinite(v.z) && __builtin_isfinite(v.w);
+                *reinterpret_cast<f32x4 *>(orow + 32 * m + 8 * i + 4 * hh) = v;
             }
+        if (!finite)
+            raise_flag(a.flags, TAV_FLAG_ATTN_RANGE);
+    } else {
+        const int64_t P = ((int64_t)bh * a.RB + rb) * a.S + s;
+        const int rloc = wave * 32 + col;
+        float *po = a.part_o + (P * C::kRows + rloc) * D;
+#pragma unroll
+        for (int m = 0; m < C::kDTiles; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 v = {oacc[m][4 * i], oacc[m][4 * i + 1], oacc[m][4 * i + 2],
+                                 oacc[m][4 * i + 3]};
+                *reinterpret_cast<f32x4 *>(po + 32 * m + 8 * i + 4 * hh) = v;
+            }
+        if (hh == 0) {
+            float *pml = a.part_ml + (P * C::kRows + rloc) * 2;
+            pml[0] = (m_used == -INFINITY) ? -INFINITY : m_used * a.c;
+            pml[1] = ltot;
         }
     }
 }
@@ -623,7 +743,7 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(AttnArgs a, int 
 }
 
 struct AttnPlan {
-    int NW, CT, rows, RB, S, KS;
+    int NW, rows, RB, S, KS;
     int64_t grid;
     size_t part_o_bytes, part_ml_bytes, ws_bytes;
 };
@@ -633,40 +753,36 @@ size_t round_up(size_t v, size_t al) { return (v + al - 1) / al * al; }
 constexpr int kMinTilesPerSplit = 4;   // below this, partials cost more than the split gains
 
 template <int D>
-const void *kernel_for(int NW, int CT)
+const void *kernel_for(int NW)
 {
-    (void)CT;
     switch (NW) {
     case 8:
-        return reinterpret_cast<const void *>(tree_attn_kernel<D, 8, 1>);
+        return reinterpret_cast<const void *>(tree_attn_kernel<D, 8>);
     case 4:
-        return reinterpret_cast<const void *>(tree_attn_kernel<D, 4, 1>);
+        return reinterpret_cast<const void *>(tree_attn_kernel<D, 4>);
     case 2:
-        return reinterpret_cast<const void *>(tree_attn_kernel<D, 2, 1>);
+        return reinterpret_cast<const void *>(tree_attn_kernel<D, 2>);
     default:
-        return reinterpret_cast<const void *>(tree_attn_kernel<D, 1, 1>);
+        return reinterpret_cast<const void *>(tree_attn_kernel<D, 1>);
     }
 }
 
-// Work decomposition for a shape: rows per wave (32*CT), waves per workgroup
-// (NW), row blocks (RB) and prefix splits (S), enough workgroups to fill the
+// Work decomposition for a shape: waves per workgroup (NW, 32 query rows
+// each), row blocks (RB) and prefix splits (S), enough workgroups to fill the
 // device once.
 bool attn_plan(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_prefix_len,
                AttnPlan &p)
 {
     const int G = Hq / Hkv;
     const int NG = N * G;
-    // 32 query rows per wave, up to 4 waves per workgroup; two workgroups
-    // share a CU so one's softmax overlaps the other's MFMAs
-    p.CT = 1;
     p.NW = NG > 128 ? 8 : NG > 64 ? 4 : NG > 32 ? 2 : 1;
-    p.rows = 32 * p.CT * p.NW;
+    p.rows = 32 * p.NW;
     p.RB = (int)ceil_div(NG, p.rows);
     const int cus = device_cu_count();
     if (cus <= 0)
         return false;
     int per_cu = 0;
-    const void *fn = D == 128 ? kernel_for<128>(p.NW, p.CT) : kernel_for<64>(p.NW, p.CT);
+    const void *fn = D == 128 ? kernel_for<128>(p.NW) : kernel_for<64>(p.NW);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, p.NW * 64, 0) != hipSuccess ||
         per_cu <= 0)
         return false;
@@ -698,10 +814,10 @@ bool attn_shape_ok(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
            (D == 64 || D == 128) && (int64_t)(Hq / Hkv) * N <= 4096 && max_prefix_len >= 0;
 }
 
-template <int D, int NW, int CT>
+template <int D, int NW>
 hipError_t launch_main(const AttnPlan &p, const AttnArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL((tree_attn_kernel<D, NW, CT>), dim3((unsigned)p.grid), dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((tree_attn_kernel<D, NW>), dim3((unsigned)p.grid), dim3(NW * 64), 0, s, a);
     return hipGetLastError();
 }
 
@@ -710,13 +826,13 @@ hipError_t launch_main_d(const AttnPlan &p, const AttnArgs &a, hipStream_t s)
 {
     switch (p.NW) {
     case 8:
-        return launch_main<D, 8, 1>(p, a, s);
+        return launch_main<D, 8>(p, a, s);
     case 4:
-        return launch_main<D, 4, 1>(p, a, s);
+        return launch_main<D, 4>(p, a, s);
     case 2:
-        return launch_main<D, 2, 1>(p, a, s);
+        return launch_main<D, 2>(p, a, s);
     default:
-        return launch_main<D, 1, 1>(p, a, s);
+        return launch_main<D, 1>(p, a, s);
     }
 }
 
