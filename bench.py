@@ -10,9 +10,13 @@ copies of the paged caches rotate across steps so the 256 MB last-level cache
 cannot hold the step's KV working set.
 
 Prints one JSON line: verified tree nodes/s (B*N per step time), with the
-attention kernel's roofline and the CPU oracle's rate on this host.
+attention launch's roofline and the CPU oracle's rate on this host. The
+attention launch (main kernel + combine) is timed with events on its stream
+inside the timed region; its HBM traffic comes from the rocprofv3 counter
+record under profiles/ while that record matches the kernel source.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config llama70b] [--no-cpu]
+    python bench.py --copy-calibration     # a plain copy of known size, for the counters
 """
 
 from __future__ import annotations
@@ -31,6 +35,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "tree_attn_llama70b_hbm_traffic.txt")
+COPY_BYTES = 1 << 30           # each of the calibration copy's read and write
 
 
 def workload_desc(w) -> str:
@@ -125,12 +131,16 @@ def run_gpu(args, w):
                         w.block, slots, new_len, flags, stream),
         ))
 
-    def step(i, ev=None):
+    def step(i, ev=None, attn_ev=None):
         c = calls[i % len(calls)]
         if ev:
             ev[0].record(stream)
         for k in range(4):
+            if attn_ev and k == 1:
+                attn_ev[0].record(stream)
             c[k]()
+            if attn_ev and k == 1:
+                attn_ev[1].record(stream)
             if ev:
                 ev[k + 1].record(stream)
 
@@ -138,15 +148,18 @@ def run_gpu(args, w):
         step(i)
     torch.cuda.synchronize()
 
-    # the timed region: exactly `steps` steps between two synchronised events
+    # the timed region: exactly `steps` steps between two synchronised events;
+    # the attention launch of every step is bracketed by events on its stream
+    attn_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i)
+        step(args.warmup + i, attn_ev=attn_evs[i])
     stop.record(stream)
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(stop) / args.steps
+    ms_attn = float(np.mean([e[0].elapsed_time(e[1]) for e in attn_evs]))
 
     # per-stage times with events on the launch stream (a second pass)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
@@ -157,8 +170,20 @@ def run_gpu(args, w):
     stage = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in evs])
     stage_ms = stage.mean(axis=0)
     assert int(flags.item()) == 0, f"device flags {int(flags.item()):#x}"
-    return dict(ms_step=ms_step, stage_ms=stage_ms, depth=to_numpy(depth), path=to_numpy(path),
-                n_acc=to_numpy(n_acc))
+    return dict(ms_step=ms_step, ms_attn=ms_attn, stage_ms=stage_ms, depth=to_numpy(depth),
+                path=to_numpy(path), n_acc=to_numpy(n_acc))
+
+
+def copy_calibration(reps=5):
+    """A plain device copy of COPY_BYTES (read and written once each), for
+    scaling the HBM counters of the attention launch."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.add(src, 0.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "reps": reps}), flush=True)
 
 
 def cpu_baseline(w, min_seconds=10.0):
@@ -190,29 +215,37 @@ def main():
     ap.add_argument("--config", default="llama70b")
     ap.add_argument("--cache-copies", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain copy of known size (for the HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
               "(the path is single-GPU; see DESIGN.md for how it would shard)", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
     from synth import make_workload
+    from tree_attention_verification_ancestor_amd.profiling import current_traffic
     w = make_workload(args.config)
     g = run_gpu(args, w)
 
     attn_bytes, attn_flops = attention_work(w, g["depth"])
-    t_attn = g["stage_ms"][1] * 1e-3
+    t_attn = g["ms_attn"] * 1e-3
     tflops = attn_flops / t_attn / 1e12
     gbs = attn_bytes / t_attn / 1e9
     t_hbm = attn_bytes / (HBM_PEAK_GBS * 1e9)
     t_mfma = attn_flops / (MFMA_PEAK_TFLOPS * 1e12)
     bound = "mfma" if t_mfma >= t_hbm else "hbm"
+    traffic = current_traffic(TRAFFIC_RECORD) if args.config == "llama70b" else None
     if bound == "mfma":
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": traffic}
     else:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
 
     step_bytes = attn_bytes + sampler_bytes(w, g["path"], g["n_acc"]) + commit_bytes(w, g["n_acc"])
     t_floor = max(step_bytes / (HBM_PEAK_GBS * 1e9), attn_flops / (MFMA_PEAK_TFLOPS * 1e12))
@@ -238,7 +271,8 @@ def main():
         "stages_us": {k: round(v * 1e3, 2) for k, v in
                       zip(["tree_mask_build", "tree_attn_verify", "spec_verify_sample",
                            "kv_commit_path"], g["stage_ms"])},
-        "tree_attn": {"hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "tree_attn": {"us": round(t_attn * 1e6, 2),
+                      "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                       "tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
                       "algorithmic_bytes": attn_bytes, "algorithmic_flops": attn_flops,
                       "roofline_frac": round(max(t_hbm, t_mfma) / t_attn, 4)},
