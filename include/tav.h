@@ -116,7 +116,8 @@ size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, 
  *   workspace      device buffer of >= tree_attn_workspace_bytes(...) bytes
  *                  (256-byte aligned; NULL allowed when that is 0)
  *   Supported: D in {64, 128}, block_size == 16, Hq % Hkv == 0,
- *   1 <= N <= 256, Hq/Hkv * N <= 4096. bf16 tensors 16-byte aligned.
+ *   1 <= N <= 256, Hq/Hkv * N <= 4096, num_blocks * Hkv < 2^32 (cache
+ *   block-heads are indexed with 32 bits). bf16 tensors 16-byte aligned.
  *   Precision: Q·K runs as a bf16 MFMA with fp32 accumulation; the weights
  *   and V enter the P·V MFMA as fp16 (V converts from bf16 exactly while
  *   |v| < 65520), accumulating in fp32.

@@ -57,6 +57,7 @@ def _attn(**kw):
     (dict(D=96), tav.ERR_UNSUPPORTED), (dict(Hq=7), tav.ERR_UNSUPPORTED),
     (dict(block_size=32), tav.ERR_UNSUPPORTED), (dict(N=300), tav.ERR_UNSUPPORTED),
     (dict(N=256, Hq=64, Hkv=2), tav.ERR_UNSUPPORTED),
+    (dict(num_blocks=(1 << 31) - 1, Hq=8, Hkv=4), tav.ERR_UNSUPPORTED),
     (dict(q=ctypes.c_void_p(0x10008)), tav.ERR_ARG),
 ])
 def test_attention_rejects_bad_arguments(kw, code):

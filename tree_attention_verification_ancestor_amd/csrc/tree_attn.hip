@@ -868,7 +868,8 @@ extern "C" tav_status tree_attn_verify(const uint16_t *q, const uint16_t *k_tree
     if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || num_blocks < 1 || max_blocks < 1 ||
         max_prefix_len < 0 || !(scale > 0.0f) || !(scale < INFINITY))
         return TAV_ERR_ARG;
-    if (!attn_shape_ok(B, N, Hq, Hkv, D, max_prefix_len) || block_size != kBlock)
+    if (!attn_shape_ok(B, N, Hq, Hkv, D, max_prefix_len) || block_size != kBlock ||
+        (int64_t)num_blocks * Hkv > (int64_t)UINT32_MAX)
         return TAV_ERR_UNSUPPORTED;
     if (!aligned(q, 16) || !aligned(k_tree, 16) || !aligned(v_tree, 16) || !aligned(k_cache, 16) ||
         !aligned(v_cache, 16) || !aligned(mask, 8) || !aligned(out, 16) || !aligned(block_table, 4) ||
