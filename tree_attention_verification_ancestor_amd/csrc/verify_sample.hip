@@ -1,5 +1,6 @@
 // spec_verify_sample: target/draft softmax over the vocabulary and the
-// root-down rejection-sampling walk, all in float64.
+// root-down rejection-sampling walk, in float64 arithmetic (the per-token
+// exponentials of the vocabulary-wide sums to 1e-7 relative, see exp_bulk).
 //
 // The rule (radar-34b blog §2, rejection-sampling acceptance condition): a
 // draft x drawn from q is kept with probability min(1, p(x)/q(x)); on a
@@ -16,15 +17,18 @@
 // threads), so every pass over a row after the first is register-resident.
 // The walk is serial; for each visited node u the group
 //   1. takes its chunk of target row u (and draft row u if u has children)
-//      and the logits of u's children's tokens, reduces a local
-//      (max, sum exp) per row and exchanges it (one group sync). Every
-//      workgroup merges the wpg pairs in the same order, so all hold
-//      bit-identical normalisers and per-chunk masses;
-//   2. tests the children in order. p(x), q(x) and the residual at x are
-//      recomputed from the logits at x with the same instructions in every
-//      workgroup, so every workgroup takes the same decision. Meanwhile the
-//      rows of u's first child, the likeliest next node, are already being
-//      fetched, so a walk down first children never waits on memory;
+//      and the logits of u's children's tokens; each wave reduces a local
+//      (max, sum exp) per row with DPP, wave 0 merges the waves' pairs and
+//      exchanges the chunk's pair with the group (one group sync), then
+//      merges the wpg pairs in member order, so every workgroup holds
+//      bit-identical normalisers and per-chunk masses. Wave 0 also takes
+//      p(x) and q(x) of every child's token (one lane per child);
+//   2. tests the children in order against the running residual, from those
+//      values and the node's Philox uniforms (all computed once per
+//      sequence), the same instructions in every workgroup, so every
+//      workgroup takes the same decision. Meanwhile the rows of u's first
+//      child, the likeliest next node, are already being fetched, so a walk
+//      down first children never waits on memory;
 //   3. after each rejection exchanges the chunk sums of max(0, p_res - q)
 //      (one group sync), which give the new normaliser and the new chunk
 //      masses, and updates its registers;
@@ -38,7 +42,7 @@
 // split in two). Words are written and read with agent-scope 64-bit atomics,
 // which are single-copy atomic and stay coherent across XCDs at the memory
 // side, so no cache is flushed or invalidated and no write has to be
-// acknowledged before another: a reader polls a member's words (one lane per
+// acknowledged before another: wave 0 polls a member's words (one lane per
 // member) until every one carries the current generation. Two parities
 // suffice: a member can only reuse a slot after every member has arrived at
 // the sync in between, i.e. after everyone has read it. The grid never
@@ -48,10 +52,11 @@
 // a device shared with other work. The last workgroup to finish clears every
 // slot, so each call leaves the workspace as it found it (zero-filled).
 //
-// exp. Every exponential is exp_f64 below: a 64-entry table of 2^(j/64) and
-// a degree-6 polynomial on |r| <= ln2/128 (a few ulp), about a third of the
-// instructions of the general-purpose routine, which matters because the
-// stats pass takes one exp per vocabulary entry and row.
+// exp. The stats pass takes one exponential per vocabulary entry and row,
+// which makes it bound by the vector ALUs; those use exp_bulk (an fp32
+// head and an fp64 tail, 1e-7 relative). The few exponentials a decision
+// reads directly (p and q at a child's token, the merges) use exp_f64, a
+// table-free fp64 routine within one ulp.
 
 #include <algorithm>
 
@@ -91,39 +96,53 @@ struct SvArgs {
 };
 
 // ---------------------------------------------------------------------------
-// exp in float64: x = (n/64) ln2 + r, exp(x) = 2^(n>>6) * 2^((n&63)/64) * e^r.
+// exp in float64 without a table: x = n ln2 + r with |r| <= ln2/2 (ln 2 in
+// two parts, so n*hi is exact), e^r - 1 = r + r^2 (1/2! + r/3! + ... +
+// r^11/13!) with the bracket evaluated by Estrin's scheme (a short dependency
+// chain), then 2^n (1 + (e^r - 1)). The truncation error is below 5e-18;
+// the result is within one ulp (checked on the CPU against a 40-digit
+// reference over 45000 arguments).
 
-struct ExpTable {
-    double t[64];   // 2^(j/64)
-};
-
-__device__ __forceinline__ double exp_f64(double x, const ExpTable &T)
+__device__ __forceinline__ double exp_f64(double x)
 {
     if (x < -746.0)
-        return 0.0;   // below the smallest subnormal (also x = -inf); NaN falls through
-    constexpr double kScale = 0x1.71547652b82fep+6;        // 64 / ln 2
-    constexpr double kLn2Hi = 0x1.62e42fee00000p-1 / 64.0;  // ln 2 / 64, high part (exact n*hi)
-    constexpr double kLn2Lo = 0x1.a39ef35793c76p-33 / 64.0; // ln 2 / 64, low part
+        return 0.0;   // below the smallest subnormal (also x = -inf)
+    constexpr double kLog2e = 0x1.71547652b82fep+0;
+    constexpr double kLn2Hi = 0x1.62e42fee00000p-1;
+    constexpr double kLn2Lo = 0x1.a39ef35793c76p-33;
     constexpr double kRound = 0x1.8p52;
     x = fmin(x, 709.0);
-    const double nd = (x * kScale + kRound) - kRound;        // nearest integer to 64x/ln2
+    const double nd = (x * kLog2e + kRound) - kRound;   // nearest integer to x/ln2
     const int n = (int)nd;
     double r = fma(-nd, kLn2Hi, x);
     r = fma(-nd, kLn2Lo, r);
-    // e^r - 1 = r + r^2 (1/2 + r (1/6 + r (1/24 + r (1/120 + r/720))))
-    double p = fma(r, 1.0 / 720.0, 1.0 / 120.0);
-    p = fma(r, p, 1.0 / 24.0);
-    p = fma(r, p, 1.0 / 6.0);
-    p = fma(r, p, 0.5);
-    p = fma(r * r, p, r);
-    const double t = T.t[n & 63];
-    return ldexp(fma(t, p, t), n >> 6);
+    const double r2 = r * r, r4 = r2 * r2, r8 = r4 * r4;
+    const double a0 = fma(1.0 / 6.0, r, 1.0 / 2.0);
+    const double a1 = fma(1.0 / 120.0, r, 1.0 / 24.0);
+    const double a2 = fma(1.0 / 5040.0, r, 1.0 / 720.0);
+    const double a3 = fma(1.0 / 362880.0, r, 1.0 / 40320.0);
+    const double a4 = fma(1.0 / 39916800.0, r, 1.0 / 3628800.0);
+    const double a5 = fma(1.0 / 6227020800.0, r, 1.0 / 479001600.0);
+    const double b0 = fma(a1, r2, a0), b1 = fma(a3, r2, a2), b2 = fma(a5, r2, a4);
+    const double q = fma(b2, r8, fma(b1, r4, b0));
+    return ldexp(1.0 + fma(r2, q, r), n);
 }
 
-__device__ void exp_table_init(ExpTable &T)
+// The vocabulary-wide terms exp(y), y <= 0: 2^t with t = y log2(e) split into
+// an fp32 head (v_exp_f32, under one fp32 ulp) and an fp64 tail, 2^tl taken to
+// first order. Within 1e-7 relative (8.2e-8 measured over [-80, 0]); terms
+// below 2^-126 of the row's maximum flush to zero. Sums and decisions stay in
+// fp64, so a decision can differ from an all-fp64 one only for a draw within
+// about 1e-7 of its boundary.
+__device__ __forceinline__ double exp_bulk(double y)
 {
-    if (threadIdx.x < 64)
-        T.t[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+    constexpr double kLog2e = 0x1.71547652b82fep+0;
+    constexpr double kLn2 = 0x1.62e42fefa39efp-1;
+    const double t = y * kLog2e;
+    const float th = (float)t;
+    const double tl = t - (double)th;
+    const float e = __builtin_amdgcn_exp2f(th);
+    return y < -745.0 ? 0.0 : (double)e * fma(tl, kLn2, 1.0);
 }
 
 // ---------------------------------------------------------------------------
@@ -235,37 +254,22 @@ __device__ __forceinline__ uint64_t tag_word(uint32_t gen, uint32_t payload)
     return ((uint64_t)gen << 32) | payload;
 }
 
-// Threads 0..NW-1 publish word i = mine[i] (32 payload bits) in this
-// workgroup's slot for generation `gen`; on return (true) thread t < wpg holds
-// member t's payloads in got[0..NW). A group of one workgroup exchanges
-// nothing. Returns false on a timeout.
+// Wave 0 only. Lanes 0..NW-1 publish word i = mine (lane i's payload) in
+// this workgroup's slot for generation `gen`; then lane l polls members l,
+// l+64, ... and stores member m's payloads in got[m][0..NW) (LDS, read back
+// by the same lane). Returns false on a timeout (every lane).
 template <int NW>
-__device__ bool group_sync(uint64_t *box, int wpg, int rank, uint32_t gen,
-                           const uint32_t (&mine)[NW], uint32_t (&got)[NW], uint32_t *flags)
+__device__ bool wave0_exchange(uint64_t *box, int wpg, int rank, uint32_t gen, uint32_t mine,
+                               uint32_t (*got)[kSlotWords])
 {
-    if (wpg == 1) {
-#pragma unroll
-        for (int i = 0; i < NW; ++i)
-            got[i] = mine[i];
-        return true;
-    }
+    const int lane = threadIdx.x & 63;
     uint64_t *base = box + (size_t)(gen & 1u) * wpg * kSlotWords;
-    __syncthreads();
-    if (threadIdx.x < NW) {
-        uint32_t v = 0;
-#pragma unroll
-        for (int i = 0; i < NW; ++i)
-            if ((int)threadIdx.x == i)
-                v = mine[i];
-        __hip_atomic_store(base + (size_t)rank * kSlotWords + threadIdx.x, tag_word(gen, v),
+    if (lane < NW)
+        __hip_atomic_store(base + (size_t)rank * kSlotWords + lane, tag_word(gen, mine),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
     bool ok = true;
-#pragma unroll
-    for (int i = 0; i < NW; ++i)
-        got[i] = 0u;
-    if ((int)threadIdx.x < wpg) {
-        uint64_t *slot = base + (size_t)threadIdx.x * kSlotWords;
+    for (int m = lane; m < wpg && ok; m += 64) {
+        uint64_t *slot = base + (size_t)m * kSlotWords;
         uint32_t polls = 0;
         for (;;) {
             uint64_t word[NW];
@@ -276,7 +280,7 @@ __device__ bool group_sync(uint64_t *box, int wpg, int rank, uint32_t gen,
 #pragma unroll
             for (int i = 0; i < NW; ++i) {
                 all &= (uint32_t)(word[i] >> 32) == gen;
-                got[i] = (uint32_t)word[i];
+                got[m][i] = (uint32_t)word[i];
             }
             if (all)
                 break;
@@ -287,10 +291,7 @@ __device__ bool group_sync(uint64_t *box, int wpg, int rank, uint32_t gen,
             }
         }
     }
-    ok = __syncthreads_and(ok);
-    if (!ok && threadIdx.x == 0)
-        raise_flag(flags, TAV_FLAG_SYNC_TIMEOUT);
-    return ok;
+    return !__any(!ok);
 }
 
 __device__ __forceinline__ uint32_t f32_bits(float v) { return __builtin_bit_cast(uint32_t, v); }
@@ -309,7 +310,6 @@ __device__ __forceinline__ double bits_f64(uint32_t hi, uint32_t lo)
 
 __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
 {
-    __shared__ ExpTable s_exp;
     __shared__ int32_t s_par[kMaxNodes];
     __shared__ int32_t s_first[kMaxNodes];
     __shared__ int32_t s_next[kMaxNodes];
@@ -317,6 +317,14 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
     __shared__ float s_tx[kMaxNodes];     // target logit of child c's token in its parent's row
     __shared__ float s_dx[kMaxNodes];     // draft logit of the same
     __shared__ double s_red[2 * kSvWaves];
+    __shared__ double s_wq[4 * kSvWaves];   // per wave: raw max t, sum t, raw max q, sum q
+    __shared__ double s_norm[4];            // Mp, Zp, Mq, Zq of the whole row
+    __shared__ double s_uacc[kMaxNodes];    // node i's acceptance uniform
+    __shared__ double s_ures[kMaxNodes];    // node i's resampling uniform
+    __shared__ double s_px[kMaxNodes];      // p and q of child c's token at its parent
+    __shared__ double s_qx[kMaxNodes];
+    __shared__ int s_sync_ok;
+    __shared__ uint32_t s_words[kMaxWpg][kSlotWords];   // the group's payloads, as wave 0 received them
     __shared__ double s_mass[kMaxWpg];    // mass of every member's chunk in the current distribution
     __shared__ double s_zhist[kMaxNodes]; // residual normalisers after each rejection at u
     __shared__ double s_slot[kSvEpt * kSvWaves];
@@ -338,7 +346,6 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
     const double invT = 1.0 / a.T;
     uint32_t gen = 0;
     bool alive = true;
-    exp_table_init(s_exp);
 
     for (int b = g; b < a.B && alive; b += a.ngroups) {
         const int64_t rowbase = (int64_t)b * N;
@@ -372,6 +379,12 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
         __syncthreads();
         if (tid < N && s_first[tid] == N)
             s_first[tid] = -1;
+        // every node's uniforms at once (they are indexed by node, not walk order)
+        for (int i = tid; i < N; i += kSvThreads) {
+            const NodeUniforms r = node_uniforms(a.seed, a.offset, b, i);
+            s_uacc[i] = r.acc;
+            s_ures[i] = r.res;
+        }
         __syncthreads();
 
         const bool lead = rank == 0 && tid == 0;
@@ -422,7 +435,10 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     s_dx[tid] = drow[x];
                 }
             }
-            // maxima of the raw fp32 logits (exact); x -> x/T is monotone
+            // Maxima of the raw fp32 logits (exact; x -> x/T is monotone) and
+            // sums of exp relative to them, per wave (DPP, no barrier). A NaN
+            // logit makes the sum NaN.
+            const int lane = tid & 63, wave = tid >> 6;
             bool nan_seen = false;
             double mt_d = -INFINITY, mq_d = -INFINITY;
 #pragma unroll
@@ -431,21 +447,27 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 mt_d = fmax(mt_d, (double)tf[e]);
                 mq_d = fmax(mq_d, (double)df[e]);
             }
-            block_max2(mt_d, mq_d, s_red);
-            const float mt_raw = (float)mt_d, mq_raw = (float)mq_d;
-            const double mts = (double)mt_raw * invT, mqs = (double)mq_raw * invT;
+            const float wmt = (float)wave_max(mt_d), wmq = (float)wave_max(mq_d);
+            const double wts = (double)wmt * invT, wqs = (double)wmq * invT;
             double pr[kSvEpt], qv[kSvEpt];
             double zt = 0.0, zq = 0.0;
 #pragma unroll
             for (int e = 0; e < kSvEpt; ++e) {
-                pr[e] = (mt_raw == -INFINITY) ? 0.0 : exp_f64((double)tf[e] * invT - mts, s_exp);
-                qv[e] = (mq_raw == -INFINITY) ? 0.0 : exp_f64((double)df[e] * invT - mqs, s_exp);
+                pr[e] = (wmt == -INFINITY) ? 0.0 : exp_bulk((double)tf[e] * invT - wts);
+                qv[e] = (wmq == -INFINITY) ? 0.0 : exp_bulk((double)df[e] * invT - wqs);
                 zt += pr[e];
                 zq += qv[e];
             }
-            block_sum2(zt, zq, s_red);
-            if (__syncthreads_or(nan_seen))
+            if (nan_seen)
                 zt = NAN;
+            zt = wave_sum(zt);
+            zq = wave_sum(zq);
+            if (lane == 0) {
+                s_wq[4 * wave + 0] = (double)wmt;
+                s_wq[4 * wave + 1] = zt;
+                s_wq[4 * wave + 2] = (double)wmq;
+                s_wq[4 * wave + 3] = zq;
+            }
 
             // the first child's rows and its children's logits, for the next level
             if (has_kids) {
@@ -471,34 +493,87 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     pf_dx = d1[x];
                 }
             }
+            __syncthreads();   // s_wq (and s_tx, s_dx) visible
 
-            double m_got = -INFINITY, z_got = 0.0, mq_got = -INFINITY, zq_got = 0.0;
-            {
-                const uint32_t mine[6] = {f32_bits(mt_raw), f64_hi(zt), f64_lo(zt),
-                                          f32_bits(mq_raw), f64_hi(zq), f64_lo(zq)};
-                uint32_t words[6];
-                if (!group_sync<6>(box, wpg, rank, ++gen, mine, words, a.flags)) {
-                    alive = false;
-                    break;
+            // Wave 0: the chunk's (max, sum) from its waves' in wave order,
+            // exchanged with the group, and the members' pairs merged in
+            // member order, so every workgroup of the group holds the same
+            // bits. Then one barrier hands the results to the other waves.
+            if (wave == 0) {
+                const bool wl = lane < kSvWaves;
+                const double m_w = wl ? s_wq[4 * lane + 0] : -INFINITY;
+                const double z_w = wl ? s_wq[4 * lane + 1] : 0.0;
+                const double mq_w = wl ? s_wq[4 * lane + 2] : -INFINITY;
+                const double zq_w = wl ? s_wq[4 * lane + 3] : 0.0;
+                const float mt_raw = (float)wave_max(m_w), mq_raw = (float)wave_max(mq_w);
+                // a NaN sum travels through; an empty wave adds nothing
+                const double zt_c = wave_sum(m_w == -INFINITY ? (z_w != z_w ? z_w : 0.0)
+                                                              : z_w * exp_f64((m_w - (double)mt_raw) * invT));
+                const double zq_c = wave_sum(mq_w == -INFINITY ? 0.0
+                                                               : zq_w * exp_f64((mq_w - (double)mq_raw) * invT));
+                const uint32_t mine6[6] = {f32_bits(mt_raw), f64_hi(zt_c), f64_lo(zt_c),
+                                           f32_bits(mq_raw), f64_hi(zq_c), f64_lo(zq_c)};
+                uint32_t mine = 0;
+#pragma unroll
+                for (int i = 0; i < 6; ++i)
+                    if (lane == i)
+                        mine = mine6[i];
+                bool ok = true;
+                if (wpg == 1) {
+                    if (lane == 0) {
+#pragma unroll
+                        for (int i = 0; i < 6; ++i)
+                            s_words[0][i] = mine6[i];
+                    }
+                } else {
+                    ok = wave0_exchange<6>(box, wpg, rank, ++gen, mine, s_words);
                 }
-                if (tid < wpg) {
-                    m_got = (double)bits_f32(words[0]) * invT;
-                    z_got = bits_f64(words[1], words[2]);
-                    mq_got = (double)bits_f32(words[3]) * invT;
-                    zq_got = bits_f64(words[4], words[5]);
+                // member maxima first, then the rebased sums, in member order
+                double Mp = -INFINITY, Mq = -INFINITY;
+                for (int m = lane; m < wpg; m += 64) {
+                    Mp = fmax(Mp, (double)bits_f32(s_words[m][0]) * invT);
+                    Mq = fmax(Mq, (double)bits_f32(s_words[m][3]) * invT);
+                }
+                Mp = wave_max(Mp);
+                Mq = wave_max(Mq);
+                double Zp = 0.0, Zq = 0.0;
+                for (int m = lane; m < wpg; m += 64) {
+                    const double mk = (double)bits_f32(s_words[m][0]) * invT;
+                    const double zk = bits_f64(s_words[m][1], s_words[m][2]);
+                    const double zm = (mk == -INFINITY) ? (zk != zk ? zk : 0.0) : zk * exp_f64(mk - Mp);
+                    s_mass[m] = zm;   // divided by Zp below
+                    Zp += zm;
+                    const double mqk = (double)bits_f32(s_words[m][3]) * invT;
+                    const double zqk = bits_f64(s_words[m][4], s_words[m][5]);
+                    Zq += (mqk == -INFINITY) ? 0.0 : zqk * exp_f64(mqk - Mq);
+                }
+                Zp = wave_sum(Zp);
+                Zq = wave_sum(Zq);
+                for (int m = lane; m < wpg; m += 64)
+                    s_mass[m] /= Zp;
+                if (lane == 0) {
+                    s_norm[0] = Mp;
+                    s_norm[1] = Zp;
+                    s_norm[2] = Mq;
+                    s_norm[3] = Zq;
+                    s_sync_ok = ok;
+                }
+                // p and q of every child's token, one lane per child
+                for (int c = lane + 1; c < N; c += 64) {
+                    if (s_par[c] == u) {
+                        s_px[c] = exp_f64((double)s_tx[c] * invT - Mp) / Zp;
+                        s_qx[c] = exp_f64((double)s_dx[c] * invT - Mq) / Zq;
+                    }
                 }
             }
-            // merge the members' (max, sum) pairs in a fixed order
-            double Mp = m_got, Mq = mq_got;
-            block_max2(Mp, Mq, s_red);
-            double em = 0.0, Zp = 0.0, Zq = 0.0;
-            if (tid < wpg) {
-                em = (m_got == -INFINITY) ? 0.0 : exp_f64(m_got - Mp, s_exp);
-                // a NaN sum travels through; an empty chunk adds nothing
-                Zp = (m_got == -INFINITY) ? (z_got != z_got ? z_got : 0.0) : z_got * em;
-                Zq = (mq_got == -INFINITY) ? 0.0 : zq_got * exp_f64(mq_got - Mq, s_exp);
+            __syncthreads();   // s_norm, s_mass visible
+            if (!s_sync_ok) {
+                if (tid == 0)
+                    raise_flag(a.flags, TAV_FLAG_SYNC_TIMEOUT);
+                alive = false;
+                break;
             }
-            block_sum2(Zp, Zq, s_red);
+            const double Mp = s_norm[0], Zp = s_norm[1], Mq = s_norm[2], Zq = s_norm[3];
             const bool bad_p = !(Zp > 0.0) || Mp == -INFINITY || __builtin_isinf(Mp) ||
                                __builtin_isnan(Zp) || __builtin_isinf(Zp);
             const bool bad_q = has_kids && (!(Zq > 0.0) || Mq == -INFINITY ||
@@ -509,27 +584,24 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 failed = true;
                 break;
             }
-            // chunk masses of p, and p and q of this chunk in registers
-            if (tid < wpg)
-                s_mass[tid] = z_got * em / Zp;
+            // p and q of this chunk in registers, rebased from the wave's max
             {
-                const double sp = (mt_raw == -INFINITY) ? 0.0 : exp_f64(mts - Mp, s_exp) / Zp;
-                const double sq = (mq_raw == -INFINITY) ? 0.0 : exp_f64(mqs - Mq, s_exp) / Zq;
+                const double sp = (wmt == -INFINITY) ? 0.0 : exp_f64(wts - Mp) / Zp;
+                const double sq = (wmq == -INFINITY) ? 0.0 : exp_f64(wqs - Mq) / Zq;
 #pragma unroll
                 for (int e = 0; e < kSvEpt; ++e) {
                     pr[e] *= sp;
                     qv[e] *= sq;
                 }
             }
-            __syncthreads();   // s_mass, s_tx, s_dx visible
 
             // ---- 2./3. children in ascending order against the running residual
             int k = 0;
             bool accepted = false;
             for (int c = s_first[u]; c >= 0; c = s_next[c]) {
                 const int x = s_tok[c];
-                const double px = exp_f64((double)s_tx[c] * invT - Mp, s_exp) / Zp;
-                const double qx = exp_f64((double)s_dx[c] * invT - Mq, s_exp) / Zq;
+                const double px = s_px[c];
+                const double qx = s_qx[c];
                 double prx = px;
                 for (int j = 0; j < k; ++j) {
                     const double zj = s_zhist[j];
@@ -538,8 +610,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                         prx = (d > 0.0 ? d : 0.0) / zj;
                     }
                 }
-                const NodeUniforms r = node_uniforms(a.seed, a.offset, b, c);
-                if (r.acc * qx < prx) {
+                if (s_uacc[c] * qx < prx) {
                     if (lead) {
                         a.out_tok[rowbase + nacc] = x;
                         a.path[rowbase + nacc + 1] = c;
@@ -549,30 +620,53 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     accepted = true;
                     break;
                 }
-                // rejected: chunk sums of the residual, exchanged
-                double s = 0.0, unused = 0.0;
+                // rejected: the chunk's residual mass, per wave, then in wave
+                // 0 exchanged with the group and summed in member order
+                double rsum = 0.0;
 #pragma unroll
                 for (int e = 0; e < kSvEpt; ++e) {
                     const double d = pr[e] - qv[e];
-                    s += d > 0.0 ? d : 0.0;
+                    rsum += d > 0.0 ? d : 0.0;
                 }
-                block_sum2(s, unused, s_red);
-                double rs = 0.0;
-                {
-                    const uint32_t mine[2] = {f64_hi(s), f64_lo(s)};
-                    uint32_t words[2];
-                    if (!group_sync<2>(box, wpg, rank, ++gen, mine, words, a.flags)) {
-                        alive = false;
-                        break;
+                rsum = wave_sum(rsum);
+                // (wave 0 read s_wq before the last barrier)
+                if (lane == 0)
+                    s_wq[wave] = rsum;
+                __syncthreads();
+                if (wave == 0) {
+                    const double sc = wave_sum(lane < kSvWaves ? s_wq[lane] : 0.0);
+                    const uint32_t mine = lane == 0 ? f64_hi(sc) : lane == 1 ? f64_lo(sc) : 0u;
+                    bool ok = true;
+                    if (wpg == 1) {
+                        if (lane == 0) {
+                            s_words[0][0] = f64_hi(sc);
+                            s_words[0][1] = f64_lo(sc);
+                        }
+                    } else {
+                        ok = wave0_exchange<2>(box, wpg, rank, ++gen, mine, s_words);
                     }
-                    if (tid < wpg)
-                        rs = bits_f64(words[0], words[1]);
+                    double Zr = 0.0;
+                    for (int m = lane; m < wpg; m += 64)
+                        Zr += bits_f64(s_words[m][0], s_words[m][1]);
+                    Zr = wave_sum(Zr);
+                    if (Zr > 0.0) {
+                        for (int m = lane; m < wpg; m += 64)
+                            s_mass[m] = bits_f64(s_words[m][0], s_words[m][1]) / Zr;
+                    }
+                    if (lane == 0) {
+                        s_zhist[k] = Zr;
+                        s_sync_ok = ok;
+                    }
                 }
-                double Z = rs, unused2 = 0.0;
-                block_sum2(Z, unused2, s_red);
+                __syncthreads();   // s_zhist, s_mass visible
+                if (!s_sync_ok) {
+                    if (tid == 0)
+                        raise_flag(a.flags, TAV_FLAG_SYNC_TIMEOUT);
+                    alive = false;
+                    break;
+                }
+                const double Z = s_zhist[k];
                 if (Z > 0.0) {
-                    if (tid < wpg)
-                        s_mass[tid] = rs / Z;
                     const double inv = 1.0 / Z;
 #pragma unroll
                     for (int e = 0; e < kSvEpt; ++e) {
@@ -580,10 +674,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                         pr[e] = (d > 0.0 ? d : 0.0) * inv;
                     }
                 }
-                if (tid == 0)
-                    s_zhist[k] = Z;
                 ++k;
-                __syncthreads();   // s_zhist, s_mass visible
             }
             if (!alive)
                 break;
@@ -609,7 +700,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             __syncthreads();
             const double before = s_red[0], total = s_red[1];
             const double mass = s_mass[rank];
-            const double target = node_uniforms(a.seed, a.offset, b, u).res * total;
+            const double target = s_ures[u] * total;
             __syncthreads();
             if (!(total > 0.0)) {
                 if (lead)
@@ -766,9 +857,7 @@ __global__ __launch_bounds__(kSvThreads) void target_probs_kernel(const float *l
                                                                   int32_t V, double T,
                                                                   double *p, uint32_t *flags)
 {
-    __shared__ ExpTable s_exp;
     __shared__ double red[2 * kSvWaves];
-    exp_table_init(s_exp);
     const float *row = logits + (int64_t)blockIdx.x * V;
     double *out = p + (int64_t)blockIdx.x * V;
     const double invT = 1.0 / T;
@@ -782,7 +871,7 @@ __global__ __launch_bounds__(kSvThreads) void target_probs_kernel(const float *l
     const double ms = (double)(float)m * invT;
     double z = 0.0, unused2 = 0.0;
     for (int x = threadIdx.x; x < V; x += kSvThreads)
-        z += exp_f64((double)row[x] * invT - ms, s_exp);
+        z += exp_f64((double)row[x] * invT - ms);
     block_sum2(z, unused2, red);
     if (__syncthreads_or(nan_seen) || m == -INFINITY || __builtin_isinf(m)) {
         if (threadIdx.x == 0)
@@ -790,7 +879,7 @@ __global__ __launch_bounds__(kSvThreads) void target_probs_kernel(const float *l
         return;
     }
     for (int x = threadIdx.x; x < V; x += kSvThreads)
-        out[x] = exp_f64((double)row[x] * invT - ms, s_exp) / z;
+        out[x] = exp_f64((double)row[x] * invT - ms) / z;
 }
 
 } // namespace
