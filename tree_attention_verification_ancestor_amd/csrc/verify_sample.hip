@@ -53,10 +53,10 @@
 // slot, so each call leaves the workspace as it found it (zero-filled).
 //
 // exp. The stats pass takes one exponential per vocabulary entry and row,
-// which makes it bound by the vector ALUs; those use exp_bulk (an fp32
-// head and an fp64 tail, 1e-7 relative). The few exponentials a decision
-// reads directly (p and q at a child's token, the merges) use exp_f64, a
-// table-free fp64 routine within one ulp.
+// which makes it bound by the vector ALUs; those, and the rebasing of the
+// partial sums to the row's maximum, use exp_bulk (an fp32 head and an fp64
+// tail, 1e-7 relative). p and q at a child's token, which a decision reads
+// directly, use exp_f64, a table-free fp64 routine within one ulp.
 
 #include <algorithm>
 
@@ -508,9 +508,9 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 const float mt_raw = (float)wave_max(m_w), mq_raw = (float)wave_max(mq_w);
                 // a NaN sum travels through; an empty wave adds nothing
                 const double zt_c = wave_sum(m_w == -INFINITY ? (z_w != z_w ? z_w : 0.0)
-                                                              : z_w * exp_f64((m_w - (double)mt_raw) * invT));
+                                                              : z_w * exp_bulk((m_w - (double)mt_raw) * invT));
                 const double zq_c = wave_sum(mq_w == -INFINITY ? 0.0
-                                                               : zq_w * exp_f64((mq_w - (double)mq_raw) * invT));
+                                                               : zq_w * exp_bulk((mq_w - (double)mq_raw) * invT));
                 const uint32_t mine6[6] = {f32_bits(mt_raw), f64_hi(zt_c), f64_lo(zt_c),
                                            f32_bits(mq_raw), f64_hi(zq_c), f64_lo(zq_c)};
                 uint32_t mine = 0;
@@ -540,17 +540,18 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 for (int m = lane; m < wpg; m += 64) {
                     const double mk = (double)bits_f32(s_words[m][0]) * invT;
                     const double zk = bits_f64(s_words[m][1], s_words[m][2]);
-                    const double zm = (mk == -INFINITY) ? (zk != zk ? zk : 0.0) : zk * exp_f64(mk - Mp);
+                    const double zm = (mk == -INFINITY) ? (zk != zk ? zk : 0.0) : zk * exp_bulk(mk - Mp);
                     s_mass[m] = zm;   // divided by Zp below
                     Zp += zm;
                     const double mqk = (double)bits_f32(s_words[m][3]) * invT;
                     const double zqk = bits_f64(s_words[m][4], s_words[m][5]);
-                    Zq += (mqk == -INFINITY) ? 0.0 : zqk * exp_f64(mqk - Mq);
+                    Zq += (mqk == -INFINITY) ? 0.0 : zqk * exp_bulk(mqk - Mq);
                 }
                 Zp = wave_sum(Zp);
                 Zq = wave_sum(Zq);
+                const double inv_zp = 1.0 / Zp, inv_zq = 1.0 / Zq;
                 for (int m = lane; m < wpg; m += 64)
-                    s_mass[m] /= Zp;
+                    s_mass[m] *= inv_zp;
                 if (lane == 0) {
                     s_norm[0] = Mp;
                     s_norm[1] = Zp;
@@ -561,8 +562,8 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 // p and q of every child's token, one lane per child
                 for (int c = lane + 1; c < N; c += 64) {
                     if (s_par[c] == u) {
-                        s_px[c] = exp_f64((double)s_tx[c] * invT - Mp) / Zp;
-                        s_qx[c] = exp_f64((double)s_dx[c] * invT - Mq) / Zq;
+                        s_px[c] = exp_f64((double)s_tx[c] * invT - Mp) * inv_zp;
+                        s_qx[c] = exp_f64((double)s_dx[c] * invT - Mq) * inv_zq;
                     }
                 }
             }
@@ -586,8 +587,8 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             }
             // p and q of this chunk in registers, rebased from the wave's max
             {
-                const double sp = (wmt == -INFINITY) ? 0.0 : exp_f64(wts - Mp) / Zp;
-                const double sq = (wmq == -INFINITY) ? 0.0 : exp_f64(wqs - Mq) / Zq;
+                const double sp = (wmt == -INFINITY) ? 0.0 : exp_bulk(wts - Mp) * (1.0 / Zp);
+                const double sq = (wmq == -INFINITY) ? 0.0 : exp_bulk(wqs - Mq) * (1.0 / Zq);
 #pragma unroll
                 for (int e = 0; e < kSvEpt; ++e) {
                     pr[e] *= sp;
