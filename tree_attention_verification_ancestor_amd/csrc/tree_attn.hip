@@ -72,10 +72,8 @@ struct Cfg {
     static constexpr int kVTileBytes = kKT * D * 2;
     static constexpr int kBufBytes = kKTileBytes + kVTileBytes;
     static constexpr int kChunks = kKT * kCpr;           // 16-byte chunks per K (or V) tile
-    static constexpr int kLoadsPerWave = kChunks / 64 / NW;   // direct loads per wave per K (or V) tile
     static constexpr int kChPerThread = kChunks / kThreads;
     static_assert(kChunks % kThreads == 0, "tile chunks must split evenly");
-    static_assert(kLoadsPerWave * 64 * NW == kChunks, "direct loads must split evenly");
 };
 
 struct AttnArgs {
@@ -173,14 +171,17 @@ __device__ __forceinline__ void wait_vmem()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// sched_group_barrier instruction classes
-constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100, kSgDsWrite = 0x200;
-
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
 {
     using C = Cfg<D, NW>;
-    constexpr int LPW = C::kLoadsPerWave;
+    // Which waves issue the direct tile loads. A wave stalls at each one until
+    // the CU's load path takes it (about 14 cycles per kilobyte, every wave of
+    // the CU in one queue), so with 8 waves the four whose work per tile is
+    // the shorter chain (see "Overlap") issue them all and the other four none.
+    constexpr int kIssuers = NW == 8 ? NW / 2 : NW;
+    constexpr int LPW = C::kChunks / 64 / kIssuers;   // loads per issuing wave per K (or V) tile
+    static_assert(LPW * 64 * kIssuers == C::kChunks, "direct loads must split evenly");
     constexpr int KTB = C::kKTileBytes, VTB = C::kVTileBytes;
     // K tiles live in a ring of 3 slots and V tiles in a ring of 5: tile t's
     // K is read in step t only, its V in step t+1 or t+2 (P.V runs one or
@@ -259,19 +260,26 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
         }
     }
     const uint64_t mrow0 = (n_tree > 0 && row_ok) ? a.mask[((int64_t)b * a.N + node) * a.W] : 1;
+    // Wait for these loads here, before any tile load is in flight. The
+    // compiler does not see the direct tile loads (inline assembly), so a
+    // register load it still counts as outstanding inside the tile loop would
+    // make it wait for every vector memory operation, prefetched tiles
+    // included, at the first use.
+    wait_vmem<0>();
 
     // ---- direct-load descriptors, fixed for the whole kernel ------------------
-    // Load j of a tile fills LDS chunks [64j, 64j+64) in lane order; this wave
-    // issues loads j = wave + i*NW. The chunks of one load always come from a
+    // Load j of a tile fills LDS chunks [64j, 64j+64) in lane order; issuing
+    // wave w issues loads j = w + i*kIssuers. The chunks of one load always come from a
     // single 16-key cache block (4 or 8 whole MFMA rows of K, whose keys differ
     // only in their low bits; or 64 feature halves of one V block): the
     // block's address is a wave-uniform base and each lane adds a byte offset
     // below 4 KB.
+    const bool issuer = wave < kIssuers;
     int kbb[LPW], vbb[LPW];          // which of the tile's four blocks
     uint32_t koff[LPW], voff[LPW];   // this lane's byte offset inside it
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-        const int j = wave + i * NW;
+        const int j = wave % kIssuers + i * kIssuers;
         const int row0 = j * 64 / C::kCpr;   // first MFMA row of this load
         kbb[i] = ((row0 & ~31) | perm32(row0 & 31)) >> 4;
         const int q = j * 64 + lane;
@@ -307,12 +315,12 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             const uint32_t hb = __builtin_amdgcn_readfirstlane(ids.k[i]);
-            load_lds16(a.k_cache + (uint64_t)hb * (kBlock * D), koff[i], kdst + (wave + i * NW) * 1024u);
+            load_lds16(a.k_cache + (uint64_t)hb * (kBlock * D), koff[i], kdst + (wave + i * kIssuers) * 1024u);
         }
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             const uint32_t hb = __builtin_amdgcn_readfirstlane(ids.v[i]);
-            load_lds16(a.v_cache + (uint64_t)hb * (kBlock * D), voff[i], vdst + (wave + i * NW) * 1024u);
+            load_lds16(a.v_cache + (uint64_t)hb * (kBlock * D), voff[i], vdst + (wave + i * kIssuers) * 1024u);
         }
     };
 
@@ -325,13 +333,12 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
         for (int r = 0; r < C::kChPerThread; ++r)
             cv[r] = *lds_at<u32x4>(vaddr + (tid + r * C::kThreads) * 16);
     };
-    auto convert_store = [&](int it, uint32_t vaddr, u32x4 (&cv)[C::kChPerThread], bool masked)
-                             __attribute__((always_inline)) {
+    auto convert_store_chunk = [&](int it, uint32_t vaddr, const u32x4 &c, int r, bool masked)
+                                   __attribute__((always_inline)) {
         const int p0 = (t_begin + it) * kKT;
-#pragma unroll
-        for (int r = 0; r < C::kChPerThread; ++r) {
+        {
             const int q = tid + r * C::kThreads;
-            uint32_t w[4] = {cv[r].x, cv[r].y, cv[r].z, cv[r].w};
+            uint32_t w[4] = {c.x, c.y, c.z, c.w};
             if (masked) {
                 const int bi = q / (2 * D), rem = q % (2 * D);
                 const int d = rem >> 1, hpos = rem & 1;
@@ -348,6 +355,12 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
             h.w = bf16x2_to_f16x2(w[3]);
             *lds_at<u32x4>(vaddr + q * 16) = h;
         }
+    };
+    auto convert_store = [&](int it, uint32_t vaddr, u32x4 (&cv)[C::kChPerThread], bool masked)
+                             __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < C::kChPerThread; ++r)
+            convert_store_chunk(it, vaddr, cv[r], r, masked);
     };
 
     // Tree tile: through registers. K rows go to their MFMA rows; V rows are
@@ -385,26 +398,43 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     // LDS, B = this wave's Q^T in registers). K fragment k of row 32t + col
     // sits at col*2D + ((2k ^ x) << 4) + t*64D with x = hh ^ k_swz(col): a
     // per-lane offset for each k, and a constant for t.
+    //
+    // Fragment reads run kDepth MFMAs ahead of their use, each into its own
+    // registers, and a scheduling fence after every MFMA keeps that order: left
+    // free, the scheduler pulls each read down next to its MFMA (fewer live
+    // registers), and every MFMA then waits out a full LDS round trip. MFMA j
+    // takes k = j/2 and half t = j%2, so consecutive MFMAs feed different
+    // accumulators. `between(j)` runs after MFMA j (vector work to hide).
     uint32_t kfrag[C::kKSteps];
 #pragma unroll
     for (int k = 0; k < C::kKSteps; ++k)
         kfrag[k] = (uint32_t)(col * (2 * D) + (((2 * k) ^ hh ^ k_swz<D>(col)) << 4));
-    auto qk = [&](uint32_t kaddr, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
+    constexpr int kDepth = 4;
+    constexpr int kQkN = 2 * C::kKSteps;
+    static_assert(kQkN >= kDepth, "read pipeline deeper than the MFMA sequence");
+    auto qk = [&](uint32_t kaddr, f32x16 (&sacc)[2], auto &&between) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 sacc[t][e] = 0.f;
+        bf16x8 kb[kDepth];
 #pragma unroll
-        for (int k = 0; k < C::kKSteps; ++k) {
-            const uint32_t ka = kaddr + kfrag[k];
+        for (int j = 0; j < kDepth; ++j)
+            kb[j] = *lds_at<bf16x8>(kaddr + kfrag[j >> 1] + (j & 1) * (64 * D));
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const bf16x8 av = *lds_at<bf16x8>(ka + t * (64 * D));
-                sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[k], sacc[t], 0, 0, 0);
+        for (int j = 0; j < kQkN; ++j) {
+            sacc[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[j % kDepth], qf[j >> 1], sacc[j & 1], 0, 0, 0);
+            if (j + kDepth < kQkN) {
+                const int n = j + kDepth;
+                kb[j % kDepth] = *lds_at<bf16x8>(kaddr + kfrag[n >> 1] + (n & 1) * (64 * D));
             }
+            between(j);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
+    auto no_work = [](int) __attribute__((always_inline)) {};
 
     // ---- accumulators --------------------------------------------------------
     f32x16 oacc[C::kDTiles];
@@ -499,19 +529,42 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     // byte address vaddr, B = the weights). Feature d = 32m + col of block bi
     // sits at v_off(bi, d, hh) = bi*32D + 1024m + v_off(0, col, hh): one
     // per-lane base register and constant offsets that fit the LDS
-    // instruction's offset field.
+    // instruction's offset field. MFMA j takes block bi = j / kDTiles (weights
+    // pb[bi/2][bi%2]) and feature tile m = j % kDTiles. The same read pipeline
+    // as the scores; pv_begin issues the first kDepth reads, so a caller can
+    // put vector work between them and the MFMAs.
+    constexpr int kPvN = 4 * C::kDTiles;
+    static_assert(kPvN >= kDepth, "read pipeline deeper than the MFMA sequence");
+    struct VReads {
+        uint32_t base;
+        f16x8 vb[kDepth];
+    };
+    auto pv_begin = [&](uint32_t vaddr) __attribute__((always_inline)) {
+        VReads r;
+        r.base = vaddr + (uint32_t)v_off<D>(0, col, hh);
+        asm("" : "+v"(r.base));   // keep the sum in one register
+#pragma unroll
+        for (int j = 0; j < kDepth; ++j)
+            r.vb[j] = *lds_at<f16x8>(r.base + (uint32_t)((j / C::kDTiles) * (D * 32) + (j % C::kDTiles) * 1024));
+        return r;
+    };
+    auto pv_finish = [&](const f16x8 (&pb)[2][2], VReads &r) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < kPvN; ++j) {
+            const int bi = j / C::kDTiles, m = j % C::kDTiles;
+            oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(r.vb[j % kDepth], pb[bi >> 1][bi & 1], oacc[m], 0, 0, 0);
+            if (j + kDepth < kPvN) {
+                const int n = j + kDepth;
+                r.vb[j % kDepth] =
+                    *lds_at<f16x8>(r.base + (uint32_t)((n / C::kDTiles) * (D * 32) + (n % C::kDTiles) * 1024));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
     auto pv = [&](const f16x8 (&pb)[2][2], uint32_t vaddr) __attribute__((always_inline)) {
-        uint32_t base = vaddr + (uint32_t)v_off<D>(0, col, hh);
-        asm("" : "+v"(base));   // keep the sum in one register
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                for (int m = 0; m < C::kDTiles; ++m) {
-                    const f16x8 av = *lds_at<f16x8>(base + (uint32_t)((2 * t + h2) * (D * 32) + m * 1024));
-                    oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[t][h2], oacc[m], 0, 0, 0);
-                }
+        VReads r = pv_begin(vaddr);
+        pv_finish(pb, r);
     };
 
     // ---- the tile pipeline ---------------------------------------------------
@@ -533,8 +586,10 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     const bool lag = NW == 8 && wave >= NW / 2;
     auto fill = [&](int t, const TileIds &ids) __attribute__((always_inline)) {
         const int kslot = t % kKSlots, vslot = t % kVSlots;
-        if (t < n_pre)
-            issue_prefix_tile(ids, k_lds + kslot * KTB, v_lds + vslot * VTB);
+        if (t < n_pre) {
+            if (issuer)
+                issue_prefix_tile(ids, k_lds + kslot * KTB, v_lds + vslot * VTB);
+        }
         else if (t < n_tiles)
             stage_tree_tile(t, s_k + kslot * KTB, s_v + vslot * VTB);
     };
@@ -564,29 +619,23 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     // Q(it): scores of tile it into sacc.
     auto phase_q = [&](int it, uint32_t kcur, uint32_t vcur) __attribute__((always_inline)) {
         if (it < n_pre && (t_begin + it + 1) * kKT <= L) {
-            // a whole prefix tile: its V conversion hides under the S MFMAs
+            // a whole prefix tile: its V conversion runs between the S MFMAs,
+            // chunk r after MFMA (2r + 1) * kQkN / (2 * chunks), in [0, kQkN)
             u32x4 cv[C::kChPerThread];
             convert_load(vcur, cv);
-            qk(kcur, sacc);
-            convert_store(it, vcur, cv, false);
-            // K fragment reads run four MFMAs ahead
+            qk(kcur, sacc, [&](int j) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < C::kChPerThread + 4; ++i)
-                __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 1);
-#pragma unroll
-            for (int i = 0; i < 2 * C::kKSteps; ++i) {
-                __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 1);
-                if (i + 4 < 2 * C::kKSteps)
-                    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 1);
-                __builtin_amdgcn_sched_group_barrier(kSgValu, 2, 1);
-            }
+                for (int r = 0; r < C::kChPerThread; ++r)
+                    if (j == (2 * r + 1) * kQkN / (2 * C::kChPerThread))
+                        convert_store_chunk(it, vcur, cv[r], r, false);
+            });
         } else {
             if (it < n_pre) {
                 u32x4 cv[C::kChPerThread];
                 convert_load(vcur, cv);
                 convert_store(it, vcur, cv, true);
             }
-            qk(kcur, sacc);
+            qk(kcur, sacc, no_work);
             apply_mask(it, sacc);
         }
     };
@@ -595,13 +644,14 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     auto phase_r = [&](uint32_t vprev) __attribute__((always_inline)) {
         f16x8 pb[2][2];
         float alpha;
-        // The softmax first, as one stretch of vector work with no LDS waits
-        // in it (a wave issues in order: a wait would hold up everything
-        // behind it), then P.V of the tile before.
+        // The first V reads, then the softmax as one stretch of vector work
+        // with no LDS waits in it (a wave issues in order: a wait would hold
+        // up everything behind it), then P.V of the tile before.
+        VReads vr = pv_begin(vprev);   // their latency passes under the softmax
+        __builtin_amdgcn_sched_barrier(0);
         softmax(sacc, pb, alpha);
         asm volatile("" ::"v"(pb[0][0]), "v"(pb[0][1]), "v"(pb[1][0]), "v"(pb[1][1]), "v"(lsum));
-        __builtin_amdgcn_sched_barrier(0);
-        pv(pb_prev, vprev);
+        pv_finish(pb_prev, vr);
         if (__any(alpha != 1.0f)) {
 #pragma unroll
             for (int m = 0; m < C::kDTiles; ++m)
@@ -627,7 +677,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
         };
         for (int it = 0; it < n_tiles; ++it) {
             TileIds ids{};
-            if (it + 2 < n_pre)
+            if (issuer && it + 2 < n_pre)
                 ids = read_ids(it + 2);
             if (it + 1 < n_pre)
                 wait_vmem<(2 * LPW < 64 ? 2 * LPW : 63)>();   // beyond the counter's range: waits longer
