@@ -171,6 +171,9 @@ __device__ __forceinline__ void wait_vmem()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// sched_group_barrier instruction classes
+constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100;
+
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
 {
@@ -548,8 +551,15 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
             r.vb[j] = *lds_at<f16x8>(r.base + (uint32_t)((j / C::kDTiles) * (D * 32) + (j % C::kDTiles) * 1024));
         return r;
     };
-    auto pv_finish = [&](const f16x8 (&pb)[2][2], VReads &r) __attribute__((always_inline)) {
-        __builtin_amdgcn_sched_barrier(0);
+    // kValuPerMfma > 0: no fences; instead the scheduler is asked for MFMA j,
+    // then the read of fragment j + kDepth, then up to kValuPerMfma vector
+    // instructions from the same region (the caller's independent vector work
+    // written before this call), so that work issues while the MFMAs run.
+    constexpr int kValuPerMfma = 10;
+    auto pv_finish = [&](const f16x8 (&pb)[2][2], VReads &r, auto interleave) __attribute__((always_inline)) {
+        constexpr bool kMix = decltype(interleave)::value;
+        if constexpr (!kMix)
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < kPvN; ++j) {
             const int bi = j / C::kDTiles, m = j % C::kDTiles;
@@ -559,12 +569,23 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
                 r.vb[j % kDepth] =
                     *lds_at<f16x8>(r.base + (uint32_t)((n / C::kDTiles) * (D * 32) + (n % C::kDTiles) * 1024));
             }
+            if constexpr (!kMix)
+                __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (kMix) {
+#pragma unroll
+            for (int j = 0; j < kPvN; ++j) {
+                __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 2);
+                if (j + kDepth < kPvN)
+                    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 2);
+                __builtin_amdgcn_sched_group_barrier(kSgValu, kValuPerMfma, 2);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
     auto pv = [&](const f16x8 (&pb)[2][2], uint32_t vaddr) __attribute__((always_inline)) {
         VReads r = pv_begin(vaddr);
-        pv_finish(pb, r);
+        pv_finish(pb, r, std::false_type{});
     };
 
     // ---- the tile pipeline ---------------------------------------------------
@@ -644,14 +665,16 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     auto phase_r = [&](uint32_t vprev) __attribute__((always_inline)) {
         f16x8 pb[2][2];
         float alpha;
-        // The first V reads, then the softmax as one stretch of vector work
-        // with no LDS waits in it (a wave issues in order: a wait would hold
-        // up everything behind it), then P.V of the tile before.
-        VReads vr = pv_begin(vprev);   // their latency passes under the softmax
+        // The first V reads, then P.V of the tile before with the softmax of
+        // this tile (independent of it) spread between its MFMAs. The V reads
+        // run ahead of their MFMAs, so the waits for them rarely hold up the
+        // vector work behind them (a wave issues in order).
+        VReads vr = pv_begin(vprev);
         __builtin_amdgcn_sched_barrier(0);
         softmax(sacc, pb, alpha);
+        pv_finish(pb_prev, vr, std::true_type{});
+        // every weight computed before the branch (the compiler would sink them)
         asm volatile("" ::"v"(pb[0][0]), "v"(pb[0][1]), "v"(pb[1][0]), "v"(pb[1][1]), "v"(lsum));
-        pv_finish(pb_prev, vr);
         if (__any(alpha != 1.0f)) {
 #pragma unroll
             for (int m = 0; m < C::kDTiles; ++m)
