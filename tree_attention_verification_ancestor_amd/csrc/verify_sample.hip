@@ -1,6 +1,6 @@
 // spec_verify_sample: target/draft softmax over the vocabulary and the
-// root-down rejection-sampling walk, in float64 arithmetic (the per-token
-// exponentials of the vocabulary-wide sums to 1e-7 relative, see exp_bulk).
+// root-down rejection-sampling walk, in float64 arithmetic except the
+// per-token exponentials of the vocabulary-wide sums (see "exp." below).
 //
 // The rule (radar-34b blog §2, rejection-sampling acceptance condition): a
 // draft x drawn from q is kept with probability min(1, p(x)/q(x)); on a
@@ -53,10 +53,12 @@
 // slot, so each call leaves the workspace as it found it (zero-filled).
 //
 // exp. The stats pass takes one exponential per vocabulary entry and row,
-// which makes it bound by the vector ALUs; those, and the rebasing of the
-// partial sums to the row's maximum, use exp_bulk (an fp32 head and an fp64
-// tail, 1e-7 relative). p and q at a child's token, which a decision reads
-// directly, use exp_f64, a table-free fp64 routine within one ulp.
+// which makes it bound by the vector ALUs; those are fp32 (y = x/T - m to
+// one rounding, then v_exp_f32) and are summed in fp64, so the entries that
+// carry a sum are within a few 1e-7. The rebasing of partial sums to the
+// row's maximum uses exp_bulk (an fp32 head and an fp64 tail, 1e-7
+// relative). p and q at a child's token, which a decision reads directly,
+// use exp_f64, a table-free fp64 routine within one ulp.
 
 #include <algorithm>
 
@@ -344,6 +346,11 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
     const int64_t lim = std::min<int64_t>((int64_t)a.V, base + a.chunk);
     uint64_t *box = a.box + (size_t)g * 2 * wpg * kSlotWords;
     const double invT = 1.0 / a.T;
+    // The reference maxima that the vocabulary-wide sums are taken against
+    // are fp32 products fl(m * invT32), the same values in every rebase, so
+    // the sums stay consistent with each other (and exact in m for T = 1).
+    const float invT32 = (float)invT;
+    constexpr float kLog2eF = 0x1.715476p+0f;
     uint32_t gen = 0;
     bool alive = true;
 
@@ -448,13 +455,20 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 mq_d = fmax(mq_d, (double)df[e]);
             }
             const float wmt = (float)wave_max(mt_d), wmq = (float)wave_max(mq_d);
-            const double wts = (double)wmt * invT, wqs = (double)wmq * invT;
+            const float wts32 = wmt * invT32, wqs32 = wmq * invT32;
+            const double wts = wts32, wqs = wqs32;
+            // e^(x/T - wts) per entry in fp32: y to one rounding, then
+            // v_exp_f32 (under one ulp); summed in fp64. An entry's relative
+            // error is about |y| 2^-24, so the entries that carry the sum
+            // (|y| of a few units) are within a few 1e-7.
             double pr[kSvEpt], qv[kSvEpt];
             double zt = 0.0, zq = 0.0;
 #pragma unroll
             for (int e = 0; e < kSvEpt; ++e) {
-                pr[e] = (wmt == -INFINITY) ? 0.0 : exp_bulk((double)tf[e] * invT - wts);
-                qv[e] = (wmq == -INFINITY) ? 0.0 : exp_bulk((double)df[e] * invT - wqs);
+                pr[e] = (wmt == -INFINITY) ? 0.0
+                                           : (double)__builtin_amdgcn_exp2f(fmaf(tf[e], invT32, -wts32) * kLog2eF);
+                qv[e] = (wmq == -INFINITY) ? 0.0
+                                           : (double)__builtin_amdgcn_exp2f(fmaf(df[e], invT32, -wqs32) * kLog2eF);
                 zt += pr[e];
                 zq += qv[e];
             }
@@ -507,10 +521,12 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 const double zq_w = wl ? s_wq[4 * lane + 3] : 0.0;
                 const float mt_raw = (float)wave_max(m_w), mq_raw = (float)wave_max(mq_w);
                 // a NaN sum travels through; an empty wave adds nothing
-                const double zt_c = wave_sum(m_w == -INFINITY ? (z_w != z_w ? z_w : 0.0)
-                                                              : z_w * exp_bulk((m_w - (double)mt_raw) * invT));
-                const double zq_c = wave_sum(mq_w == -INFINITY ? 0.0
-                                                               : zq_w * exp_bulk((mq_w - (double)mq_raw) * invT));
+                const double zt_c =
+                    wave_sum(m_w == -INFINITY ? (z_w != z_w ? z_w : 0.0)
+                                              : z_w * exp_bulk((double)((float)m_w * invT32) - (double)(mt_raw * invT32)));
+                const double zq_c =
+                    wave_sum(mq_w == -INFINITY ? 0.0
+                                               : zq_w * exp_bulk((double)((float)mq_w * invT32) - (double)(mq_raw * invT32)));
                 const uint32_t mine6[6] = {f32_bits(mt_raw), f64_hi(zt_c), f64_lo(zt_c),
                                            f32_bits(mq_raw), f64_hi(zq_c), f64_lo(zq_c)};
                 uint32_t mine = 0;
@@ -531,19 +547,19 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 // member maxima first, then the rebased sums, in member order
                 double Mp = -INFINITY, Mq = -INFINITY;
                 for (int m = lane; m < wpg; m += 64) {
-                    Mp = fmax(Mp, (double)bits_f32(s_words[m][0]) * invT);
-                    Mq = fmax(Mq, (double)bits_f32(s_words[m][3]) * invT);
+                    Mp = fmax(Mp, (double)(bits_f32(s_words[m][0]) * invT32));
+                    Mq = fmax(Mq, (double)(bits_f32(s_words[m][3]) * invT32));
                 }
                 Mp = wave_max(Mp);
                 Mq = wave_max(Mq);
                 double Zp = 0.0, Zq = 0.0;
                 for (int m = lane; m < wpg; m += 64) {
-                    const double mk = (double)bits_f32(s_words[m][0]) * invT;
+                    const double mk = (double)(bits_f32(s_words[m][0]) * invT32);
                     const double zk = bits_f64(s_words[m][1], s_words[m][2]);
                     const double zm = (mk == -INFINITY) ? (zk != zk ? zk : 0.0) : zk * exp_bulk(mk - Mp);
                     s_mass[m] = zm;   // divided by Zp below
                     Zp += zm;
-                    const double mqk = (double)bits_f32(s_words[m][3]) * invT;
+                    const double mqk = (double)(bits_f32(s_words[m][3]) * invT32);
                     const double zqk = bits_f64(s_words[m][4], s_words[m][5]);
                     Zq += (mqk == -INFINITY) ? 0.0 : zqk * exp_bulk(mqk - Mq);
                 }
