@@ -194,6 +194,20 @@ __device__ __forceinline__ double wave_max(double v)
     return fmax(fmax(lane_f64(v, 0), lane_f64(v, 16)), fmax(lane_f64(v, 32), lane_f64(v, 48)));
 }
 
+// The same for fp32 values (32-bit DPP: half the moves of the fp64 form).
+__device__ __forceinline__ float wave_max_f32(float v)
+{
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kQuadSwap1, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kQuadSwap2, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kRowHalfMirror, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kRowMirror, 0xF, 0xF, false)));
+    const int u = __builtin_bit_cast(int, v);
+    return fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 0)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 16))),
+                 fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 32)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 48))));
+}
+
 // Sum over the wave in lane order (an inclusive scan's last value).
 __device__ __forceinline__ double wave_sum_ordered(double v)
 {
@@ -447,14 +461,14 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             // logit makes the sum NaN.
             const int lane = tid & 63, wave = tid >> 6;
             bool nan_seen = false;
-            double mt_d = -INFINITY, mq_d = -INFINITY;
+            float mt_l = -INFINITY, mq_l = -INFINITY;
 #pragma unroll
             for (int e = 0; e < kSvEpt; ++e) {
                 nan_seen |= __builtin_isnan(tf[e]) || __builtin_isnan(df[e]);
-                mt_d = fmax(mt_d, (double)tf[e]);
-                mq_d = fmax(mq_d, (double)df[e]);
+                mt_l = fmaxf(mt_l, tf[e]);
+                mq_l = fmaxf(mq_l, df[e]);
             }
-            const float wmt = (float)wave_max(mt_d), wmq = (float)wave_max(mq_d);
+            const float wmt = wave_max_f32(mt_l), wmq = wave_max_f32(mq_l);
             const float wts32 = wmt * invT32, wqs32 = wmq * invT32;
             const double wts = wts32, wqs = wqs32;
             // e^(x/T - wts) per entry in fp32: y to one rounding, then
@@ -519,7 +533,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 const double z_w = wl ? s_wq[4 * lane + 1] : 0.0;
                 const double mq_w = wl ? s_wq[4 * lane + 2] : -INFINITY;
                 const double zq_w = wl ? s_wq[4 * lane + 3] : 0.0;
-                const float mt_raw = (float)wave_max(m_w), mq_raw = (float)wave_max(mq_w);
+                const float mt_raw = wave_max_f32((float)m_w), mq_raw = wave_max_f32((float)mq_w);
                 // a NaN sum travels through; an empty wave adds nothing
                 const double zt_c =
                     wave_sum(m_w == -INFINITY ? (z_w != z_w ? z_w : 0.0)
@@ -545,13 +559,25 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     ok = wave0_exchange<6>(box, wpg, rank, ++gen, mine, s_words);
                 }
                 // member maxima first, then the rebased sums, in member order
-                double Mp = -INFINITY, Mq = -INFINITY;
+                float Mp32 = -INFINITY, Mq32 = -INFINITY;
                 for (int m = lane; m < wpg; m += 64) {
-                    Mp = fmax(Mp, (double)(bits_f32(s_words[m][0]) * invT32));
-                    Mq = fmax(Mq, (double)(bits_f32(s_words[m][3]) * invT32));
+                    Mp32 = fmaxf(Mp32, bits_f32(s_words[m][0]) * invT32);
+                    Mq32 = fmaxf(Mq32, bits_f32(s_words[m][3]) * invT32);
                 }
-                Mp = wave_max(Mp);
-                Mq = wave_max(Mq);
+                const double Mp = wave_max_f32(Mp32), Mq = wave_max_f32(Mq32);
+                // e^(x/T - M) of the children's tokens (one lane per child)
+                // first: they need only the maxima, so their long fp64
+                // chains overlap the sums' reductions
+                double ex_p[kMaxNodes / 64], ex_q[kMaxNodes / 64];
+#pragma unroll
+                for (int k = 0; k < kMaxNodes / 64; ++k) {
+                    const int c = lane + 1 + 64 * k;
+                    ex_p[k] = ex_q[k] = 0.0;
+                    if (c < N && s_par[c] == u) {
+                        ex_p[k] = exp_f64((double)s_tx[c] * invT - Mp);
+                        ex_q[k] = exp_f64((double)s_dx[c] * invT - Mq);
+                    }
+                }
                 double Zp = 0.0, Zq = 0.0;
                 for (int m = lane; m < wpg; m += 64) {
                     const double mk = (double)(bits_f32(s_words[m][0]) * invT32);
@@ -576,10 +602,12 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     s_sync_ok = ok;
                 }
                 // p and q of every child's token, one lane per child
-                for (int c = lane + 1; c < N; c += 64) {
-                    if (s_par[c] == u) {
-                        s_px[c] = exp_f64((double)s_tx[c] * invT - Mp) * inv_zp;
-                        s_qx[c] = exp_f64((double)s_dx[c] * invT - Mq) * inv_zq;
+#pragma unroll
+                for (int k = 0; k < kMaxNodes / 64; ++k) {
+                    const int c = lane + 1 + 64 * k;
+                    if (c < N && s_par[c] == u) {
+                        s_px[c] = ex_p[k] * inv_zp;
+                        s_qx[c] = ex_q[k] * inv_zq;
                     }
                 }
             }
