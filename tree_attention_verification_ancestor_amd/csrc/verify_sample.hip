@@ -272,11 +272,12 @@ __device__ __forceinline__ uint64_t tag_word(uint32_t gen, uint32_t payload)
 
 // Wave 0 only. Lanes 0..NW-1 publish word i = mine (lane i's payload) in
 // this workgroup's slot for generation `gen`; then lane l polls members l,
-// l+64, ... and stores member m's payloads in got[m][0..NW) (LDS, read back
-// by the same lane). Returns false on a timeout (every lane).
+// l+64, ... and keeps member l's payloads in w0[0..NW) (registers) and
+// member m's for m >= 64 in got[m][0..NW) (LDS, read back by the same lane).
+// Returns false on a timeout (every lane).
 template <int NW>
 __device__ bool wave0_exchange(uint64_t *box, int wpg, int rank, uint32_t gen, uint32_t mine,
-                               uint32_t (*got)[kSlotWords])
+                               uint32_t (*got)[kSlotWords], uint32_t (&w0)[NW])
 {
     const int lane = threadIdx.x & 63;
     uint64_t *base = box + (size_t)(gen & 1u) * wpg * kSlotWords;
@@ -294,12 +295,18 @@ __device__ bool wave0_exchange(uint64_t *box, int wpg, int rank, uint32_t gen, u
                 word[i] = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             bool all = true;
 #pragma unroll
-            for (int i = 0; i < NW; ++i) {
+            for (int i = 0; i < NW; ++i)
                 all &= (uint32_t)(word[i] >> 32) == gen;
-                got[m][i] = (uint32_t)word[i];
-            }
-            if (all)
+            if (all) {
+#pragma unroll
+                for (int i = 0; i < NW; ++i) {
+                    if (m == lane)
+                        w0[i] = (uint32_t)word[i];
+                    else
+                        got[m][i] = (uint32_t)word[i];
+                }
                 break;
+            }
             __builtin_amdgcn_s_sleep(1);
             if (++polls > kSpinLimit) {
                 ok = false;
@@ -419,6 +426,11 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
         int pf_node = -1;
         float pf_t[kSvEpt], pf_d[kSvEpt];
         float pf_tx = 0.f, pf_dx = 0.f;   // logits of child `tid` of pf_node, if any
+        // node `tid`'s parent, and its token's logits in the parent's rows
+        // while the walk is at that parent (wave 0 reads them from these
+        // registers for nodes below 64)
+        const int my_par = tid < N ? s_par[tid] : -2;
+        float my_tx = 0.f, my_dx = 0.f;
 
         int u = 0;
         while (!failed) {
@@ -434,9 +446,9 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     tf[e] = pf_t[e];
                     df[e] = has_kids ? pf_d[e] : -INFINITY;
                 }
-                if (tid < N && s_par[tid] == u) {
-                    s_tx[tid] = pf_tx;
-                    s_dx[tid] = pf_dx;
+                if (my_par == u) {
+                    s_tx[tid] = my_tx = pf_tx;
+                    s_dx[tid] = my_dx = pf_dx;
                 }
             } else {
 #pragma unroll
@@ -450,10 +462,10 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                             df[e] = drow[idx];
                     }
                 }
-                if (tid < N && s_par[tid] == u) {
+                if (my_par == u) {
                     const int x = s_tok[tid];
-                    s_tx[tid] = trow[x];
-                    s_dx[tid] = drow[x];
+                    s_tx[tid] = my_tx = trow[x];
+                    s_dx[tid] = my_dx = drow[x];
                 }
             }
             // Maxima of the raw fp32 logits (exact; x -> x/T is monotone) and
@@ -549,50 +561,59 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     if (lane == i)
                         mine = mine6[i];
                 bool ok = true;
+                uint32_t w6[6] = {0, 0, 0, 0, 0, 0};   // member `lane`'s payloads
                 if (wpg == 1) {
-                    if (lane == 0) {
 #pragma unroll
-                        for (int i = 0; i < 6; ++i)
-                            s_words[0][i] = mine6[i];
-                    }
+                    for (int i = 0; i < 6; ++i)
+                        w6[i] = mine6[i];
                 } else {
-                    ok = wave0_exchange<6>(box, wpg, rank, ++gen, mine, s_words);
+                    ok = wave0_exchange<6>(box, wpg, rank, ++gen, mine, s_words, w6);
                 }
+                auto word6 = [&](int m, int i) __attribute__((always_inline)) {
+                    return m == lane ? w6[i] : s_words[m][i];
+                };
                 // member maxima first, then the rebased sums, in member order
                 float Mp32 = -INFINITY, Mq32 = -INFINITY;
                 for (int m = lane; m < wpg; m += 64) {
-                    Mp32 = fmaxf(Mp32, bits_f32(s_words[m][0]) * invT32);
-                    Mq32 = fmaxf(Mq32, bits_f32(s_words[m][3]) * invT32);
+                    Mp32 = fmaxf(Mp32, bits_f32(word6(m, 0)) * invT32);
+                    Mq32 = fmaxf(Mq32, bits_f32(word6(m, 3)) * invT32);
                 }
                 const double Mp = wave_max_f32(Mp32), Mq = wave_max_f32(Mq32);
                 // e^(x/T - M) of the children's tokens (one lane per child)
                 // first: they need only the maxima, so their long fp64
                 // chains overlap the sums' reductions
+                // child c = lane + 64 k; for k = 0 its logits are this lane's
                 double ex_p[kMaxNodes / 64], ex_q[kMaxNodes / 64];
 #pragma unroll
                 for (int k = 0; k < kMaxNodes / 64; ++k) {
-                    const int c = lane + 1 + 64 * k;
+                    const int c = lane + 64 * k;
                     ex_p[k] = ex_q[k] = 0.0;
-                    if (c < N && s_par[c] == u) {
-                        ex_p[k] = exp_f64((double)s_tx[c] * invT - Mp);
-                        ex_q[k] = exp_f64((double)s_dx[c] * invT - Mq);
+                    if (k == 0 ? my_par == u : (c < N && s_par[c] == u)) {
+                        const float tx = k == 0 ? my_tx : s_tx[c], dx = k == 0 ? my_dx : s_dx[c];
+                        ex_p[k] = exp_bulk((double)tx * invT - Mp);
+                        ex_q[k] = exp_bulk((double)dx * invT - Mq);
                     }
                 }
-                double Zp = 0.0, Zq = 0.0;
+                double Zp = 0.0, Zq = 0.0, zm0 = 0.0;
                 for (int m = lane; m < wpg; m += 64) {
-                    const double mk = (double)(bits_f32(s_words[m][0]) * invT32);
-                    const double zk = bits_f64(s_words[m][1], s_words[m][2]);
+                    const double mk = (double)(bits_f32(word6(m, 0)) * invT32);
+                    const double zk = bits_f64(word6(m, 1), word6(m, 2));
                     const double zm = (mk == -INFINITY) ? (zk != zk ? zk : 0.0) : zk * exp_bulk(mk - Mp);
-                    s_mass[m] = zm;   // divided by Zp below
+                    if (m == lane)
+                        zm0 = zm;
+                    else
+                        s_mass[m] = zm;   // divided by Zp below
                     Zp += zm;
-                    const double mqk = (double)(bits_f32(s_words[m][3]) * invT32);
-                    const double zqk = bits_f64(s_words[m][4], s_words[m][5]);
+                    const double mqk = (double)(bits_f32(word6(m, 3)) * invT32);
+                    const double zqk = bits_f64(word6(m, 4), word6(m, 5));
                     Zq += (mqk == -INFINITY) ? 0.0 : zqk * exp_bulk(mqk - Mq);
                 }
                 Zp = wave_sum(Zp);
                 Zq = wave_sum(Zq);
                 const double inv_zp = 1.0 / Zp, inv_zq = 1.0 / Zq;
-                for (int m = lane; m < wpg; m += 64)
+                if (lane < wpg)
+                    s_mass[lane] = zm0 * inv_zp;
+                for (int m = lane + 64; m < wpg; m += 64)
                     s_mass[m] *= inv_zp;
                 if (lane == 0) {
                     s_norm[0] = Mp;
@@ -604,8 +625,8 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 // p and q of every child's token, one lane per child
 #pragma unroll
                 for (int k = 0; k < kMaxNodes / 64; ++k) {
-                    const int c = lane + 1 + 64 * k;
-                    if (c < N && s_par[c] == u) {
+                    const int c = lane + 64 * k;
+                    if (k == 0 ? my_par == u : (c < N && s_par[c] == u)) {
                         s_px[c] = ex_p[k] * inv_zp;
                         s_qx[c] = ex_q[k] * inv_zq;
                     }
@@ -682,21 +703,19 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     const double sc = wave_sum(lane < kSvWaves ? s_wq[lane] : 0.0);
                     const uint32_t mine = lane == 0 ? f64_hi(sc) : lane == 1 ? f64_lo(sc) : 0u;
                     bool ok = true;
-                    if (wpg == 1) {
-                        if (lane == 0) {
-                            s_words[0][0] = f64_hi(sc);
-                            s_words[0][1] = f64_lo(sc);
-                        }
-                    } else {
-                        ok = wave0_exchange<2>(box, wpg, rank, ++gen, mine, s_words);
-                    }
+                    uint32_t w2[2] = {f64_hi(sc), f64_lo(sc)};   // member `lane`'s payloads
+                    if (wpg > 1)
+                        ok = wave0_exchange<2>(box, wpg, rank, ++gen, mine, s_words, w2);
+                    auto word2 = [&](int m, int i) __attribute__((always_inline)) {
+                        return m == lane ? w2[i] : s_words[m][i];
+                    };
                     double Zr = 0.0;
                     for (int m = lane; m < wpg; m += 64)
-                        Zr += bits_f64(s_words[m][0], s_words[m][1]);
+                        Zr += bits_f64(word2(m, 0), word2(m, 1));
                     Zr = wave_sum(Zr);
                     if (Zr > 0.0) {
                         for (int m = lane; m < wpg; m += 64)
-                            s_mass[m] = bits_f64(s_words[m][0], s_words[m][1]) / Zr;
+                            s_mass[m] = bits_f64(word2(m, 0), word2(m, 1)) / Zr;
                     }
                     if (lane == 0) {
                         s_zhist[k] = Zr;
