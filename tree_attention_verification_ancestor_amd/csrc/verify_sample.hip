@@ -56,9 +56,10 @@
 // which makes it bound by the vector ALUs; those are fp32 (y = x/T - m to
 // one rounding, then v_exp_f32) and are summed in fp64, so the entries that
 // carry a sum are within a few 1e-7. The rebasing of partial sums to the
-// row's maximum uses exp_bulk (an fp32 head and an fp64 tail, 1e-7
-// relative). p and q at a child's token, which a decision reads directly,
-// use exp_f64, a table-free fp64 routine within one ulp.
+// row's maximum and p and q at a child's token use exp_bulk (an fp32 head and
+// an fp64 tail, 1e-7 relative): a decision can then differ from one taken in
+// exact arithmetic only for a draw within a few 1e-7 of its boundary. exp_f64,
+// a table-free fp64 routine within one ulp, serves tav_target_probs.
 
 #include <algorithm>
 
