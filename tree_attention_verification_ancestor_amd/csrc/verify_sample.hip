@@ -96,6 +96,7 @@ struct SvArgs {
     uint64_t *box;    // [ngroups][2][wpg][kSlotWords]
     uint32_t *flags;
     int32_t wpg, ngroups, chunk;
+    int32_t vec4;     // rows can be read 16 bytes at a time (V % 4 == 0, aligned logits)
 };
 
 // ---------------------------------------------------------------------------
@@ -366,6 +367,35 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
     const int wpg = a.wpg;
     const int64_t base = (int64_t)rank * a.chunk;
     const int64_t lim = std::min<int64_t>((int64_t)a.V, base + a.chunk);
+    // This thread's entries of the chunk: run h (of two) holds tokens
+    // base + h * 4 * 512 + 4 tid + j, j < 4, read as one 16-byte load where
+    // the row allows it (the chunk is a multiple of 4 tokens).
+    constexpr int kRun = 4 * kSvThreads;
+    auto tok = [&](int e) __attribute__((always_inline)) {
+        return base + (int64_t)(e >> 2) * kRun + 4 * tid + (e & 3);
+    };
+    auto load_row = [&](const float *row, float (&v)[kSvEpt]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < kSvEpt / 4; ++h) {
+            const int64_t i0 = base + (int64_t)h * kRun + 4 * tid;
+            if (a.vec4 && i0 + 3 < lim) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(row + i0);
+                v[4 * h] = x.x;
+                v[4 * h + 1] = x.y;
+                v[4 * h + 2] = x.z;
+                v[4 * h + 3] = x.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    v[4 * h + j] = i0 + j < lim ? row[i0 + j] : -INFINITY;
+            }
+        }
+    };
+    auto no_row = [&](float (&v)[kSvEpt]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < kSvEpt; ++e)
+            v[e] = -INFINITY;
+    };
     uint64_t *box = a.box + (size_t)g * 2 * wpg * kSlotWords;
     const double invT = 1.0 / a.T;
     // The reference maxima that the vocabulary-wide sums are taken against
@@ -452,17 +482,11 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     s_dx[tid] = my_dx = pf_dx;
                 }
             } else {
-#pragma unroll
-                for (int e = 0; e < kSvEpt; ++e) {
-                    const int64_t idx = base + (int64_t)e * kSvThreads + tid;
-                    tf[e] = -INFINITY;
-                    df[e] = -INFINITY;
-                    if (idx < lim) {
-                        tf[e] = trow[idx];
-                        if (has_kids)
-                            df[e] = drow[idx];
-                    }
-                }
+                load_row(trow, tf);
+                if (has_kids)
+                    load_row(drow, df);
+                else
+                    no_row(df);
                 if (my_par == u) {
                     const int x = s_tok[tid];
                     s_tx[tid] = my_tx = trow[x];
@@ -517,17 +541,11 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 const float *t1 = a.tl + (rowbase + c1) * a.V;
                 const float *d1 = a.dl + (rowbase + c1) * a.V;
                 const bool c1_kids = s_first[c1] >= 0;
-#pragma unroll
-                for (int e = 0; e < kSvEpt; ++e) {
-                    const int64_t idx = base + (int64_t)e * kSvThreads + tid;
-                    pf_t[e] = -INFINITY;
-                    pf_d[e] = -INFINITY;
-                    if (idx < lim) {
-                        pf_t[e] = t1[idx];
-                        if (c1_kids)
-                            pf_d[e] = d1[idx];
-                    }
-                }
+                load_row(t1, pf_t);
+                if (c1_kids)
+                    load_row(d1, pf_d);
+                else
+                    no_row(pf_d);
                 if (tid < N && s_par[tid] == c1) {
                     const int x = s_tok[tid];
                     pf_tx = t1[x];
@@ -774,21 +792,24 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 break;
             }
             if (mass > 0.0 && before <= target && target < before + mass) {
-                // element e of thread t is token base + e*512 + t, so token
-                // order is (e, wave, lane). Totals of every (e, wave) slot
-                // first, in that order; then the one wave holding the target
-                // scans its lanes.
+                // Token order is (run h, wave, lane, entry j). Totals of every
+                // (run, wave) slot first, in that order; then the wave holding
+                // the target scans its lanes' run sums, and the lane its four
+                // entries.
                 const int lane = tid & 63, wave = tid >> 6;
+                auto run_sum = [&](int h) __attribute__((always_inline)) {
+                    return ((pr[4 * h] + pr[4 * h + 1]) + pr[4 * h + 2]) + pr[4 * h + 3];
+                };
 #pragma unroll
-                for (int e = 0; e < kSvEpt; ++e) {
-                    const double t = wave_sum_ordered(pr[e]);
+                for (int h = 0; h < kSvEpt / 4; ++h) {
+                    const double t = wave_sum_ordered(run_sum(h));
                     if (lane == 0)
-                        s_slot[e * kSvWaves + wave] = t;
+                        s_slot[h * kSvWaves + wave] = t;
                 }
                 __syncthreads();
                 if (tid == 0) {
                     double run = before;
-                    for (int k2 = 0; k2 < kSvEpt * kSvWaves; ++k2) {
+                    for (int k2 = 0; k2 < (kSvEpt / 4) * kSvWaves; ++k2) {
                         const double nxt = run + s_slot[k2];
                         if (s_slot[k2] > 0.0 && run <= target && target < nxt) {
                             s_hit = k2;
@@ -801,12 +822,16 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 __syncthreads();
                 const int hit = s_hit;
                 if (hit >= 0 && wave == hit % kSvWaves) {
-                    const int e_hit = hit / kSvWaves;
-                    double v = 0.0;
+                    const int h_hit = hit / kSvWaves;
+                    double v = 0.0, pe[4];
 #pragma unroll
-                    for (int e = 0; e < kSvEpt; ++e)
-                        if (e == e_hit)
-                            v = pr[e];
+                    for (int h = 0; h < kSvEpt / 4; ++h)
+                        if (h == h_hit) {
+                            v = run_sum(h);
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                pe[j] = pr[4 * h + j];
+                        }
                     double incl = v;
 #pragma unroll
                     for (int o = 1; o < 64; o <<= 1) {
@@ -818,11 +843,26 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     if (lane == 0)
                         excl = 0.0;
                     const double lo = s_hit_off + excl, hi = s_hit_off + incl;
-                    const int64_t idx = base + (int64_t)e_hit * kSvThreads + tid;
+                    const int64_t i0 = base + (int64_t)h_hit * kRun + 4 * tid;
                     if (v > 0.0) {
-                        atomicMax(&s_last_live, (int)idx);
+                        int last = -1, found = -1;
+                        double r = lo;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const double nx = r + pe[j];
+                            if (pe[j] > 0.0) {
+                                last = j;
+                                if (found < 0 && r <= target && target < nx)
+                                    found = j;
+                            }
+                            r = nx;
+                        }
+                        atomicMax(&s_last_live, (int)(i0 + last));
+                        // at most one lane's run holds the target; rounding
+                        // between its sum and its entries' running sum gives
+                        // the run's last live entry
                         if (lo <= target && target < hi)
-                            s_found = (int)idx;   // at most one lane qualifies
+                            s_found = (int)(i0 + (found >= 0 ? found : last));
                     }
                 }
                 // rounding left the target past the chunk's summed slots: the
@@ -831,7 +871,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
 #pragma unroll
                     for (int e = 0; e < kSvEpt; ++e)
                         if (pr[e] > 0.0)
-                            atomicMax(&s_last_live, (int)(base + (int64_t)e * kSvThreads + tid));
+                            atomicMax(&s_last_live, (int)tok(e));
                 }
                 __syncthreads();
                 if (tid == 0)
@@ -897,7 +937,7 @@ bool sv_plan(int32_t B, int32_t V, SvPlan &p)
     p.wpg = (int)ceil_div(V, kSvChunk);
     if (p.wpg > resident || p.wpg > kMaxWpg)
         return false;
-    p.chunk = (int)ceil_div(V, p.wpg);
+    p.chunk = (int)(ceil_div(ceil_div(V, p.wpg), 4) * 4);   // whole 16-byte runs
     p.ngroups = (int)std::min<int64_t>(B, resident / p.wpg);
     p.box_bytes = (size_t)p.ngroups * 2 * p.wpg * kSlotWords * sizeof(uint64_t);
     return true;
@@ -1005,6 +1045,7 @@ extern "C" tav_status spec_verify_sample(const float *target_logits, const float
     a.wpg = p.wpg;
     a.ngroups = p.ngroups;
     a.chunk = p.chunk;
+    a.vec4 = V % 4 == 0 && aligned(target_logits, 16) && aligned(draft_logits, 16);
     hipLaunchKernelGGL(spec_verify_kernel, dim3(p.wpg * p.ngroups), dim3(kSvThreads), 0,
                        as_stream(stream), a);
     return hipGetLastError() == hipSuccess ? TAV_OK : TAV_ERR_LAUNCH;
