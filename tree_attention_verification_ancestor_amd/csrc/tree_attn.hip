@@ -35,14 +35,19 @@
 // five, filled two tiles ahead. Prefix tiles move from HBM straight into LDS
 // (global_load_lds_dwordx4: 16 bytes per lane, no staging registers), with
 // the block table resolved once per split into head-block indices in LDS;
-// each tile's V is then turned from bf16 into fp16 in place, keys past the
-// prefix zeroed, while the S MFMAs run. The few tree tiles go through
-// registers (their V rows need a transpose). One barrier per tile.
-// Overlap. A wave's work per tile is an MFMA phase (S) and a phase that is
-// mostly vector ALU work (the softmax, then P.V of the tile before). In an
-// 8-wave workgroup the two waves that share a SIMD run these in opposite
-// order, one a tile behind the other, so one's vector work runs under the
-// other's MFMAs.
+// in an 8-wave workgroup the four waves with the shorter chain of work per
+// tile issue every load (an issuing wave stalls until the CU's load path
+// takes each one). Each tile's V is turned from bf16 into fp16 in place,
+// one 16-byte chunk at a time between the S MFMAs, keys past the prefix
+// zeroed. The few tree tiles go through registers (their V rows need a
+// transpose). One barrier per tile.
+// Operand reads. The S and P.V MFMAs take their LDS operands from reads
+// issued four MFMAs ahead into separate registers, held in that order by a
+// scheduling fence after each MFMA.
+// Overlap. A wave's work per tile is an MFMA phase (S) and a phase that
+// mixes vector ALU work and MFMAs: the softmax of the tile spread between the
+// P.V MFMAs of the tile before. In an 8-wave workgroup the two waves that
+// share a SIMD run these in opposite order, one a tile behind the other.
 // Splits of the prefix write unnormalised partials (O, max, sum) that a
 // combine kernel merges with log-sum-exp; the last split also takes the tree
 // tiles (keys masked by the ancestor bitmask).
