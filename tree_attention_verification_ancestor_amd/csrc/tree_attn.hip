@@ -8,7 +8,7 @@
 //
 // Work decomposition. For one sequence b and KV head kvh, the N*G query rows
 // (node i, head g of the group) share every key and value, so a workgroup
-// takes a block of 32*NW of those rows and one split of the prefix; the K/V
+// takes a block of 32*NW of those rows and one split of the key tiles; the K/V
 // tiles it stages in LDS are read by all its rows (the tree's queries are the
 // M of a small dense contraction, which is what makes MFMA pay here).
 //
@@ -48,9 +48,10 @@
 // mixes vector ALU work and MFMAs: the softmax of the tile spread between the
 // P.V MFMAs of the tile before. In an 8-wave workgroup the two waves that
 // share a SIMD run these in opposite order, one a tile behind the other.
-// Splits of the prefix write unnormalised partials (O, max, sum) that a
-// combine kernel merges with log-sum-exp; the last split also takes the tree
-// tiles (keys masked by the ancestor bitmask).
+// The key tiles of a (sequence, KV head) are its prefix tiles and then its
+// tree tiles (keys masked by the ancestor bitmask), split evenly; splits
+// write unnormalised partials (O, max, sum) that a combine kernel merges
+// with log-sum-exp.
 
 #include <algorithm>
 #include <type_traits>
@@ -225,11 +226,17 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
             raise_flag(a.flags, TAV_FLAG_CAPACITY);
         L = std::max(0, std::min(L, std::min(a.max_prefix_len, a.max_blocks * kBlock)));
     }
+    // The unit's tiles are its Tb prefix tiles and then its tree tiles; split
+    // s takes [s U / S, (s + 1) U / S) of them, so the tree tiles count in the
+    // balance of the splits.
     const int Tb = (L + kKT - 1) / kKT;
-    const int t_begin = (int)((int64_t)s * Tb / a.S);
-    const int t_end = (int)((int64_t)(s + 1) * Tb / a.S);
+    const int Ub = Tb + (a.N + kKT - 1) / kKT;
+    const int u0 = (int)((int64_t)s * Ub / a.S), u1 = (int)((int64_t)(s + 1) * Ub / a.S);
+    const int t_begin = std::min(u0, Tb);
+    const int t_end = std::min(u1, Tb);
     const int n_pre = t_end - t_begin;
-    const int n_tree = (s == a.S - 1) ? (a.N + kKT - 1) / kKT : 0;
+    const int tt0 = std::max(u0, Tb) - Tb;               // first tree tile of the split
+    const int n_tree = std::max(0, u1 - std::max(u0, Tb));
     const int n_tiles = n_pre + n_tree;
     // The split's block-table slice, validated once. Entries past the prefix
     // (and bad ones, which also raise a flag) name block 0 of this head, a
@@ -267,7 +274,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
             qf[k] = __builtin_bit_cast(bf16x8, v);
         }
     }
-    const uint64_t mrow0 = (n_tree > 0 && row_ok) ? a.mask[((int64_t)b * a.N + node) * a.W] : 1;
+    const uint64_t mrow0 = (n_tree > 0 && row_ok) ? a.mask[((int64_t)b * a.N + node) * a.W + tt0] : 1;
     // Wait for these loads here, before any tile load is in flight. The
     // compiler does not see the direct tile loads (inline assembly), so a
     // register load it still counts as outstanding inside the tile loop would
@@ -374,7 +381,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     // Tree tile: through registers. K rows go to their MFMA rows; V rows are
     // feature-contiguous, so 8 features of a key are scattered (as fp16).
     auto stage_tree_tile = [&](int it, char *kl, char *vl) __attribute__((always_inline)) {
-        const int j0 = (it - n_pre) * kKT;
+        const int j0 = (it - n_pre + tt0) * kKT;
 #pragma unroll 1   // keeps one chunk's registers live
         for (int r = 0; r < C::kChPerThread; ++r) {
             const int ci = tid + r * C::kThreads;
@@ -463,10 +470,10 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
         uint64_t mw;   // bit k: key k of the tile is visible
         int lim;       // keys at or past it are not keys
         if (it >= n_pre) {
-            const int tt = it - n_pre;
+            const int tt = it - n_pre + tt0;
             mw = 1;    // a padding row sees key 0 only
             if (row_ok)
-                mw = tt == 0 ? mrow0 : a.mask[((int64_t)b * a.N + node) * a.W + tt];
+                mw = tt == tt0 ? mrow0 : a.mask[((int64_t)b * a.N + node) * a.W + tt];
             lim = a.N - tt * kKT;
         } else {
             mw = ~0ull;
