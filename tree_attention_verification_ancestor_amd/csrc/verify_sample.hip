@@ -338,6 +338,8 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
     __shared__ int32_t s_par[kMaxNodes];
     __shared__ int32_t s_first[kMaxNodes];
     __shared__ int32_t s_next[kMaxNodes];
+    constexpr int kKidWords = kMaxNodes / 64;
+    __shared__ unsigned long long s_kids[kMaxNodes][kKidWords];   // children of each node, as bits
     __shared__ int32_t s_tok[kMaxNodes];
     __shared__ float s_tx[kMaxNodes];     // target logit of child c's token in its parent's row
     __shared__ float s_dx[kMaxNodes];     // draft logit of the same
@@ -408,41 +410,74 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
 
     for (int b = g; b < a.B && alive; b += a.ngroups) {
         const int64_t rowbase = (int64_t)b * N;
+        // ---- the root's rows first: the walk starts there --------------------
+        int pf_node = 0;   // rows of the likeliest next node, fetched a level ahead
+        float pf_t[kSvEpt], pf_d[kSvEpt];
+        float pf_tx = 0.f, pf_dx = 0.f;   // logits of child `tid` of pf_node, if any
+        load_row(a.tl + rowbase * a.V, pf_t);
+        load_row(a.dl + rowbase * a.V, pf_d);
         // ---- tree structure in LDS, validated ------------------------------
+        // Each node's children as a bitmask (bit c of word c / 64), so first
+        // child and next sibling are find-first-set operations; meanwhile the
+        // upper half of the workgroup draws every node's uniforms (indexed by
+        // node, not walk order).
         __syncthreads();
+        // node `tid`'s parent and token, and its token's logits in the
+        // parent's rows while the walk is at that parent (wave 0 reads them
+        // from these registers for nodes below 64)
+        int my_par = -2, my_tok = 0;
+        float my_tx = 0.f, my_dx = 0.f;
         if (tid == 0)
             s_bad = 0;
         if (tid < N) {
-            s_par[tid] = a.parent[rowbase + tid];
-            s_tok[tid] = a.token[rowbase + tid];
-            s_first[tid] = N;
-            s_next[tid] = -1;
-        }
-        __syncthreads();
-        if (tid < N) {
-            const int p = s_par[tid];
-            if (tid == 0 ? p != -1 : (p < 0 || p >= tid))
-                atomicOr(&s_bad, 1);
-            if (tid > 0 && (s_tok[tid] < 0 || s_tok[tid] >= a.V))
-                atomicOr(&s_bad, 2);
-        }
-        __syncthreads();
-        if (s_bad == 0 && tid >= 1 && tid < N) {
-            atomicMin(&s_first[s_par[tid]], tid);
-            for (int c2 = tid + 1; c2 < N; ++c2)
-                if (s_par[c2] == s_par[tid]) {
-                    s_next[tid] = c2;
-                    break;
-                }
-        }
-        __syncthreads();
-        if (tid < N && s_first[tid] == N)
-            s_first[tid] = -1;
-        // every node's uniforms at once (they are indexed by node, not walk order)
-        for (int i = tid; i < N; i += kSvThreads) {
+            my_par = a.parent[rowbase + tid];
+            my_tok = a.token[rowbase + tid];
+            s_par[tid] = my_par;
+            s_tok[tid] = my_tok;
+#pragma unroll
+            for (int w = 0; w < kKidWords; ++w)
+                s_kids[tid][w] = 0ull;
+            if (tid >= 1 && my_par == 0 && my_tok >= 0 && my_tok < a.V) {
+                pf_tx = a.tl[rowbase * a.V + my_tok];
+                pf_dx = a.dl[rowbase * a.V + my_tok];
+            }
+        } else if (tid >= kSvThreads / 2 && tid - kSvThreads / 2 < N) {
+            const int i = tid - kSvThreads / 2;
             const NodeUniforms r = node_uniforms(a.seed, a.offset, b, i);
             s_uacc[i] = r.acc;
             s_ures[i] = r.res;
+        }
+        __syncthreads();
+        if (tid < N) {
+            const bool bad_p = tid == 0 ? my_par != -1 : (my_par < 0 || my_par >= tid);
+            if (bad_p)
+                atomicOr(&s_bad, 1);
+            if (tid > 0 && (my_tok < 0 || my_tok >= a.V))
+                atomicOr(&s_bad, 2);
+            if (tid >= 1 && !bad_p)
+                atomicOr(&s_kids[my_par][tid >> 6], 1ull << (tid & 63));
+        }
+        __syncthreads();
+        if (tid < N) {
+            int first = -1, next = -1;
+#pragma unroll
+            for (int w = 0; w < kKidWords; ++w) {
+                const uint64_t m = s_kids[tid][w];
+                if (first < 0 && m != 0ull)
+                    first = 64 * w + __builtin_ctzll(m);
+            }
+            if (tid >= 1 && my_par >= 0 && my_par < tid) {
+#pragma unroll
+                for (int w = 0; w < kKidWords; ++w) {
+                    uint64_t m = w >= (tid >> 6) ? s_kids[my_par][w] : 0ull;
+                    if (w == (tid >> 6))
+                        m &= ~((2ull << (tid & 63)) - 1ull);   // siblings after tid
+                    if (next < 0 && m != 0ull)
+                        next = 64 * w + __builtin_ctzll(m);
+                }
+            }
+            s_first[tid] = first;
+            s_next[tid] = next;
         }
         __syncthreads();
 
@@ -452,16 +487,6 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
         if (failed && lead)
             raise_flag(a.flags, (s_bad & 1 ? TAV_FLAG_BAD_PARENT : 0u) |
                                     (s_bad & 2 ? TAV_FLAG_BAD_TOKEN : 0u));
-
-        // rows of the likeliest next node, fetched a level ahead
-        int pf_node = -1;
-        float pf_t[kSvEpt], pf_d[kSvEpt];
-        float pf_tx = 0.f, pf_dx = 0.f;   // logits of child `tid` of pf_node, if any
-        // node `tid`'s parent, and its token's logits in the parent's rows
-        // while the walk is at that parent (wave 0 reads them from these
-        // registers for nodes below 64)
-        const int my_par = tid < N ? s_par[tid] : -2;
-        float my_tx = 0.f, my_dx = 0.f;
 
         int u = 0;
         while (!failed) {
@@ -881,19 +906,22 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
         }
 
         // ---- outputs owned by the group leader ------------------------------
-        if (lead) {
-            if (failed || !alive) {
+        if (failed || !alive) {
+            if (lead) {
                 for (int i = 0; i < N; ++i) {
                     a.path[rowbase + i] = i == 0 ? 0 : -1;
                     a.out_tok[rowbase + i] = -1;
                 }
                 a.n_acc[b] = 0;
-            } else {
+            }
+        } else if (rank == 0) {
+            // the padding past the emitted entries, which the walk never wrote
+            for (int i = nacc + 1 + tid; i < N; i += kSvThreads) {
+                a.path[rowbase + i] = -1;
+                a.out_tok[rowbase + i] = -1;
+            }
+            if (lead) {
                 a.path[rowbase] = 0;
-                for (int i = nacc + 1; i < N; ++i) {
-                    a.path[rowbase + i] = -1;
-                    a.out_tok[rowbase + i] = -1;
-                }
                 a.n_acc[b] = nacc;
             }
         }
