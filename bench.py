@@ -10,12 +10,16 @@ copies of the paged caches rotate across steps so the 256 MB last-level cache
 cannot hold the step's KV working set.
 
 Prints one JSON line: verified tree nodes/s (B*N per step time), with the
-attention launch's roofline and the CPU oracle's rate on this host. The
+attention launch's roofline and the CPU oracle's rate on this host; per-stage
+and per-step percentiles from a second pass with events between the calls;
+and, outside the timed regions, the walk's acceptance over many Philox
+offsets (mean accepted length, emitted tokens, rows visited). The
 attention launch (main kernel + combine) is timed with events on its stream
 inside the timed region; its HBM traffic comes from the rocprofv3 counter
 record under profiles/ while that record matches the kernel source.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config llama70b] [--no-cpu]
+                    [--offsets 1000]
     python bench.py --copy-calibration     # a plain copy of known size, for the counters
 """
 
@@ -169,9 +173,26 @@ def run_gpu(args, w):
     torch.cuda.synchronize()
     stage = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in evs])
     stage_ms = stage.mean(axis=0)
+    step_ms = np.array([e[0].elapsed_time(e[4]) for e in evs])
     assert int(flags.item()) == 0, f"device flags {int(flags.item()):#x}"
-    return dict(ms_step=ms_step, ms_attn=ms_attn, stage_ms=stage_ms, depth=to_numpy(depth),
-                path=to_numpy(path), n_acc=to_numpy(n_acc))
+    out = dict(ms_step=ms_step, ms_attn=ms_attn, stage_ms=stage_ms, stage_all=stage,
+               step_all=step_ms, depth=to_numpy(depth), path=to_numpy(path), n_acc=to_numpy(n_acc))
+
+    # acceptance over many Philox offsets (outside the timed regions): the
+    # mean accepted length and the rows the walk visits, for the byte count
+    n_off = args.offsets
+    paths = torch.empty((n_off, B, N), dtype=torch.int32, device=dev)
+    naccs = torch.empty((n_off, B), dtype=torch.int32, device=dev)
+    toks_o = torch.empty((n_off, B, N), dtype=torch.int32, device=dev)
+    for o in range(n_off):
+        tav.spec_verify_sample(d["target_logits"], d["draft_logits"], d["parent"], d["token"],
+                               w.temperature, w.philox_seed, o, paths[o], naccs[o], toks_o[o],
+                               ws_s, flags, stream)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0, f"device flags {int(flags.item()):#x}"
+    out["offset_paths"] = to_numpy(paths)
+    out["offset_naccs"] = to_numpy(naccs)
+    return out
 
 
 def copy_calibration(reps=5):
@@ -210,10 +231,12 @@ def cpu_baseline(w, min_seconds=10.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="llama70b")
     ap.add_argument("--cache-copies", type=int, default=3)
+    ap.add_argument("--offsets", type=int, default=1000,
+                    help="Philox offsets of the acceptance statistics run")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain copy of known size (for the HBM counters)")
@@ -248,6 +271,20 @@ def main():
                 "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
 
     step_bytes = attn_bytes + sampler_bytes(w, g["path"], g["n_acc"]) + commit_bytes(w, g["n_acc"])
+    pct = lambda a: {"p10": round(float(np.percentile(a, 10)) * 1e3, 2),
+                     "p50": round(float(np.percentile(a, 50)) * 1e3, 2),
+                     "p90": round(float(np.percentile(a, 90)) * 1e3, 2)}
+    offp, offn = g["offset_paths"], g["offset_naccs"]
+    samp_mean = float(np.mean([sampler_bytes(w, offp[o], offn[o]) for o in range(len(offn))]))
+    acceptance = {
+        "offsets": int(len(offn)),
+        "mean_accepted_per_seq": round(float(offn.mean()), 4),
+        "mean_emitted_per_step": round(float((offn + 1).sum(axis=1).mean()), 3),
+        "mean_sampler_bytes": round(samp_mean),
+        "step_floor_us_at_mean": round(max((attn_bytes + samp_mean + float(np.mean(
+            [commit_bytes(w, offn[o]) for o in range(len(offn))]))) / (HBM_PEAK_GBS * 1e9),
+            attn_flops / (MFMA_PEAK_TFLOPS * 1e12)) * 1e6, 2),
+    }
     t_floor = max(step_bytes / (HBM_PEAK_GBS * 1e9), attn_flops / (MFMA_PEAK_TFLOPS * 1e12))
     ms = g["ms_step"]
     rec = {
@@ -271,6 +308,10 @@ def main():
         "stages_us": {k: round(v * 1e3, 2) for k, v in
                       zip(["tree_mask_build", "tree_attn_verify", "spec_verify_sample",
                            "kv_commit_path"], g["stage_ms"])},
+        "stages_us_pctl": {k: pct(g["stage_all"][:, i]) for i, k in
+                           enumerate(["tree_mask_build", "tree_attn_verify",
+                                      "spec_verify_sample", "kv_commit_path"])},
+        "step_us_pctl": pct(g["step_all"]),
         "tree_attn": {"us": round(t_attn * 1e6, 2),
                       "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                       "tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
@@ -279,6 +320,7 @@ def main():
         "step_roofline": {"algorithmic_bytes": step_bytes, "floor_us": round(t_floor * 1e6, 2),
                           "frac": round(t_floor / (ms * 1e-3), 4)},
         "accepted": g["n_acc"].tolist(),
+        "acceptance": acceptance,
     }
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w)
