@@ -26,6 +26,10 @@ __global__ __launch_bounds__(256) void kv_commit_kernel(
 {
     constexpr int CPR = D / 8; // 16-byte chunks per row
     const int b = blockIdx.y;
+    // this thread's first work item's path entry (t0 < N always)
+    const int64_t it0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int t0 = (int)std::min<int64_t>(it0 / ((int64_t)CPR * Hkv), N - 1);
+    const int32_t node0 = path[(int64_t)b * N + t0];
     const int32_t m = n_accepted[b];
     const int32_t L = prefix_len[b];
     const bool m_ok = m >= 0 && m < N;
@@ -54,14 +58,16 @@ __global__ __launch_bounds__(256) void kv_commit_kernel(
     if (!m_ok || L < 0)
         return;
 
-    // Row copies: work item = (t, kv head, chunk).
+    // Row copies: work item = (t, kv head, chunk). The launch covers every
+    // t < N, so each thread reads its path entry alongside n_accepted and
+    // prefix_len instead of after them.
     const int64_t items = (int64_t)(m + 1) * Hkv * CPR;
     for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items;
          it += (int64_t)gridDim.x * blockDim.x) {
         const int c = (int)(it % CPR);
         const int h = (int)((it / CPR) % Hkv);
         const int t = (int)(it / ((int64_t)CPR * Hkv));
-        const int32_t node = path[(int64_t)b * N + t];
+        const int32_t node = t == t0 ? node0 : path[(int64_t)b * N + t];
         if (node < 0 || node >= N) {
             raise_flag(flags, TAV_FLAG_BAD_PARENT);
             continue;

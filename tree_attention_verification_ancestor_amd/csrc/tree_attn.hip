@@ -804,20 +804,44 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(AttnArgs a, int 
     const int b = (int)(bh / a.Hkv), kvh = (int)(bh % a.Hkv);
     const int node = row / a.G, head = kvh * a.G + row % a.G;
     const int64_t P0 = ((int64_t)bh * a.RB + rb) * a.S;
+    // The (max, sum) pair and O chunk of up to kCombineBatch splits are
+    // requested before any is used, so the loads overlap instead of waiting
+    // on one another (the common split counts fit one batch). A split that
+    // saw no key has max -inf, O = 0 and sum 0; it is skipped.
+    constexpr int kCombineBatch = 4;
+    f32x2 ml[kCombineBatch];
+    f32x4 v[kCombineBatch];
+    auto load_batch = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < kCombineBatch; ++k) {
+            if (s0 + k < a.S) {
+                const int64_t pr = (P0 + s0 + k) * rows_per_block + rloc;
+                ml[k] = *reinterpret_cast<const f32x2 *>(a.part_ml + pr * 2);
+                v[k] = *reinterpret_cast<const f32x4 *>(a.part_o + pr * D + dq * 4);
+            }
+        }
+    };
+    load_batch(0);
     float M = -INFINITY;
-    for (int s = 0; s < a.S; ++s)
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k)
+        if (k < a.S)
+            M = fmaxf(M, ml[k].x);
+    for (int s = kCombineBatch; s < a.S; ++s)
         M = fmaxf(M, a.part_ml[((P0 + s) * rows_per_block + rloc) * 2]);
     float lsum = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.S; ++s) {
-        const int64_t pr = (P0 + s) * rows_per_block + rloc;
-        const float ms = a.part_ml[pr * 2];
-        if (ms == -INFINITY)
-            continue;
-        const float w = __builtin_amdgcn_exp2f(ms - M);
-        lsum += w * a.part_ml[pr * 2 + 1];
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(a.part_o + pr * D + dq * 4);
-        o += w * v;
+    for (int s0 = 0; s0 < a.S; s0 += kCombineBatch) {
+        if (s0 > 0)
+            load_batch(s0);
+#pragma unroll
+        for (int k = 0; k < kCombineBatch; ++k) {
+            if (s0 + k < a.S && ml[k].x != -INFINITY) {
+                const float w = __builtin_amdgcn_exp2f(ml[k].x - M);
+                lsum += w * ml[k].y;
+                o += w * v[k];
+            }
+        }
     }
     const float inv = 1.0f / lsum;
     const f32x4 r = o * inv;
