@@ -180,7 +180,7 @@ def run_gpu(args, w):
 
     # acceptance over many Philox offsets (outside the timed regions): the
     # mean accepted length and the rows the walk visits, for the byte count
-    n_off = args.offsets
+    n_off = max(0, args.offsets)
     paths = torch.empty((n_off, B, N), dtype=torch.int32, device=dev)
     naccs = torch.empty((n_off, B), dtype=torch.int32, device=dev)
     toks_o = torch.empty((n_off, B, N), dtype=torch.int32, device=dev)
@@ -275,16 +275,18 @@ def main():
                      "p50": round(float(np.percentile(a, 50)) * 1e3, 2),
                      "p90": round(float(np.percentile(a, 90)) * 1e3, 2)}
     offp, offn = g["offset_paths"], g["offset_naccs"]
-    samp_mean = float(np.mean([sampler_bytes(w, offp[o], offn[o]) for o in range(len(offn))]))
-    acceptance = {
-        "offsets": int(len(offn)),
-        "mean_accepted_per_seq": round(float(offn.mean()), 4),
-        "mean_emitted_per_step": round(float((offn + 1).sum(axis=1).mean()), 3),
-        "mean_sampler_bytes": round(samp_mean),
-        "step_floor_us_at_mean": round(max((attn_bytes + samp_mean + float(np.mean(
-            [commit_bytes(w, offn[o]) for o in range(len(offn))]))) / (HBM_PEAK_GBS * 1e9),
-            attn_flops / (MFMA_PEAK_TFLOPS * 1e12)) * 1e6, 2),
-    }
+    acceptance = None
+    if len(offn) > 0:
+        samp_mean = float(np.mean([sampler_bytes(w, offp[o], offn[o]) for o in range(len(offn))]))
+        acceptance = {
+            "offsets": int(len(offn)),
+            "mean_accepted_per_seq": round(float(offn.mean()), 4),
+            "mean_emitted_per_step": round(float((offn + 1).sum(axis=1).mean()), 3),
+            "mean_sampler_bytes": round(samp_mean),
+            "step_floor_us_at_mean": round(max((attn_bytes + samp_mean + float(np.mean(
+                [commit_bytes(w, offn[o]) for o in range(len(offn))]))) / (HBM_PEAK_GBS * 1e9),
+                attn_flops / (MFMA_PEAK_TFLOPS * 1e12)) * 1e6, 2),
+        }
     t_floor = max(step_bytes / (HBM_PEAK_GBS * 1e9), attn_flops / (MFMA_PEAK_TFLOPS * 1e12))
     ms = g["ms_step"]
     rec = {
