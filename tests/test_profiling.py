@@ -51,3 +51,22 @@ def test_kernel_names_map_to_short_names():
     assert profiling.short_name(
         "void at::native::vectorized_elementwise_kernel<4, at::native::CUDAFunctorOnSelf_add<float>, "
         "std::array<char*, 2ul> >(int)") == "copy"
+
+
+def test_counter_summary_derives_ratios(tmp_path):
+    # 2 XCDs of 1000 active cycles each, 4 SIMDs: 1000 SIMD-cycles per SIMD
+    c = {"GRBM_GUI_ACTIVE": 2000.0, "SQ_VALU_MFMA_BUSY_CYCLES": 1000.0, "SQ_WAVE_CYCLES": 400.0,
+         "SQ_WAIT_INST_ANY": 100.0, "SQ_LDS_IDX_ACTIVE": 50.0, "SQ_LDS_BANK_CONFLICT": 5.0,
+         "SQ_INSTS_VALU_MFMA_MOPS_BF16": 3.0, "SQ_INSTS_VALU_MFMA_MOPS_F16": 1.0}
+    d = profiling.derived_counters(c, xcds=2, simds=4)
+    vals = {k.split(" = ")[0]: v for k, v in d.items()}
+    assert vals["mfma_busy"] == 0.25
+    assert d["SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES"] == 0.25
+    assert d["SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE"] == 0.1
+    assert vals["mfma_flops"] == 4 * 512
+    out = tmp_path / "sq.txt"
+    res = profiling.write_counter_summary(str(out), [{"tree_attn_kernel": c}], ["tree_attn_kernel"],
+                                          2, 4, "x ;; y")
+    text = out.read_text()
+    assert "[tree_attn_kernel]" in text and "#   x" in text and "#   y" in text
+    assert res["tree_attn_kernel"]["SQ_WAVE_CYCLES"] == 400.0

@@ -10,6 +10,12 @@ different source treats the figure as stale.
     python -m tree_attention_verification_ancestor_amd.profiling \\
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \\
         --copy-bytes N --out profiles/FILE.txt --command "..."
+    python -m tree_attention_verification_ancestor_amd.profiling \\
+        --counters DIR [DIR ...] --out profiles/FILE.txt --command "..."
+
+The second form writes per-kernel counter means over several counter passes
+(each pass within the hardware's per-block counter limits) and the ratios
+derived from them.
 """
 
 from __future__ import annotations
@@ -49,7 +55,7 @@ def counter_means(run_dir: str) -> dict:
 
 
 def short_name(kernel: str) -> str:
-    for k in ATTN_KERNELS:
+    for k in ATTN_KERNELS + ("spec_verify_kernel",):
         if k in kernel:
             return k
     if "FunctorOnSelf_add" in kernel:     # torch.add(src, 0, out=dst): the calibration copy
@@ -110,16 +116,76 @@ def current_traffic(path: str):
     return int(float(rec["traffic_bytes_per_launch"]))
 
 
+MOPS_FLOPS = 512   # FLOPs per unit of the SQ_INSTS_VALU_MFMA_MOPS_* counters
+
+
+def derived_counters(c: dict, xcds: int, simds: int) -> dict:
+    """Ratios from one kernel's counter means (each formula is in its key):
+    the MFMA pipes' busy share of SIMD-cycles (GRBM_GUI_ACTIVE is summed over
+    the XCDs), wave-cycles spent waiting, LDS bank conflicts per LDS-active
+    cycle, and the MFMA FLOPs the op counters imply."""
+    d = {}
+    gui = c.get("GRBM_GUI_ACTIVE")
+    if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+        d["mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / xcds * simds)"] = \
+            c["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui / xcds * simds)
+    if c.get("SQ_WAVE_CYCLES"):
+        for k in ("SQ_WAIT_INST_ANY", "SQ_WAIT_ANY"):
+            if k in c:
+                d[f"{k} / SQ_WAVE_CYCLES"] = c[k] / c["SQ_WAVE_CYCLES"]
+    if c.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in c:
+        d["SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE"] = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]
+    mops = sum(v for k, v in c.items() if k.startswith("SQ_INSTS_VALU_MFMA_MOPS_"))
+    if mops:
+        d[f"mfma_flops = sum(SQ_INSTS_VALU_MFMA_MOPS_*) * {MOPS_FLOPS}"] = mops * MOPS_FLOPS
+    return d
+
+
+def write_counter_summary(out: str, runs: list, kernels: list, xcds: int, simds: int,
+                          command: str) -> dict:
+    """Per-kernel counter means (per dispatch) over several counter passes,
+    with the derived ratios; returns {kernel: {name: value}}."""
+    merged = defaultdict(dict)
+    for run in runs:
+        for k, cs in run.items():
+            merged[k].update(cs)
+    lines = ["# rocprofv3 counter means per dispatch, by kernel, with derived ratios",
+             "# commands (from the repository root):"] + [f"#   {c}" for c in command.split(" ;; ")] + [
+             f"kernel_source_sha256 = {source_sha256()}", f"xcds = {xcds}", f"simds = {simds}"]
+    result = {}
+    for k in kernels:
+        if k not in merged:
+            continue
+        c = dict(sorted(merged[k].items()))
+        c.update(derived_counters(merged[k], xcds, simds))
+        result[k] = c
+        lines.append(f"[{k}]")
+        lines += [f"{n} = {v:.6g}" for n, v in c.items()]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return result
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
-    ap.add_argument("--copy-fetch", required=True)
-    ap.add_argument("--copy-write", required=True)
-    ap.add_argument("--copy-bytes", type=int, required=True)
     ap.add_argument("--out", required=True)
     ap.add_argument("--command", required=True, help="the commands that made the runs, ' ;; '-separated")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--copy-fetch")
+    ap.add_argument("--copy-write")
+    ap.add_argument("--copy-bytes", type=int)
+    ap.add_argument("--counters", nargs="+", help="counter-pass directories: write a counter summary")
+    ap.add_argument("--kernels", nargs="+", default=list(ATTN_KERNELS) + ["spec_verify_kernel"])
+    ap.add_argument("--xcds", type=int, default=8)
+    ap.add_argument("--simds", type=int, default=1024)
     a = ap.parse_args()
+    if a.counters:
+        print(write_counter_summary(a.out, [counter_means(d) for d in a.counters], a.kernels, a.xcds,
+                                    a.simds, a.command))
+        return
+    if not (a.fetch and a.write and a.copy_fetch and a.copy_write and a.copy_bytes):
+        ap.error("the traffic record needs --fetch, --write, --copy-fetch, --copy-write, --copy-bytes")
     rec = write_record(a.out, counter_means(a.fetch), counter_means(a.write), counter_means(a.copy_fetch),
                        counter_means(a.copy_write), a.copy_bytes, a.command)
     print(rec)
