@@ -195,6 +195,27 @@ def run_gpu(args, w):
     return out
 
 
+def measured_copy_gbs(reps=5):
+    """HBM rate of a plain 1 GiB device copy (read + write), timed with
+    events: the streaming rate this machine reaches, beside the 8 TB/s figure."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.add(src, 0.0, out=dst)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.add(src, 0.0, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * COPY_BYTES / sec / 1e9
+
+
 def copy_calibration(reps=5):
     """A plain device copy of COPY_BYTES (read and written once each), for
     scaling the HBM counters of the attention launch."""
@@ -254,6 +275,7 @@ def main():
     from tree_attention_verification_ancestor_amd.profiling import current_traffic
     w = make_workload(args.config)
     g = run_gpu(args, w)
+    copy_gbs = measured_copy_gbs()
 
     attn_bytes, attn_flops = attention_work(w, g["depth"])
     t_attn = g["ms_attn"] * 1e-3
@@ -316,6 +338,8 @@ def main():
         "step_us_pctl": pct(g["step_all"]),
         "tree_attn": {"us": round(t_attn * 1e6, 2),
                       "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                      "measured_copy_gbs": round(copy_gbs, 1),
+                      "hbm_frac_of_copy": round(gbs / copy_gbs, 4),
                       "tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
                       "algorithmic_bytes": attn_bytes, "algorithmic_flops": attn_flops,
                       "roofline_frac": round(max(t_hbm, t_mfma) / t_attn, 4)},
