@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import dataclasses
 import heapq
+import os
 from typing import Optional, Sequence
 
 import numpy as np
@@ -218,6 +219,24 @@ class Workload:
         return float(1.0 / np.sqrt(self.D))
 
 
+SWEEP_SIGMA = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                           "tests", "golden", "sweep_sigma.txt")
+
+
+def sweep_sigma(accept: float) -> float:
+    """Draft-noise sigma of the sweep workloads for a mean acceptance, read
+    from the table that tests/golden/sweep_sigma.py computed with the
+    oracle's softmax (this module computes no softmax)."""
+    with open(SWEEP_SIGMA) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            a, s, _ = line.split()
+            if abs(float(a) - accept) < 1e-9:
+                return float(s)
+    raise ValueError(f"no sweep sigma for acceptance {accept}")
+
+
 # Named presets. Seeds are the preset's position in this table.
 CONFIGS = {
     # 5-node worked-example tree, one head, head_dim 64, 128-token prefix.
@@ -229,11 +248,12 @@ CONFIGS = {
     # Llama-3-70B-shaped layer, batch 8, prefixes 6144..8192, depth 6 width <= 4.
     "llama70b": dict(seed=2, B=8, N=64, Hq=64, Hkv=8, D=128, V=128256, L=(6144, 8192),
                      sigma_t=3.0, sigma_d=1.0, tree="best_first", widths=(4,) * 6),
-    # Batch-sweep shapes: 16-node tree (depth 4, width <= 3) and a gamma=5 chain.
+    # Batch-sweep shapes: 16-node tree (depth 4, width <= 3) and a gamma=5 chain;
+    # the draft noise is set by the mean acceptance (0.5, 0.8 or 0.9).
     "sweep_tree16": dict(seed=3, B=1, N=16, Hq=32, Hkv=8, D=128, V=128256, L=(2048, 2048),
-                         sigma_t=3.0, sigma_d=1.0, tree="best_first", widths=(3, 3, 3, 3)),
+                         sigma_t=3.0, accept=0.8, tree="best_first", widths=(3, 3, 3, 3)),
     "sweep_chain6": dict(seed=3, B=1, N=6, Hq=32, Hkv=8, D=128, V=128256, L=(2048, 2048),
-                         sigma_t=3.0, sigma_d=1.0, tree="chain"),
+                         sigma_t=3.0, accept=0.8, tree="chain"),
     # Long context: 70B-shaped layer, 32K paged prefix, 128-node depth-8 tree.
     "long": dict(seed=4, B=4, N=128, Hq=64, Hkv=8, D=128, V=151936, L=(32768, 32768),
                  sigma_t=3.0, sigma_d=0.7, tree="best_first", widths=(4,) * 8),
@@ -246,10 +266,13 @@ def make_workload(name: str, *, seed: Optional[int] = None, with_logits: bool = 
 
     Overrides: B, N, Hq, Hkv, D, V, L=(lo, hi) inclusive prefix-length range,
     sigma_t, sigma_d, tree ('example' | 'chain' | 'random' | 'best_first'),
-    widths, temperature, philox_seed, philox_offset.
+    widths, temperature, philox_seed, philox_offset, accept (the sweep
+    presets' mean acceptance, which sets sigma_d).
     """
     cfg = dict(CONFIGS[name])
     cfg.update(over)
+    if cfg.get("accept") is not None and "sigma_d" not in over:
+        cfg["sigma_d"] = sweep_sigma(float(cfg["accept"]))
     seed = cfg["seed"] if seed is None else seed
     rng = np.random.default_rng(seed)
     B, N, Hq, Hkv, D, V = (int(cfg[k]) for k in ("B", "N", "Hq", "Hkv", "D", "V"))

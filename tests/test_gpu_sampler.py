@@ -47,6 +47,8 @@ def test_target_probs_match_oracle(V, T):
     ("llama8b", {}),
     ("llama70b", {}),
     ("long", {}),
+    ("sweep_tree16", dict(B=16, accept=0.5)),
+    ("sweep_chain6", dict(B=64, accept=0.8)),
 ])
 def test_walk_matches_oracle(name, over):
     say(f"sampler: walk {name} {over}")

@@ -39,6 +39,9 @@ def _step(w, d, dev):
     ("tiny", dict(N=40, B=5, Hq=8, Hkv=2, D=128, L=(10, 400), V=5000, tree="random", seed=1), None),
     ("llama8b", {}, None),
     ("llama70b", {}, ([2, 6], [1, 5])),
+    # the batch sweep at its largest batch, tree and chain
+    ("sweep_tree16", dict(B=128), ([0, 63, 127], [0, 5])),
+    ("sweep_chain6", dict(B=128, accept=0.9), ([1, 126], [7])),
 ])
 def test_step_matches_oracle(name, over, sample):
     say(f"step: {name} {over}")
