@@ -694,7 +694,36 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 failed = true;
                 break;
             }
-            // p and q of this chunk in registers, rebased from the wave's max
+            // ---- 2./3. children in ascending order against the running residual
+            // Child c, tried after k rejections at u: its token's p under the
+            // residual after those k rejections, against r * q.
+            auto accepts = [&](int c, int k) __attribute__((always_inline)) {
+                const double qx = s_qx[c];
+                double prx = s_px[c];
+                for (int j = 0; j < k; ++j) {
+                    const double zj = s_zhist[j];
+                    if (zj > 0.0) {
+                        const double d = prx - qx;
+                        prx = (d > 0.0 ? d : 0.0) / zj;
+                    }
+                }
+                return s_uacc[c] * qx < prx;
+            };
+            auto accept = [&](int c) __attribute__((always_inline)) {
+                if (lead) {
+                    a.out_tok[rowbase + nacc] = s_tok[c];
+                    a.path[rowbase + nacc + 1] = c;
+                }
+                ++nacc;
+                u = c;
+            };
+            int c = s_first[u];
+            if (c >= 0 && accepts(c, 0)) {
+                accept(c);
+                continue;   // the first child needs only the normalisers
+            }
+            // A rejection or the final draw follows: p and q of this chunk in
+            // registers, rebased from the wave's max.
             {
                 const double sp = (wmt == -INFINITY) ? 0.0 : exp_bulk(wts - Mp) * (1.0 / Zp);
                 const double sq = (wmq == -INFINITY) ? 0.0 : exp_bulk(wqs - Mq) * (1.0 / Zq);
@@ -704,32 +733,9 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     qv[e] *= sq;
                 }
             }
-
-            // ---- 2./3. children in ascending order against the running residual
             int k = 0;
             bool accepted = false;
-            for (int c = s_first[u]; c >= 0; c = s_next[c]) {
-                const int x = s_tok[c];
-                const double px = s_px[c];
-                const double qx = s_qx[c];
-                double prx = px;
-                for (int j = 0; j < k; ++j) {
-                    const double zj = s_zhist[j];
-                    if (zj > 0.0) {
-                        const double d = prx - qx;
-                        prx = (d > 0.0 ? d : 0.0) / zj;
-                    }
-                }
-                if (s_uacc[c] * qx < prx) {
-                    if (lead) {
-                        a.out_tok[rowbase + nacc] = x;
-                        a.path[rowbase + nacc + 1] = c;
-                    }
-                    ++nacc;
-                    u = c;
-                    accepted = true;
-                    break;
-                }
+            while (c >= 0) {
                 // rejected: the chunk's residual mass, per wave, then in wave
                 // 0 exchanged with the group and summed in member order
                 double rsum = 0.0;
@@ -783,6 +789,12 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     }
                 }
                 ++k;
+                c = s_next[c];
+                if (c >= 0 && accepts(c, k)) {
+                    accept(c);
+                    accepted = true;
+                    break;
+                }
             }
             if (!alive)
                 break;
