@@ -20,6 +20,6 @@ Functions pinned only by properties that the pages do not fix are marked
 from .mask import tree_mask, ancestor_matrix  # noqa: F401
 from .attention import tree_attention, bf16_bits_to_f64  # noqa: F401
 from .sampling import (softmax, philox4x64_10, node_uniforms,  # noqa: F401
-                       verify_walk, WalkResult)
+                       verify_walk, verify_greedy, WalkResult)
 from .commit import kv_commit  # noqa: F401
 from .step import verify_step_ref  # noqa: F401

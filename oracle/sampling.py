@@ -124,3 +124,52 @@ def verify_walk(target_logits, draft_logits, parent, token, temperature: float =
     if rc:
         raise ValueError(f"oracle walk: {_ERRORS.get(rc, rc)} (sequence {int(bad[0])})")
     return WalkResult(path, n_acc, out_tok, draws, near, first_near, min_margin)
+
+
+def verify_greedy(target_logits, parent, token) -> WalkResult:
+    """Greedy (temperature 0) verification of a batch of trees.
+
+    LLM Primer VI ch. 9, section 9.1: the longest prefix of candidates that
+    matches the target's own choice is accepted, and at the first mismatch
+    the engine commits to the target's choice. Read on a tree, root-down
+    (jisaku.com glossary, SpecInfer paragraph): at node u the target's choice
+    is the argmax of target row u (the lowest token id among equal maxima);
+    the first child of u, in ascending node index, whose token is that choice
+    is accepted and the walk moves there; if none is, the choice is emitted
+    and the walk stops. At a leaf the choice is the bonus token. Every step
+    emits accepted + 1 tokens; no uniform is drawn.
+
+    target_logits float32 [B, N, V]; parent, token int [B, N]. Raises
+    ValueError on an invalid tree or token, or on a visited row whose
+    maximum is not finite or that holds a NaN.
+    """
+    tl = np.asarray(target_logits, dtype=np.float32)
+    par = np.asarray(parent)
+    tok = np.asarray(token)
+    B, N, V = tl.shape
+    path = np.full((B, N), -1, np.int32)
+    n_acc = np.zeros(B, np.int32)
+    out_tok = np.full((B, N), -1, np.int32)
+    for b in range(B):
+        if par[b, 0] != -1 or any(not (0 <= par[b, i] < i) for i in range(1, N)):
+            raise ValueError(f"oracle greedy: bad parent array (sequence {b})")
+        if any(not (0 <= tok[b, i] < V) for i in range(1, N)):
+            raise ValueError(f"oracle greedy: token out of range (sequence {b})")
+        u, m = 0, 0
+        path[b, 0] = 0
+        while True:
+            row = tl[b, u]
+            if np.isnan(row).any() or not np.isfinite(row.max()):
+                raise ValueError(f"oracle greedy: non-finite logits (sequence {b})")
+            x = int(np.argmax(row))            # first index of the maximum
+            out_tok[b, m] = x
+            hit = next((c for c in range(1, N) if par[b, c] == u and tok[b, c] == x), None)
+            if hit is None:
+                break
+            m += 1
+            path[b, m] = hit
+            u = hit
+        n_acc[b] = m
+    zeros = np.zeros(B, np.int32)
+    return WalkResult(path, n_acc, out_tok, zeros, zeros.copy(), np.full(B, -1, np.int32),
+                      np.full(B, np.inf))
