@@ -178,6 +178,25 @@ def run_gpu(args, w):
     out = dict(ms_step=ms_step, ms_attn=ms_attn, stage_ms=stage_ms, stage_all=stage,
                step_all=step_ms, depth=to_numpy(depth), path=to_numpy(path), n_acc=to_numpy(n_acc))
 
+    # greedy verification (temperature 0) of the same batch, timed on its own
+    # with events on the launch stream
+    g_path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    g_nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+    g_toks = torch.empty((B, N), dtype=torch.int32, device=dev)
+    greedy = tav.prepare("spec_verify_sample", d["target_logits"], None, d["parent"], d["token"],
+                         B, N, V, 0.0, 0, 0, g_path, g_nacc, g_toks, ws_s, ws_s_n, flags, stream)
+    for _ in range(args.warmup):
+        greedy()
+    g_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e in g_evs:
+        e[0].record(stream)
+        greedy()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    out["greedy_ms"] = np.array([e[0].elapsed_time(e[1]) for e in g_evs])
+    out["greedy_nacc"] = to_numpy(g_nacc)
+
     # acceptance over many Philox offsets (outside the timed regions): the
     # mean accepted length and the rows the walk visits, for the byte count
     n_off = max(0, args.offsets)
@@ -347,6 +366,8 @@ def main():
                           "frac": round(t_floor / (ms * 1e-3), 4)},
         "accepted": g["n_acc"].tolist(),
         "acceptance": acceptance,
+        "greedy": {"spec_verify_sample_us": pct(g["greedy_ms"]),
+                   "accepted": g["greedy_nacc"].tolist()},
     }
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w)

@@ -161,10 +161,19 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t N, int32_t V);
  * gives r_acc(b,i), word 1 gives r_res(b,i), as (w >> 40) * 2^-24.
  * All softmax, residual and CDF arithmetic is float64.
  *
+ * temperature == 0 selects greedy verification (LLM Primer ch. 9, §9.1: the
+ * longest prefix matching the target's own choice is accepted, then the
+ * target's choice is committed): at u the choice x* is the argmax of
+ * target_logits[b][u], the lowest token among equal maxima; the first child
+ * (ascending node index) whose token is x* is accepted and becomes u; if
+ * none is, x* is emitted and the walk stops (at a leaf, x* is the bonus).
+ * No draft row and no uniform is read; draft_logits may be NULL.
+ *
  *   target_logits, draft_logits  fp32 [B][N][V]; draft row u is the
  *                                distribution u's children were drawn from
  *   parent, token                int32 [B][N]; token[b][0] is ignored
- *   temperature                  > 0 and finite (float64, used as given)
+ *   temperature                  >= 0 and finite (float64, used as given);
+ *                                0 is greedy verification
  *   path        int32 [B][N] out: accepted nodes from the root (path[b][0] = 0), -1 padded
  *   n_accepted  int32 [B] out: accepted children (path length - 1)
  *   out_tokens  int32 [B][N] out: emitted tokens, n_accepted[b] + 1 of them, -1 padded

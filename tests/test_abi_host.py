@@ -74,8 +74,10 @@ def _sample(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(tl=None), tav.ERR_ARG), (dict(path=None), tav.ERR_ARG), (dict(B=0), tav.ERR_ARG),
-    (dict(V=0), tav.ERR_ARG), (dict(T=0.0), tav.ERR_ARG), (dict(T=-1.0), tav.ERR_ARG),
+    (dict(V=0), tav.ERR_ARG), (dict(T=float("nan")), tav.ERR_ARG), (dict(T=-1.0), tav.ERR_ARG),
     (dict(T=float("inf")), tav.ERR_ARG), (dict(N=257), tav.ERR_UNSUPPORTED),
+    # the draft rows are required unless the temperature is 0 (greedy)
+    (dict(dl=None), tav.ERR_ARG), (dict(dl=None, T=0.0, tl=None), tav.ERR_ARG),
     (dict(V=(1 << 21) + 1), tav.ERR_UNSUPPORTED),
 ])
 def test_sampler_rejects_bad_arguments(kw, code):

@@ -248,11 +248,13 @@ def new_sampler_workspace(B, N, V, device=None) -> torch.Tensor:
 def spec_verify_sample(target_logits, draft_logits, parent, token, temperature: float = 1.0,
                        seed: int = 0, offset: int = 0, path=None, n_accepted=None,
                        out_tokens=None, workspace=None, dev_flags=None, stream=None):
-    """Rejection-sampling walk; returns (path [B,N], n_accepted [B], out_tokens [B,N])."""
+    """Rejection-sampling walk, or greedy verification at temperature 0 (then
+    draft_logits may be None); returns (path [B,N], n_accepted [B], out_tokens [B,N])."""
     _need(target_logits, "target_logits", (torch.float32,))
     B, N, V = target_logits.shape
     dev = target_logits.device
-    _need(draft_logits, "draft_logits", (torch.float32,), (B, N, V), dev)
+    if draft_logits is not None or temperature != 0:
+        _need(draft_logits, "draft_logits", (torch.float32,), (B, N, V), dev)
     _need(parent, "parent", _I32T, (B, N), dev)
     _need(token, "token", _I32T, (B, N), dev)
     if path is None:

@@ -958,6 +958,311 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Greedy verification (temperature 0). The target's choice at a node is the
+// argmax of its target row, the lowest token id among equal maxima; the first
+// child (ascending node index) carrying it is accepted, otherwise the choice
+// is emitted and the walk stops (LLM Primer ch. 9, §9.1: the longest prefix
+// matching the target's own choice, then the target's choice). No draft row
+// and no uniform is read.
+//
+// Same group layout as spec_verify_kernel: workgroup r of a group owns
+// vocabulary entries [r*chunk, (r+1)*chunk) of the node's target row. Each
+// thread reduces its entries to a 64-bit key, the value's order-preserving
+// bits above the complement of the token id, so the largest key is the
+// largest value at its lowest token; waves reduce keys with DPP, wave 0
+// merges the waves' keys and exchanges its workgroup's key (and a NaN flag)
+// through the mailbox, and every workgroup takes the largest key of the
+// group, so all hold the same choice. The first child's row is fetched
+// while the current node is decided.
+
+// Order-preserving map of a float that is not NaN to 32 bits (-0 as +0).
+__device__ __forceinline__ uint32_t ordered_bits(float v)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, v == 0.0f ? 0.0f : v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float from_ordered_bits(uint32_t o)
+{
+    return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF,
+                                                              false);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int lane)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// The largest key of the wave, in every lane (0 is the identity).
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v)
+{
+    v = max_u64(v, dpp_u64<kQuadSwap1>(v));
+    v = max_u64(v, dpp_u64<kQuadSwap2>(v));
+    v = max_u64(v, dpp_u64<kRowHalfMirror>(v));
+    v = max_u64(v, dpp_u64<kRowMirror>(v));
+    return max_u64(max_u64(lane_u64(v, 0), lane_u64(v, 16)), max_u64(lane_u64(v, 32), lane_u64(v, 48)));
+}
+
+__global__ __launch_bounds__(kSvThreads) void spec_verify_greedy_kernel(SvArgs a)
+{
+    __shared__ int32_t s_par[kMaxNodes];
+    __shared__ int32_t s_first[kMaxNodes];
+    __shared__ int32_t s_next[kMaxNodes];
+    __shared__ int32_t s_tok[kMaxNodes];
+    constexpr int kKidWords = kMaxNodes / 64;
+    __shared__ unsigned long long s_kids[kMaxNodes][kKidWords];   // children of each node, as bits
+    __shared__ uint64_t s_key[kSvWaves];
+    __shared__ uint32_t s_words[kMaxWpg][kSlotWords];   // the group's payloads, as wave 0 received them
+    __shared__ int s_wnan[kSvWaves];   // a wave saw a NaN logit
+    __shared__ uint64_t s_choice;      // the group's largest key
+    __shared__ int s_gnan;             // a NaN anywhere in the row
+    __shared__ int s_sync_ok;
+    __shared__ int s_bad;
+    __shared__ int s_is_last;
+
+    const int g = blockIdx.x % a.ngroups;
+    const int rank = blockIdx.x / a.ngroups;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int N = a.N;
+    const int wpg = a.wpg;
+    const int64_t base = (int64_t)rank * a.chunk;
+    const int64_t lim = std::min<int64_t>((int64_t)a.V, base + a.chunk);
+    // entries of the chunk as in spec_verify_kernel: run h holds tokens
+    // base + h * 4 * 512 + 4 tid + j, j < 4
+    constexpr int kRun = 4 * kSvThreads;
+    auto load_row = [&](const float *row, float (&v)[kSvEpt]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < kSvEpt / 4; ++h) {
+            const int64_t i0 = base + (int64_t)h * kRun + 4 * tid;
+            if (a.vec4 && i0 + 3 < lim) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(row + i0);
+                v[4 * h] = x.x;
+                v[4 * h + 1] = x.y;
+                v[4 * h + 2] = x.z;
+                v[4 * h + 3] = x.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    v[4 * h + j] = i0 + j < lim ? row[i0 + j] : -INFINITY;
+            }
+        }
+    };
+    uint64_t *box = a.box + (size_t)g * 2 * wpg * kSlotWords;
+    uint32_t gen = 0;
+    bool alive = true;
+
+    for (int b = g; b < a.B && alive; b += a.ngroups) {
+        const int64_t rowbase = (int64_t)b * N;
+        // the root's row first: the walk starts there
+        int pf_node = 0;
+        float pf[kSvEpt];
+        load_row(a.tl + rowbase * a.V, pf);
+        // ---- tree structure in LDS, validated (children as bitmasks) --------
+        __syncthreads();
+        int my_par = -2, my_tok = 0;
+        if (tid == 0)
+            s_bad = 0;
+        if (tid < N) {
+            my_par = a.parent[rowbase + tid];
+            my_tok = a.token[rowbase + tid];
+            s_par[tid] = my_par;
+            s_tok[tid] = my_tok;
+#pragma unroll
+            for (int w = 0; w < kKidWords; ++w)
+                s_kids[tid][w] = 0ull;
+        }
+        __syncthreads();
+        if (tid < N) {
+            const bool bad_p = tid == 0 ? my_par != -1 : (my_par < 0 || my_par >= tid);
+            if (bad_p)
+                atomicOr(&s_bad, 1);
+            if (tid > 0 && (my_tok < 0 || my_tok >= a.V))
+                atomicOr(&s_bad, 2);
+            if (tid >= 1 && !bad_p)
+                atomicOr(&s_kids[my_par][tid >> 6], 1ull << (tid & 63));
+        }
+        __syncthreads();
+        if (tid < N) {
+            int first = -1, next = -1;
+#pragma unroll
+            for (int w = 0; w < kKidWords; ++w) {
+                const uint64_t m = s_kids[tid][w];
+                if (first < 0 && m != 0ull)
+                    first = 64 * w + __builtin_ctzll(m);
+            }
+            if (tid >= 1 && my_par >= 0 && my_par < tid) {
+#pragma unroll
+                for (int w = 0; w < kKidWords; ++w) {
+                    uint64_t m = w >= (tid >> 6) ? s_kids[my_par][w] : 0ull;
+                    if (w == (tid >> 6))
+                        m &= ~((2ull << (tid & 63)) - 1ull);   // siblings after tid
+                    if (next < 0 && m != 0ull)
+                        next = 64 * w + __builtin_ctzll(m);
+                }
+            }
+            s_first[tid] = first;
+            s_next[tid] = next;
+        }
+        __syncthreads();
+
+        const bool lead = rank == 0 && tid == 0;
+        int nacc = 0;
+        bool failed = s_bad != 0;
+        if (failed && lead)
+            raise_flag(a.flags, (s_bad & 1 ? TAV_FLAG_BAD_PARENT : 0u) |
+                                    (s_bad & 2 ? TAV_FLAG_BAD_TOKEN : 0u));
+
+        int u = 0;
+        while (!failed) {
+            float tf[kSvEpt];
+            if (pf_node == u) {
+#pragma unroll
+                for (int e = 0; e < kSvEpt; ++e)
+                    tf[e] = pf[e];
+            } else {
+                load_row(a.tl + (rowbase + u) * a.V, tf);
+            }
+            // this thread's key: its largest entry at its lowest token
+            bool nan_seen = false;
+            uint64_t key = 0;
+#pragma unroll
+            for (int e = 0; e < kSvEpt; ++e) {
+                nan_seen |= __builtin_isnan(tf[e]);
+                const int64_t t = base + (int64_t)(e >> 2) * kRun + 4 * tid + (e & 3);
+                const uint64_t k = __builtin_isnan(tf[e]) || t >= lim
+                                       ? 0ull
+                                       : ((uint64_t)ordered_bits(tf[e]) << 32) | (0xFFFFFFFFu - (uint32_t)t);
+                key = max_u64(key, k);
+            }
+            key = wave_max_key(key);
+            const bool wave_nan = __any(nan_seen);
+            if (lane == 0) {
+                s_key[wave] = key;
+                s_wnan[wave] = wave_nan;
+            }
+            // the first child's row, for the next level
+            const int c1 = s_first[u];
+            if (c1 >= 0) {
+                pf_node = c1;
+                load_row(a.tl + (rowbase + c1) * a.V, pf);
+            }
+            __syncthreads();   // s_key, s_wnan visible
+            if (wave == 0) {
+                const uint64_t wk = wave_max_key(lane < kSvWaves ? s_key[lane] : 0ull);
+                const bool wn = __any(lane < kSvWaves && s_wnan[lane] != 0);
+                const uint32_t mine3[3] = {(uint32_t)(wk >> 32), (uint32_t)wk, (uint32_t)wn};
+                uint32_t mine = 0;
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+                    if (lane == i)
+                        mine = mine3[i];
+                bool ok = true;
+                uint32_t w3[3] = {0, 0, 0};   // member `lane`'s payloads
+                if (wpg == 1) {
+#pragma unroll
+                    for (int i = 0; i < 3; ++i)
+                        w3[i] = mine3[i];
+                } else {
+                    ok = wave0_exchange<3>(box, wpg, rank, ++gen, mine, s_words, w3);
+                }
+                uint64_t gk = 0;
+                bool gnan = false;
+                for (int m = lane; m < wpg; m += 64) {
+                    const uint32_t hi = m == lane ? w3[0] : s_words[m][0];
+                    const uint32_t lo = m == lane ? w3[1] : s_words[m][1];
+                    const uint32_t nn = m == lane ? w3[2] : s_words[m][2];
+                    gk = max_u64(gk, ((uint64_t)hi << 32) | lo);
+                    gnan |= nn != 0;
+                }
+                gk = wave_max_key(gk);
+                gnan = __any(gnan);
+                if (lane == 0) {
+                    s_choice = gk;
+                    s_gnan = gnan;
+                    s_sync_ok = ok;
+                }
+            }
+            __syncthreads();   // s_choice, s_gnan, s_sync_ok visible
+            if (!s_sync_ok) {
+                if (tid == 0)
+                    raise_flag(a.flags, TAV_FLAG_SYNC_TIMEOUT);
+                alive = false;
+                break;
+            }
+            const uint64_t ck = s_choice;
+            const float cv = from_ordered_bits((uint32_t)(ck >> 32));
+            if (s_gnan || ck == 0ull || !__builtin_isfinite(cv)) {
+                if (lead)
+                    raise_flag(a.flags, TAV_FLAG_NONFINITE_LOGITS);
+                failed = true;
+                break;
+            }
+            const int x = (int)(0xFFFFFFFFu - (uint32_t)ck);
+            int c = s_first[u];
+            while (c >= 0 && s_tok[c] != x)
+                c = s_next[c];
+            if (lead)
+                a.out_tok[rowbase + nacc] = x;
+            if (c < 0)
+                break;   // the target's choice is emitted; the walk stops
+            if (lead)
+                a.path[rowbase + nacc + 1] = c;
+            ++nacc;
+            u = c;
+        }
+
+        // ---- outputs owned by the group's first workgroup ----------------------
+        if (failed || !alive) {
+            if (lead) {
+                for (int i = 0; i < N; ++i) {
+                    a.path[rowbase + i] = i == 0 ? 0 : -1;
+                    a.out_tok[rowbase + i] = -1;
+                }
+                a.n_acc[b] = 0;
+            }
+        } else if (rank == 0) {
+            for (int i = nacc + 1 + tid; i < N; i += kSvThreads) {
+                a.path[rowbase + i] = -1;
+                a.out_tok[rowbase + i] = -1;
+            }
+            if (lead) {
+                a.path[rowbase] = 0;
+                a.n_acc[b] = nacc;
+            }
+        }
+    }
+
+    // ---- exit: the last workgroup out clears every mailbox word -------------
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t out =
+            __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_is_last = out == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (s_is_last) {
+        const int64_t words = (int64_t)a.ngroups * 2 * wpg * kSlotWords;
+        for (int64_t i = tid; i < words; i += kSvThreads)
+            __hip_atomic_store(a.box + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0)
+            __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 struct SvPlan {
     int wpg, ngroups, chunk;
     size_t box_bytes;
@@ -968,10 +1273,16 @@ bool sv_plan(int32_t B, int32_t V, SvPlan &p)
     const int cus = device_cu_count();
     if (cus <= 0)
         return false;
-    int per_cu = 0;
+    // the grid must be resident at once for either kernel (the group syncs
+    // wait on each other), so the smaller of their occupancies counts
+    int per_cu = 0, per_cu_g = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, spec_verify_kernel, kSvThreads,
                                                      0) != hipSuccess ||
-        per_cu <= 0)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_g, spec_verify_greedy_kernel,
+                                                     kSvThreads, 0) != hipSuccess)
+        return false;
+    per_cu = std::min(per_cu, per_cu_g);
+    if (per_cu <= 0)
         return false;
     const int64_t resident = (int64_t)per_cu * cus;
     p.wpg = (int)ceil_div(V, kSvChunk);
@@ -1049,14 +1360,16 @@ extern "C" tav_status spec_verify_sample(const float *target_logits, const float
                                          uint32_t *dev_flags, void *stream)
 {
     using namespace tav;
-    if (!target_logits || !draft_logits || !parent || !token || !path || !n_accepted ||
-        !out_tokens)
+    // temperature 0 selects greedy verification, which reads no draft row
+    const bool greedy = temperature == 0.0;
+    if (!target_logits || (!draft_logits && !greedy) || !parent || !token || !path ||
+        !n_accepted || !out_tokens)
         return TAV_ERR_ARG;
-    if (B < 1 || N < 1 || V < 1 || !(temperature > 0.0) || !(temperature < INFINITY))
+    if (B < 1 || N < 1 || V < 1 || !(temperature >= 0.0) || !(temperature < INFINITY))
         return TAV_ERR_ARG;
     if (N > kMaxNodes || V > kMaxVocab)
         return TAV_ERR_UNSUPPORTED;
-    if (!aligned(target_logits, 4) || !aligned(draft_logits, 4))
+    if (!aligned(target_logits, 4) || (!greedy && !aligned(draft_logits, 4)))
         return TAV_ERR_ARG;
     SvPlan p;
     if (!sv_plan(B, V, p))
@@ -1085,9 +1398,13 @@ extern "C" tav_status spec_verify_sample(const float *target_logits, const float
     a.wpg = p.wpg;
     a.ngroups = p.ngroups;
     a.chunk = p.chunk;
-    a.vec4 = V % 4 == 0 && aligned(target_logits, 16) && aligned(draft_logits, 16);
-    hipLaunchKernelGGL(spec_verify_kernel, dim3(p.wpg * p.ngroups), dim3(kSvThreads), 0,
-                       as_stream(stream), a);
+    a.vec4 = V % 4 == 0 && aligned(target_logits, 16) && (greedy || aligned(draft_logits, 16));
+    if (greedy)
+        hipLaunchKernelGGL(spec_verify_greedy_kernel, dim3(p.wpg * p.ngroups), dim3(kSvThreads), 0,
+                           as_stream(stream), a);
+    else
+        hipLaunchKernelGGL(spec_verify_kernel, dim3(p.wpg * p.ngroups), dim3(kSvThreads), 0,
+                           as_stream(stream), a);
     return hipGetLastError() == hipSuccess ? TAV_OK : TAV_ERR_LAUNCH;
 }
 
