@@ -21,5 +21,5 @@ from .mask import tree_mask, ancestor_matrix  # noqa: F401
 from .attention import tree_attention, bf16_bits_to_f64  # noqa: F401
 from .sampling import (softmax, philox4x64_10, node_uniforms,  # noqa: F401
                        verify_walk, verify_greedy, WalkResult)
-from .commit import kv_commit  # noqa: F401
+from .commit import kv_commit, kv_commit_inplace  # noqa: F401
 from .step import verify_step_ref  # noqa: F401
