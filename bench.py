@@ -197,6 +197,23 @@ def run_gpu(args, w):
     out["greedy_ms"] = np.array([e[0].elapsed_time(e[1]) for e in g_evs])
     out["greedy_nacc"] = to_numpy(g_nacc)
 
+    # the zero-copy rollback on the same paths, timed on its own: it moves
+    # rows only inside each sequence's tree positions L..L+N-1, which the
+    # attention never reads
+    inplace = tav.prepare("kv_commit_inplace", path, n_acc, nblk, d["block_table"], maxb,
+                          d["prefix_len"], copies[0][0], copies[0][1], B, N, w.Hkv, w.D, w.block,
+                          slots, new_len, flags, stream)
+    for _ in range(args.warmup):
+        inplace()
+    i_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e in i_evs:
+        e[0].record(stream)
+        inplace()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    out["inplace_ms"] = np.array([e[0].elapsed_time(e[1]) for e in i_evs])
+
     # acceptance over many Philox offsets (outside the timed regions): the
     # mean accepted length and the rows the walk visits, for the byte count
     n_off = max(0, args.offsets)
@@ -368,6 +385,7 @@ def main():
         "acceptance": acceptance,
         "greedy": {"spec_verify_sample_us": pct(g["greedy_ms"]),
                    "accepted": g["greedy_nacc"].tolist()},
+        "kv_commit_inplace_us": pct(g["inplace_ms"]),
     }
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w)

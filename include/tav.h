@@ -6,6 +6,7 @@
  *   tree_attn_verify    tree attention over a paged KV prefix plus ancestors
  *   spec_verify_sample  target/draft softmax and the rejection-sampling walk
  *   kv_commit_path      copy the accepted path's K/V into the paged cache
+ *   kv_commit_inplace   the same when the tree's K/V already sit in the cache
  *
  * Conventions for every entry point:
  *   - Pointers are device pointers unless stated otherwise. All tensors are
@@ -221,6 +222,40 @@ tav_status kv_commit_path(const uint16_t *k_tree, const uint16_t *v_tree, const 
                           int32_t B, int32_t N, int32_t Hkv, int32_t D, int32_t block_size,
                           int32_t *commit_slots, int32_t *new_prefix_len, uint32_t *dev_flags,
                           void *stream);
+
+/*
+ * kv_commit_inplace — zero-copy rollback: the tree's K/V already sit in the
+ * cache, node i of sequence b at position prefix_len[b] + i (written there
+ * by the forward pass), and only the accepted path's rows that are out of
+ * place move.
+ *
+ * Engines branch and roll back the tree through paged block-table operations
+ * without copying: radar-34b blog §5 (KV-cache management); entries off the
+ * accepted path are pruned and the cache rolled back to the right position:
+ * jisaku.com glossary, KV-cache section.
+ *
+ * For t = 0..n_accepted[b], position prefix_len[b] + t receives what position
+ * prefix_len[b] + path[b][t] held (every such row is read before any is
+ * written, so overlapping moves are safe); rows with path[b][t] == t do not
+ * move. new_prefix_len[b] = prefix_len[b] + n_accepted[b] + 1; positions past
+ * it are abandoned (left as they are, not freed). commit_slots as in
+ * kv_commit_path. Nothing else in the caches is written.
+ *
+ *   path, n_accepted as written by spec_verify_sample (read on the device)
+ *   block_table      must map positions prefix_len[b] .. prefix_len[b] + N - 1
+ *   k_cache, v_cache the paged caches, updated in place
+ *   commit_slots     int32 [B][N] out;  new_prefix_len int32 [B] out
+ *   Supported: D in {64, 128}, block_size == 16, 1 <= N <= 256, B <= 65535.
+ *   Flags: TAV_FLAG_CAPACITY (table shorter than the tree: nothing moves),
+ *   TAV_FLAG_BAD_BLOCK, TAV_FLAG_BAD_PARENT (path entry outside [0, N) or
+ *   n_accepted outside [0, N)).
+ */
+tav_status kv_commit_inplace(const int32_t *path, const int32_t *n_accepted, int32_t num_blocks,
+                             const int32_t *block_table, int32_t max_blocks,
+                             const int32_t *prefix_len, uint16_t *k_cache, uint16_t *v_cache,
+                             int32_t B, int32_t N, int32_t Hkv, int32_t D, int32_t block_size,
+                             int32_t *commit_slots, int32_t *new_prefix_len, uint32_t *dev_flags,
+                             void *stream);
 
 /*
  * tav_philox_uniforms — the uniforms spec_verify_sample draws, for checking:

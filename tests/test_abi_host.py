@@ -102,6 +102,24 @@ def test_commit_rejects_bad_arguments(kw, code):
     assert _commit(**kw) == code
 
 
+def _inplace(**kw):
+    args = dict(path=FAKE, n_acc=FAKE, num_blocks=10, block_table=FAKE, max_blocks=4,
+                prefix_len=FAKE, k_cache=FAKE, v_cache=FAKE, B=1, N=5, Hkv=2, D=128,
+                block_size=16, slots=FAKE, new_len=FAKE, flags=None, stream=None)
+    args.update(kw)
+    return tav.lib().kv_commit_inplace(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(path=None), tav.ERR_ARG), (dict(v_cache=None), tav.ERR_ARG), (dict(B=0), tav.ERR_ARG),
+    (dict(max_blocks=0), tav.ERR_ARG), (dict(D=80), tav.ERR_UNSUPPORTED),
+    (dict(block_size=32), tav.ERR_UNSUPPORTED), (dict(N=257), tav.ERR_UNSUPPORTED),
+    (dict(B=70000), tav.ERR_UNSUPPORTED), (dict(k_cache=ctypes.c_void_p(0x10008)), tav.ERR_ARG),
+])
+def test_inplace_commit_rejects_bad_arguments(kw, code):
+    assert _inplace(**kw) == code
+
+
 def test_helpers_reject_bad_arguments():
     lib = tav.lib()
     assert lib.tav_philox_uniforms(0, 0, 1, 1, None, None) == tav.ERR_ARG

@@ -131,3 +131,105 @@ def test_commit_flags_short_table_without_writing_past_it():
     assert int(flags.item()) & tav.FLAG_CAPACITY
     assert (to_numpy(slots) == -1).all()
     assert torch.equal(before_k, d["k_cache"])
+
+
+def _scatter_tree(w):
+    """The tree's rows at positions L..L+N-1, written by the pinned oracle commit."""
+    ident = np.tile(np.arange(w.N, dtype=np.int32), (w.B, 1))
+    full = np.full(w.B, w.N - 1, np.int32)
+    k, v, _, _ = oracle.kv_commit(w.k_tree, w.v_tree, ident, full, w.block_table, w.prefix_len,
+                                  w.k_cache, w.v_cache)
+    return k, v
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(N=5, B=1, D=64, Hkv=1, L=(128, 128)),
+    dict(N=40, B=6, D=128, Hkv=8, L=(0, 50)),
+    dict(N=64, B=8, D=128, Hkv=8, L=(6144, 8192)),
+    dict(N=256, B=3, D=128, Hkv=4, L=(15, 17)),
+    dict(N=200, B=3, D=64, Hkv=2, L=(1, 300)),
+])
+def test_inplace_commit_matches_oracle(cfg):
+    say(f"commit in place: {cfg}")
+    w = make_workload("tiny", tree="random", with_logits=False, Hq=cfg["Hkv"], seed=cfg["N"] + 1,
+                      **cfg)
+    path, n_acc = _random_paths(w, np.random.default_rng(2))
+    k_c, v_c = _scatter_tree(w)
+    dev = device()
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    kc, vc = t(k_c.view(np.int16)), t(v_c.view(np.int16))
+    d = upload(w, dev, logits=False)
+    flags = tav.new_flags(dev)
+    slots, new_len = tav.kv_commit_inplace(t(path), t(n_acc), d["block_table"], d["prefix_len"],
+                                           kc, vc, dev_flags=flags)
+    torch.cuda.synchronize()
+    k2, v2, ref_slots, ref_len = oracle.kv_commit_inplace(path, n_acc, w.block_table,
+                                                          w.prefix_len, k_c, v_c)
+    assert int(flags.item()) == 0
+    np.testing.assert_array_equal(to_numpy(slots), ref_slots)
+    np.testing.assert_array_equal(to_numpy(new_len), ref_len)
+    np.testing.assert_array_equal(to_numpy(kc, np.uint16), k2)
+    np.testing.assert_array_equal(to_numpy(vc, np.uint16), v2)
+
+
+def test_inplace_commit_of_walk_paths_equals_the_copying_commit():
+    # the sampler's own paths on the 70B-shaped batch: rolling back in place
+    # leaves the accepted positions as the copying commit writes them
+    say("commit in place: sampler paths, 70B-shaped batch")
+    w = make_workload("llama70b")
+    dev = device()
+    d = upload(w, dev)
+    flags = tav.new_flags(dev)
+    path, n_acc, _ = tav.spec_verify_sample(d["target_logits"], d["draft_logits"], d["parent"],
+                                            d["token"], 1.0, 0, 0, dev_flags=flags)
+    k_c, v_c = _scatter_tree(w)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    kc, vc = t(k_c.view(np.int16)), t(v_c.view(np.int16))
+    s1, l1 = tav.kv_commit_inplace(path, n_acc, d["block_table"], d["prefix_len"], kc, vc,
+                                   dev_flags=flags)
+    s2, l2 = tav.kv_commit_path(d["k_tree"], d["v_tree"], path, n_acc, d["block_table"],
+                                d["prefix_len"], d["k_cache"], d["v_cache"], dev_flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    assert torch.equal(s1, s2) and torch.equal(l1, l2)
+    slots = to_numpy(s1)
+    kc_n, vc_n = to_numpy(kc, np.uint16), to_numpy(vc, np.uint16)
+    k2, v2 = to_numpy(d["k_cache"], np.uint16), to_numpy(d["v_cache"], np.uint16)
+    for b in range(w.B):
+        for tt in range(int(to_numpy(n_acc)[b]) + 1):
+            blk, s = divmod(int(slots[b, tt]), w.block)
+            np.testing.assert_array_equal(kc_n[blk, :, s, :], k2[blk, :, s, :])
+            np.testing.assert_array_equal(vc_n[blk, :, :, s], v2[blk, :, :, s])
+
+
+def test_inplace_commit_of_a_root_chain_moves_nothing_and_short_tables_flag():
+    say("commit in place: root chain, short table")
+    w = make_workload("tiny", N=12, L=(30, 90), B=4, tree="chain", with_logits=False, seed=7)
+    k_c, v_c = _scatter_tree(w)
+    dev = device()
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    n_acc = np.array([0, 3, 7, 11], np.int32)
+    path = np.full((w.B, w.N), -1, np.int32)
+    for b in range(w.B):
+        path[b, :n_acc[b] + 1] = np.arange(n_acc[b] + 1)
+    kc, vc = t(k_c.view(np.int16)), t(v_c.view(np.int16))
+    d = upload(w, dev, logits=False)
+    flags = tav.new_flags(dev)
+    tav.kv_commit_inplace(t(path), t(n_acc), d["block_table"], d["prefix_len"], kc, vc,
+                          dev_flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    np.testing.assert_array_equal(to_numpy(kc, np.uint16), k_c)
+    np.testing.assert_array_equal(to_numpy(vc, np.uint16), v_c)
+    # a table that cannot hold the tree: flagged, nothing moves
+    w2 = make_workload("tiny", N=5, L=(126, 126), with_logits=False, seed=0)
+    d2 = upload(w2, dev, logits=False)
+    table = d2["block_table"][:, :8].contiguous()
+    before = d2["k_cache"].clone()
+    flags = tav.new_flags(dev)
+    slots, _ = tav.kv_commit_inplace(t(np.array([[0, 2, -1, -1, -1]], np.int32)),
+                                     t(np.array([1], np.int32)), table, d2["prefix_len"],
+                                     d2["k_cache"], d2["v_cache"], dev_flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) & tav.FLAG_CAPACITY
+    assert (to_numpy(slots) == -1).all() and torch.equal(before, d2["k_cache"])

@@ -68,6 +68,8 @@ _SIGNATURES = {
                                   _P, _P, _SZ, _P, _P]),
     "kv_commit_path": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _P, _I32, _I32, _I32,
                               _I32, _I32, _P, _P, _P, _P]),
+    "kv_commit_inplace": (_I32, [_P, _P, _I32, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                 _P, _P, _P, _P]),
     "tav_philox_uniforms": (_I32, [_U64, _U64, _I32, _I32, _P, _P]),
     "tav_target_probs": (_I32, [_P, _I64, _I32, _F64, _P, _P, _P]),
 }
@@ -298,6 +300,33 @@ def kv_commit_path(k_tree, v_tree, path, n_accepted, block_table, prefix_len, k_
         _ptr(k_tree), _ptr(v_tree), _ptr(path), _ptr(n_accepted), nblk, _ptr(block_table),
         block_table.shape[1], _ptr(prefix_len), _ptr(k_cache), _ptr(v_cache), B, N, Hkv, D,
         BLOCK, _ptr(commit_slots), _ptr(new_prefix_len), _ptr(dev_flags), _stream(stream)))
+    return commit_slots, new_prefix_len
+
+
+def kv_commit_inplace(path, n_accepted, block_table, prefix_len, k_cache, v_cache,
+                      commit_slots=None, new_prefix_len=None, dev_flags=None, stream=None):
+    """Zero-copy rollback (the tree's rows already at positions L..L+N-1 of
+    the cache); returns (commit_slots [B,N], new_prefix_len [B])."""
+    _need(path, "path", _I32T)
+    B, N = path.shape
+    dev = path.device
+    _need(n_accepted, "n_accepted", _I32T, (B,), dev)
+    _need(block_table, "block_table", _I32T, None, dev)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    _need(prefix_len, "prefix_len", _I32T, (B,), dev)
+    _need(k_cache, "k_cache", _BF16, None, dev)
+    nblk, Hkv, _, D = k_cache.shape
+    _need(k_cache, "k_cache", _BF16, (nblk, Hkv, BLOCK, D), dev)
+    _need(v_cache, "v_cache", _BF16, (nblk, Hkv, D, BLOCK), dev)
+    if commit_slots is None:
+        commit_slots = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if new_prefix_len is None:
+        new_prefix_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check("kv_commit_inplace", lib().kv_commit_inplace(
+        _ptr(path), _ptr(n_accepted), nblk, _ptr(block_table), block_table.shape[1],
+        _ptr(prefix_len), _ptr(k_cache), _ptr(v_cache), B, N, Hkv, D, BLOCK,
+        _ptr(commit_slots), _ptr(new_prefix_len), _ptr(dev_flags), _stream(stream)))
     return commit_slots, new_prefix_len
 
 
