@@ -6,7 +6,8 @@ computes, in float64:
   * ``attention`` - tree attention over a paged prefix plus tree ancestors;
   * ``sampling``  - softmax of target/draft logits, Philox4x64-10 uniforms and
                     the root-down rejection-sampling walk (plain C, fp64);
-  * ``commit``    - the KV commit of the accepted path;
+  * ``commit``    - the KV commit of the accepted path (copying and in place);
+  * ``expand``    - top-k draft tokens, log-probabilities and entropy per row;
   * ``step``      - the four composed.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
@@ -22,4 +23,5 @@ from .attention import tree_attention, bf16_bits_to_f64  # noqa: F401
 from .sampling import (softmax, philox4x64_10, node_uniforms,  # noqa: F401
                        verify_walk, verify_greedy, WalkResult)
 from .commit import kv_commit, kv_commit_inplace  # noqa: F401
+from .expand import expand_topk  # noqa: F401
 from .step import verify_step_ref  # noqa: F401
