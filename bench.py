@@ -214,6 +214,29 @@ def run_gpu(args, w):
     torch.cuda.synchronize()
     out["inplace_ms"] = np.array([e[0].elapsed_time(e[1]) for e in i_evs])
 
+    # tree expansion over every node's draft row (top-4 tokens, log q,
+    # entropy): one read of B*N vocabulary rows
+    ex_rows = d["draft_logits"].view(B * N, V)
+    ex_k = 4
+    ex_tok = torch.empty((B * N, ex_k), dtype=torch.int32, device=dev)
+    ex_lq = torch.empty((B * N, ex_k), dtype=torch.float64, device=dev)
+    ex_ent = torch.empty((B * N,), dtype=torch.float64, device=dev)
+    ex_ws = torch.empty(tav.tree_expand_workspace_bytes(B * N, V, ex_k), dtype=torch.uint8,
+                        device=dev)
+    expand = tav.prepare("tree_expand_topk", ex_rows, B * N, V, ex_k, 1.0, ex_tok, ex_lq, ex_ent,
+                         ex_ws, ex_ws.numel(), flags, stream)
+    for _ in range(args.warmup):
+        expand()
+    x_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e in x_evs:
+        e[0].record(stream)
+        expand()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    out["expand_ms"] = np.array([e[0].elapsed_time(e[1]) for e in x_evs])
+    out["expand_rows"] = B * N
+
     # acceptance over many Philox offsets (outside the timed regions): the
     # mean accepted length and the rows the walk visits, for the byte count
     n_off = max(0, args.offsets)
@@ -386,6 +409,12 @@ def main():
         "greedy": {"spec_verify_sample_us": pct(g["greedy_ms"]),
                    "accepted": g["greedy_nacc"].tolist()},
         "kv_commit_inplace_us": pct(g["inplace_ms"]),
+        "tree_expand_topk": {"rows": g["expand_rows"], "k": 4, "us": pct(g["expand_ms"]),
+                             "hbm_gbs": round(g["expand_rows"] * w.V * 4
+                                              / (float(np.median(g["expand_ms"])) * 1e-3) / 1e9, 1),
+                             "hbm_frac": round(g["expand_rows"] * w.V * 4
+                                               / (float(np.median(g["expand_ms"])) * 1e-3)
+                                               / (HBM_PEAK_GBS * 1e9), 4)},
     }
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w)

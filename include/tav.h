@@ -7,6 +7,7 @@
  *   spec_verify_sample  target/draft softmax and the rejection-sampling walk
  *   kv_commit_path      copy the accepted path's K/V into the paged cache
  *   kv_commit_inplace   the same when the tree's K/V already sit in the cache
+ *   tree_expand_topk    top-k draft tokens, log q and entropy per frontier row
  *
  * Conventions for every entry point:
  *   - Pointers are device pointers unless stated otherwise. All tensors are
@@ -256,6 +257,42 @@ tav_status kv_commit_inplace(const int32_t *path, const int32_t *n_accepted, int
                              int32_t B, int32_t N, int32_t Hkv, int32_t D, int32_t block_size,
                              int32_t *commit_slots, int32_t *new_prefix_len, uint32_t *dev_flags,
                              void *stream);
+
+/*
+ * tree_expand_workspace_bytes — device workspace tree_expand_topk needs for
+ * R rows of V logits and k tokens per row. Returns 0 for unsupported sizes.
+ */
+size_t tree_expand_workspace_bytes(int64_t R, int32_t V, int32_t k);
+
+/*
+ * tree_expand_topk — what tree construction reads from each frontier node's
+ * draft row: its k most likely tokens with their log-probabilities, and the
+ * entropy of the draft distribution. Top-k branching expands a node by its
+ * draft's k most likely tokens; entropy-based branching gives a node more
+ * branches the higher its entropy (jisaku.com glossary, tree-topology
+ * strategies).
+ *
+ * For row r, q = softmax(draft_logits[r] / T):
+ *   top_token[r][i]  the i-th most likely token (i < k), the lower token
+ *                    first among equal logits;
+ *   top_logq[r][i]   log q of that token (fp64);
+ *   entropy[r]       -sum q log q over tokens with q > 0 (fp64).
+ * Each token's exponential is taken in fp32 and the sums in fp64, so log q
+ * and the entropy are within about 1e-6 of exact arithmetic; the token
+ * ranking compares the fp32 logits themselves and is exact.
+ *
+ *   draft_logits  fp32 [R][V], 4-byte aligned
+ *   k             1 <= k <= min(16, V);  temperature > 0 and finite
+ *   workspace     device buffer of >= tree_expand_workspace_bytes(R, V, k)
+ *                 bytes, 16-byte aligned (no initial contents needed)
+ *   Supported: V <= 2^21.
+ *   Flags: TAV_FLAG_NONFINITE_LOGITS for a row with a NaN or a maximum that
+ *   is not finite (its tokens are -1, its log q and entropy NaN).
+ */
+tav_status tree_expand_topk(const float *draft_logits, int64_t R, int32_t V, int32_t k,
+                            double temperature, int32_t *top_token, double *top_logq,
+                            double *entropy, void *workspace, size_t ws_bytes,
+                            uint32_t *dev_flags, void *stream);
 
 /*
  * tav_philox_uniforms — the uniforms spec_verify_sample draws, for checking:

@@ -120,6 +120,30 @@ def test_inplace_commit_rejects_bad_arguments(kw, code):
     assert _inplace(**kw) == code
 
 
+def _expand(**kw):
+    args = dict(x=FAKE, R=4, V=1000, k=4, T=1.0, tok=FAKE, logq=FAKE, ent=FAKE, ws=FAKE,
+                ws_bytes=1 << 20, flags=None, stream=None)
+    args.update(kw)
+    return tav.lib().tree_expand_topk(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), tav.ERR_ARG), (dict(ent=None), tav.ERR_ARG), (dict(R=0), tav.ERR_ARG),
+    (dict(k=0), tav.ERR_ARG), (dict(k=1001), tav.ERR_ARG), (dict(T=0.0), tav.ERR_ARG),
+    (dict(k=17, V=5000), tav.ERR_UNSUPPORTED), (dict(V=(1 << 21) + 1), tav.ERR_UNSUPPORTED),
+    (dict(ws=None), tav.ERR_WORKSPACE), (dict(ws_bytes=10), tav.ERR_WORKSPACE),
+])
+def test_expand_rejects_bad_arguments(kw, code):
+    assert _expand(**kw) == code
+
+
+def test_expand_workspace_sizes():
+    lib = tav.lib()
+    assert lib.tree_expand_workspace_bytes(0, 100, 4) == 0
+    assert lib.tree_expand_workspace_bytes(3, 100, 17) == 0
+    assert lib.tree_expand_workspace_bytes(3, 16384, 4) < lib.tree_expand_workspace_bytes(3, 16385, 4)
+
+
 def test_helpers_reject_bad_arguments():
     lib = tav.lib()
     assert lib.tav_philox_uniforms(0, 0, 1, 1, None, None) == tav.ERR_ARG

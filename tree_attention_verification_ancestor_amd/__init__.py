@@ -70,6 +70,8 @@ _SIGNATURES = {
                               _I32, _I32, _P, _P, _P, _P]),
     "kv_commit_inplace": (_I32, [_P, _P, _I32, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                  _P, _P, _P, _P]),
+    "tree_expand_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
+    "tree_expand_topk": (_I32, [_P, _I64, _I32, _I32, _F64, _P, _P, _P, _P, _SZ, _P, _P]),
     "tav_philox_uniforms": (_I32, [_U64, _U64, _I32, _I32, _P, _P]),
     "tav_target_probs": (_I32, [_P, _I64, _I32, _F64, _P, _P, _P]),
 }
@@ -328,6 +330,39 @@ def kv_commit_inplace(path, n_accepted, block_table, prefix_len, k_cache, v_cach
         _ptr(prefix_len), _ptr(k_cache), _ptr(v_cache), B, N, Hkv, D, BLOCK,
         _ptr(commit_slots), _ptr(new_prefix_len), _ptr(dev_flags), _stream(stream)))
     return commit_slots, new_prefix_len
+
+
+def tree_expand_workspace_bytes(R: int, V: int, k: int) -> int:
+    return int(lib().tree_expand_workspace_bytes(R, V, k))
+
+
+def tree_expand_topk(draft_logits, k: int, temperature: float = 1.0, top_token=None,
+                     top_logq=None, entropy=None, workspace=None, dev_flags=None, stream=None):
+    """Top-k draft tokens, their log q and the entropy of every row of
+    draft_logits fp32 [R, V]; returns (top_token int32 [R, k], top_logq
+    float64 [R, k], entropy float64 [R])."""
+    _need(draft_logits, "draft_logits", (torch.float32,))
+    if draft_logits.dim() != 2:
+        raise ValueError("draft_logits must be [R, V]")
+    R, V = draft_logits.shape
+    dev = draft_logits.device
+    if top_token is None:
+        top_token = torch.empty((R, k), dtype=torch.int32, device=dev)
+    if top_logq is None:
+        top_logq = torch.empty((R, k), dtype=torch.float64, device=dev)
+    if entropy is None:
+        entropy = torch.empty((R,), dtype=torch.float64, device=dev)
+    _need(top_token, "top_token", _I32T, (R, k), dev)
+    _need(top_logq, "top_logq", (torch.float64,), (R, k), dev)
+    _need(entropy, "entropy", (torch.float64,), (R,), dev)
+    if workspace is None:
+        n = tree_expand_workspace_bytes(R, V, k)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("tree_expand_topk", lib().tree_expand_topk(
+        _ptr(draft_logits), R, V, int(k), float(temperature), _ptr(top_token), _ptr(top_logq),
+        _ptr(entropy), _ptr(workspace), ws_bytes, _ptr(dev_flags), _stream(stream)))
+    return top_token, top_logq, entropy
 
 
 def philox_uniforms(seed: int, offset: int, B: int, N: int, out=None, device=None, stream=None):

@@ -1,0 +1,405 @@
+// tree_expand_topk: for each draft row, the k most likely tokens with their
+// log-probabilities and the distribution's entropy. Top-k branching expands a
+// node by its draft's k most likely tokens, and entropy-based branching gives
+// a node more branches the higher its draft entropy (jisaku.com glossary,
+// tree-topology strategies); both read these per frontier node.
+//
+// With q = softmax(x / T), M the row maximum and y = (x - M) / T:
+//   log q(x) = y_x - log S0,  H(q) = log S0 - S1 / S0,
+//   S0 = sum e^y,  S1 = sum y e^y.
+// Two kernels. The first splits each row into 2048-entry shares, one per
+// wave (32 entries per lane, 16-byte loads): each wave takes its k best
+// (value, token) keys in k rounds of a wave-wide 64-bit key maximum (the
+// value's order-preserving bits above the complement of the token, so ties go
+// to the lower token) and its (max, S0, S1) relative to its own maximum, with
+// each term's exponential in fp32 and the sums in fp64, and writes them: no
+// barrier. The second, one workgroup per row, rebases the partial sums to the
+// row maximum (S1 -> e^d (S1 + d S0), S0 -> e^d S0 with d = (m - M) / T) and
+// takes the k best keys among the waves' candidates.
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace tav {
+namespace {
+
+constexpr int kExThreads = 512;
+constexpr int kExWaves = kExThreads / 64;
+constexpr int kExEpt = 32;                      // entries per thread
+constexpr int kExChunk = kExThreads * kExEpt;   // entries per workgroup
+constexpr int kExWaveChunk = 64 * kExEpt;       // entries per wave
+constexpr int kExMaxK = 16;
+constexpr int kExMaxWpr = 128;                  // workgroups per row (V <= 2^21)
+constexpr int kExMaxParts = kExMaxWpr * kExWaves;   // wave partials per row
+constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
+
+struct ExPart {          // one wave's share of a row
+    double s0, s1;
+    float m;             // maximum of its entries (-inf if none)
+    int32_t nan;
+    uint64_t key[kExMaxK];
+};
+
+__device__ __forceinline__ uint32_t ordered_bits(float v)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, v == 0.0f ? 0.0f : v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float from_ordered_bits(uint32_t o)
+{
+    return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+__device__ __forceinline__ uint64_t make_key(float v, int64_t t)
+{
+    return ((uint64_t)ordered_bits(v) << 32) | (0xFFFFFFFFu - (uint32_t)t);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF,
+                                                              false);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int lane)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v)
+{
+    v = max_u64(v, dpp_u64<kQuadSwap1>(v));
+    v = max_u64(v, dpp_u64<kQuadSwap2>(v));
+    v = max_u64(v, dpp_u64<kRowHalfMirror>(v));
+    v = max_u64(v, dpp_u64<kRowMirror>(v));
+    return max_u64(max_u64(lane_u64(v, 0), lane_u64(v, 16)), max_u64(lane_u64(v, 32), lane_u64(v, 48)));
+}
+
+// The largest key over the workgroup, in every thread (0 is the identity).
+__device__ __forceinline__ uint64_t block_max_key(uint64_t v, uint64_t *red)
+{
+    v = wave_max_key(v);
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0)
+        red[wave] = v;
+    __syncthreads();
+    uint64_t r = 0;
+#pragma unroll
+    for (int w = 0; w < kExWaves; ++w)
+        r = max_u64(r, red[w]);
+    return r;
+}
+
+__device__ __forceinline__ double wave_sum(double v)
+{
+    auto dpp = [](double x, auto ctrl) __attribute__((always_inline)) {
+        constexpr int C = decltype(ctrl)::value;
+        const uint64_t u = __builtin_bit_cast(uint64_t, x);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, C, 0xF, 0xF, false);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), C, 0xF, 0xF, false);
+        return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+    };
+    v += dpp(v, std::integral_constant<int, kQuadSwap1>{});
+    v += dpp(v, std::integral_constant<int, kQuadSwap2>{});
+    v += dpp(v, std::integral_constant<int, kRowHalfMirror>{});
+    v += dpp(v, std::integral_constant<int, kRowMirror>{});
+    auto rl = [](double x, int l) __attribute__((always_inline)) {
+        const uint64_t u = __builtin_bit_cast(uint64_t, x);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+        return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+    };
+    return (rl(v, 0) + rl(v, 16)) + (rl(v, 32) + rl(v, 48));
+}
+
+__device__ __forceinline__ void block_sum2(double &a, double &b, double *red)
+{
+    a = wave_sum(a);
+    b = wave_sum(b);
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) {
+        red[wave] = a;
+        red[kExWaves + wave] = b;
+    }
+    __syncthreads();
+    a = 0.0;
+    b = 0.0;
+#pragma unroll
+    for (int w = 0; w < kExWaves; ++w) {
+        a += red[w];
+        b += red[kExWaves + w];
+    }
+}
+
+struct ExArgs {
+    const float *x;
+    int64_t R;
+    int32_t V, k, wpr, vec4;
+    float invT32;
+    double invT;
+    ExPart *part;        // [R][wpr * kExWaves]
+    int32_t *top_token;  // [R][k]
+    double *top_logq;    // [R][k]
+    double *entropy;     // [R]
+    uint32_t *flags;
+};
+
+__global__ __launch_bounds__(kExThreads) void expand_part_kernel(ExArgs a)
+{
+    // Each wave owns kExWaveChunk consecutive entries of one row: lane l holds
+    // tokens wbase + 256 h + 4 l + j (h < 8, j < 4), read 16 bytes at a time,
+    // so a lane's entries rise in token order. No barrier: every wave writes
+    // its own partial.
+    const int64_t r = blockIdx.x / a.wpr;
+    const int w = (int)(blockIdx.x % a.wpr);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const float *row = a.x + r * a.V;
+    const int64_t wbase = (int64_t)w * kExChunk + (int64_t)wave * kExWaveChunk;
+    const int64_t lim = a.V;
+    float v[kExEpt];
+#pragma unroll
+    for (int h = 0; h < kExEpt / 4; ++h) {
+        const int64_t i0 = wbase + (int64_t)h * 256 + 4 * lane;
+        if (a.vec4 && i0 + 3 < lim) {
+            const f32x4 q = *reinterpret_cast<const f32x4 *>(row + i0);
+            v[4 * h] = q.x;
+            v[4 * h + 1] = q.y;
+            v[4 * h + 2] = q.z;
+            v[4 * h + 3] = q.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                v[4 * h + j] = i0 + j < lim ? row[i0 + j] : NAN;   // NaN: not an entry
+        }
+    }
+    auto tok = [&](int e) __attribute__((always_inline)) {
+        return wbase + (int64_t)(e >> 2) * 256 + 4 * lane + (e & 3);
+    };
+    bool nan_seen = false;
+#pragma unroll
+    for (int e = 0; e < kExEpt; ++e)
+        nan_seen |= __builtin_isnan(v[e]) && tok(e) < lim;
+    // The wave's k best keys. Fast path: each lane's best entry (the first of
+    // equal values, i.e. its lower token) as a key, and the k best of those
+    // in k rounds of a wave-wide key maximum; tau, the k-th of them, bounds
+    // every entry of the wave's top k from below (k lanes hold an entry of
+    // at least tau). If no lane holds two entries >= tau, the wave's top k
+    // are those lane keys. Otherwise every round rescans: each lane offers
+    // its best entry not yet taken, and the winner's lane marks it taken.
+    ExPart *out = a.part + (r * a.wpr + w) * kExWaves + wave;
+    float lm = 0.f;
+    int le = -1;
+#pragma unroll
+    for (int e = 0; e < kExEpt; ++e) {
+        if (!__builtin_isnan(v[e]) && (le < 0 || v[e] > lm)) {
+            lm = v[e];
+            le = e;
+        }
+    }
+    const uint64_t lkey = le < 0 ? 0ull : make_key(lm, tok(le));
+    uint64_t first = 0, last = 0;
+    {
+        uint64_t offer = lkey;
+        for (int i = 0; i < a.k; ++i) {
+            const uint64_t win = wave_max_key(offer);
+            if (offer == win)
+                offer = 0ull;
+            if (i == 0)
+                first = win;
+            last = win;
+            if (lane == 0)
+                out->key[i] = win;
+        }
+    }
+    const float tau = last == 0ull ? -INFINITY : from_ordered_bits((uint32_t)(last >> 32));
+    int above = 0;
+#pragma unroll
+    for (int e = 0; e < kExEpt; ++e)
+        above += (!__builtin_isnan(v[e]) && v[e] >= tau) ? 1 : 0;
+    if (last == 0ull || __any(above > 1)) {
+        uint32_t taken = 0;
+        for (int i = 0; i < a.k; ++i) {
+            float bv = 0.f;
+            int be = -1;
+#pragma unroll
+            for (int e = 0; e < kExEpt; ++e) {
+                const bool ok = !((taken >> e) & 1u) && !__builtin_isnan(v[e]);
+                if (ok && (be < 0 || v[e] > bv)) {
+                    bv = v[e];
+                    be = e;
+                }
+            }
+            const uint64_t mine = be < 0 ? 0ull : make_key(bv, tok(be));
+            const uint64_t win = wave_max_key(mine);
+            if (be >= 0 && mine == win)
+                taken |= 1u << be;
+            if (lane == 0)
+                out->key[i] = win;
+        }
+    }
+    // sums relative to the wave's maximum (-inf when it holds no entry)
+    const float m = first == 0ull ? -INFINITY : from_ordered_bits((uint32_t)(first >> 32));
+    const float ms = m * a.invT32;
+    double s0 = 0.0, s1 = 0.0;
+    if (m != -INFINITY) {
+#pragma unroll
+        for (int e = 0; e < kExEpt; ++e) {
+            if (v[e] != -INFINITY && !__builtin_isnan(v[e])) {
+                const float y = fmaf(v[e], a.invT32, -ms);   // one rounding
+                const double ev = (double)__builtin_amdgcn_exp2f(y * 0x1.715476p+0f);
+                s0 += ev;
+                s1 = fma((double)y, ev, s1);
+            }
+        }
+    }
+    s0 = wave_sum(s0);
+    s1 = wave_sum(s1);
+    const bool wnan = __any(nan_seen);
+    if (lane == 0) {
+        out->s0 = s0;
+        out->s1 = s1;
+        out->m = m;
+        out->nan = wnan;
+    }
+}
+
+__global__ __launch_bounds__(kExThreads) void expand_merge_kernel(ExArgs a)
+{
+    __shared__ uint64_t s_red[kExWaves];
+    __shared__ double s_sum[2 * kExWaves];
+    const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int np = a.wpr * kExWaves;
+    const ExPart *p = a.part + r * np;
+    // the row maximum and any NaN
+    uint64_t mk = 0;
+    bool nan_seen = false;
+    for (int w = tid; w < np; w += kExThreads) {
+        mk = max_u64(mk, p[w].key[0]);
+        nan_seen |= p[w].nan != 0;
+    }
+    const uint64_t top = block_max_key(mk, s_red);
+    const bool any_nan = __syncthreads_or(nan_seen);
+    const float M = top == 0ull ? -INFINITY : from_ordered_bits((uint32_t)(top >> 32));
+    if (any_nan || !__builtin_isfinite(M)) {
+        if (tid == 0)
+            raise_flag(a.flags, TAV_FLAG_NONFINITE_LOGITS);
+        for (int i = tid; i < a.k; i += kExThreads) {
+            a.top_token[r * a.k + i] = -1;
+            a.top_logq[r * a.k + i] = NAN;
+        }
+        if (tid == 0)
+            a.entropy[r] = NAN;
+        return;
+    }
+    // partial sums rebased to the row maximum, summed in workgroup order
+    const double Ms = (double)(M * a.invT32);
+    double s0 = 0.0, s1 = 0.0;
+    for (int w = tid; w < np; w += kExThreads) {
+        if (p[w].m == -INFINITY)
+            continue;
+        const double d = (double)(p[w].m * a.invT32) - Ms;   // <= 0
+        const double e = exp(d);
+        s0 += e * p[w].s0;
+        s1 += e * (p[w].s1 + d * p[w].s0);
+    }
+    block_sum2(s0, s1, s_sum);
+    const double logS0 = log(s0);
+    // the k best keys among every workgroup's k candidates: round i takes the
+    // largest key below round i-1's (keys are unique: they carry the token)
+    constexpr int kSlots = kExMaxParts * kExMaxK / kExThreads;
+    const int ncand = np * a.k;
+    uint64_t cand[kSlots];
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) {
+        const int c = tid + j * kExThreads;
+        cand[j] = c < ncand ? p[c / a.k].key[c % a.k] : 0ull;
+    }
+    uint64_t prev = ~0ull;
+    for (int i = 0; i < a.k; ++i) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int j = 0; j < kSlots; ++j)
+            if (cand[j] < prev)
+                best = max_u64(best, cand[j]);
+        const uint64_t win = block_max_key(best, s_red);
+        prev = win;
+        if (tid == 0) {
+            const float x = from_ordered_bits((uint32_t)(win >> 32));
+            a.top_token[r * a.k + i] = win == 0ull ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)win);
+            a.top_logq[r * a.k + i] =
+                win == 0ull ? -INFINITY : (double)fmaf(x, a.invT32, -(float)Ms) - logS0;
+        }
+    }
+    if (tid == 0)
+        a.entropy[r] = logS0 - s1 / s0;
+}
+
+bool ex_plan(int32_t V, int32_t &wpr)
+{
+    wpr = (int32_t)ceil_div(V, kExChunk);
+    return wpr <= kExMaxWpr;
+}
+
+} // namespace
+} // namespace tav
+
+extern "C" size_t tree_expand_workspace_bytes(int64_t R, int32_t V, int32_t k)
+{
+    using namespace tav;
+    int32_t wpr = 0;
+    if (R < 1 || V < 1 || k < 1 || k > kExMaxK || k > V || !ex_plan(V, wpr))
+        return 0;
+    return (size_t)R * wpr * kExWaves * sizeof(ExPart);
+}
+
+extern "C" tav_status tree_expand_topk(const float *draft_logits, int64_t R, int32_t V, int32_t k,
+                                       double temperature, int32_t *top_token, double *top_logq,
+                                       double *entropy, void *workspace, size_t ws_bytes,
+                                       uint32_t *dev_flags, void *stream)
+{
+    using namespace tav;
+    if (!draft_logits || !top_token || !top_logq || !entropy)
+        return TAV_ERR_ARG;
+    if (R < 1 || V < 1 || k < 1 || k > V || !(temperature > 0.0) || !(temperature < INFINITY))
+        return TAV_ERR_ARG;
+    int32_t wpr = 0;
+    if (k > kExMaxK || !ex_plan(V, wpr) || R * wpr > (int64_t)INT32_MAX)
+        return TAV_ERR_UNSUPPORTED;
+    if (!aligned(draft_logits, 4) || !aligned(top_logq, 8) || !aligned(entropy, 8))
+        return TAV_ERR_ARG;
+    const size_t need = (size_t)R * wpr * kExWaves * sizeof(ExPart);
+    if (!workspace || ws_bytes < need || !aligned(workspace, 16))
+        return TAV_ERR_WORKSPACE;
+    ExArgs a;
+    a.x = draft_logits;
+    a.R = R;
+    a.V = V;
+    a.k = k;
+    a.wpr = wpr;
+    a.vec4 = V % 4 == 0 && aligned(draft_logits, 16);
+    a.invT = 1.0 / temperature;
+    a.invT32 = (float)a.invT;
+    a.part = static_cast<ExPart *>(workspace);
+    a.top_token = top_token;
+    a.top_logq = top_logq;
+    a.entropy = entropy;
+    a.flags = dev_flags;
+    hipStream_t s = as_stream(stream);
+    hipLaunchKernelGGL(expand_part_kernel, dim3((unsigned)(R * wpr)), dim3(kExThreads), 0, s, a);
+    if (hipGetLastError() != hipSuccess)
+        return TAV_ERR_LAUNCH;
+    hipLaunchKernelGGL(expand_merge_kernel, dim3((unsigned)R), dim3(kExThreads), 0, s, a);
+    return hipGetLastError() == hipSuccess ? TAV_OK : TAV_ERR_LAUNCH;
+}
