@@ -15,7 +15,9 @@
 // each term's exponential in fp32 and the sums in fp64, and writes them: no
 // barrier. The second, one workgroup per row, rebases the partial sums to the
 // row maximum (S1 -> e^d (S1 + d S0), S0 -> e^d S0 with d = (m - M) / T) and
-// takes the k best keys among the waves' candidates.
+// takes the k best keys among the waves' candidates. Within a lane, each run
+// of four terms is summed in fp32 (same-sign terms: within three roundings)
+// and the run totals in fp64.
 
 #include <algorithm>
 
@@ -251,16 +253,24 @@ __global__ __launch_bounds__(kExThreads) void expand_part_kernel(ExArgs a)
     // sums relative to the wave's maximum (-inf when it holds no entry)
     const float m = first == 0ull ? -INFINITY : from_ordered_bits((uint32_t)(first >> 32));
     const float ms = m * a.invT32;
+    // Each run of four entries is summed in fp32 (same-sign terms, so within
+    // three fp32 roundings of exact), the run totals in fp64.
     double s0 = 0.0, s1 = 0.0;
     if (m != -INFINITY) {
 #pragma unroll
-        for (int e = 0; e < kExEpt; ++e) {
-            if (v[e] != -INFINITY && !__builtin_isnan(v[e])) {
-                const float y = fmaf(v[e], a.invT32, -ms);   // one rounding
-                const double ev = (double)__builtin_amdgcn_exp2f(y * 0x1.715476p+0f);
-                s0 += ev;
-                s1 = fma((double)y, ev, s1);
+        for (int h = 0; h < kExEpt / 4; ++h) {
+            float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float x = v[4 * h + j];
+                const float y = fmaf(x, a.invT32, -ms);   // one rounding
+                const float ev = __builtin_amdgcn_exp2f(y * 0x1.715476p+0f);
+                const bool live = x != -INFINITY && !__builtin_isnan(x);
+                r0 += live ? ev : 0.f;
+                r1 = live ? fmaf(y, ev, r1) : r1;
             }
+            s0 += (double)r0;
+            s1 += (double)r1;
         }
     }
     s0 = wave_sum(s0);
