@@ -157,41 +157,18 @@ struct ExArgs {
     uint32_t *flags;
 };
 
-__global__ __launch_bounds__(kExThreads) void expand_part_kernel(ExArgs a)
+// One wave's partial of a row from its entries v (lane order: tokens rise
+// with e). kClean: every entry is in the row and none is NaN, so the
+// per-entry tests drop out.
+template <bool kClean, typename Tok>
+__device__ __forceinline__ void wave_partial(const ExArgs &a, const float (&v)[kExEpt], Tok tok,
+                                             int lane, ExPart *out)
 {
-    // Each wave owns kExWaveChunk consecutive entries of one row: lane l holds
-    // tokens wbase + 256 h + 4 l + j (h < 8, j < 4), read 16 bytes at a time,
-    // so a lane's entries rise in token order. No barrier: every wave writes
-    // its own partial.
-    const int64_t r = blockIdx.x / a.wpr;
-    const int w = (int)(blockIdx.x % a.wpr);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const float *row = a.x + r * a.V;
-    const int64_t wbase = (int64_t)w * kExChunk + (int64_t)wave * kExWaveChunk;
     const int64_t lim = a.V;
-    float v[kExEpt];
-#pragma unroll
-    for (int h = 0; h < kExEpt / 4; ++h) {
-        const int64_t i0 = wbase + (int64_t)h * 256 + 4 * lane;
-        if (a.vec4 && i0 + 3 < lim) {
-            const f32x4 q = *reinterpret_cast<const f32x4 *>(row + i0);
-            v[4 * h] = q.x;
-            v[4 * h + 1] = q.y;
-            v[4 * h + 2] = q.z;
-            v[4 * h + 3] = q.w;
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                v[4 * h + j] = i0 + j < lim ? row[i0 + j] : NAN;   // NaN: not an entry
-        }
-    }
-    auto tok = [&](int e) __attribute__((always_inline)) {
-        return wbase + (int64_t)(e >> 2) * 256 + 4 * lane + (e & 3);
-    };
     bool nan_seen = false;
 #pragma unroll
     for (int e = 0; e < kExEpt; ++e)
-        nan_seen |= __builtin_isnan(v[e]) && tok(e) < lim;
+        nan_seen |= (!kClean && __builtin_isnan(v[e])) && tok(e) < lim;
     // The wave's k best keys. Fast path: each lane's best entry (the first of
     // equal values, i.e. its lower token) as a key, and the k best of those
     // in k rounds of a wave-wide key maximum; tau, the k-th of them, bounds
@@ -199,12 +176,11 @@ __global__ __launch_bounds__(kExThreads) void expand_part_kernel(ExArgs a)
     // at least tau). If no lane holds two entries >= tau, the wave's top k
     // are those lane keys. Otherwise every round rescans: each lane offers
     // its best entry not yet taken, and the winner's lane marks it taken.
-    ExPart *out = a.part + (r * a.wpr + w) * kExWaves + wave;
     float lm = 0.f;
     int le = -1;
 #pragma unroll
     for (int e = 0; e < kExEpt; ++e) {
-        if (!__builtin_isnan(v[e]) && (le < 0 || v[e] > lm)) {
+        if (!(!kClean && __builtin_isnan(v[e])) && (le < 0 || v[e] > lm)) {
             lm = v[e];
             le = e;
         }
@@ -228,7 +204,7 @@ __global__ __launch_bounds__(kExThreads) void expand_part_kernel(ExArgs a)
     int above = 0;
 #pragma unroll
     for (int e = 0; e < kExEpt; ++e)
-        above += (!__builtin_isnan(v[e]) && v[e] >= tau) ? 1 : 0;
+        above += (!(!kClean && __builtin_isnan(v[e])) && v[e] >= tau) ? 1 : 0;
     if (last == 0ull || __any(above > 1)) {
         uint32_t taken = 0;
         for (int i = 0; i < a.k; ++i) {
@@ -236,7 +212,7 @@ __global__ __launch_bounds__(kExThreads) void expand_part_kernel(ExArgs a)
             int be = -1;
 #pragma unroll
             for (int e = 0; e < kExEpt; ++e) {
-                const bool ok = !((taken >> e) & 1u) && !__builtin_isnan(v[e]);
+                const bool ok = !((taken >> e) & 1u) && !(!kClean && __builtin_isnan(v[e]));
                 if (ok && (be < 0 || v[e] > bv)) {
                     bv = v[e];
                     be = e;
@@ -265,9 +241,15 @@ __global__ __launch_bounds__(kExThreads) void expand_part_kernel(ExArgs a)
                 const float x = v[4 * h + j];
                 const float y = fmaf(x, a.invT32, -ms);   // one rounding
                 const float ev = __builtin_amdgcn_exp2f(y * 0x1.715476p+0f);
-                const bool live = x != -INFINITY && !__builtin_isnan(x);
-                r0 += live ? ev : 0.f;
-                r1 = live ? fmaf(y, ev, r1) : r1;
+                if constexpr (kClean) {
+                    // -inf gives ev = 0; y clamped so y * 0 stays 0
+                    r0 += ev;
+                    r1 = fmaf(fmaxf(y, -1.0e4f), ev, r1);
+                } else {
+                    const bool live = x != -INFINITY && !__builtin_isnan(x);
+                    r0 += live ? ev : 0.f;
+                    r1 = live ? fmaf(y, ev, r1) : r1;
+                }
             }
             s0 += (double)r0;
             s1 += (double)r1;
@@ -282,6 +264,68 @@ __global__ __launch_bounds__(kExThreads) void expand_part_kernel(ExArgs a)
         out->m = m;
         out->nan = wnan;
     }
+}
+
+__global__ __launch_bounds__(kExThreads) void expand_part_kernel(ExArgs a)
+{
+    // Each wave owns kExWaveChunk consecutive entries of one row: lane l holds
+    // tokens wbase + 256 h + 4 l + j (h < 8, j < 4), read 16 bytes at a time,
+    // so a lane's entries rise in token order. No barrier: every wave writes
+    // its own partial.
+    const int64_t r = blockIdx.x / a.wpr;
+    const int w = (int)(blockIdx.x % a.wpr);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const float *row = a.x + r * a.V;
+    const int64_t wbase = (int64_t)w * kExChunk + (int64_t)wave * kExWaveChunk;
+    const int64_t lim = a.V;
+    // A share wholly inside the row (every share but a row's last) is read
+    // without per-entry range tests; if it also holds no NaN (one
+    // NaN-propagating maximum tells), the passes below skip the per-entry
+    // NaN tests too.
+    const bool full = a.vec4 && wbase + kExWaveChunk <= lim;   // wave-uniform
+    float v[kExEpt];
+    if (full) {
+#pragma unroll
+        for (int h = 0; h < kExEpt / 4; ++h) {
+            const f32x4 q = *reinterpret_cast<const f32x4 *>(row + wbase + (int64_t)h * 256 + 4 * lane);
+            v[4 * h] = q.x;
+            v[4 * h + 1] = q.y;
+            v[4 * h + 2] = q.z;
+            v[4 * h + 3] = q.w;
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < kExEpt / 4; ++h) {
+            const int64_t i0 = wbase + (int64_t)h * 256 + 4 * lane;
+            if (a.vec4 && i0 + 3 < lim) {
+                const f32x4 q = *reinterpret_cast<const f32x4 *>(row + i0);
+                v[4 * h] = q.x;
+                v[4 * h + 1] = q.y;
+                v[4 * h + 2] = q.z;
+                v[4 * h + 3] = q.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    v[4 * h + j] = i0 + j < lim ? row[i0 + j] : NAN;   // NaN: not an entry
+            }
+        }
+    }
+    bool clean = false;
+    if (full) {
+        float mx = v[0];
+#pragma unroll
+        for (int e = 1; e < kExEpt; ++e)
+            mx = __builtin_elementwise_maximum(mx, v[e]);   // NaN-propagating
+        clean = !__any(__builtin_isnan(mx));
+    }
+    auto tok = [&](int e) __attribute__((always_inline)) {
+        return wbase + (int64_t)(e >> 2) * 256 + 4 * lane + (e & 3);
+    };
+    ExPart *out = a.part + (r * a.wpr + w) * kExWaves + wave;
+    if (clean)
+        wave_partial<true>(a, v, tok, lane, out);
+    else
+        wave_partial<false>(a, v, tok, lane, out);
 }
 
 __global__ __launch_bounds__(kExThreads) void expand_merge_kernel(ExArgs a)
