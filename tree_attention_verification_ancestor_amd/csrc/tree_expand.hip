@@ -15,7 +15,7 @@
 // each term's exponential in fp32 and the sums in fp64, and writes them: no
 // barrier. The second, one workgroup per row, rebases the partial sums to the
 // row maximum (S1 -> e^d (S1 + d S0), S0 -> e^d S0 with d = (m - M) / T) and
-// takes the k best keys among the waves' candidates. Within a lane, each run
+// takes the k best keys among the waves' candidates; one wave per row does it. Within a lane, each run
 // of four terms is summed in fp32 (same-sign terms: within three roundings)
 // and the run totals in fp64.
 
@@ -33,7 +33,6 @@ constexpr int kExChunk = kExThreads * kExEpt;   // entries per workgroup
 constexpr int kExWaveChunk = 64 * kExEpt;       // entries per wave
 constexpr int kExMaxK = 16;
 constexpr int kExMaxWpr = 128;                  // workgroups per row (V <= 2^21)
-constexpr int kExMaxParts = kExMaxWpr * kExWaves;   // wave partials per row
 constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
 
 struct ExPart {          // one wave's share of a row
@@ -86,22 +85,6 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t v)
     return max_u64(max_u64(lane_u64(v, 0), lane_u64(v, 16)), max_u64(lane_u64(v, 32), lane_u64(v, 48)));
 }
 
-// The largest key over the workgroup, in every thread (0 is the identity).
-__device__ __forceinline__ uint64_t block_max_key(uint64_t v, uint64_t *red)
-{
-    v = wave_max_key(v);
-    const int wave = threadIdx.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0)
-        red[wave] = v;
-    __syncthreads();
-    uint64_t r = 0;
-#pragma unroll
-    for (int w = 0; w < kExWaves; ++w)
-        r = max_u64(r, red[w]);
-    return r;
-}
-
 __device__ __forceinline__ double wave_sum(double v)
 {
     auto dpp = [](double x, auto ctrl) __attribute__((always_inline)) {
@@ -122,26 +105,6 @@ __device__ __forceinline__ double wave_sum(double v)
         return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
     };
     return (rl(v, 0) + rl(v, 16)) + (rl(v, 32) + rl(v, 48));
-}
-
-__device__ __forceinline__ void block_sum2(double &a, double &b, double *red)
-{
-    a = wave_sum(a);
-    b = wave_sum(b);
-    const int wave = threadIdx.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) {
-        red[wave] = a;
-        red[kExWaves + wave] = b;
-    }
-    __syncthreads();
-    a = 0.0;
-    b = 0.0;
-#pragma unroll
-    for (int w = 0; w < kExWaves; ++w) {
-        a += red[w];
-        b += red[kExWaves + w];
-    }
 }
 
 struct ExArgs {
@@ -328,39 +291,41 @@ __global__ __launch_bounds__(kExThreads) void expand_part_kernel(ExArgs a)
         wave_partial<false>(a, v, tok, lane, out);
 }
 
-__global__ __launch_bounds__(kExThreads) void expand_merge_kernel(ExArgs a)
+// One wave per row: a row has wpr * 8 partials (64 for a 128256-entry row),
+// so the merge needs no barrier.
+constexpr int kMergeThreads = 64;
+
+__global__ __launch_bounds__(kMergeThreads) void expand_merge_kernel(ExArgs a)
 {
-    __shared__ uint64_t s_red[kExWaves];
-    __shared__ double s_sum[2 * kExWaves];
     const int64_t r = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x;
     const int np = a.wpr * kExWaves;
     const ExPart *p = a.part + r * np;
     // the row maximum and any NaN
     uint64_t mk = 0;
     bool nan_seen = false;
-    for (int w = tid; w < np; w += kExThreads) {
+    for (int w = lane; w < np; w += kMergeThreads) {
         mk = max_u64(mk, p[w].key[0]);
         nan_seen |= p[w].nan != 0;
     }
-    const uint64_t top = block_max_key(mk, s_red);
-    const bool any_nan = __syncthreads_or(nan_seen);
+    const uint64_t top = wave_max_key(mk);
+    const bool any_nan = __any(nan_seen);
     const float M = top == 0ull ? -INFINITY : from_ordered_bits((uint32_t)(top >> 32));
     if (any_nan || !__builtin_isfinite(M)) {
-        if (tid == 0)
+        if (lane == 0)
             raise_flag(a.flags, TAV_FLAG_NONFINITE_LOGITS);
-        for (int i = tid; i < a.k; i += kExThreads) {
+        for (int i = lane; i < a.k; i += kMergeThreads) {
             a.top_token[r * a.k + i] = -1;
             a.top_logq[r * a.k + i] = NAN;
         }
-        if (tid == 0)
+        if (lane == 0)
             a.entropy[r] = NAN;
         return;
     }
-    // partial sums rebased to the row maximum, summed in workgroup order
+    // partial sums rebased to the row maximum
     const double Ms = (double)(M * a.invT32);
     double s0 = 0.0, s1 = 0.0;
-    for (int w = tid; w < np; w += kExThreads) {
+    for (int w = lane; w < np; w += kMergeThreads) {
         if (p[w].m == -INFINITY)
             continue;
         const double d = (double)(p[w].m * a.invT32) - Ms;   // <= 0
@@ -368,35 +333,30 @@ __global__ __launch_bounds__(kExThreads) void expand_merge_kernel(ExArgs a)
         s0 += e * p[w].s0;
         s1 += e * (p[w].s1 + d * p[w].s0);
     }
-    block_sum2(s0, s1, s_sum);
+    s0 = wave_sum(s0);
+    s1 = wave_sum(s1);
     const double logS0 = log(s0);
-    // the k best keys among every workgroup's k candidates: round i takes the
+    // the k best keys among every wave's k candidates: round i takes the
     // largest key below round i-1's (keys are unique: they carry the token)
-    constexpr int kSlots = kExMaxParts * kExMaxK / kExThreads;
     const int ncand = np * a.k;
-    uint64_t cand[kSlots];
-#pragma unroll
-    for (int j = 0; j < kSlots; ++j) {
-        const int c = tid + j * kExThreads;
-        cand[j] = c < ncand ? p[c / a.k].key[c % a.k] : 0ull;
-    }
     uint64_t prev = ~0ull;
     for (int i = 0; i < a.k; ++i) {
         uint64_t best = 0;
-#pragma unroll
-        for (int j = 0; j < kSlots; ++j)
-            if (cand[j] < prev)
-                best = max_u64(best, cand[j]);
-        const uint64_t win = block_max_key(best, s_red);
+        for (int c = lane; c < ncand; c += kMergeThreads) {
+            const uint64_t kk = p[c / a.k].key[c % a.k];
+            if (kk < prev)
+                best = max_u64(best, kk);
+        }
+        const uint64_t win = wave_max_key(best);
         prev = win;
-        if (tid == 0) {
+        if (lane == 0) {
             const float x = from_ordered_bits((uint32_t)(win >> 32));
             a.top_token[r * a.k + i] = win == 0ull ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)win);
             a.top_logq[r * a.k + i] =
                 win == 0ull ? -INFINITY : (double)fmaf(x, a.invT32, -(float)Ms) - logS0;
         }
     }
-    if (tid == 0)
+    if (lane == 0)
         a.entropy[r] = logS0 - s1 / s0;
 }
 
@@ -454,6 +414,6 @@ extern "C" tav_status tree_expand_topk(const float *draft_logits, int64_t R, int
     hipLaunchKernelGGL(expand_part_kernel, dim3((unsigned)(R * wpr)), dim3(kExThreads), 0, s, a);
     if (hipGetLastError() != hipSuccess)
         return TAV_ERR_LAUNCH;
-    hipLaunchKernelGGL(expand_merge_kernel, dim3((unsigned)R), dim3(kExThreads), 0, s, a);
+    hipLaunchKernelGGL(expand_merge_kernel, dim3((unsigned)R), dim3(kMergeThreads), 0, s, a);
     return hipGetLastError() == hipSuccess ? TAV_OK : TAV_ERR_LAUNCH;
 }
