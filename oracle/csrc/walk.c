@@ -17,7 +17,13 @@
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *  - children of a node are tried in ascending node index, each against the
- *    running residual of the same draft distribution q_u;
+ *    running residual; under the i.i.d. sibling rule every child is tested
+ *    with the same draft distribution q_u (siblings drawn independently from
+ *    q_u), under the without-replacement rule a rejected child's token then
+ *    leaves q: its entry is set to zero and the rest is divided by its sum
+ *    (siblings drawn from q_u without replacement); if no draft mass is
+ *    left, q stays zero and a later child is accepted iff its residual is
+ *    positive;
  *  - the test is written without division: accept iff r*q(x) < p_res(x);
  *  - the residual normaliser is summed directly; if it is zero the
  *    distribution is left unchanged;
@@ -42,6 +48,11 @@
 #define PHILOX_M1 0xCA5A826395121157ULL
 #define PHILOX_W0 0x9E3779B97F4A7C15ULL
 #define PHILOX_W1 0xBB67AE8584CAA73BULL
+
+enum {
+    ORACLE_RULE_IID = 0,                 /* siblings drawn independently from q */
+    ORACLE_RULE_WITHOUT_REPLACEMENT = 1, /* siblings drawn from q without replacement */
+};
 
 enum {
     ORACLE_OK = 0,
@@ -145,7 +156,7 @@ static void log_draw(draw_log *lg, double margin, double eps, int32_t n_acc)
  * -1 padded) and returns the accepted count through *n_acc_out.
  */
 static int walk_one(const float *target, const float *draft, const int32_t *parent,
-                    const int32_t *token, int32_t N, int32_t V, double T,
+                    const int32_t *token, int32_t N, int32_t V, double T, int32_t rule,
                     uint64_t seed, uint64_t offset, int64_t b, double eps,
                     int32_t *path, int32_t *out_tokens, int32_t *n_acc_out,
                     draw_log *lg, double *p, double *q, double *pr)
@@ -208,6 +219,15 @@ static int walk_one(const float *target, const float *draft, const int32_t *pare
                             pr[y] = (d > 0.0 ? d : 0.0) / z;
                         }
                     }
+                    if (rule == ORACLE_RULE_WITHOUT_REPLACEMENT) {
+                        q[x] = 0.0;
+                        double s = 0.0;
+                        for (int32_t y = 0; y < V; ++y)
+                            s += q[y];
+                        if (s > 0.0)
+                            for (int32_t y = 0; y < V; ++y)
+                                q[y] /= s;
+                    }
                 }
             }
             if (accepted)
@@ -248,19 +268,21 @@ static int walk_one(const float *target, const float *draft, const int32_t *pare
 }
 
 /*
- * Batch entry.  target/draft: float32 [B][N][V]; parent/token: int32 [B][N].
+ * Batch entry.  target/draft: float32 [B][N][V]; parent/token: int32 [B][N];
+ * rule: ORACLE_RULE_IID or ORACLE_RULE_WITHOUT_REPLACEMENT.
  * Outputs: path, out_tokens int32 [B][N]; n_accepted int32 [B]; per sequence
  * draws/near/first_near int32 [B] and min_margin double [B].  Returns 0 or the
  * first error code met (then *bad_seq names the sequence).
  */
 int oracle_verify_walk(const float *target, const float *draft, const int32_t *parent,
                        const int32_t *token, int64_t B, int32_t N, int32_t V, double T,
-                       uint64_t seed, uint64_t offset, double eps,
+                       uint64_t seed, uint64_t offset, double eps, int32_t rule,
                        int32_t *path, int32_t *n_accepted, int32_t *out_tokens,
                        int32_t *draws, int32_t *near, int32_t *first_near,
                        double *min_margin, int64_t *bad_seq)
 {
-    if (B < 0 || N < 1 || V < 1 || !(T > 0.0))
+    if (B < 0 || N < 1 || V < 1 || !(T > 0.0) ||
+        (rule != ORACLE_RULE_IID && rule != ORACLE_RULE_WITHOUT_REPLACEMENT))
         return ORACLE_BAD_ARG;
     double *buf = (double *)malloc(sizeof(double) * (size_t)V * 3);
     if (!buf)
@@ -270,7 +292,7 @@ int oracle_verify_walk(const float *target, const float *draft, const int32_t *p
         draw_log lg = {0, 0, -1, INFINITY};
         size_t row0 = (size_t)b * (size_t)N;
         rc = walk_one(target + row0 * V, draft + row0 * V, parent + row0, token + row0,
-                      N, V, T, seed, offset, b, eps, path + row0, out_tokens + row0,
+                      N, V, T, rule, seed, offset, b, eps, path + row0, out_tokens + row0,
                       n_accepted + b, &lg, buf, buf + V, buf + 2 * (size_t)V);
         if (rc) {
             *bad_seq = b;

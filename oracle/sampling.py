@@ -37,8 +37,8 @@ def _load():
         lib.oracle_verify_walk.restype = ctypes.c_int
         lib.oracle_verify_walk.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_double, ctypes.c_uint64,
-                                           ctypes.c_uint64, ctypes.c_double, P, P, P, P, P, P,
-                                           P, P]
+                                           ctypes.c_uint64, ctypes.c_double, ctypes.c_int32,
+                                           P, P, P, P, P, P, P, P]
         lib.oracle_uniform_table.restype = None
         lib.oracle_uniform_table.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
                                              ctypes.c_int32, P]
@@ -95,11 +95,21 @@ _ERRORS = {1: "bad parent array", 2: "token out of range", 3: "non-finite logits
 
 
 def verify_walk(target_logits, draft_logits, parent, token, temperature: float = 1.0,
-                seed: int = 0, offset: int = 0, near_eps: float = NEAR_EPS) -> WalkResult:
+                seed: int = 0, offset: int = 0, near_eps: float = NEAR_EPS,
+                without_replacement: bool = False) -> WalkResult:
     """Root-down rejection-sampling walk for a batch of trees.
 
     target_logits, draft_logits: float32 [B, N, V]; row u of the draft is the
     distribution node u's children were drawn from. parent, token: int [B, N].
+
+    Sibling rule: by default every child of u is tested with q_u, which is
+    lossless when siblings are independent draws from q_u. With
+    ``without_replacement`` a rejected child's token then leaves q_u (its
+    entry zeroed, the rest renormalised by their sum) before the next sibling
+    is tried, which is lossless when siblings are drawn from q_u without
+    replacement. The rejection step itself (radar-34b blog section 2) is the
+    same under both: the residual is the normalised positive part of the
+    current p minus the current q.
     Raises ValueError on an invalid tree, token or logit row.
     """
     tl = np.ascontiguousarray(target_logits, dtype=np.float32)
@@ -119,8 +129,9 @@ def verify_walk(target_logits, draft_logits, parent, token, temperature: float =
     bad = np.zeros(1, np.int64)
     rc = _load().oracle_verify_walk(_ptr(tl), _ptr(dl), _ptr(par), _ptr(tok), B, N, V,
                                     float(temperature), int(seed), int(offset), float(near_eps),
-                                    _ptr(path), _ptr(n_acc), _ptr(out_tok), _ptr(draws),
-                                    _ptr(near), _ptr(first_near), _ptr(min_margin), _ptr(bad))
+                                    1 if without_replacement else 0, _ptr(path), _ptr(n_acc),
+                                    _ptr(out_tok), _ptr(draws), _ptr(near), _ptr(first_near),
+                                    _ptr(min_margin), _ptr(bad))
     if rc:
         raise ValueError(f"oracle walk: {_ERRORS.get(rc, rc)} (sequence {int(bad[0])})")
     return WalkResult(path, n_acc, out_tok, draws, near, first_near, min_margin)
