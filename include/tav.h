@@ -5,6 +5,7 @@
  *   tree_mask_build     parent[] -> packed ancestor-or-self bitmasks
  *   tree_attn_verify    tree attention over a paged KV prefix plus ancestors
  *   spec_verify_sample  target/draft softmax and the rejection-sampling walk
+ *   spec_verify_sample_wor  the same walk for siblings drawn without replacement
  *   kv_commit_path      copy the accepted path's K/V into the paged cache
  *   kv_commit_inplace   the same when the tree's K/V already sit in the cache
  *   tree_expand_topk    top-k draft tokens, log q and entropy per frontier row
@@ -193,6 +194,34 @@ tav_status spec_verify_sample(const float *target_logits, const float *draft_log
                               int32_t *path, int32_t *n_accepted, int32_t *out_tokens,
                               void *workspace, size_t ws_bytes, uint32_t *dev_flags,
                               void *stream);
+
+/*
+ * spec_verify_sample_wor — spec_verify_sample for trees whose siblings were
+ * drawn from q_u without replacement (distinct tokens per parent).
+ *
+ * The rejection step is the one above (radar-34b blog §2: accept with
+ * min(1, p/q), else continue from the normalised positive part of p - q);
+ * what changes is the draft distribution the next sibling is tested with. The
+ * pages give top-k branching (jisaku.com glossary, tree-topology strategies) but no
+ * sibling rule; testing every sibling against q_u is lossless only for
+ * independent draws, so for draws without replacement the rejected token is
+ * taken out of q: after sibling j (token x_j) is rejected at u,
+ *   p_res <- max(0, p_res - q_j) / sum(...)   (as above, with the current q_j)
+ *   q_{j+1}(y) = q_j(y) / sum_{z != x_j} q_j(z) for y != x_j, q_{j+1}(x_j) = 0,
+ * with q_0 = q_u; if no draft mass is left q_{j+1} is zero, and a later
+ * sibling with q(x) = 0 is accepted iff p_res(x) > 0. Sibling c after j
+ * rejections is accepted iff r_acc(b,c) * q_j(x_c) < p_res(x_c). A repeated
+ * token (not a draw without replacement) has q = 0 from its second
+ * occurrence on. Everything else (uniforms, final draw, outputs, workspace,
+ * greedy at temperature 0, flags, limits) is as for spec_verify_sample; the
+ * workspace size is spec_verify_workspace_bytes(B, N, V).
+ */
+tav_status spec_verify_sample_wor(const float *target_logits, const float *draft_logits,
+                                  const int32_t *parent, const int32_t *token, int32_t B,
+                                  int32_t N, int32_t V, double temperature, uint64_t seed,
+                                  uint64_t offset, int32_t *path, int32_t *n_accepted,
+                                  int32_t *out_tokens, void *workspace, size_t ws_bytes,
+                                  uint32_t *dev_flags, void *stream);
 
 /*
  * kv_commit_path — keep the accepted path's K/V, discarding the rest.

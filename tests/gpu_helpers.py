@@ -48,10 +48,11 @@ def run_attention(w, dev, mask=None):
     return to_numpy(out), int(flags.item())
 
 
-def run_walk(w, dev, seed=None, offset=None):
+def run_walk(w, dev, seed=None, offset=None, wor=False):
     d = upload(w, dev)
     flags = tav.new_flags(dev)
-    path, n_acc, toks = tav.spec_verify_sample(
+    fn = tav.spec_verify_sample_wor if wor else tav.spec_verify_sample
+    path, n_acc, toks = fn(
         d["target_logits"], d["draft_logits"], d["parent"], d["token"], w.temperature,
         w.philox_seed if seed is None else seed, w.philox_offset if offset is None else offset,
         dev_flags=flags)
@@ -59,13 +60,14 @@ def run_walk(w, dev, seed=None, offset=None):
     return to_numpy(path), to_numpy(n_acc), to_numpy(toks), int(flags.item())
 
 
-def walk_arrays(tl, dl, parent, token, T, seed, offset, dev):
-    """Run the device walk on raw numpy arrays."""
+def walk_arrays(tl, dl, parent, token, T, seed, offset, dev, wor=False):
+    """Run the device walk on raw numpy arrays (``wor``: the without-replacement
+    sibling rule)."""
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     flags = tav.new_flags(dev)
-    path, n_acc, toks = tav.spec_verify_sample(t(tl), t(dl), t(parent.astype(np.int32)),
-                                               t(token.astype(np.int32)), T, seed, offset,
-                                               dev_flags=flags)
+    fn = tav.spec_verify_sample_wor if wor else tav.spec_verify_sample
+    path, n_acc, toks = fn(t(tl), t(dl), t(parent.astype(np.int32)), t(token.astype(np.int32)),
+                           T, seed, offset, dev_flags=flags)
     torch.cuda.synchronize()
     return to_numpy(path), to_numpy(n_acc), to_numpy(toks), int(flags.item())
 

@@ -12,7 +12,7 @@ import tree_attention_verification_ancestor_amd as tav
 def test_library_exports_every_declared_function():
     names = tav.header_functions()
     assert set(names) >= {"tree_mask_build", "tree_attn_verify", "spec_verify_sample",
-                          "kv_commit_path", "tree_attn_workspace_bytes",
+                          "spec_verify_sample_wor", "kv_commit_path", "tree_attn_workspace_bytes",
                           "spec_verify_workspace_bytes", "tav_philox_uniforms",
                           "tav_target_probs", "tav_status_string", "tav_abi_version"}
     lib = tav.lib()
@@ -64,12 +64,12 @@ def test_attention_rejects_bad_arguments(kw, code):
     assert _attn(**kw) == code
 
 
-def _sample(**kw):
+def _sample(fn="spec_verify_sample", **kw):
     args = dict(tl=FAKE, dl=FAKE, parent=FAKE, token=FAKE, B=2, N=5, V=1000, T=1.0, seed=0,
                 offset=0, path=FAKE, n_acc=FAKE, out_tok=FAKE, ws=FAKE, ws_bytes=1 << 20,
                 flags=None, stream=None)
     args.update(kw)
-    return tav.lib().spec_verify_sample(*args.values())
+    return getattr(tav.lib(), fn)(*args.values())
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -80,8 +80,9 @@ def _sample(**kw):
     (dict(dl=None), tav.ERR_ARG), (dict(dl=None, T=0.0, tl=None), tav.ERR_ARG),
     (dict(V=(1 << 21) + 1), tav.ERR_UNSUPPORTED),
 ])
-def test_sampler_rejects_bad_arguments(kw, code):
-    assert _sample(**kw) == code
+@pytest.mark.parametrize("fn", ["spec_verify_sample", "spec_verify_sample_wor"])
+def test_sampler_rejects_bad_arguments(fn, kw, code):
+    assert _sample(fn, **kw) == code
 
 
 def _commit(**kw):

@@ -66,6 +66,8 @@ _SIGNATURES = {
     "spec_verify_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "spec_verify_sample": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _F64, _U64, _U64, _P, _P,
                                   _P, _P, _SZ, _P, _P]),
+    "spec_verify_sample_wor": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _F64, _U64, _U64, _P, _P,
+                                  _P, _P, _SZ, _P, _P]),
     "kv_commit_path": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _P, _I32, _I32, _I32,
                               _I32, _I32, _P, _P, _P, _P]),
     "kv_commit_inplace": (_I32, [_P, _P, _I32, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
@@ -249,11 +251,8 @@ def new_sampler_workspace(B, N, V, device=None) -> torch.Tensor:
     return torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
 
 
-def spec_verify_sample(target_logits, draft_logits, parent, token, temperature: float = 1.0,
-                       seed: int = 0, offset: int = 0, path=None, n_accepted=None,
-                       out_tokens=None, workspace=None, dev_flags=None, stream=None):
-    """Rejection-sampling walk, or greedy verification at temperature 0 (then
-    draft_logits may be None); returns (path [B,N], n_accepted [B], out_tokens [B,N])."""
+def _verify_sample(name, target_logits, draft_logits, parent, token, temperature, seed, offset,
+                   path, n_accepted, out_tokens, workspace, dev_flags, stream):
     _need(target_logits, "target_logits", (torch.float32,))
     B, N, V = target_logits.shape
     dev = target_logits.device
@@ -273,11 +272,34 @@ def spec_verify_sample(target_logits, draft_logits, parent, token, temperature: 
     if workspace is None:
         workspace = new_sampler_workspace(B, N, V, dev)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check("spec_verify_sample", lib().spec_verify_sample(
+    _check(name, getattr(lib(), name)(
         _ptr(target_logits), _ptr(draft_logits), _ptr(parent), _ptr(token), B, N, V,
         float(temperature), int(seed), int(offset), _ptr(path), _ptr(n_accepted),
         _ptr(out_tokens), _ptr(workspace), ws_bytes, _ptr(dev_flags), _stream(stream)))
     return path, n_accepted, out_tokens
+
+
+def spec_verify_sample(target_logits, draft_logits, parent, token, temperature: float = 1.0,
+                       seed: int = 0, offset: int = 0, path=None, n_accepted=None,
+                       out_tokens=None, workspace=None, dev_flags=None, stream=None):
+    """Rejection-sampling walk with siblings tested against q_u each time
+    (drawn i.i.d.), or greedy verification at temperature 0 (then
+    draft_logits may be None); returns (path [B,N], n_accepted [B], out_tokens [B,N])."""
+    return _verify_sample("spec_verify_sample", target_logits, draft_logits, parent, token,
+                          temperature, seed, offset, path, n_accepted, out_tokens, workspace,
+                          dev_flags, stream)
+
+
+def spec_verify_sample_wor(target_logits, draft_logits, parent, token,
+                           temperature: float = 1.0, seed: int = 0, offset: int = 0, path=None,
+                           n_accepted=None, out_tokens=None, workspace=None, dev_flags=None,
+                           stream=None):
+    """As ``spec_verify_sample`` for siblings drawn from q_u without
+    replacement: a rejected sibling's token leaves q_u (the rest
+    renormalised) before the next sibling is tried."""
+    return _verify_sample("spec_verify_sample_wor", target_logits, draft_logits, parent, token,
+                          temperature, seed, offset, path, n_accepted, out_tokens, workspace,
+                          dev_flags, stream)
 
 
 def kv_commit_path(k_tree, v_tree, path, n_accepted, block_table, prefix_len, k_cache, v_cache,

@@ -333,6 +333,11 @@ __device__ __forceinline__ double bits_f64(uint32_t hi, uint32_t lo)
 
 // ---------------------------------------------------------------------------
 
+// kWor selects the sibling rule: false, every child of u is tested with q_u
+// (siblings drawn independently from q_u); true, a rejected child's token
+// leaves q_u, the rest renormalised, before the next sibling is tried
+// (siblings drawn from q_u without replacement).
+template <bool kWor>
 __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
 {
     __shared__ int32_t s_par[kMaxNodes];
@@ -354,6 +359,10 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
     __shared__ uint32_t s_words[kMaxWpg][kSlotWords];   // the group's payloads, as wave 0 received them
     __shared__ double s_mass[kMaxWpg];    // mass of every member's chunk in the current distribution
     __shared__ double s_zhist[kMaxNodes]; // residual normalisers after each rejection at u
+    // without replacement: after j rejections at u, q_j = q * s_qs[j] off the
+    // removed tokens (s_qs[0] = 1 is implied); s_rtok[j] = token rejected at step j
+    __shared__ double s_qs[kWor ? kMaxNodes + 1 : 1];
+    __shared__ int32_t s_rtok[kWor ? kMaxNodes : 1];
     __shared__ double s_slot[kSvEpt * kSvWaves];
     __shared__ double s_hit_off;
     __shared__ int s_bad;
@@ -700,14 +709,31 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             auto accepts = [&](int c, int k) __attribute__((always_inline)) {
                 const double qx = s_qx[c];
                 double prx = s_px[c];
-                for (int j = 0; j < k; ++j) {
-                    const double zj = s_zhist[j];
-                    if (zj > 0.0) {
-                        const double d = prx - qx;
-                        prx = (d > 0.0 ? d : 0.0) / zj;
+                if constexpr (kWor) {
+                    // q_j(x) after j removals; zero once x itself was removed
+                    const int x = s_tok[c];
+                    bool gone = false;
+                    for (int j = 0; j < k; ++j) {
+                        const double qj = gone ? 0.0 : (j == 0 ? qx : qx * s_qs[j]);
+                        const double zj = s_zhist[j];
+                        if (zj > 0.0) {
+                            const double d = prx - qj;
+                            prx = (d > 0.0 ? d : 0.0) / zj;
+                        }
+                        gone |= s_rtok[j] == x;
                     }
+                    const double qk = gone ? 0.0 : (k == 0 ? qx : qx * s_qs[k]);
+                    return s_uacc[c] * qk < prx;
+                } else {
+                    for (int j = 0; j < k; ++j) {
+                        const double zj = s_zhist[j];
+                        if (zj > 0.0) {
+                            const double d = prx - qx;
+                            prx = (d > 0.0 ? d : 0.0) / zj;
+                        }
+                    }
+                    return s_uacc[c] * qx < prx;
                 }
-                return s_uacc[c] * qx < prx;
             };
             auto accept = [&](int c) __attribute__((always_inline)) {
                 if (lead) {
@@ -735,44 +761,87 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             }
             int k = 0;
             bool accepted = false;
+            // without replacement: q_k = qv * sk, where qv holds q with the
+            // removed tokens' entries zeroed
+            double sk = 1.0;
             while (c >= 0) {
                 // rejected: the chunk's residual mass, per wave, then in wave
                 // 0 exchanged with the group and summed in member order
-                double rsum = 0.0;
+                double rsum = 0.0, qrem = 0.0;
+                // without replacement, this thread's entry of the rejected
+                // token, if it holds it: its q leaves the remaining mass now
+                // and its register after the residual pass
+                int ex = -1;
+                if constexpr (kWor) {
+                    const int64_t off = (int64_t)s_tok[c] - base;
+                    if (off >= 0 && off < lim - base && (int)((off % kRun) >> 2) == tid)
+                        ex = (int)((off / kRun) * 4 + (off & 3));
+                }
 #pragma unroll
                 for (int e = 0; e < kSvEpt; ++e) {
-                    const double d = pr[e] - qv[e];
+                    const double d = pr[e] - (kWor ? qv[e] * sk : qv[e]);
                     rsum += d > 0.0 ? d : 0.0;
+                    if constexpr (kWor)
+                        qrem += e == ex ? 0.0 : qv[e];
                 }
                 rsum = wave_sum(rsum);
+                if constexpr (kWor)
+                    qrem = wave_sum(qrem);
                 // (wave 0 read s_wq before the last barrier)
-                if (lane == 0)
+                if (lane == 0) {
                     s_wq[wave] = rsum;
+                    if constexpr (kWor)
+                        s_wq[kSvWaves + wave] = qrem;
+                }
                 __syncthreads();
                 if (wave == 0) {
+                    constexpr int kNW = kWor ? 4 : 2;
                     const double sc = wave_sum(lane < kSvWaves ? s_wq[lane] : 0.0);
-                    const uint32_t mine = lane == 0 ? f64_hi(sc) : lane == 1 ? f64_lo(sc) : 0u;
+                    double sqr = 0.0;
+                    if constexpr (kWor)
+                        sqr = wave_sum(lane < kSvWaves ? s_wq[kSvWaves + lane] : 0.0);
+                    const uint32_t mine = lane == 0   ? f64_hi(sc)
+                                          : lane == 1 ? f64_lo(sc)
+                                          : lane == 2 ? f64_hi(sqr)
+                                          : lane == 3 ? f64_lo(sqr)
+                                                      : 0u;
                     bool ok = true;
-                    uint32_t w2[2] = {f64_hi(sc), f64_lo(sc)};   // member `lane`'s payloads
+                    uint32_t wv[kNW];   // member `lane`'s payloads
+                    wv[0] = f64_hi(sc);
+                    wv[1] = f64_lo(sc);
+                    if constexpr (kWor) {
+                        wv[2] = f64_hi(sqr);
+                        wv[3] = f64_lo(sqr);
+                    }
                     if (wpg > 1)
-                        ok = wave0_exchange<2>(box, wpg, rank, ++gen, mine, s_words, w2);
-                    auto word2 = [&](int m, int i) __attribute__((always_inline)) {
-                        return m == lane ? w2[i] : s_words[m][i];
+                        ok = wave0_exchange<kNW>(box, wpg, rank, ++gen, mine, s_words, wv);
+                    auto wordn = [&](int m, int i) __attribute__((always_inline)) {
+                        return m == lane ? wv[i] : s_words[m][i];
                     };
-                    double Zr = 0.0;
-                    for (int m = lane; m < wpg; m += 64)
-                        Zr += bits_f64(word2(m, 0), word2(m, 1));
+                    double Zr = 0.0, Qr = 0.0;
+                    for (int m = lane; m < wpg; m += 64) {
+                        Zr += bits_f64(wordn(m, 0), wordn(m, 1));
+                        if constexpr (kWor)
+                            Qr += bits_f64(wordn(m, 2), wordn(m, 3));
+                    }
                     Zr = wave_sum(Zr);
+                    if constexpr (kWor)
+                        Qr = wave_sum(Qr);
                     if (Zr > 0.0) {
                         for (int m = lane; m < wpg; m += 64)
-                            s_mass[m] = bits_f64(word2(m, 0), word2(m, 1)) / Zr;
+                            s_mass[m] = bits_f64(wordn(m, 0), wordn(m, 1)) / Zr;
                     }
                     if (lane == 0) {
                         s_zhist[k] = Zr;
+                        if constexpr (kWor) {
+                            // no draft mass left: every later q is zero
+                            s_qs[k + 1] = Qr > 0.0 ? 1.0 / Qr : 0.0;
+                            s_rtok[k] = s_tok[c];
+                        }
                         s_sync_ok = ok;
                     }
                 }
-                __syncthreads();   // s_zhist, s_mass visible
+                __syncthreads();   // s_zhist, s_mass (and s_qs, s_rtok) visible
                 if (!s_sync_ok) {
                     if (tid == 0)
                         raise_flag(a.flags, TAV_FLAG_SYNC_TIMEOUT);
@@ -784,9 +853,16 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     const double inv = 1.0 / Z;
 #pragma unroll
                     for (int e = 0; e < kSvEpt; ++e) {
-                        const double d = pr[e] - qv[e];
+                        const double d = pr[e] - (kWor ? qv[e] * sk : qv[e]);
                         pr[e] = (d > 0.0 ? d : 0.0) * inv;
                     }
+                }
+                if constexpr (kWor) {
+#pragma unroll
+                    for (int e = 0; e < kSvEpt; ++e)
+                        if (e == ex)
+                            qv[e] = 0.0;
+                    sk = s_qs[k + 1];
                 }
                 ++k;
                 c = s_next[c];
@@ -1276,12 +1352,15 @@ bool sv_plan(int32_t B, int32_t V, SvPlan &p)
     // the grid must be resident at once for either kernel (the group syncs
     // wait on each other), so the smaller of their occupancies counts
     int per_cu = 0, per_cu_g = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, spec_verify_kernel, kSvThreads,
-                                                     0) != hipSuccess ||
+    int per_cu_w = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, spec_verify_kernel<false>,
+                                                     kSvThreads, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_w, spec_verify_kernel<true>,
+                                                     kSvThreads, 0) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_g, spec_verify_greedy_kernel,
                                                      kSvThreads, 0) != hipSuccess)
         return false;
-    per_cu = std::min(per_cu, per_cu_g);
+    per_cu = std::min(std::min(per_cu, per_cu_w), per_cu_g);
     if (per_cu <= 0)
         return false;
     const int64_t resident = (int64_t)per_cu * cus;
@@ -1352,12 +1431,13 @@ extern "C" size_t spec_verify_workspace_bytes(int32_t B, int32_t N, int32_t V)
     return kHeaderBytes + p.box_bytes;
 }
 
-extern "C" tav_status spec_verify_sample(const float *target_logits, const float *draft_logits,
-                                         const int32_t *parent, const int32_t *token, int32_t B,
-                                         int32_t N, int32_t V, double temperature, uint64_t seed,
-                                         uint64_t offset, int32_t *path, int32_t *n_accepted,
-                                         int32_t *out_tokens, void *workspace, size_t ws_bytes,
-                                         uint32_t *dev_flags, void *stream)
+namespace {
+
+tav_status sv_launch(const float *target_logits, const float *draft_logits,
+                     const int32_t *parent, const int32_t *token, int32_t B, int32_t N, int32_t V,
+                     double temperature, uint64_t seed, uint64_t offset, int32_t *path,
+                     int32_t *n_accepted, int32_t *out_tokens, void *workspace, size_t ws_bytes,
+                     uint32_t *dev_flags, void *stream, bool wor)
 {
     using namespace tav;
     // temperature 0 selects greedy verification, which reads no draft row
@@ -1402,10 +1482,40 @@ extern "C" tav_status spec_verify_sample(const float *target_logits, const float
     if (greedy)
         hipLaunchKernelGGL(spec_verify_greedy_kernel, dim3(p.wpg * p.ngroups), dim3(kSvThreads), 0,
                            as_stream(stream), a);
+    else if (wor)
+        hipLaunchKernelGGL(spec_verify_kernel<true>, dim3(p.wpg * p.ngroups), dim3(kSvThreads),
+                           0, as_stream(stream), a);
     else
-        hipLaunchKernelGGL(spec_verify_kernel, dim3(p.wpg * p.ngroups), dim3(kSvThreads), 0,
-                           as_stream(stream), a);
+        hipLaunchKernelGGL(spec_verify_kernel<false>, dim3(p.wpg * p.ngroups), dim3(kSvThreads),
+                           0, as_stream(stream), a);
     return hipGetLastError() == hipSuccess ? TAV_OK : TAV_ERR_LAUNCH;
+}
+
+} // namespace
+
+extern "C" tav_status spec_verify_sample(const float *target_logits, const float *draft_logits,
+                                         const int32_t *parent, const int32_t *token, int32_t B,
+                                         int32_t N, int32_t V, double temperature, uint64_t seed,
+                                         uint64_t offset, int32_t *path, int32_t *n_accepted,
+                                         int32_t *out_tokens, void *workspace, size_t ws_bytes,
+                                         uint32_t *dev_flags, void *stream)
+{
+    return sv_launch(target_logits, draft_logits, parent, token, B, N, V, temperature, seed,
+                     offset, path, n_accepted, out_tokens, workspace, ws_bytes, dev_flags, stream,
+                     false);
+}
+
+extern "C" tav_status spec_verify_sample_wor(const float *target_logits,
+                                             const float *draft_logits, const int32_t *parent,
+                                             const int32_t *token, int32_t B, int32_t N,
+                                             int32_t V, double temperature, uint64_t seed,
+                                             uint64_t offset, int32_t *path, int32_t *n_accepted,
+                                             int32_t *out_tokens, void *workspace,
+                                             size_t ws_bytes, uint32_t *dev_flags, void *stream)
+{
+    return sv_launch(target_logits, draft_logits, parent, token, B, N, V, temperature, seed,
+                     offset, path, n_accepted, out_tokens, workspace, ws_bytes, dev_flags, stream,
+                     true);
 }
 
 extern "C" tav_status tav_philox_uniforms(uint64_t seed, uint64_t offset, int32_t B, int32_t N,
