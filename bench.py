@@ -178,41 +178,42 @@ def run_gpu(args, w):
     out = dict(ms_step=ms_step, ms_attn=ms_attn, stage_ms=stage_ms, stage_all=stage,
                step_all=step_ms, depth=to_numpy(depth), path=to_numpy(path), n_acc=to_numpy(n_acc))
 
+    def time_leg(call):
+        """Per-call ms of `call` over `steps` launches, events on the launch stream."""
+        for _ in range(args.warmup):
+            call()
+        evs_ = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for e in evs_:
+            e[0].record(stream)
+            call()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([e[0].elapsed_time(e[1]) for e in evs_])
+
     # greedy verification (temperature 0) of the same batch, timed on its own
-    # with events on the launch stream
     g_path = torch.empty((B, N), dtype=torch.int32, device=dev)
     g_nacc = torch.empty((B,), dtype=torch.int32, device=dev)
     g_toks = torch.empty((B, N), dtype=torch.int32, device=dev)
-    greedy = tav.prepare("spec_verify_sample", d["target_logits"], None, d["parent"], d["token"],
-                         B, N, V, 0.0, 0, 0, g_path, g_nacc, g_toks, ws_s, ws_s_n, flags, stream)
-    for _ in range(args.warmup):
-        greedy()
-    g_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for e in g_evs:
-        e[0].record(stream)
-        greedy()
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    out["greedy_ms"] = np.array([e[0].elapsed_time(e[1]) for e in g_evs])
+    out["greedy_ms"] = time_leg(tav.prepare(
+        "spec_verify_sample", d["target_logits"], None, d["parent"], d["token"], B, N, V, 0.0, 0,
+        0, g_path, g_nacc, g_toks, ws_s, ws_s_n, flags, stream))
     out["greedy_nacc"] = to_numpy(g_nacc)
+
+    # the walk under the without-replacement sibling rule (the trees' siblings
+    # are distinct tokens), same inputs and uniforms as the step's
+    out["wor_ms"] = time_leg(tav.prepare(
+        "spec_verify_sample_wor", d["target_logits"], d["draft_logits"], d["parent"], d["token"],
+        B, N, V, w.temperature, w.philox_seed, w.philox_offset, g_path, g_nacc, g_toks, ws_s,
+        ws_s_n, flags, stream))
+    out["wor_nacc"] = to_numpy(g_nacc)
 
     # the zero-copy rollback on the same paths, timed on its own: it moves
     # rows only inside each sequence's tree positions L..L+N-1, which the
     # attention never reads
-    inplace = tav.prepare("kv_commit_inplace", path, n_acc, nblk, d["block_table"], maxb,
-                          d["prefix_len"], copies[0][0], copies[0][1], B, N, w.Hkv, w.D, w.block,
-                          slots, new_len, flags, stream)
-    for _ in range(args.warmup):
-        inplace()
-    i_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for e in i_evs:
-        e[0].record(stream)
-        inplace()
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    out["inplace_ms"] = np.array([e[0].elapsed_time(e[1]) for e in i_evs])
+    out["inplace_ms"] = time_leg(tav.prepare(
+        "kv_commit_inplace", path, n_acc, nblk, d["block_table"], maxb, d["prefix_len"],
+        copies[0][0], copies[0][1], B, N, w.Hkv, w.D, w.block, slots, new_len, flags, stream))
 
     # tree expansion over every node's draft row (top-4 tokens, log q,
     # entropy): one read of B*N vocabulary rows
@@ -223,18 +224,9 @@ def run_gpu(args, w):
     ex_ent = torch.empty((B * N,), dtype=torch.float64, device=dev)
     ex_ws = torch.empty(tav.tree_expand_workspace_bytes(B * N, V, ex_k), dtype=torch.uint8,
                         device=dev)
-    expand = tav.prepare("tree_expand_topk", ex_rows, B * N, V, ex_k, 1.0, ex_tok, ex_lq, ex_ent,
-                         ex_ws, ex_ws.numel(), flags, stream)
-    for _ in range(args.warmup):
-        expand()
-    x_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for e in x_evs:
-        e[0].record(stream)
-        expand()
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    out["expand_ms"] = np.array([e[0].elapsed_time(e[1]) for e in x_evs])
+    out["expand_ms"] = time_leg(tav.prepare(
+        "tree_expand_topk", ex_rows, B * N, V, ex_k, 1.0, ex_tok, ex_lq, ex_ent, ex_ws,
+        ex_ws.numel(), flags, stream))
     out["expand_rows"] = B * N
 
     # acceptance over many Philox offsets (outside the timed regions): the
@@ -408,6 +400,8 @@ def main():
         "acceptance": acceptance,
         "greedy": {"spec_verify_sample_us": pct(g["greedy_ms"]),
                    "accepted": g["greedy_nacc"].tolist()},
+        "without_replacement": {"spec_verify_sample_wor_us": pct(g["wor_ms"]),
+                                "accepted": g["wor_nacc"].tolist()},
         "kv_commit_inplace_us": pct(g["inplace_ms"]),
         "tree_expand_topk": {"rows": g["expand_rows"], "k": 4, "us": pct(g["expand_ms"]),
                              "hbm_gbs": round(g["expand_rows"] * w.V * 4
