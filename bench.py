@@ -229,6 +229,29 @@ def run_gpu(args, w):
         ex_ws.numel(), flags, stream))
     out["expand_rows"] = B * N
 
+    # the budget step of tree construction: keep 64 of a 357-node candidate
+    # tree per sequence (widths 4, 4, 3, 2, 2) by cumulative log q
+    sel_widths, sel_M = (4, 4, 3, 2, 2), 64
+    sel_par = [-1]
+    sel_depth = [0]
+    i = 0
+    while i < len(sel_par):
+        if sel_depth[i] < len(sel_widths):
+            for _ in range(sel_widths[sel_depth[i]]):
+                sel_par.append(i)
+                sel_depth.append(sel_depth[i] + 1)
+        i += 1
+    Nc = len(sel_par)
+    gen = torch.Generator(device="cpu").manual_seed(17)
+    sel_parent = torch.tensor(sel_par, dtype=torch.int32).repeat(B, 1).to(dev)
+    sel_token = torch.randint(0, V, (B, Nc), generator=gen, dtype=torch.int32).to(dev)
+    sel_logq = torch.log(torch.rand((B, Nc), generator=gen, dtype=torch.float64)).to(dev)
+    sel_out = [torch.empty((B, sel_M), dtype=torch.int32, device=dev) for _ in range(3)]
+    out["select_ms"] = time_leg(tav.prepare(
+        "tree_select_topm", sel_parent, sel_token, sel_logq, B, Nc, sel_M, *sel_out, flags,
+        stream))
+    out["select_shape"] = (B, Nc, sel_M)
+
     # acceptance over many Philox offsets (outside the timed regions): the
     # mean accepted length and the rows the walk visits, for the byte count
     n_off = max(0, args.offsets)
@@ -403,6 +426,8 @@ def main():
         "without_replacement": {"spec_verify_sample_wor_us": pct(g["wor_ms"]),
                                 "accepted": g["wor_nacc"].tolist()},
         "kv_commit_inplace_us": pct(g["inplace_ms"]),
+        "tree_select_topm": {"B": g["select_shape"][0], "Nc": g["select_shape"][1],
+                             "M": g["select_shape"][2], "us": pct(g["select_ms"])},
         "tree_expand_topk": {"rows": g["expand_rows"], "k": 4, "us": pct(g["expand_ms"]),
                              "hbm_gbs": round(g["expand_rows"] * w.V * 4
                                               / (float(np.median(g["expand_ms"])) * 1e-3) / 1e9, 1),

@@ -9,6 +9,7 @@
  *   kv_commit_path      copy the accepted path's K/V into the paged cache
  *   kv_commit_inplace   the same when the tree's K/V already sit in the cache
  *   tree_expand_topk    top-k draft tokens, log q and entropy per frontier row
+ *   tree_select_topm    the budget's best M-node subtree of a candidate tree
  *
  * Conventions for every entry point:
  *   - Pointers are device pointers unless stated otherwise. All tensors are
@@ -337,6 +338,38 @@ tav_status tav_philox_uniforms(uint64_t seed, uint64_t offset, int32_t B, int32_
  */
 tav_status tav_target_probs(const float *logits, int64_t rows, int32_t V, double temperature,
                             double *p, uint32_t *dev_flags, void *stream);
+
+/*
+ * tree_select_topm — the budget step of tree construction: keep the M best
+ * nodes of each candidate tree and renumber them as a tree.
+ *
+ * The budget rule caps the node count and allots branches to maximise the
+ * expected number of accepted tokens (jisaku.com glossary, tree-topology
+ * strategies, budget-constrained optimisation); EAGLE-2 grows the draft
+ * tree dynamically and keeps the most promising paths (LLM Primer ch. 9,
+ * §9.2). A node's acceptance is estimated by the draft as the product of q
+ * along its path: score(0) = 0, score(i) = score(parent[i]) + min(logq[i], 0)
+ * in fp64, one addition per node. The kept set is the M nodes of largest
+ * score, the lower index first among equal scores; since no child scores
+ * above its parent it is a subtree, and it maximises the sum of exp(score)
+ * over all M-node subtrees.
+ *
+ *   parent  int32 [B][Nc] candidate trees (topological, as for every call)
+ *   token   int32 [B][Nc] candidate tokens (copied through, not checked)
+ *   logq    fp64 [B][Nc] log q of node i's token in its parent's draft row
+ *           (e.g. tree_expand_topk's top_logq); entry 0 is ignored; -inf allowed
+ *   out_parent int32 [B][M] out: the kept nodes' parents, as new indices
+ *   out_token  int32 [B][M] out: their tokens
+ *   out_src    int32 [B][M] out: their candidate indices, ascending
+ * The kept nodes keep their relative order, so the output is topological
+ * with the root at 0. 1 <= M <= Nc <= 1024.
+ * Flags: TAV_FLAG_BAD_PARENT, TAV_FLAG_NONFINITE_LOGITS (a NaN log q); the
+ * sequence's outputs are then not written.
+ */
+tav_status tree_select_topm(const int32_t *parent, const int32_t *token, const double *logq,
+                            int32_t B, int32_t Nc, int32_t M, int32_t *out_parent,
+                            int32_t *out_token, int32_t *out_src, uint32_t *dev_flags,
+                            void *stream);
 
 #ifdef __cplusplus
 }

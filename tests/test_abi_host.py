@@ -145,6 +145,23 @@ def test_expand_workspace_sizes():
     assert lib.tree_expand_workspace_bytes(3, 16384, 4) < lib.tree_expand_workspace_bytes(3, 16385, 4)
 
 
+def _select(**kw):
+    args = dict(parent=FAKE, token=FAKE, logq=FAKE, B=2, Nc=100, M=64, op=FAKE, ot=FAKE,
+                src=FAKE, flags=None, stream=None)
+    args.update(kw)
+    return tav.lib().tree_select_topm(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(parent=None), tav.ERR_ARG), (dict(logq=None), tav.ERR_ARG), (dict(src=None), tav.ERR_ARG),
+    (dict(B=0), tav.ERR_ARG), (dict(M=0), tav.ERR_ARG), (dict(M=101), tav.ERR_ARG),
+    (dict(Nc=1025, M=10), tav.ERR_UNSUPPORTED),
+    (dict(logq=ctypes.c_void_p(0x10004)), tav.ERR_ARG),
+])
+def test_select_rejects_bad_arguments(kw, code):
+    assert _select(**kw) == code
+
+
 def test_helpers_reject_bad_arguments():
     lib = tav.lib()
     assert lib.tav_philox_uniforms(0, 0, 1, 1, None, None) == tav.ERR_ARG

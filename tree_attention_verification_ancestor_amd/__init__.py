@@ -74,6 +74,7 @@ _SIGNATURES = {
                                  _P, _P, _P, _P]),
     "tree_expand_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
     "tree_expand_topk": (_I32, [_P, _I64, _I32, _I32, _F64, _P, _P, _P, _P, _SZ, _P, _P]),
+    "tree_select_topm": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "tav_philox_uniforms": (_I32, [_U64, _U64, _I32, _I32, _P, _P]),
     "tav_target_probs": (_I32, [_P, _I64, _I32, _F64, _P, _P, _P]),
 }
@@ -410,3 +411,26 @@ def target_probs(logits: torch.Tensor, temperature: float = 1.0, out=None, dev_f
                                                       _ptr(out), _ptr(dev_flags),
                                                       _stream(stream)))
     return out
+
+
+def tree_select_topm(parent, token, logq, M: int, out_parent=None, out_token=None, out_src=None,
+                     dev_flags=None, stream=None):
+    """Keep the M best nodes of each candidate tree by cumulative log q;
+    returns (out_parent [B,M], out_token [B,M], out_src [B,M])."""
+    _need(parent, "parent", _I32T)
+    B, Nc = parent.shape
+    dev = parent.device
+    _need(token, "token", _I32T, (B, Nc), dev)
+    _need(logq, "logq", (torch.float64,), (B, Nc), dev)
+    if out_parent is None:
+        out_parent = torch.empty((B, M), dtype=torch.int32, device=dev)
+    if out_token is None:
+        out_token = torch.empty((B, M), dtype=torch.int32, device=dev)
+    if out_src is None:
+        out_src = torch.empty((B, M), dtype=torch.int32, device=dev)
+    for t, n in ((out_parent, "out_parent"), (out_token, "out_token"), (out_src, "out_src")):
+        _need(t, n, _I32T, (B, M), dev)
+    _check("tree_select_topm", lib().tree_select_topm(
+        _ptr(parent), _ptr(token), _ptr(logq), B, Nc, int(M), _ptr(out_parent), _ptr(out_token),
+        _ptr(out_src), _ptr(dev_flags), _stream(stream)))
+    return out_parent, out_token, out_src
