@@ -9,6 +9,7 @@ computes, in float64:
   * ``commit``    - the KV commit of the accepted path (copying and in place);
   * ``expand``    - top-k draft tokens, log-probabilities and entropy per row;
   * ``select``    - the budget-constrained top-M subtree by cumulative log q;
+  * ``cost``      - the speedup model and the per-position overhead fit;
   * ``step``      - the four composed.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
@@ -26,4 +27,5 @@ from .sampling import (softmax, philox4x64_10, node_uniforms,  # noqa: F401
 from .commit import kv_commit, kv_commit_inplace  # noqa: F401
 from .expand import expand_topk  # noqa: F401
 from .select import select_topm  # noqa: F401
+from . import cost  # noqa: F401
 from .step import verify_step_ref  # noqa: F401
