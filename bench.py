@@ -43,6 +43,21 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "tree_attn_llama70b_hbm_traffic.
 COPY_BYTES = 1 << 30           # each of the calibration copy's read and write
 
 
+def speedup_model(sizes, size_us):
+    """The pages' speedup model fed by this GPU's step times: alpha from the
+    times at tree sizes 1..N, then the best chain length and its model
+    speedup at acceptance 0.8 and 0.9 with no draft cost."""
+    import tree_attention_verification_ancestor_amd as tav
+
+    alpha = tav.fit_alpha(sizes, size_us)
+    rec = {"n": sizes, "step_us": [round(t, 2) for t in size_us], "alpha": round(alpha, 5),
+           "ceiling": round(1.0 / alpha, 2) if alpha > 0 else None, "best_chain": {}}
+    for p in (0.8, 0.9):
+        n, s = tav.best_chain_length(p, 0.0, alpha, 1024)
+        rec["best_chain"][str(p)] = {"n": n, "speedup": round(s, 3)}
+    return rec
+
+
 def workload_desc(w) -> str:
     return (f"{w.name}: B={w.B}, N={w.N}-node trees, {w.Hq}/{w.Hkv} heads, D={w.D}, "
             f"paged prefix {int(w.prefix_len.min())}..{int(w.prefix_len.max())} "
@@ -252,6 +267,48 @@ def run_gpu(args, w):
         stream))
     out["select_shape"] = (B, Nc, sel_M)
 
+    # the speedup model's overhead per candidate position: the whole step at
+    # tree sizes 1..N, each the first n nodes of the same best-first trees
+    # (a best-first tree's first n nodes are its budget-n tree), timed alone
+    sizes = [n for n in (1, 2, 4, 8, 16, 32, 64, 128, 256) if n <= N]
+    size_us = []
+    for n in sizes:
+        sl = {k: d[k][:, :n].contiguous() for k in ("parent", "token", "q", "k_tree", "v_tree",
+                                                     "target_logits", "draft_logits")}
+        m_n = torch.empty((B, n, (n + 63) // 64), dtype=torch.int64, device=dev)
+        dep_n = torch.empty((B, n), dtype=torch.int32, device=dev)
+        o_n = torch.empty((B, n, w.Hq, w.D), dtype=torch.float32, device=dev)
+        wa = torch.empty(max(1, tav.tree_attn_workspace_bytes(B, n, w.Hq, w.Hkv, w.D,
+                                                              w.max_prefix_len)),
+                         dtype=torch.uint8, device=dev)
+        ws = tav.new_sampler_workspace(B, n, V, dev)
+        pa = torch.empty((B, n), dtype=torch.int32, device=dev)
+        na = torch.empty((B,), dtype=torch.int32, device=dev)
+        tk = torch.empty((B, n), dtype=torch.int32, device=dev)
+        sl_slots = torch.empty((B, n), dtype=torch.int32, device=dev)
+        nl = torch.empty((B,), dtype=torch.int32, device=dev)
+        kc, vc = copies[0]
+        seq = (
+            tav.prepare("tree_mask_build", sl["parent"], B, n, m_n, dep_n, flags, stream),
+            tav.prepare("tree_attn_verify", sl["q"], sl["k_tree"], sl["v_tree"], kc, vc, nblk,
+                        d["block_table"], maxb, d["prefix_len"], w.max_prefix_len, m_n, B, n,
+                        w.Hq, w.Hkv, w.D, w.block, w.scale, o_n, wa, wa.numel(), flags, stream),
+            tav.prepare("spec_verify_sample", sl["target_logits"], sl["draft_logits"],
+                        sl["parent"], sl["token"], B, n, V, w.temperature, w.philox_seed,
+                        w.philox_offset, pa, na, tk, ws, ws.numel(), flags, stream),
+            tav.prepare("kv_commit_path", sl["k_tree"], sl["v_tree"], pa, na, nblk,
+                        d["block_table"], maxb, d["prefix_len"], kc, vc, B, n, w.Hkv, w.D,
+                        w.block, sl_slots, nl, flags, stream),
+        )
+
+        def step_n(seq=seq):
+            for c in seq:
+                c()
+        size_us.append(float(np.median(time_leg(step_n))) * 1e3)
+        del sl, m_n, dep_n, o_n, wa, ws
+    out["size_n"] = sizes
+    out["size_us"] = size_us
+
     # acceptance over many Philox offsets (outside the timed regions): the
     # mean accepted length and the rows the walk visits, for the byte count
     n_off = max(0, args.offsets)
@@ -426,6 +483,7 @@ def main():
         "without_replacement": {"spec_verify_sample_wor_us": pct(g["wor_ms"]),
                                 "accepted": g["wor_nacc"].tolist()},
         "kv_commit_inplace_us": pct(g["inplace_ms"]),
+        "speedup_model": speedup_model(g["size_n"], g["size_us"]),
         "tree_select_topm": {"B": g["select_shape"][0], "Nc": g["select_shape"][1],
                              "M": g["select_shape"][2], "us": pct(g["select_ms"])},
         "tree_expand_topk": {"rows": g["expand_rows"], "k": 4, "us": pct(g["expand_ms"]),

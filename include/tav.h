@@ -10,6 +10,8 @@
  *   kv_commit_inplace   the same when the tree's K/V already sit in the cache
  *   tree_expand_topk    top-k draft tokens, log q and entropy per frontier row
  *   tree_select_topm    the budget's best M-node subtree of a candidate tree
+ *   tav_model_speedup, tav_best_chain_length, tav_fit_alpha
+ *                       the speedup model, on the host, fed by measured times
  *
  * Conventions for every entry point:
  *   - Pointers are device pointers unless stated otherwise. All tensors are
@@ -370,6 +372,31 @@ tav_status tree_select_topm(const int32_t *parent, const int32_t *token, const d
                             int32_t B, int32_t Nc, int32_t M, int32_t *out_parent,
                             int32_t *out_token, int32_t *out_src, uint32_t *dev_flags,
                             void *stream);
+
+/*
+ * The speedup model of a speculative step (LLM Primer ch. 9, §9.3): speedup =
+ * E[emitted] / (T_draft/T_decode + 1 + alpha*N), alpha the verification
+ * overhead per candidate position. Host functions: no device pointer, no
+ * stream, nothing launched.
+ *
+ * tav_model_speedup — that ratio; NaN for n < 0, a negative or NaN argument
+ * or a non-positive denominator.
+ *
+ * tav_best_chain_length — the chain length N in [1, n_max] with the largest
+ * model speedup when each candidate is accepted with probability p, so a
+ * chain emits sum_{i<=N} p^i tokens on average (jisaku.com glossary,
+ * linear-speculation closed form); the smallest such N on ties. Writes the
+ * speedup to *speedup_out if it is not NULL. Returns 0 for p outside [0, 1],
+ * n_max < 1 or a negative or non-finite ratio or alpha.
+ *
+ * tav_fit_alpha — alpha from verification times t_us[k] measured at tree
+ * sizes n[k] (host arrays, count >= 2, n[0] = 1): the least-squares slope of
+ * t(N)/t(1) - 1 against N - 1, through the origin. NaN on bad input.
+ */
+double tav_model_speedup(double expected_emitted, double draft_ratio, double alpha, int32_t n);
+int32_t tav_best_chain_length(double p, double draft_ratio, double alpha, int32_t n_max,
+                              double *speedup_out);
+double tav_fit_alpha(const int32_t *n, const double *t_us, int32_t count);
 
 #ifdef __cplusplus
 }

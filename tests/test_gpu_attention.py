@@ -30,6 +30,10 @@ CASES = [
     dict(N=6, B=3, Hq=32, Hkv=8, D=128, L=(2048, 2048), tree="chain"),
     dict(N=20, B=2, Hq=8, Hkv=2, D=128, L=(1000, 1100), tree="random"),    # 80 rows: 4 waves x 32
     dict(N=48, B=1, Hq=64, Hkv=8, D=64, L=(513, 700), tree="random"),      # 384 rows, D=64, 2 row blocks
+    # the small trees of the tree-size sweep at 70B-shaped heads (8 to 32 rows)
+    dict(N=1, B=2, Hq=64, Hkv=8, D=128, L=(700, 900), tree="chain"),
+    dict(N=2, B=2, Hq=64, Hkv=8, D=128, L=(700, 900), tree="chain"),
+    dict(N=4, B=2, Hq=64, Hkv=8, D=128, L=(300, 1500), tree="random"),
 ]
 
 

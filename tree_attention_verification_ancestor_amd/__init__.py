@@ -75,6 +75,9 @@ _SIGNATURES = {
     "tree_expand_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
     "tree_expand_topk": (_I32, [_P, _I64, _I32, _I32, _F64, _P, _P, _P, _P, _SZ, _P, _P]),
     "tree_select_topm": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
+    "tav_model_speedup": (ctypes.c_double, [_F64, _F64, _F64, _I32]),
+    "tav_best_chain_length": (_I32, [_F64, _F64, _F64, _I32, _P]),
+    "tav_fit_alpha": (ctypes.c_double, [_P, _P, _I32]),
     "tav_philox_uniforms": (_I32, [_U64, _U64, _I32, _I32, _P, _P]),
     "tav_target_probs": (_I32, [_P, _I64, _I32, _F64, _P, _P, _P]),
 }
@@ -434,3 +437,25 @@ def tree_select_topm(parent, token, logq, M: int, out_parent=None, out_token=Non
         _ptr(parent), _ptr(token), _ptr(logq), B, Nc, int(M), _ptr(out_parent), _ptr(out_token),
         _ptr(out_src), _ptr(dev_flags), _stream(stream)))
     return out_parent, out_token, out_src
+
+
+def model_speedup(expected_emitted: float, draft_ratio: float, alpha: float, n: int) -> float:
+    """E[emitted] / (T_draft/T_decode + 1 + alpha * N) (NaN on bad input)."""
+    return float(lib().tav_model_speedup(float(expected_emitted), float(draft_ratio),
+                                         float(alpha), int(n)))
+
+
+def best_chain_length(p: float, draft_ratio: float, alpha: float, n_max: int):
+    """(N, speedup) of the best chain length under the model; N = 0 on bad input."""
+    s = ctypes.c_double(float("nan"))
+    n = int(lib().tav_best_chain_length(float(p), float(draft_ratio), float(alpha), int(n_max),
+                                        ctypes.byref(s)))
+    return n, s.value
+
+
+def fit_alpha(n_values, t_us) -> float:
+    """Per-position verification overhead from times t_us measured at tree
+    sizes n_values (the first must be 1)."""
+    n = (ctypes.c_int32 * len(n_values))(*[int(x) for x in n_values])
+    t = (ctypes.c_double * len(t_us))(*[float(x) for x in t_us])
+    return float(lib().tav_fit_alpha(n, t, len(n_values)))
