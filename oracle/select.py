@@ -58,3 +58,31 @@ def select_topm(parent, token, logq, M: int):
             out_token[b, j] = tok[b, old]
             out_parent[b, j] = -1 if old == 0 else new[int(par[b, old])]
     return out_parent, out_token, out_src
+
+
+def widths_by_entropy(entropy, w_min: int, w_max: int):
+    """Entropy-based branching widths for one frontier per row.
+
+    jisaku.com glossary, tree-topology strategies (entropy-based branching):
+    a node whose draft distribution has higher entropy gets more branches.
+    Reading: the frontier nodes of a row are ranked by entropy, ascending
+    (the lower index first among equal entropies); the node of rank r among
+    F gets w_min + floor((w_max - w_min + 1) * r / F) branches, so with
+    widths 1..4 each quartile of the frontier gets one width.
+
+    entropy float64 [B, F] -> int32 [B, F]. Raises ValueError on a NaN or
+    w_min > w_max or w_min < 0.
+    """
+    h = np.asarray(entropy, dtype=np.float64)
+    if not 0 <= w_min <= w_max:
+        raise ValueError("need 0 <= w_min <= w_max")
+    if np.isnan(h).any():
+        raise ValueError("NaN entropy")
+    B, F = h.shape
+    out = np.empty((B, F), np.int32)
+    span = w_max - w_min + 1
+    for b in range(B):
+        order = sorted(range(F), key=lambda i: (h[b, i], i))
+        for r, i in enumerate(order):
+            out[b, i] = w_min + (span * r) // F
+    return out

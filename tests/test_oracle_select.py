@@ -186,3 +186,35 @@ def test_invalid_inputs_raise():
         oracle.select_topm(np.array([[-1, 2, 0]]), par, np.zeros((1, 3)), 2)
     with pytest.raises(ValueError):
         oracle.select_topm(par, par, np.array([[0.0, np.nan, 0.0]]), 2)
+
+
+# ---- entropy-ranked widths -------------------------------------------------
+
+def test_widths_split_the_frontier_into_equal_rank_groups():
+    """With F a multiple of the number of widths, each width goes to exactly
+    F / span nodes, and a node never gets fewer branches than one of lower
+    entropy (the glossary's entropy-based branching)."""
+    rng = np.random.default_rng(7)
+    for F, (lo, hi) in [(8, (1, 4)), (40, (1, 4)), (12, (2, 3)), (30, (0, 2))]:
+        h = rng.exponential(2.0, (5, F))
+        w = oracle.widths_by_entropy(h, lo, hi)
+        for b in range(5):
+            counts = np.bincount(w[b] - lo, minlength=hi - lo + 1)
+            assert (counts == F // (hi - lo + 1)).all()
+            order = np.argsort(h[b], kind="stable")
+            assert (np.diff(w[b][order]) >= 0).all()
+
+
+def test_widths_special_cases():
+    assert oracle.widths_by_entropy(np.array([[3.0]]), 1, 4).tolist() == [[1]]
+    # equal entropies: rank by index
+    assert oracle.widths_by_entropy(np.zeros((1, 4)), 1, 4).tolist() == [[1, 2, 3, 4]]
+    assert oracle.widths_by_entropy(np.array([[5.0, 1.0, 3.0, 2.0]]), 1, 4).tolist() == [[4, 1, 3, 2]]
+    # a constant width when w_min == w_max
+    assert (oracle.widths_by_entropy(np.random.default_rng(1).random((2, 9)), 3, 3) == 3).all()
+    # F = 5 over 4 widths: ranks 0..4 -> 1 + floor(4 r / 5) = 1, 1, 2, 3, 4
+    assert sorted(oracle.widths_by_entropy(np.arange(5.0)[None], 1, 4)[0].tolist()) == [1, 1, 2, 3, 4]
+    with pytest.raises(ValueError):
+        oracle.widths_by_entropy(np.array([[np.nan, 1.0]]), 1, 4)
+    with pytest.raises(ValueError):
+        oracle.widths_by_entropy(np.zeros((1, 2)), 3, 2)
