@@ -267,6 +267,12 @@ def run_gpu(args, w):
         stream))
     out["select_shape"] = (B, Nc, sel_M)
 
+    # entropy-ranked widths (1..4) for a 64-node frontier per sequence
+    wid_h = (torch.rand((B, 64), generator=gen, dtype=torch.float64) * 5).to(dev)
+    wid_out = torch.empty((B, 64), dtype=torch.int32, device=dev)
+    out["widths_ms"] = time_leg(tav.prepare("tree_widths_by_entropy", wid_h, B, 64, 1, 4, wid_out,
+                                            flags, stream))
+
     # the speedup model's overhead per candidate position: the whole step at
     # tree sizes 1..N, each the first n nodes of the same best-first trees
     # (a best-first tree's first n nodes are its budget-n tree), timed alone
@@ -484,6 +490,7 @@ def main():
                                 "accepted": g["wor_nacc"].tolist()},
         "kv_commit_inplace_us": pct(g["inplace_ms"]),
         "speedup_model": speedup_model(g["size_n"], g["size_us"]),
+        "tree_widths_by_entropy": {"B": w.B, "F": 64, "us": pct(g["widths_ms"])},
         "tree_select_topm": {"B": g["select_shape"][0], "Nc": g["select_shape"][1],
                              "M": g["select_shape"][2], "us": pct(g["select_ms"])},
         "tree_expand_topk": {"rows": g["expand_rows"], "k": 4, "us": pct(g["expand_ms"]),

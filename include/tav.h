@@ -10,6 +10,7 @@
  *   kv_commit_inplace   the same when the tree's K/V already sit in the cache
  *   tree_expand_topk    top-k draft tokens, log q and entropy per frontier row
  *   tree_select_topm    the budget's best M-node subtree of a candidate tree
+ *   tree_widths_by_entropy  branching widths from the frontier's entropy ranks
  *   tav_model_speedup, tav_best_chain_length, tav_fit_alpha
  *                       the speedup model, on the host, fed by measured times
  *
@@ -372,6 +373,23 @@ tav_status tree_select_topm(const int32_t *parent, const int32_t *token, const d
                             int32_t B, int32_t Nc, int32_t M, int32_t *out_parent,
                             int32_t *out_token, int32_t *out_src, uint32_t *dev_flags,
                             void *stream);
+
+/*
+ * tree_widths_by_entropy — entropy-based branching: a frontier node whose
+ * draft distribution has higher entropy gets more branches (jisaku.com
+ * glossary, tree-topology strategies). The F frontier nodes of row b are
+ * ranked by entropy, ascending, the lower index first among equal values;
+ * the node of rank r gets w_min + floor((w_max - w_min + 1) * r / F)
+ * branches, so with widths 1..4 each quartile of the frontier gets one width.
+ *
+ *   entropy  fp64 [B][F] (e.g. tree_expand_topk's entropy of the frontier rows)
+ *   width    int32 [B][F] out
+ * 1 <= F <= 1024, 0 <= w_min <= w_max. Flags: TAV_FLAG_NONFINITE_LOGITS (a
+ * NaN entropy; the row's widths are then not written).
+ */
+tav_status tree_widths_by_entropy(const double *entropy, int32_t B, int32_t F, int32_t w_min,
+                                  int32_t w_max, int32_t *width, uint32_t *dev_flags,
+                                  void *stream);
 
 /*
  * The speedup model of a speculative step (LLM Primer ch. 9, §9.3): speedup =

@@ -162,6 +162,17 @@ def test_select_rejects_bad_arguments(kw, code):
     assert _select(**kw) == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(h=None), tav.ERR_ARG), (dict(w=None), tav.ERR_ARG), (dict(B=0), tav.ERR_ARG),
+    (dict(F=0), tav.ERR_ARG), (dict(lo=-1), tav.ERR_ARG), (dict(lo=3, hi=2), tav.ERR_ARG),
+    (dict(F=1025), tav.ERR_UNSUPPORTED), (dict(h=ctypes.c_void_p(0x10004)), tav.ERR_ARG),
+])
+def test_widths_reject_bad_arguments(kw, code):
+    args = dict(h=FAKE, B=2, F=16, lo=1, hi=4, w=FAKE, flags=None, stream=None)
+    args.update(kw)
+    assert tav.lib().tree_widths_by_entropy(*args.values()) == code
+
+
 def test_helpers_reject_bad_arguments():
     lib = tav.lib()
     assert lib.tav_philox_uniforms(0, 0, 1, 1, None, None) == tav.ERR_ARG

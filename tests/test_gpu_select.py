@@ -1,6 +1,7 @@
-"""GPU parity: tree_select_topm (budget-constrained top-M subtree) against
-the oracle, bit for bit, and the construction pipeline tree_expand_topk ->
-tree_select_topm against the oracle's expand_topk -> select_topm."""
+"""GPU parity: tree_select_topm (budget-constrained top-M subtree) and
+tree_widths_by_entropy (entropy-ranked branching) against the oracle, bit
+for bit, and the construction pipeline tree_expand_topk -> tree_select_topm
+(and -> widths) against the oracle's."""
 
 import numpy as np
 import pytest
@@ -142,3 +143,59 @@ def test_expand_then_select_pipeline():
             np.testing.assert_array_equal(src[b], rs[b])
             np.testing.assert_array_equal(op[b], rp[b])
             np.testing.assert_array_equal(ot[b], rtk[b])
+
+
+# ---- entropy-ranked widths ---------------------------------------------------
+
+def _widths(h, lo, hi):
+    dev = device()
+    flags = tav.new_flags(dev)
+    w = tav.tree_widths_by_entropy(torch.from_numpy(np.ascontiguousarray(h)).to(dev), lo, hi,
+                                   dev_flags=flags)
+    torch.cuda.synchronize()
+    return to_numpy(w), int(flags.item())
+
+
+@pytest.mark.parametrize("B,F,lo,hi", [
+    (4, 1, 1, 4), (8, 7, 1, 4), (8, 64, 1, 4), (4, 65, 2, 5), (16, 200, 1, 4), (3, 513, 0, 7),
+    (2, 1024, 1, 4), (64, 16, 1, 1),
+])
+def test_widths_match_oracle(B, F, lo, hi):
+    say(f"widths: B={B} F={F} w={lo}..{hi}")
+    rng = np.random.default_rng(F * 10 + lo)
+    h = np.round(rng.exponential(2.0, (B, F)) * 4) / 4     # coarse: many equal entropies
+    h[rng.random((B, F)) < 0.05] = np.inf
+    w, flags = _widths(h, lo, hi)
+    assert flags == 0
+    np.testing.assert_array_equal(w, oracle.widths_by_entropy(h, lo, hi))
+
+
+def test_widths_from_expansion_entropy():
+    """Entropies from tree_expand_topk on the GPU against the oracle's
+    expand_topk, ranked on both sides; a row may differ only where two
+    entropies are within the expansion's tolerance of each other."""
+    say("widths: from expansion entropies")
+    rng = np.random.default_rng(31)
+    B, F, V = 8, 24, 4096
+    rows = (rng.standard_normal((B * F, V)) * rng.uniform(0.5, 4, (B * F, 1))).astype(np.float32)
+    dev = device()
+    _, _, ent = tav.tree_expand_topk(torch.from_numpy(rows).to(dev), 4, 1.0)
+    w, flags = _widths(to_numpy(ent).reshape(B, F), 1, 4)
+    assert flags == 0
+    _, _, r_ent = oracle.expand_topk(rows, 4, 1.0)
+    r_ent = r_ent.reshape(B, F)
+    ref = oracle.widths_by_entropy(r_ent, 1, 4)
+    compared = 0
+    for b in range(B):
+        gaps = np.diff(np.sort(r_ent[b]))
+        if gaps.min() > 1e-4:
+            np.testing.assert_array_equal(w[b], ref[b])
+            compared += 1
+    assert compared == B   # these inputs leave every row's entropies well apart
+
+
+def test_widths_flag_nan():
+    h = np.zeros((1, 5))
+    h[0, 3] = np.nan
+    _, flags = _widths(h, 1, 4)
+    assert flags == 0x4

@@ -75,6 +75,7 @@ _SIGNATURES = {
     "tree_expand_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
     "tree_expand_topk": (_I32, [_P, _I64, _I32, _I32, _F64, _P, _P, _P, _P, _SZ, _P, _P]),
     "tree_select_topm": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
+    "tree_widths_by_entropy": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "tav_model_speedup": (ctypes.c_double, [_F64, _F64, _F64, _I32]),
     "tav_best_chain_length": (_I32, [_F64, _F64, _F64, _I32, _P]),
     "tav_fit_alpha": (ctypes.c_double, [_P, _P, _I32]),
@@ -437,6 +438,22 @@ def tree_select_topm(parent, token, logq, M: int, out_parent=None, out_token=Non
         _ptr(parent), _ptr(token), _ptr(logq), B, Nc, int(M), _ptr(out_parent), _ptr(out_token),
         _ptr(out_src), _ptr(dev_flags), _stream(stream)))
     return out_parent, out_token, out_src
+
+
+def tree_widths_by_entropy(entropy, w_min: int, w_max: int, width=None, dev_flags=None,
+                           stream=None):
+    """Branching widths from the entropy rank of each frontier node;
+    entropy fp64 [B, F] -> width int32 [B, F]."""
+    _need(entropy, "entropy", (torch.float64,))
+    B, F = entropy.shape
+    dev = entropy.device
+    if width is None:
+        width = torch.empty((B, F), dtype=torch.int32, device=dev)
+    _need(width, "width", _I32T, (B, F), dev)
+    _check("tree_widths_by_entropy", lib().tree_widths_by_entropy(
+        _ptr(entropy), B, F, int(w_min), int(w_max), _ptr(width), _ptr(dev_flags),
+        _stream(stream)))
+    return width
 
 
 def model_speedup(expected_emitted: float, draft_ratio: float, alpha: float, n: int) -> float:

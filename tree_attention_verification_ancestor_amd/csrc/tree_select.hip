@@ -1,4 +1,5 @@
-// tree_select_topm: keep the M best nodes of a candidate tree, renumbered.
+// tree_select_topm: keep the M best nodes of a candidate tree, renumbered;
+// tree_widths_by_entropy: branching widths from the frontier's entropy ranks.
 //
 // The budget rule of tree construction (jisaku.com glossary, tree-topology
 // strategies, budget-constrained optimisation) caps the node count and
@@ -26,6 +27,49 @@ namespace tav {
 namespace {
 
 constexpr int kSelThreads = 1024;
+
+// Nodes ahead of node n among the scores s[0, W) (padded past the real
+// count with values that never count), over the share [j_begin, j_end) of
+// them: descending order counts #{j < n: s_j >= s_n} + #{j > n: s_j > s_n},
+// ascending the mirror image. Sixteen scores per step, as eight 16-byte LDS
+// reads that every lane of the wave shares; a block wholly below or above
+// the wave's 64 nodes needs one comparison per score.
+template <bool kDescending>
+__device__ __forceinline__ int count_ahead(const double *s, int n, double sn, int j_begin,
+                                           int j_end)
+{
+    auto before = [&](double v) __attribute__((always_inline)) {   // j < n
+        return kDescending ? v >= sn : v <= sn;
+    };
+    auto after = [&](double v) __attribute__((always_inline)) {    // j > n
+        return kDescending ? v > sn : v < sn;
+    };
+    const int w0 = n & ~63;
+    int r = 0;
+    for (int j0 = j_begin; j0 < j_end; j0 += 16) {
+        double2 v[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            v[t] = *reinterpret_cast<const double2 *>(&s[j0 + 2 * t]);
+        if (j0 + 16 <= w0) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                r += (int)before(v[t].x) + (int)before(v[t].y);
+        } else if (j0 >= w0 + 64) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                r += (int)after(v[t].x) + (int)after(v[t].y);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int j = j0 + 2 * t;
+                r += (int)(j < n ? before(v[t].x) : after(v[t].x));
+                r += (int)(j + 1 < n ? before(v[t].y) : after(v[t].y));
+            }
+        }
+    }
+    return r;
+}
 
 __global__ __launch_bounds__(kSelThreads) void tree_select_kernel(
     const int32_t *__restrict__ parent, const int32_t *__restrict__ token,
@@ -98,42 +142,14 @@ __global__ __launch_bounds__(kSelThreads) void tree_select_kernel(
         __syncthreads();
     }
 
-    // rank of node n: the nodes ahead of it, #{j < n: s_j >= s_n} +
-    // #{j > n: s_j > s_n}. The workgroup holds blockDim / W threads per node,
-    // each counting one contiguous share of j. Sixteen scores per step, read
-    // as eight 16-byte LDS reads that every lane of the wave shares; a block
-    // wholly below or above the wave's 64 nodes takes one comparison per
-    // score.
+    // rank of node n: the nodes ahead of it, counted by blockDim / W
+    // threads per node over contiguous shares of the scores
     {
         const int n = i % W;
         const int part = i / W;
         const int share = W / (blockDim.x / W);
-        const int w0 = n & ~63;
-        const double sn = s_score[n];   // -inf past Nc
-        int r = 0;
-        for (int j0 = part * share; j0 < (part + 1) * share; j0 += 16) {
-            double2 v[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-                v[t] = *reinterpret_cast<const double2 *>(&s_score[j0 + 2 * t]);
-            if (j0 + 16 <= w0) {
-#pragma unroll
-                for (int t = 0; t < 8; ++t)
-                    r += (int)(v[t].x >= sn) + (int)(v[t].y >= sn);
-            } else if (j0 >= w0 + 64) {
-#pragma unroll
-                for (int t = 0; t < 8; ++t)
-                    r += (int)(v[t].x > sn) + (int)(v[t].y > sn);
-            } else {
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const int j = j0 + 2 * t;
-                    r += (int)(j < n ? v[t].x >= sn : v[t].x > sn);
-                    r += (int)(j + 1 < n ? v[t].y >= sn : v[t].y > sn);
-                }
-            }
-        }
-        atomicAdd(&s_rank[n], r);
+        atomicAdd(&s_rank[n],
+                  count_ahead<true>(s_score, n, s_score[n], part * share, (part + 1) * share));
     }
     __syncthreads();
     const bool sel = live && s_rank[i] < M;
@@ -156,6 +172,56 @@ __global__ __launch_bounds__(kSelThreads) void tree_select_kernel(
     }
 }
 
+// Entropy-ranked widths: one workgroup per frontier, the same rank counts
+// in ascending order; width = w_min + span * rank / F.
+__global__ __launch_bounds__(kSelThreads) void widths_kernel(const double *__restrict__ entropy,
+                                                             int32_t F, int32_t w_min,
+                                                             int32_t span,
+                                                             int32_t *__restrict__ width,
+                                                             uint32_t *flags)
+{
+    __shared__ __align__(16) double s_h[kSelThreads];
+    __shared__ int32_t s_rank[kSelThreads];
+    __shared__ int s_bad;
+    const int b = blockIdx.x;
+    const int i = threadIdx.x;
+    const int W = ((F + 63) >> 6) * 64;
+    if (i == 0)
+        s_bad = 0;
+    if (i < W) {
+        // past F: +inf at a higher index than any node, never ahead of one
+        const double h = i < F ? entropy[(int64_t)b * F + i] : INFINITY;
+        s_h[i] = h;
+        s_rank[i] = 0;
+    }
+    __syncthreads();
+    if (i < F && __builtin_isnan(s_h[i]))
+        atomicOr(&s_bad, 1);
+    __syncthreads();
+    if (s_bad) {
+        if (i == 0)
+            raise_flag(flags, TAV_FLAG_NONFINITE_LOGITS);
+        return;
+    }
+    {
+        const int n = i % W;
+        const int part = i / W;
+        const int share = W / (blockDim.x / W);
+        atomicAdd(&s_rank[n], count_ahead<false>(s_h, n, s_h[n], part * share, (part + 1) * share));
+    }
+    __syncthreads();
+    if (i < F)
+        width[(int64_t)b * F + i] = w_min + (int32_t)(((int64_t)span * s_rank[i]) / F);
+}
+
+int rank_threads(int32_t n)
+{
+    // a thread per node (whole waves), and up to four per node for the
+    // rank counts while they fit in 1024
+    const int W = (int)ceil_div(n, 64) * 64;
+    return W * (W <= 256 ? 4 : W <= 512 ? 2 : 1);
+}
+
 } // namespace
 } // namespace tav
 
@@ -174,11 +240,23 @@ extern "C" tav_status tree_select_topm(const int32_t *parent, const int32_t *tok
     if (!aligned(parent, 4) || !aligned(token, 4) || !aligned(logq, 8) ||
         !aligned(out_parent, 4) || !aligned(out_token, 4) || !aligned(out_src, 4))
         return TAV_ERR_ARG;
-    // one thread per node (W of them, Nc rounded up to whole waves), and
-    // up to four per node for the rank counts while they fit in 1024
-    const int W = (int)ceil_div(Nc, 64) * 64;
-    const int threads = W * (W <= 256 ? 4 : W <= 512 ? 2 : 1);
-    hipLaunchKernelGGL(tree_select_kernel, dim3(B), dim3(threads), 0, as_stream(stream), parent,
-                       token, logq, Nc, M, out_parent, out_token, out_src, dev_flags);
+    hipLaunchKernelGGL(tree_select_kernel, dim3(B), dim3(rank_threads(Nc)), 0, as_stream(stream),
+                       parent, token, logq, Nc, M, out_parent, out_token, out_src, dev_flags);
+    return hipGetLastError() == hipSuccess ? TAV_OK : TAV_ERR_LAUNCH;
+}
+
+extern "C" tav_status tree_widths_by_entropy(const double *entropy, int32_t B, int32_t F,
+                                             int32_t w_min, int32_t w_max, int32_t *width,
+                                             uint32_t *dev_flags, void *stream)
+{
+    using namespace tav;
+    if (!entropy || !width || B < 1 || F < 1 || w_min < 0 || w_max < w_min)
+        return TAV_ERR_ARG;
+    if (F > kSelThreads)
+        return TAV_ERR_UNSUPPORTED;
+    if (!aligned(entropy, 8) || !aligned(width, 4))
+        return TAV_ERR_ARG;
+    hipLaunchKernelGGL(widths_kernel, dim3(B), dim3(rank_threads(F)), 0, as_stream(stream),
+                       entropy, F, w_min, w_max - w_min + 1, width, dev_flags);
     return hipGetLastError() == hipSuccess ? TAV_OK : TAV_ERR_LAUNCH;
 }
