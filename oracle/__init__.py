@@ -7,7 +7,8 @@ computes, in float64:
   * ``sampling``  - softmax of target/draft logits, Philox4x64-10 uniforms and
                     the root-down rejection-sampling walk (plain C, fp64);
   * ``commit``    - the KV commit of the accepted path (copying and in place);
-  * ``expand``    - top-k draft tokens, log-probabilities and entropy per row;
+  * ``expand``    - top-k (or sampled without replacement) draft tokens,
+                    log-probabilities and entropy per row;
   * ``select``    - the budget-constrained top-M subtree by cumulative log q,
                     and entropy-ranked branching widths;
   * ``cost``      - the speedup model and the per-position overhead fit;
@@ -26,7 +27,7 @@ from .attention import tree_attention, bf16_bits_to_f64  # noqa: F401
 from .sampling import (softmax, philox4x64_10, node_uniforms,  # noqa: F401
                        verify_walk, verify_greedy, WalkResult)
 from .commit import kv_commit, kv_commit_inplace  # noqa: F401
-from .expand import expand_topk  # noqa: F401
+from .expand import expand_topk, expand_sample, gumbel_keys  # noqa: F401
 from .select import select_topm, widths_by_entropy  # noqa: F401
 from . import cost  # noqa: F401
 from .step import verify_step_ref  # noqa: F401
