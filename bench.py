@@ -243,6 +243,10 @@ def run_gpu(args, w):
         "tree_expand_topk", ex_rows, B * N, V, ex_k, 1.0, ex_tok, ex_lq, ex_ent, ex_ws,
         ex_ws.numel(), flags, stream))
     out["expand_rows"] = B * N
+    # the same rows with the k tokens drawn without replacement
+    out["expand_sample_ms"] = time_leg(tav.prepare(
+        "tree_expand_sample", ex_rows, B * N, V, ex_k, 1.0, w.philox_seed, w.philox_offset,
+        ex_tok, ex_lq, ex_ent, ex_ws, ex_ws.numel(), flags, stream))
 
     # the budget step of tree construction: keep 64 of a 357-node candidate
     # tree per sequence (widths 4, 4, 3, 2, 2) by cumulative log q
@@ -491,6 +495,7 @@ def main():
         "kv_commit_inplace_us": pct(g["inplace_ms"]),
         "speedup_model": speedup_model(g["size_n"], g["size_us"]),
         "tree_widths_by_entropy": {"B": w.B, "F": 64, "us": pct(g["widths_ms"])},
+        "tree_expand_sample": {"rows": g["expand_rows"], "k": 4, "us": pct(g["expand_sample_ms"])},
         "tree_select_topm": {"B": g["select_shape"][0], "Nc": g["select_shape"][1],
                              "M": g["select_shape"][2], "us": pct(g["select_ms"])},
         "tree_expand_topk": {"rows": g["expand_rows"], "k": 4, "us": pct(g["expand_ms"]),

@@ -9,6 +9,7 @@
  *   kv_commit_path      copy the accepted path's K/V into the paged cache
  *   kv_commit_inplace   the same when the tree's K/V already sit in the cache
  *   tree_expand_topk    top-k draft tokens, log q and entropy per frontier row
+ *   tree_expand_sample  the same with the k tokens drawn without replacement
  *   tree_select_topm    the budget's best M-node subtree of a candidate tree
  *   tree_widths_by_entropy  branching widths from the frontier's entropy ranks
  *   tav_model_speedup, tav_best_chain_length, tav_fit_alpha
@@ -341,6 +342,28 @@ tav_status tav_philox_uniforms(uint64_t seed, uint64_t offset, int32_t B, int32_
  */
 tav_status tav_target_probs(const float *logits, int64_t rows, int32_t V, double temperature,
                             double *p, uint32_t *dev_flags, void *stream);
+
+/*
+ * tree_expand_sample — tree_expand_topk for a sampled tree: the k tokens of
+ * each row are drawn from q = softmax(row / T) without replacement, the
+ * order of the draws kept, so a tree grown from them is one for which
+ * spec_verify_sample_wor is lossless. The glossary's top-k branching
+ * (jisaku.com glossary, tree-topology strategies) with the k most likely
+ * tokens replaced by k draws; the draw is the Gumbel-top-k construction:
+ * each token gets the key fl32(fl32(x * fl32(1/T)) + fl32(G)), G = -log(-log
+ * u) in fp64 with u = ((w >> 11) + 1/2) * 2^-53 from Philox4x64-10 word
+ * (token mod 4) at counter (offset, row, token / 4, 1) under key (seed, 0)
+ * (the node uniforms of spec_verify_sample use counter word 3 = 0), and the
+ * k largest keys, the lower token first among equal keys, are the draws in
+ * order. Keys are rounded to fp32, so the draw follows q to about 1e-6
+ * relative. top_logq and entropy are as in tree_expand_topk; arguments,
+ * workspace (tree_expand_workspace_bytes), limits and flags too.
+ */
+tav_status tree_expand_sample(const float *draft_logits, int64_t R, int32_t V, int32_t k,
+                              double temperature, uint64_t seed, uint64_t offset,
+                              int32_t *top_token, double *top_logq, double *entropy,
+                              void *workspace, size_t ws_bytes, uint32_t *dev_flags,
+                              void *stream);
 
 /*
  * tree_select_topm — the budget step of tree construction: keep the M best

@@ -138,6 +138,18 @@ def test_expand_rejects_bad_arguments(kw, code):
     assert _expand(**kw) == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), tav.ERR_ARG), (dict(R=0), tav.ERR_ARG), (dict(k=0), tav.ERR_ARG),
+    (dict(T=0.0), tav.ERR_ARG), (dict(k=17, V=5000), tav.ERR_UNSUPPORTED),
+    (dict(ws=None), tav.ERR_WORKSPACE),
+])
+def test_sampled_expand_rejects_bad_arguments(kw, code):
+    args = dict(x=FAKE, R=4, V=1000, k=4, T=1.0, seed=1, offset=2, tok=FAKE, logq=FAKE, ent=FAKE,
+                ws=FAKE, ws_bytes=1 << 20, flags=None, stream=None)
+    args.update(kw)
+    assert tav.lib().tree_expand_sample(*args.values()) == code
+
+
 def test_expand_workspace_sizes():
     lib = tav.lib()
     assert lib.tree_expand_workspace_bytes(0, 100, 4) == 0

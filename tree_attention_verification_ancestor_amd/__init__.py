@@ -74,6 +74,7 @@ _SIGNATURES = {
                                  _P, _P, _P, _P]),
     "tree_expand_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
     "tree_expand_topk": (_I32, [_P, _I64, _I32, _I32, _F64, _P, _P, _P, _P, _SZ, _P, _P]),
+    "tree_expand_sample": (_I32, [_P, _I64, _I32, _I32, _F64, _U64, _U64, _P, _P, _P, _P, _SZ, _P, _P]),
     "tree_select_topm": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "tree_widths_by_entropy": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "tav_model_speedup": (ctypes.c_double, [_F64, _F64, _F64, _I32]),
@@ -368,6 +369,12 @@ def tree_expand_topk(draft_logits, k: int, temperature: float = 1.0, top_token=N
     """Top-k draft tokens, their log q and the entropy of every row of
     draft_logits fp32 [R, V]; returns (top_token int32 [R, k], top_logq
     float64 [R, k], entropy float64 [R])."""
+    return _expand(draft_logits, k, temperature, top_token, top_logq, entropy, workspace,
+                   dev_flags, stream, None)
+
+
+def _expand(draft_logits, k, temperature, top_token, top_logq, entropy, workspace, dev_flags,
+            stream, sample):
     _need(draft_logits, "draft_logits", (torch.float32,))
     if draft_logits.dim() != 2:
         raise ValueError("draft_logits must be [R, V]")
@@ -386,10 +393,27 @@ def tree_expand_topk(draft_logits, k: int, temperature: float = 1.0, top_token=N
         n = tree_expand_workspace_bytes(R, V, k)
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check("tree_expand_topk", lib().tree_expand_topk(
-        _ptr(draft_logits), R, V, int(k), float(temperature), _ptr(top_token), _ptr(top_logq),
-        _ptr(entropy), _ptr(workspace), ws_bytes, _ptr(dev_flags), _stream(stream)))
+    if sample is None:
+        _check("tree_expand_topk", lib().tree_expand_topk(
+            _ptr(draft_logits), R, V, int(k), float(temperature), _ptr(top_token),
+            _ptr(top_logq), _ptr(entropy), _ptr(workspace), ws_bytes, _ptr(dev_flags),
+            _stream(stream)))
+    else:
+        seed, offset = sample
+        _check("tree_expand_sample", lib().tree_expand_sample(
+            _ptr(draft_logits), R, V, int(k), float(temperature), int(seed), int(offset),
+            _ptr(top_token), _ptr(top_logq), _ptr(entropy), _ptr(workspace), ws_bytes,
+            _ptr(dev_flags), _stream(stream)))
     return top_token, top_logq, entropy
+
+
+def tree_expand_sample(draft_logits, k: int, temperature: float = 1.0, seed: int = 0,
+                       offset: int = 0, top_token=None, top_logq=None, entropy=None,
+                       workspace=None, dev_flags=None, stream=None):
+    """As ``tree_expand_topk`` with the k tokens of each row drawn from q
+    without replacement (Gumbel top-k on Philox draws of (seed, offset))."""
+    return _expand(draft_logits, k, temperature, top_token, top_logq, entropy, workspace,
+                   dev_flags, stream, (seed, offset))
 
 
 def philox_uniforms(seed: int, offset: int, B: int, N: int, out=None, device=None, stream=None):

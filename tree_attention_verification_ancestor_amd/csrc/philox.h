@@ -21,15 +21,14 @@ struct NodeUniforms {
     double res;
 };
 
-__device__ __forceinline__ NodeUniforms node_uniforms(uint64_t seed, uint64_t offset, int64_t b,
-                                                      int64_t i)
+// Ten Philox4x64 rounds on counter (c0, c1, c2, c3) under key (k0, k1).
+__device__ __forceinline__ void philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
+                                              uint64_t k0, uint64_t k1, uint64_t (&w)[4])
 {
     constexpr uint64_t kMul0 = 0xD2E7470EE14C6C93ull;
     constexpr uint64_t kMul1 = 0xCA5A826395121157ull;
     constexpr uint64_t kWeyl0 = 0x9E3779B97F4A7C15ull;
     constexpr uint64_t kWeyl1 = 0xBB67AE8584CAA73Bull;
-    uint64_t c0 = offset, c1 = (uint64_t)b, c2 = (uint64_t)i, c3 = 0;
-    uint64_t k0 = seed, k1 = 0;
 #pragma unroll
     for (int round = 0; round < 10; ++round) {
         if (round) {
@@ -45,9 +44,20 @@ __device__ __forceinline__ NodeUniforms node_uniforms(uint64_t seed, uint64_t of
         c2 = n2;
         c3 = lo0;
     }
+    w[0] = c0;
+    w[1] = c1;
+    w[2] = c2;
+    w[3] = c3;
+}
+
+__device__ __forceinline__ NodeUniforms node_uniforms(uint64_t seed, uint64_t offset, int64_t b,
+                                                      int64_t i)
+{
+    uint64_t w[4];
+    philox4x64_10(offset, (uint64_t)b, (uint64_t)i, 0, seed, 0, w);
     NodeUniforms u;
-    u.acc = (double)(c0 >> 40) * 0x1p-24;
-    u.res = (double)(c1 >> 40) * 0x1p-24;
+    u.acc = (double)(w[0] >> 40) * 0x1p-24;
+    u.res = (double)(w[1] >> 40) * 0x1p-24;
     return u;
 }
 

@@ -22,6 +22,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "philox.h"
 
 namespace tav {
 namespace {
@@ -118,15 +119,20 @@ struct ExArgs {
     double *top_logq;    // [R][k]
     double *entropy;     // [R]
     uint32_t *flags;
+    int32_t sampled;     // rank by x/T + Gumbel noise instead of x
+    uint64_t seed, offset;
 };
 
 // One wave's partial of a row from its entries v (lane order: tokens rise
 // with e). kClean: every entry is in the row and none is NaN, so the
 // per-entry tests drop out.
-template <bool kClean, typename Tok>
-__device__ __forceinline__ void wave_partial(const ExArgs &a, const float (&v)[kExEpt], Tok tok,
-                                             int lane, ExPart *out)
+template <bool kClean, bool kSampled, typename Tok>
+__device__ __forceinline__ void wave_partial(const ExArgs &a, const float (&v)[kExEpt],
+                                             const float (&sk)[kExEpt], Tok tok, int lane,
+                                             ExPart *out)
 {
+    // sk: the values the k best are chosen by (v itself, or the sampling
+    // keys, which are NaN exactly where v is); v: the logits of the sums
     const int64_t lim = a.V;
     bool nan_seen = false;
 #pragma unroll
@@ -143,8 +149,8 @@ __device__ __forceinline__ void wave_partial(const ExArgs &a, const float (&v)[k
     int le = -1;
 #pragma unroll
     for (int e = 0; e < kExEpt; ++e) {
-        if (!(!kClean && __builtin_isnan(v[e])) && (le < 0 || v[e] > lm)) {
-            lm = v[e];
+        if (!(!kClean && __builtin_isnan(sk[e])) && (le < 0 || sk[e] > lm)) {
+            lm = sk[e];
             le = e;
         }
     }
@@ -167,7 +173,7 @@ __device__ __forceinline__ void wave_partial(const ExArgs &a, const float (&v)[k
     int above = 0;
 #pragma unroll
     for (int e = 0; e < kExEpt; ++e)
-        above += (!(!kClean && __builtin_isnan(v[e])) && v[e] >= tau) ? 1 : 0;
+        above += (!(!kClean && __builtin_isnan(sk[e])) && sk[e] >= tau) ? 1 : 0;
     if (last == 0ull || __any(above > 1)) {
         uint32_t taken = 0;
         for (int i = 0; i < a.k; ++i) {
@@ -175,9 +181,9 @@ __device__ __forceinline__ void wave_partial(const ExArgs &a, const float (&v)[k
             int be = -1;
 #pragma unroll
             for (int e = 0; e < kExEpt; ++e) {
-                const bool ok = !((taken >> e) & 1u) && !(!kClean && __builtin_isnan(v[e]));
-                if (ok && (be < 0 || v[e] > bv)) {
-                    bv = v[e];
+                const bool ok = !((taken >> e) & 1u) && !(!kClean && __builtin_isnan(sk[e]));
+                if (ok && (be < 0 || sk[e] > bv)) {
+                    bv = sk[e];
                     be = e;
                 }
             }
@@ -189,8 +195,24 @@ __device__ __forceinline__ void wave_partial(const ExArgs &a, const float (&v)[k
                 out->key[i] = win;
         }
     }
-    // sums relative to the wave's maximum (-inf when it holds no entry)
-    const float m = first == 0ull ? -INFINITY : from_ordered_bits((uint32_t)(first >> 32));
+    // sums relative to the wave's maximum logit (-inf when it holds no
+    // entry): the best key's value, unless the keys are sampling keys
+    float m;
+    if constexpr (kSampled) {
+        float lx = -INFINITY;
+        bool any = false;
+#pragma unroll
+        for (int e = 0; e < kExEpt; ++e) {
+            if (!(!kClean && __builtin_isnan(v[e]))) {
+                lx = any ? fmaxf(lx, v[e]) : v[e];
+                any = true;
+            }
+        }
+        const uint64_t mk = wave_max_key(any ? (uint64_t)ordered_bits(lx) << 32 : 0ull);
+        m = mk == 0ull ? -INFINITY : from_ordered_bits((uint32_t)(mk >> 32));
+    } else {
+        m = first == 0ull ? -INFINITY : from_ordered_bits((uint32_t)(first >> 32));
+    }
     const float ms = m * a.invT32;
     // Each run of four entries is summed in fp32 (same-sign terms, so within
     // three fp32 roundings of exact), the run totals in fp64.
@@ -229,6 +251,7 @@ __device__ __forceinline__ void wave_partial(const ExArgs &a, const float (&v)[k
     }
 }
 
+template <bool kSampled>
 __global__ __launch_bounds__(kExThreads) void expand_part_kernel(ExArgs a)
 {
     // Each wave owns kExWaveChunk consecutive entries of one row: lane l holds
@@ -285,10 +308,31 @@ __global__ __launch_bounds__(kExThreads) void expand_part_kernel(ExArgs a)
         return wbase + (int64_t)(e >> 2) * 256 + 4 * lane + (e & 3);
     };
     ExPart *out = a.part + (r * a.wpr + w) * kExWaves + wave;
-    if (clean)
-        wave_partial<true>(a, v, tok, lane, out);
-    else
-        wave_partial<false>(a, v, tok, lane, out);
+    if constexpr (kSampled) {
+        // sampling keys fl32(fl32(x * (1/T)) + fl32(G)), G = -log(-log u) in
+        // fp64, u from word (token mod 4) of Philox at counter (offset, row,
+        // token / 4, 1): each run of four tokens is one Philox block
+        float sk[kExEpt];
+#pragma unroll
+        for (int h = 0; h < kExEpt / 4; ++h) {
+            uint64_t wd[4];
+            philox4x64_10(a.offset, (uint64_t)r, (uint64_t)(tok(4 * h) >> 2), 1, a.seed, 0, wd);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const double u = ((double)(wd[j] >> 11) + 0.5) * 0x1p-53;
+                const float g = (float)(-log(-log(u)));
+                sk[4 * h + j] = __fadd_rn(__fmul_rn(v[4 * h + j], a.invT32), g);
+            }
+        }
+        if (clean)
+            wave_partial<true, true>(a, v, sk, tok, lane, out);
+        else
+            wave_partial<false, true>(a, v, sk, tok, lane, out);
+    } else if (clean) {
+        wave_partial<true, false>(a, v, v, tok, lane, out);
+    } else {
+        wave_partial<false, false>(a, v, v, tok, lane, out);
+    }
 }
 
 // One wave per row: a row has wpr * 8 partials (64 for a 128256-entry row),
@@ -305,7 +349,11 @@ __global__ __launch_bounds__(kMergeThreads) void expand_merge_kernel(ExArgs a)
     uint64_t mk = 0;
     bool nan_seen = false;
     for (int w = lane; w < np; w += kMergeThreads) {
-        mk = max_u64(mk, p[w].key[0]);
+        // the largest key's value is the largest logit unless the keys are
+        // sampling keys; then the partials' own maxima
+        mk = max_u64(mk, a.sampled ? (p[w].m == -INFINITY ? 0ull
+                                                          : (uint64_t)ordered_bits(p[w].m) << 32)
+                                   : p[w].key[0]);
         nan_seen |= p[w].nan != 0;
     }
     const uint64_t top = wave_max_key(mk);
@@ -350,8 +398,10 @@ __global__ __launch_bounds__(kMergeThreads) void expand_merge_kernel(ExArgs a)
         const uint64_t win = wave_max_key(best);
         prev = win;
         if (lane == 0) {
-            const float x = from_ordered_bits((uint32_t)(win >> 32));
-            a.top_token[r * a.k + i] = win == 0ull ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)win);
+            const int32_t t = win == 0ull ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)win);
+            const float x = a.sampled ? (t < 0 ? -INFINITY : a.x[r * a.V + t])
+                                      : from_ordered_bits((uint32_t)(win >> 32));
+            a.top_token[r * a.k + i] = t;
             a.top_logq[r * a.k + i] =
                 win == 0ull ? -INFINITY : (double)fmaf(x, a.invT32, -(float)Ms) - logS0;
         }
@@ -378,10 +428,12 @@ extern "C" size_t tree_expand_workspace_bytes(int64_t R, int32_t V, int32_t k)
     return (size_t)R * wpr * kExWaves * sizeof(ExPart);
 }
 
-extern "C" tav_status tree_expand_topk(const float *draft_logits, int64_t R, int32_t V, int32_t k,
-                                       double temperature, int32_t *top_token, double *top_logq,
-                                       double *entropy, void *workspace, size_t ws_bytes,
-                                       uint32_t *dev_flags, void *stream)
+namespace {
+
+tav_status ex_launch(const float *draft_logits, int64_t R, int32_t V, int32_t k,
+                     double temperature, bool sampled, uint64_t seed, uint64_t offset,
+                     int32_t *top_token, double *top_logq, double *entropy, void *workspace,
+                     size_t ws_bytes, uint32_t *dev_flags, void *stream)
 {
     using namespace tav;
     if (!draft_logits || !top_token || !top_logq || !entropy)
@@ -410,10 +462,39 @@ extern "C" tav_status tree_expand_topk(const float *draft_logits, int64_t R, int
     a.top_logq = top_logq;
     a.entropy = entropy;
     a.flags = dev_flags;
+    a.sampled = sampled ? 1 : 0;
+    a.seed = seed;
+    a.offset = offset;
     hipStream_t s = as_stream(stream);
-    hipLaunchKernelGGL(expand_part_kernel, dim3((unsigned)(R * wpr)), dim3(kExThreads), 0, s, a);
+    if (sampled)
+        hipLaunchKernelGGL(expand_part_kernel<true>, dim3((unsigned)(R * wpr)), dim3(kExThreads), 0,
+                           s, a);
+    else
+        hipLaunchKernelGGL(expand_part_kernel<false>, dim3((unsigned)(R * wpr)), dim3(kExThreads),
+                           0, s, a);
     if (hipGetLastError() != hipSuccess)
         return TAV_ERR_LAUNCH;
     hipLaunchKernelGGL(expand_merge_kernel, dim3((unsigned)R), dim3(kMergeThreads), 0, s, a);
     return hipGetLastError() == hipSuccess ? TAV_OK : TAV_ERR_LAUNCH;
+}
+
+} // namespace
+
+extern "C" tav_status tree_expand_topk(const float *draft_logits, int64_t R, int32_t V, int32_t k,
+                                       double temperature, int32_t *top_token, double *top_logq,
+                                       double *entropy, void *workspace, size_t ws_bytes,
+                                       uint32_t *dev_flags, void *stream)
+{
+    return ex_launch(draft_logits, R, V, k, temperature, false, 0, 0, top_token, top_logq,
+                     entropy, workspace, ws_bytes, dev_flags, stream);
+}
+
+extern "C" tav_status tree_expand_sample(const float *draft_logits, int64_t R, int32_t V,
+                                         int32_t k, double temperature, uint64_t seed,
+                                         uint64_t offset, int32_t *top_token, double *top_logq,
+                                         double *entropy, void *workspace, size_t ws_bytes,
+                                         uint32_t *dev_flags, void *stream)
+{
+    return ex_launch(draft_logits, R, V, k, temperature, true, seed, offset, top_token, top_logq,
+                     entropy, workspace, ws_bytes, dev_flags, stream);
 }
