@@ -193,6 +193,11 @@ def run_gpu(args, w):
     out = dict(ms_step=ms_step, ms_attn=ms_attn, stage_ms=stage_ms, stage_all=stage,
                step_all=step_ms, depth=to_numpy(depth), path=to_numpy(path), n_acc=to_numpy(n_acc))
 
+    if args.step_only:
+        out["offset_paths"] = np.zeros((0, B, N), np.int32)
+        out["offset_naccs"] = np.zeros((0, B), np.int32)
+        return out
+
     def time_leg(call):
         """Per-call ms of `call` over `steps` launches, events on the launch stream."""
         for _ in range(args.warmup):
@@ -400,6 +405,9 @@ def main():
     ap.add_argument("--offsets", type=int, default=1000,
                     help="Philox offsets of the acceptance statistics run")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the step alone: no timed legs for the other calls and no "
+                         "tree-size sweep (for counter passes)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain copy of known size (for the HBM counters)")
     args = ap.parse_args()
@@ -488,23 +496,26 @@ def main():
                           "frac": round(t_floor / (ms * 1e-3), 4)},
         "accepted": g["n_acc"].tolist(),
         "acceptance": acceptance,
-        "greedy": {"spec_verify_sample_us": pct(g["greedy_ms"]),
-                   "accepted": g["greedy_nacc"].tolist()},
-        "without_replacement": {"spec_verify_sample_wor_us": pct(g["wor_ms"]),
-                                "accepted": g["wor_nacc"].tolist()},
-        "kv_commit_inplace_us": pct(g["inplace_ms"]),
-        "speedup_model": speedup_model(g["size_n"], g["size_us"]),
-        "tree_widths_by_entropy": {"B": w.B, "F": 64, "us": pct(g["widths_ms"])},
-        "tree_expand_sample": {"rows": g["expand_rows"], "k": 4, "us": pct(g["expand_sample_ms"])},
-        "tree_select_topm": {"B": g["select_shape"][0], "Nc": g["select_shape"][1],
-                             "M": g["select_shape"][2], "us": pct(g["select_ms"])},
-        "tree_expand_topk": {"rows": g["expand_rows"], "k": 4, "us": pct(g["expand_ms"]),
-                             "hbm_gbs": round(g["expand_rows"] * w.V * 4
-                                              / (float(np.median(g["expand_ms"])) * 1e-3) / 1e9, 1),
-                             "hbm_frac": round(g["expand_rows"] * w.V * 4
-                                               / (float(np.median(g["expand_ms"])) * 1e-3)
-                                               / (HBM_PEAK_GBS * 1e9), 4)},
     }
+    if "greedy_ms" in g:
+        rec.update({
+            "greedy": {"spec_verify_sample_us": pct(g["greedy_ms"]),
+                       "accepted": g["greedy_nacc"].tolist()},
+            "without_replacement": {"spec_verify_sample_wor_us": pct(g["wor_ms"]),
+                                    "accepted": g["wor_nacc"].tolist()},
+            "kv_commit_inplace_us": pct(g["inplace_ms"]),
+            "speedup_model": speedup_model(g["size_n"], g["size_us"]),
+            "tree_widths_by_entropy": {"B": w.B, "F": 64, "us": pct(g["widths_ms"])},
+            "tree_expand_sample": {"rows": g["expand_rows"], "k": 4, "us": pct(g["expand_sample_ms"])},
+            "tree_select_topm": {"B": g["select_shape"][0], "Nc": g["select_shape"][1],
+                                 "M": g["select_shape"][2], "us": pct(g["select_ms"])},
+            "tree_expand_topk": {"rows": g["expand_rows"], "k": 4, "us": pct(g["expand_ms"]),
+                                 "hbm_gbs": round(g["expand_rows"] * w.V * 4
+                                                  / (float(np.median(g["expand_ms"])) * 1e-3) / 1e9, 1),
+                                 "hbm_frac": round(g["expand_rows"] * w.V * 4
+                                                   / (float(np.median(g["expand_ms"])) * 1e-3)
+                                                   / (HBM_PEAK_GBS * 1e9), 4)},
+        })
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)
