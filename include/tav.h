@@ -100,6 +100,20 @@ size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, 
                                  int32_t max_prefix_len);
 
 /*
+ * tav_attn_plan — how tree_attn_verify divides the work for these sizes on a
+ * device of `cus` compute units holding `per_cu` of its workgroups each. A
+ * host function (nothing launched, no device needed), for checking the plan:
+ *   plan[0] waves per workgroup, plan[1] row blocks, plan[2] prefix splits,
+ *   plan[3] the most block-table entries any split stages, over every prefix
+ *   length up to max_prefix_len, plan[4] the capacity of that staging copy
+ *   (plan[3] <= plan[4] for every supported shape).
+ * TAV_ERR_ARG for a NULL plan or cus, per_cu < 1; TAV_ERR_UNSUPPORTED for
+ * sizes tree_attn_verify rejects.
+ */
+tav_status tav_attn_plan(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                         int32_t max_prefix_len, int32_t cus, int32_t per_cu, int32_t *plan);
+
+/*
  * tree_attn_verify — one attention layer of the verification forward pass.
  *
  * The target scores all candidates in one pass over the prefix with the

@@ -191,3 +191,38 @@ def test_helpers_reject_bad_arguments():
     assert lib.tav_philox_uniforms(0, 0, 0, 1, FAKE, None) == tav.ERR_ARG
     assert lib.tav_target_probs(None, 1, 10, 1.0, FAKE, None, None) == tav.ERR_ARG
     assert lib.tav_target_probs(FAKE, 1, 10, 0.0, FAKE, None, None) == tav.ERR_ARG
+
+
+def test_attention_plan_keeps_every_split_within_its_block_table_copy():
+    """Every split of tree_attn_verify's plan stages at most the LDS copy's
+    capacity of block-table entries, tree tiles counted in the balance of the
+    splits (host arithmetic only, swept over batch, tree size, group size and
+    prefix length, for devices from one CU to a full MI355X)."""
+    worst = 0
+    for cus, per_cu in ((256, 1), (256, 2), (8, 1), (1, 1)):
+        for B in (1, 4, 8, 64, 128):
+            for N in (1, 5, 16, 64, 128, 192, 256):
+                for G in (1, 8, 16):
+                    if G * N > 4096:
+                        continue
+                    for L in (0, 1, 63, 64, 8192, 32767, 32768, 65472, 65536, 131072, 1 << 20):
+                        p = tav.attn_plan(B, N, 8 * G, 8, 128, L, cus, per_cu)
+                        assert p["max_split_blocks"] <= p["capacity"], (cus, per_cu, B, N, G, L, p)
+                        worst = max(worst, p["max_split_blocks"])
+    assert worst == 2048   # the bound is reached, so the sweep does test it
+
+
+def test_attention_plan_case_that_once_overflowed():
+    """B=64, N=192, Hq=Hkv=8, prefix up to 65472: one split used to take 513
+    prefix tiles (2052 block-table entries for a 2048-entry copy)."""
+    p = tav.attn_plan(64, 192, 8, 8, 128, 65472, 256, 1)
+    assert p["max_split_blocks"] <= p["capacity"] == 2048
+    assert p["splits"] >= 2
+
+
+def test_attention_plan_rejects_bad_arguments():
+    lib = tav.lib()
+    plan = (ctypes.c_int32 * 5)()
+    assert lib.tav_attn_plan(1, 5, 8, 2, 128, 64, 256, 1, None) == tav.ERR_ARG
+    assert lib.tav_attn_plan(1, 5, 8, 2, 128, 64, 0, 1, ctypes.cast(plan, P)) == tav.ERR_ARG
+    assert lib.tav_attn_plan(1, 5, 8, 2, 96, 64, 256, 1, ctypes.cast(plan, P)) == tav.ERR_UNSUPPORTED

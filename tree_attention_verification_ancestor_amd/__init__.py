@@ -61,6 +61,7 @@ _SIGNATURES = {
     "tav_status_string": (ctypes.c_char_p, [_I32]),
     "tree_mask_build": (_I32, [_P, _I32, _I32, _P, _P, _P, _P]),
     "tree_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "tav_attn_plan": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
     "tree_attn_verify": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _P, _I32, _I32,
                                 _I32, _I32, _I32, _I32, _F32, _P, _P, _SZ, _P, _P]),
     "spec_verify_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
@@ -203,6 +204,18 @@ def tree_mask_build(parent: torch.Tensor, mask: Optional[torch.Tensor] = None,
     _check("tree_mask_build", lib().tree_mask_build(_ptr(parent), B, N, _ptr(mask), _ptr(depth),
                                                     _ptr(dev_flags), _stream(stream)))
     return mask, depth
+
+
+def attn_plan(B, N, Hq, Hkv, D, max_prefix_len, cus, per_cu):
+    """tree_attn_verify's work decomposition on a device of ``cus`` compute
+    units holding ``per_cu`` workgroups each (host only): a dict with the
+    waves per workgroup, row blocks, splits, and the most block-table entries
+    a split stages against the capacity of its LDS copy."""
+    plan = (ctypes.c_int32 * 5)()
+    _check("tav_attn_plan", lib().tav_attn_plan(B, N, Hq, Hkv, D, max_prefix_len, cus, per_cu,
+                                                ctypes.cast(plan, ctypes.c_void_p)))
+    return {"waves": plan[0], "row_blocks": plan[1], "splits": plan[2],
+            "max_split_blocks": plan[3], "capacity": plan[4]}
 
 
 def tree_attn_workspace_bytes(B, N, Hq, Hkv, D, max_prefix_len) -> int:

@@ -238,6 +238,13 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     const int tt0 = std::max(u0, Tb) - Tb;               // first tree tile of the split
     const int n_tree = std::max(0, u1 - std::max(u0, Tb));
     const int n_tiles = n_pre + n_tree;
+    // The plan keeps every split's slice within its LDS copy; a launch that
+    // broke that rule would index past it, so it computes nothing instead.
+    if (n_pre * (kKT / kBlock) > kMaxSplitBlocks) {
+        if (tid == 0)
+            raise_flag(a.flags, TAV_FLAG_CAPACITY);
+        return;
+    }
     // The split's block-table slice, validated once. Entries past the prefix
     // (and bad ones, which also raise a flag) name block 0 of this head, a
     // valid address whose keys are masked and whose V entries are zeroed.
@@ -876,33 +883,35 @@ const void *kernel_for(int NW)
     }
 }
 
-// Work decomposition for a shape: waves per workgroup (NW, 32 query rows
-// each), row blocks (RB) and prefix splits (S), enough workgroups to fill the
-// device once.
-bool attn_plan(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_prefix_len,
-               AttnPlan &p)
+int waves_for(int32_t N, int32_t Hq, int32_t Hkv)
+{
+    const int NG = N * (Hq / Hkv);
+    return NG > 128 ? 8 : NG > 64 ? 4 : NG > 32 ? 2 : 1;
+}
+
+// Work decomposition for a shape on a device of `cus` compute units holding
+// `per_cu` workgroups each: waves per workgroup (NW, 32 query rows each), row
+// blocks (RB) and prefix splits (S), enough workgroups to fill the device
+// once. Pure arithmetic (no device call), so it can be checked on the host.
+void attn_plan_for(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                   int32_t max_prefix_len, int cus, int per_cu, AttnPlan &p)
 {
     const int G = Hq / Hkv;
     const int NG = N * G;
-    p.NW = NG > 128 ? 8 : NG > 64 ? 4 : NG > 32 ? 2 : 1;
+    p.NW = waves_for(N, Hq, Hkv);
     p.rows = 32 * p.NW;
     p.RB = (int)ceil_div(NG, p.rows);
-    const int cus = device_cu_count();
-    if (cus <= 0)
-        return false;
-    int per_cu = 0;
-    const void *fn = D == 128 ? kernel_for<128>(p.NW) : kernel_for<64>(p.NW);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, p.NW * 64, 0) != hipSuccess ||
-        per_cu <= 0)
-        return false;
     const int64_t base = (int64_t)B * Hkv * p.RB;
     const int64_t target = (int64_t)cus * per_cu;
     const int64_t tiles = std::max<int64_t>(1, ceil_div(max_prefix_len, kKT));
     int64_t S = ceil_div(target, base);
     S = std::max<int64_t>(1, std::min<int64_t>(S, tiles / kMinTilesPerSplit));
-    // a split's block-table slice must fit its LDS copy
+    // A split's block-table slice must fit its LDS copy. Split s takes units
+    // [s U / S, (s + 1) U / S) of the U = prefix tiles + tree tiles, so it
+    // can hold up to ceil(U / S) prefix tiles: the bound counts every unit.
     const int64_t max_tiles_per_split = kMaxSplitBlocks / (kKT / kBlock);
-    S = std::max<int64_t>(S, ceil_div(tiles, max_tiles_per_split));
+    const int64_t units = tiles + ceil_div(N, kKT);
+    S = std::max<int64_t>(S, ceil_div(units, max_tiles_per_split));
     p.S = (int)S;
     p.KS = (int)((int64_t)B * Hkv * p.S);
     p.grid = ceil_div(p.KS, 8) * 8 * p.RB;
@@ -913,6 +922,22 @@ bool attn_plan(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D, int32_t
         p.part_o_bytes = p.part_ml_bytes = 0;
     }
     p.ws_bytes = p.S > 1 ? round_up(p.part_o_bytes, 256) + round_up(p.part_ml_bytes, 256) : 0;
+}
+
+// The same for the current device.
+bool attn_plan(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_prefix_len,
+               AttnPlan &p)
+{
+    const int cus = device_cu_count();
+    if (cus <= 0)
+        return false;
+    const int NW = waves_for(N, Hq, Hkv);
+    int per_cu = 0;
+    const void *fn = D == 128 ? kernel_for<128>(NW) : kernel_for<64>(NW);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NW * 64, 0) != hipSuccess ||
+        per_cu <= 0)
+        return false;
+    attn_plan_for(B, N, Hq, Hkv, D, max_prefix_len, cus, per_cu, p);
     return true;
 }
 
@@ -947,6 +972,34 @@ hipError_t launch_main_d(const AttnPlan &p, const AttnArgs &a, hipStream_t s)
 
 } // namespace
 } // namespace tav
+
+extern "C" tav_status tav_attn_plan(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int32_t max_prefix_len, int32_t cus, int32_t per_cu,
+                                    int32_t *plan)
+{
+    using namespace tav;
+    if (!plan || cus < 1 || per_cu < 1)
+        return TAV_ERR_ARG;
+    if (!attn_shape_ok(B, N, Hq, Hkv, D, max_prefix_len))
+        return TAV_ERR_UNSUPPORTED;
+    AttnPlan p;
+    attn_plan_for(B, N, Hq, Hkv, D, max_prefix_len, cus, per_cu, p);
+    // the largest prefix-tile count of any split, over every prefix length up
+    // to max_prefix_len (longer prefixes give every split at least as many)
+    const int64_t Tb = ceil_div(max_prefix_len, kKT);
+    const int64_t Ub = Tb + ceil_div(N, kKT);
+    int64_t most = 0;
+    for (int64_t s = 0; s < p.S; ++s) {
+        const int64_t u0 = s * Ub / p.S, u1 = (s + 1) * Ub / p.S;
+        most = std::max(most, std::min(u1, Tb) - std::min(u0, Tb));
+    }
+    plan[0] = p.NW;
+    plan[1] = p.RB;
+    plan[2] = p.S;
+    plan[3] = (int32_t)(most * (kKT / kBlock));
+    plan[4] = kMaxSplitBlocks;
+    return TAV_OK;
+}
 
 extern "C" size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
                                             int32_t D, int32_t max_prefix_len)
