@@ -6,6 +6,7 @@
  *   tree_attn_verify    tree attention over a paged KV prefix plus ancestors
  *   spec_verify_sample  target/draft softmax and the rejection-sampling walk
  *   spec_verify_sample_wor  the same walk for siblings drawn without replacement
+ *   spec_verify_sample_probe  the walk, also writing the p and q it decides with
  *   kv_commit_path      copy the accepted path's K/V into the paged cache
  *   kv_commit_inplace   the same when the tree's K/V already sit in the cache
  *   tree_expand_topk    top-k draft tokens, log q and entropy per frontier row
@@ -243,6 +244,38 @@ tav_status spec_verify_sample_wor(const float *target_logits, const float *draft
                                   uint32_t *dev_flags, void *stream);
 
 /*
+ * spec_verify_sample_probe — spec_verify_sample (the independent-sibling
+ * rule, temperature > 0) that also writes the softmax values its decisions
+ * are taken with, so they can be checked against an exact softmax
+ * (radar-34b blog §2 defines the walk on p and q; LLM Primer ch. 9, §9.1 has
+ * one target distribution per node).
+ *
+ * For every node u the walk visits in sequence b:
+ *   p_rows[b][u][y]  p_u(y) = softmax(target_logits[b][u] / T)(y), y < V,
+ *                    as the walk holds it: each entry's exponential in fp32
+ *                    relative to its wave's maximum, rebased to the row's
+ *                    maximum and normalised in fp64;
+ *   q_rows[b][u][y]  the same for the draft row, if u has children;
+ *   child_pq[b][c][0..1]  for each child c of u: p_u(token[b][c]) and
+ *                    q_u(token[b][c]) as the child tests read them.
+ * Rows and entries of nodes the walk does not visit are left untouched.
+ * path, n_accepted and out_tokens are those spec_verify_sample returns for
+ * the same arguments. The probe writes 8 bytes per vocabulary entry of each
+ * visited row: a checking tool, not the hot path.
+ *
+ *   p_rows, q_rows  fp64 [B][N][V] (8-byte aligned); child_pq fp64 [B][N][2]
+ *   temperature > 0 (no greedy mode); everything else as spec_verify_sample,
+ *   whose workspace size applies.
+ */
+tav_status spec_verify_sample_probe(const float *target_logits, const float *draft_logits,
+                                    const int32_t *parent, const int32_t *token, int32_t B,
+                                    int32_t N, int32_t V, double temperature, uint64_t seed,
+                                    uint64_t offset, int32_t *path, int32_t *n_accepted,
+                                    int32_t *out_tokens, double *p_rows, double *q_rows,
+                                    double *child_pq, void *workspace, size_t ws_bytes,
+                                    uint32_t *dev_flags, void *stream);
+
+/*
  * kv_commit_path — keep the accepted path's K/V, discarding the rest.
  *
  * Only the accepted path survives verification; rejected branches are pruned
@@ -350,8 +383,11 @@ tav_status tav_philox_uniforms(uint64_t seed, uint64_t offset, int32_t B, int32_
                                void *stream);
 
 /*
- * tav_target_probs — p = softmax(logits / T) per row in float64, with the
- * device softmax spec_verify_sample uses (radar-34b blog §2 names p and q).
+ * tav_target_probs — p = softmax(logits / T) per row, every exponential and
+ * sum in float64 on the device (radar-34b blog §2 names p and q). A reference
+ * for the device's fp64 exponential; the walk itself takes its per-entry
+ * exponentials in fp32 (see spec_verify_sample_probe, which exposes the
+ * values the walk decides with).
  *   logits fp32 [rows][V] (16-byte aligned), p fp64 [rows][V].
  */
 tav_status tav_target_probs(const float *logits, int64_t rows, int32_t V, double temperature,

@@ -32,9 +32,66 @@ def test_target_probs_match_oracle(V, T):
     logits[1, :V // 3] = -np.inf
     p = to_numpy(tav.target_probs(torch.from_numpy(logits).to(device()), T))
     ref = oracle.softmax(logits, T)
-    assert np.abs(p - ref).max() <= P_TOL
-    assert np.abs(p - ref).max() <= 1e-12          # both sides are fp64
+    # the device's all-fp64 softmax (not the walk's: see the probe test)
+    assert np.abs(p - ref).max() <= 1e-12
     np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("name,T", [("llama70b", 1.0), ("llama70b", 0.7), ("long", 1.0),
+                                    ("long", 0.7), ("llama8b", 1.3)])
+def test_walk_softmax_matches_oracle(name, T):
+    """The p and q the walk itself decides with (its fp32 per-entry
+    exponentials, fp64 sums and rebases), at every visited node, against the
+    oracle's fp64 softmax: within 1e-5, absolute and relative; and the p, q of
+    each tested child's token likewise."""
+    say(f"sampler: probe of the walk's softmax, {name} T={T}")
+    w = make_workload(name, temperature=T)
+    dev = device()
+    from synth.device import upload
+    d = upload(w, dev)
+    flags = tav.new_flags(dev)
+    path, n_acc, toks, p_rows, q_rows, cpq = tav.spec_verify_sample_probe(
+        d["target_logits"], d["draft_logits"], d["parent"], d["token"], T, w.philox_seed,
+        w.philox_offset, dev_flags=flags)
+    path2, n_acc2, toks2 = tav.spec_verify_sample(
+        d["target_logits"], d["draft_logits"], d["parent"], d["token"], T, w.philox_seed,
+        w.philox_offset, dev_flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    # the probe takes the same decisions as the walk it instruments
+    assert torch.equal(path, path2) and torch.equal(n_acc, n_acc2) and torch.equal(toks, toks2)
+    path, n_acc = to_numpy(path), to_numpy(n_acc)
+    worst_abs = worst_rel = 0.0
+    rows = 0
+    for b in range(w.B):
+        kids = set(int(x) for x in w.parent[b, 1:])
+        for u in path[b, :n_acc[b] + 1]:
+            u = int(u)
+            for logits, got, need in ((w.target_logits[b, u], p_rows[b, u], True),
+                                      (w.draft_logits[b, u], q_rows[b, u], u in kids)):
+                if not need:
+                    continue
+                g = to_numpy(got)
+                ref = oracle.softmax(logits, T)
+                assert np.isfinite(g).all()
+                err = np.abs(g - ref)
+                worst_abs = max(worst_abs, float(err.max()))
+                nz = ref > 0
+                assert (g[~nz] == 0).all()
+                worst_rel = max(worst_rel, float((err[nz] / ref[nz]).max()))
+                rows += 1
+            pu = oracle.softmax(w.target_logits[b, u], T)
+            qu = oracle.softmax(w.draft_logits[b, u], T)
+            for c in np.nonzero(w.parent[b] == u)[0]:
+                if c == 0:
+                    continue
+                x = int(w.token[b, c])
+                gp, gq = to_numpy(cpq[b, c])
+                worst_abs = max(worst_abs, abs(gp - pu[x]), abs(gq - qu[x]))
+                worst_rel = max(worst_rel, abs(gp - pu[x]) / pu[x], abs(gq - qu[x]) / qu[x])
+    say(f"  {rows} rows, max abs {worst_abs:.2e}, max rel {worst_rel:.2e}")
+    assert worst_abs <= P_TOL
+    assert worst_rel <= P_TOL
 
 
 @pytest.mark.parametrize("name,over", [

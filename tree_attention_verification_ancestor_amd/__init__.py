@@ -69,6 +69,8 @@ _SIGNATURES = {
                                   _P, _P, _SZ, _P, _P]),
     "spec_verify_sample_wor": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _F64, _U64, _U64, _P, _P,
                                   _P, _P, _SZ, _P, _P]),
+    "spec_verify_sample_probe": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _F64, _U64, _U64, _P,
+                                        _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
     "kv_commit_path": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _P, _I32, _I32, _I32,
                               _I32, _I32, _P, _P, _P, _P]),
     "kv_commit_inplace": (_I32, [_P, _P, _I32, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
@@ -307,6 +309,36 @@ def spec_verify_sample(target_logits, draft_logits, parent, token, temperature: 
     return _verify_sample("spec_verify_sample", target_logits, draft_logits, parent, token,
                           temperature, seed, offset, path, n_accepted, out_tokens, workspace,
                           dev_flags, stream)
+
+
+def spec_verify_sample_probe(target_logits, draft_logits, parent, token,
+                             temperature: float = 1.0, seed: int = 0, offset: int = 0,
+                             workspace=None, dev_flags=None, stream=None):
+    """``spec_verify_sample`` that also returns the softmax values the walk
+    decides with: (path, n_accepted, out_tokens, p_rows [B,N,V] fp64,
+    q_rows [B,N,V] fp64, child_pq [B,N,2] fp64). Rows of nodes the walk does
+    not visit (and q rows of visited leaves) are NaN."""
+    _need(target_logits, "target_logits", (torch.float32,))
+    B, N, V = target_logits.shape
+    dev = target_logits.device
+    _need(draft_logits, "draft_logits", (torch.float32,), (B, N, V), dev)
+    _need(parent, "parent", _I32T, (B, N), dev)
+    _need(token, "token", _I32T, (B, N), dev)
+    path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    out_tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    p_rows = torch.full((B, N, V), float("nan"), dtype=torch.float64, device=dev)
+    q_rows = torch.full((B, N, V), float("nan"), dtype=torch.float64, device=dev)
+    child_pq = torch.full((B, N, 2), float("nan"), dtype=torch.float64, device=dev)
+    if workspace is None:
+        workspace = new_sampler_workspace(B, N, V, dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("spec_verify_sample_probe", lib().spec_verify_sample_probe(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(parent), _ptr(token), B, N, V,
+        float(temperature), int(seed), int(offset), _ptr(path), _ptr(n_accepted),
+        _ptr(out_tokens), _ptr(p_rows), _ptr(q_rows), _ptr(child_pq), _ptr(workspace), ws_bytes,
+        _ptr(dev_flags), _stream(stream)))
+    return path, n_accepted, out_tokens, p_rows, q_rows, child_pq
 
 
 def spec_verify_sample_wor(target_logits, draft_logits, parent, token,

@@ -36,4 +36,14 @@ inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s);
 // Compute units of the current device (0 if there is no usable device).
 int device_cu_count();
 
+// The launch behind spec_verify_sample and its variants: host checks, plan,
+// workspace check, one kernel launch. wor: the without-replacement sibling
+// rule; p_rows/q_rows/child_pq non-NULL: the probe variant.
+tav_status sv_launch(const float *target_logits, const float *draft_logits,
+                     const int32_t *parent, const int32_t *token, int32_t B, int32_t N, int32_t V,
+                     double temperature, uint64_t seed, uint64_t offset, int32_t *path,
+                     int32_t *n_accepted, int32_t *out_tokens, void *workspace, size_t ws_bytes,
+                     uint32_t *dev_flags, void *stream, bool wor, double *p_rows,
+                     double *q_rows, double *child_pq);
+
 } // namespace tav

@@ -66,6 +66,7 @@
 #include "common.h"
 #include "philox.h"
 
+
 namespace tav {
 namespace {
 
@@ -97,6 +98,11 @@ struct SvArgs {
     uint32_t *flags;
     int32_t wpg, ngroups, chunk;
     int32_t vec4;     // rows can be read 16 bytes at a time (V % 4 == 0, aligned logits)
+    // probe outputs (kProbe): the softmax rows the walk holds at each visited
+    // node, and p, q of each tested child's token as the walk decides with them
+    double *p_rows;   // [B][N][V]
+    double *q_rows;   // [B][N][V]
+    double *child_pq; // [B][N][2]
 };
 
 // ---------------------------------------------------------------------------
@@ -336,8 +342,11 @@ __device__ __forceinline__ double bits_f64(uint32_t hi, uint32_t lo)
 // kWor selects the sibling rule: false, every child of u is tested with q_u
 // (siblings drawn independently from q_u); true, a rejected child's token
 // leaves q_u, the rest renormalised, before the next sibling is tried
-// (siblings drawn from q_u without replacement).
-template <bool kWor>
+// (siblings drawn from q_u without replacement). kProbe also writes, at each
+// visited node, the normalised p and q the walk holds in registers and the
+// p, q of its children's tokens that the child tests read; nothing else
+// changes.
+template <bool kWor, bool kProbe = false>
 __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
 {
     __shared__ int32_t s_par[kMaxNodes];
@@ -702,6 +711,26 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     raise_flag(a.flags, TAV_FLAG_NONFINITE_LOGITS);
                 failed = true;
                 break;
+            }
+            if constexpr (kProbe) {
+                // the same arithmetic as the rebase before a rejection below
+                const double sp = (wmt == -INFINITY) ? 0.0 : exp_bulk(wts - Mp) * (1.0 / Zp);
+                const double sq = (wmq == -INFINITY) ? 0.0 : exp_bulk(wqs - Mq) * (1.0 / Zq);
+                double *prow = a.p_rows + (rowbase + u) * a.V;
+                double *qrow = a.q_rows + (rowbase + u) * a.V;
+#pragma unroll
+                for (int e = 0; e < kSvEpt; ++e) {
+                    const int64_t t = tok(e);
+                    if (t < lim) {
+                        prow[t] = pr[e] * sp;
+                        if (has_kids)
+                            qrow[t] = qv[e] * sq;
+                    }
+                }
+                if (rank == 0 && tid < N && s_par[tid] == u) {
+                    a.child_pq[2 * (rowbase + tid)] = s_px[tid];
+                    a.child_pq[2 * (rowbase + tid) + 1] = s_qx[tid];
+                }
             }
             // ---- 2./3. children in ascending order against the running residual
             // Child c, tried after k rejections at u: its token's p under the
@@ -1352,15 +1381,17 @@ bool sv_plan(int32_t B, int32_t V, SvPlan &p)
     // the grid must be resident at once for either kernel (the group syncs
     // wait on each other), so the smaller of their occupancies counts
     int per_cu = 0, per_cu_g = 0;
-    int per_cu_w = 0;
+    int per_cu_w = 0, per_cu_p = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, spec_verify_kernel<false>,
                                                      kSvThreads, 0) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_w, spec_verify_kernel<true>,
                                                      kSvThreads, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_p, spec_verify_kernel<false, true>,
+                                                     kSvThreads, 0) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_g, spec_verify_greedy_kernel,
                                                      kSvThreads, 0) != hipSuccess)
         return false;
-    per_cu = std::min(std::min(per_cu, per_cu_w), per_cu_g);
+    per_cu = std::min(std::min(std::min(per_cu, per_cu_w), per_cu_g), per_cu_p);
     if (per_cu <= 0)
         return false;
     const int64_t resident = (int64_t)per_cu * cus;
@@ -1431,13 +1462,14 @@ extern "C" size_t spec_verify_workspace_bytes(int32_t B, int32_t N, int32_t V)
     return kHeaderBytes + p.box_bytes;
 }
 
-namespace {
+namespace tav {
 
 tav_status sv_launch(const float *target_logits, const float *draft_logits,
                      const int32_t *parent, const int32_t *token, int32_t B, int32_t N, int32_t V,
                      double temperature, uint64_t seed, uint64_t offset, int32_t *path,
                      int32_t *n_accepted, int32_t *out_tokens, void *workspace, size_t ws_bytes,
-                     uint32_t *dev_flags, void *stream, bool wor)
+                     uint32_t *dev_flags, void *stream, bool wor, double *p_rows,
+                     double *q_rows, double *child_pq)
 {
     using namespace tav;
     // temperature 0 selects greedy verification, which reads no draft row
@@ -1479,7 +1511,14 @@ tav_status sv_launch(const float *target_logits, const float *draft_logits,
     a.ngroups = p.ngroups;
     a.chunk = p.chunk;
     a.vec4 = V % 4 == 0 && aligned(target_logits, 16) && (greedy || aligned(draft_logits, 16));
-    if (greedy)
+    a.p_rows = p_rows;
+    a.q_rows = q_rows;
+    a.child_pq = child_pq;
+    const bool probe = p_rows != nullptr;
+    if (probe)
+        hipLaunchKernelGGL((spec_verify_kernel<false, true>), dim3(p.wpg * p.ngroups),
+                           dim3(kSvThreads), 0, as_stream(stream), a);
+    else if (greedy)
         hipLaunchKernelGGL(spec_verify_greedy_kernel, dim3(p.wpg * p.ngroups), dim3(kSvThreads), 0,
                            as_stream(stream), a);
     else if (wor)
@@ -1491,7 +1530,7 @@ tav_status sv_launch(const float *target_logits, const float *draft_logits,
     return hipGetLastError() == hipSuccess ? TAV_OK : TAV_ERR_LAUNCH;
 }
 
-} // namespace
+} // namespace tav
 
 extern "C" tav_status spec_verify_sample(const float *target_logits, const float *draft_logits,
                                          const int32_t *parent, const int32_t *token, int32_t B,
@@ -1500,9 +1539,9 @@ extern "C" tav_status spec_verify_sample(const float *target_logits, const float
                                          int32_t *out_tokens, void *workspace, size_t ws_bytes,
                                          uint32_t *dev_flags, void *stream)
 {
-    return sv_launch(target_logits, draft_logits, parent, token, B, N, V, temperature, seed,
+    return tav::sv_launch(target_logits, draft_logits, parent, token, B, N, V, temperature, seed,
                      offset, path, n_accepted, out_tokens, workspace, ws_bytes, dev_flags, stream,
-                     false);
+                     false, nullptr, nullptr, nullptr);
 }
 
 extern "C" tav_status spec_verify_sample_wor(const float *target_logits,
@@ -1513,9 +1552,25 @@ extern "C" tav_status spec_verify_sample_wor(const float *target_logits,
                                              int32_t *out_tokens, void *workspace,
                                              size_t ws_bytes, uint32_t *dev_flags, void *stream)
 {
-    return sv_launch(target_logits, draft_logits, parent, token, B, N, V, temperature, seed,
+    return tav::sv_launch(target_logits, draft_logits, parent, token, B, N, V, temperature, seed,
                      offset, path, n_accepted, out_tokens, workspace, ws_bytes, dev_flags, stream,
-                     true);
+                     true, nullptr, nullptr, nullptr);
+}
+
+extern "C" tav_status spec_verify_sample_probe(
+    const float *target_logits, const float *draft_logits, const int32_t *parent,
+    const int32_t *token, int32_t B, int32_t N, int32_t V, double temperature, uint64_t seed,
+    uint64_t offset, int32_t *path, int32_t *n_accepted, int32_t *out_tokens, double *p_rows,
+    double *q_rows, double *child_pq, void *workspace, size_t ws_bytes, uint32_t *dev_flags,
+    void *stream)
+{
+    using namespace tav;
+    if (!p_rows || !q_rows || !child_pq || !aligned(p_rows, 8) || !aligned(q_rows, 8) ||
+        !aligned(child_pq, 8) || !(temperature > 0.0))
+        return TAV_ERR_ARG;
+    return tav::sv_launch(target_logits, draft_logits, parent, token, B, N, V, temperature, seed,
+                     offset, path, n_accepted, out_tokens, workspace, ws_bytes, dev_flags, stream,
+                     false, p_rows, q_rows, child_pq);
 }
 
 extern "C" tav_status tav_philox_uniforms(uint64_t seed, uint64_t offset, int32_t B, int32_t N,
