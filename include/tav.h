@@ -7,6 +7,7 @@
  *   spec_verify_sample  target/draft softmax and the rejection-sampling walk
  *   spec_verify_sample_wor  the same walk for siblings drawn without replacement
  *   spec_verify_sample_probe  the walk, also writing the p and q it decides with
+ *   spec_verify_sample_noalloc  the walk on the library's fixed scratch (no workspace)
  *   kv_commit_path      copy the accepted path's K/V into the paged cache
  *   kv_commit_inplace   the same when the tree's K/V already sit in the cache
  *   tree_expand_topk    top-k draft tokens, log q and entropy per frontier row
@@ -19,8 +20,9 @@
  * Conventions for every entry point:
  *   - Pointers are device pointers unless stated otherwise. All tensors are
  *     owned by the caller; the library keeps no pointer after a call returns
- *     and holds no mutable global state. Buffers must stay alive until the
- *     work queued on `stream` has finished.
+ *     and holds no mutable global state, except the fixed per-device scratch
+ *     of spec_verify_sample_noalloc. Buffers must stay alive until the work
+ *     queued on `stream` has finished.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call is asynchronous; the four calls chain on one stream with no
  *     host synchronisation.
@@ -274,6 +276,28 @@ tav_status spec_verify_sample_probe(const float *target_logits, const float *dra
                                     int32_t *out_tokens, double *p_rows, double *q_rows,
                                     double *child_pq, void *workspace, size_t ws_bytes,
                                     uint32_t *dev_flags, void *stream);
+
+/*
+ * spec_verify_sample_noalloc — spec_verify_sample (the independent-sibling
+ * rule, or greedy at temperature 0) for callers that cannot allocate: code
+ * under stream capture, tight serving loops, harnesses that forbid
+ * allocation. It takes no workspace; its scratch (the exit counter and the
+ * group mailbox) is a fixed 256 KiB array of the library, one per device,
+ * held until the process ends. The call allocates nothing (no hipMalloc, no
+ * allocating library routine). The first call on a device looks the array
+ * up and queues a clearing fill kernel on `stream` ahead of its own kernel;
+ * every call leaves the array zero-filled again. Calls on one device share
+ * the array, so calls that overlap in time on one device race: keep them on
+ * one stream. Results are those of spec_verify_sample for the same
+ * arguments. TAV_ERR_WORKSPACE if the plan's mailbox exceeded the array
+ * (no supported shape does: it needs at most 64 KiB); argument errors as
+ * spec_verify_sample.
+ */
+tav_status spec_verify_sample_noalloc(const float *target_logits, const float *draft_logits,
+                                      const int32_t *parent, const int32_t *token, int32_t B,
+                                      int32_t N, int32_t V, double temperature, uint64_t seed,
+                                      uint64_t offset, int32_t *path, int32_t *n_accepted,
+                                      int32_t *out_tokens, uint32_t *dev_flags, void *stream);
 
 /*
  * kv_commit_path — keep the accepted path's K/V, discarding the rest.

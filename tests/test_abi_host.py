@@ -226,3 +226,16 @@ def test_attention_plan_rejects_bad_arguments():
     assert lib.tav_attn_plan(1, 5, 8, 2, 128, 64, 256, 1, None) == tav.ERR_ARG
     assert lib.tav_attn_plan(1, 5, 8, 2, 128, 64, 0, 1, ctypes.cast(plan, P)) == tav.ERR_ARG
     assert lib.tav_attn_plan(1, 5, 8, 2, 96, 64, 256, 1, ctypes.cast(plan, P)) == tav.ERR_UNSUPPORTED
+
+
+def test_noalloc_sampler_rejects_bad_arguments_before_any_device_work():
+    lib = tav.lib()
+    fn = lib.spec_verify_sample_noalloc
+    base = dict(tl=FAKE, dl=FAKE, parent=FAKE, token=FAKE, B=2, N=5, V=1000, T=1.0, seed=0,
+                offset=0, path=FAKE, n_acc=FAKE, out_tok=FAKE, flags=None, stream=None)
+    for kw, code in [(dict(tl=None), tav.ERR_ARG), (dict(B=0), tav.ERR_ARG),
+                     (dict(T=-1.0), tav.ERR_ARG), (dict(N=257), tav.ERR_UNSUPPORTED),
+                     (dict(V=(1 << 21) + 1), tav.ERR_UNSUPPORTED), (dict(dl=None), tav.ERR_ARG)]:
+        args = dict(base)
+        args.update(kw)
+        assert fn(*args.values()) == code, kw

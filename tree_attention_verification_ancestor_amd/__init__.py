@@ -71,6 +71,8 @@ _SIGNATURES = {
                                   _P, _P, _SZ, _P, _P]),
     "spec_verify_sample_probe": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _F64, _U64, _U64, _P,
                                         _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
+    "spec_verify_sample_noalloc": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _F64, _U64, _U64,
+                                          _P, _P, _P, _P, _P]),
     "kv_commit_path": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _P, _I32, _I32, _I32,
                               _I32, _I32, _P, _P, _P, _P]),
     "kv_commit_inplace": (_I32, [_P, _P, _I32, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
@@ -339,6 +341,37 @@ def spec_verify_sample_probe(target_logits, draft_logits, parent, token,
         _ptr(out_tokens), _ptr(p_rows), _ptr(q_rows), _ptr(child_pq), _ptr(workspace), ws_bytes,
         _ptr(dev_flags), _stream(stream)))
     return path, n_accepted, out_tokens, p_rows, q_rows, child_pq
+
+
+def spec_verify_sample_noalloc(target_logits, draft_logits, parent, token,
+                               temperature: float = 1.0, seed: int = 0, offset: int = 0,
+                               path=None, n_accepted=None, out_tokens=None, dev_flags=None,
+                               stream=None):
+    """``spec_verify_sample`` on the library's fixed per-device scratch: no
+    workspace argument and no allocation inside the call (pass preallocated
+    outputs to allocate nothing at all). Calls on one device must not overlap
+    in time."""
+    _need(target_logits, "target_logits", (torch.float32,))
+    B, N, V = target_logits.shape
+    dev = target_logits.device
+    if draft_logits is not None or temperature != 0:
+        _need(draft_logits, "draft_logits", (torch.float32,), (B, N, V), dev)
+    _need(parent, "parent", _I32T, (B, N), dev)
+    _need(token, "token", _I32T, (B, N), dev)
+    if path is None:
+        path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if n_accepted is None:
+        n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    _need(path, "path", _I32T, (B, N), dev)
+    _need(n_accepted, "n_accepted", _I32T, (B,), dev)
+    _need(out_tokens, "out_tokens", _I32T, (B, N), dev)
+    _check("spec_verify_sample_noalloc", lib().spec_verify_sample_noalloc(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(parent), _ptr(token), B, N, V,
+        float(temperature), int(seed), int(offset), _ptr(path), _ptr(n_accepted),
+        _ptr(out_tokens), _ptr(dev_flags), _stream(stream)))
+    return path, n_accepted, out_tokens
 
 
 def spec_verify_sample_wor(target_logits, draft_logits, parent, token,
