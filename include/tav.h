@@ -423,15 +423,23 @@ tav_status tav_target_probs(const float *logits, int64_t rows, int32_t V, double
  * order of the draws kept, so a tree grown from them is one for which
  * spec_verify_sample_wor is lossless. The glossary's top-k branching
  * (jisaku.com glossary, tree-topology strategies) with the k most likely
- * tokens replaced by k draws; the draw is the Gumbel-top-k construction:
- * each token gets the key fl32(fl32(x * fl32(1/T)) + fl32(G)), G = -log(-log
- * u) in fp64 with u = ((w >> 11) + 1/2) * 2^-53 from Philox4x64-10 word
- * (token mod 4) at counter (offset, row, token / 4, 1) under key (seed, 0)
- * (the node uniforms of spec_verify_sample use counter word 3 = 0), and the
- * k largest keys, the lower token first among equal keys, are the draws in
- * order. Keys are rounded to fp32, so the draw follows q to about 1e-6
- * relative. top_logq and entropy are as in tree_expand_topk; arguments,
- * workspace (tree_expand_workspace_bytes), limits and flags too.
+ * tokens replaced by k draws; the draw is the Gumbel-top-k construction: the
+ * k largest keys x/T + G, the lower token first among equal keys, are the
+ * draws in order. Each key is formed in fp64 exactly as written: x/T with
+ * x widened from fp32, G = -log(-log u), u = fl64(m + 1/2) 2^-53 for the
+ * 53-bit integer m = hi 2^21 + lo of token t in row r:
+ *   hi  SplitMix64 (Steele, Lea, Flood 2014) seeded with K, output number
+ *       r 2^20 + t/2 + 1 (its high half for even t, low half for odd t),
+ *       K = word 0 of Philox4x64-10 at counter (offset, 0, 0, 3), key (seed, 0);
+ *   lo  the top 21 bits of 32-bit half (t mod 8)/4 (0: high) of word
+ *       (t mod 8) mod 4 of Philox4x64-10 at counter (offset, r, t/8, 2),
+ *       key (seed, 0)
+ * (the node uniforms of spec_verify_sample use counter word 3 = 0). The
+ * kernels bound every key from hi alone in fp32 and form the exact fp64 key
+ * only for the few tokens whose bounds reach the k-th; a result differs from
+ * exact arithmetic only where two keys agree to the last bits of the fp64
+ * log. top_logq and entropy are as in tree_expand_topk; arguments, workspace
+ * (tree_expand_workspace_bytes), limits and flags too; R < 2^44.
  */
 tav_status tree_expand_sample(const float *draft_logits, int64_t R, int32_t V, int32_t k,
                               double temperature, uint64_t seed, uint64_t offset,

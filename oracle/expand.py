@@ -45,29 +45,71 @@ def expand_topk(draft_logits, k: int, temperature: float = 1.0):
     return tok, logq, ent
 
 
-def gumbel_keys(draft_logits, temperature: float, seed: int, offset: int):
-    """float32 [R, V] sampling keys: y + G with y = x * (1/T) and G a standard
-    Gumbel draw, both rounded to float32 and added in float32.
+SPLITMIX_GAMMA = 0x9E3779B97F4A7C15
 
-    G = -log(-log u) with u = ((w >> 11) + 1/2) * 2^-53 from Philox4x64-10
-    word (token mod 4) at counter (offset, row, token div 4, 1) under key
-    (seed, 0); the walk's node uniforms use counter word 3 = 0, so the two
-    streams never meet.
+
+def splitmix64(state):
+    """SplitMix64 output for each uint64 state (the state after its Weyl
+    increment): Steele, Lea and Flood, "Fast splittable pseudorandom number
+    generators" (OOPSLA 2014), with the finalizer of Vigna's reference code:
+    z ^= z >> 30, z *= 0xBF58476D1CE4E5B9, z ^= z >> 27, z *= 0x94D049BB133111EB,
+    z ^= z >> 31 (arithmetic mod 2^64)."""
+    z = np.asarray(state, dtype=np.uint64).copy()
+    with np.errstate(over="ignore"):
+        z ^= z >> np.uint64(30)
+        z *= np.uint64(0xBF58476D1CE4E5B9)
+        z ^= z >> np.uint64(27)
+        z *= np.uint64(0x94D049BB133111EB)
+        z ^= z >> np.uint64(31)
+    return z
+
+
+def gumbel_uniforms(R: int, V: int, seed: int, offset: int):
+    """float64 [R, V] uniforms of the sampling keys: u = fl64(m + 1/2) 2^-53
+    with the 53-bit integer m = hi 2^21 + lo.
+
+    hi (32 bits) of token t in row r: SplitMix64 seeded with K, output number
+    r 2^20 + t div 2 + 1, i.e. the finalizer of K + (r 2^20 + t div 2 + 1) gamma,
+    taking its high half for even t and its low half for odd t; K is word 0 of
+    Philox4x64-10 at counter (offset, 0, 0, 3) under key (seed, 0).
+    lo (21 bits): the top 21 bits of 32-bit half (t mod 8) div 4 (0: high,
+    1: low) of word (t mod 8) mod 4 of Philox4x64-10 at counter
+    (offset, r, t div 8, 2) under key (seed, 0).
+    The walk's node uniforms use counter word 3 = 0, so no stream meets them.
     """
     from .sampling import philox4x64_10
-    x = np.asarray(draft_logits, dtype=np.float32)
-    R, V = x.shape
-    invT = np.float32(1.0 / float(temperature))
-    nq = (V + 3) // 4
-    ctr = np.zeros((R, nq, 4), np.uint64)
+    K = philox4x64_10(np.array([[offset, 0, 0, 3]], np.uint64), (seed, 0))[0, 0]
+    idx = (np.arange(R, dtype=np.uint64)[:, None] << np.uint64(20)) + \
+        (np.arange(V, dtype=np.uint64)[None, :] >> np.uint64(1)) + np.uint64(1)
+    with np.errstate(over="ignore"):
+        z = splitmix64(K + idx * np.uint64(SPLITMIX_GAMMA))
+    odd = (np.arange(V) & 1).astype(bool)[None, :]
+    hi = np.where(odd, z & np.uint64(0xFFFFFFFF), z >> np.uint64(32))
+
+    nb = (V + 7) // 8
+    ctr = np.zeros((R, nb, 4), np.uint64)
     ctr[:, :, 0] = np.uint64(offset)
     ctr[:, :, 1] = np.arange(R, dtype=np.uint64)[:, None]
-    ctr[:, :, 2] = np.arange(nq, dtype=np.uint64)[None, :]
-    ctr[:, :, 3] = np.uint64(1)
-    w = philox4x64_10(ctr.reshape(-1, 4), (seed, 0)).reshape(R, nq * 4)[:, :V]
-    u = ((w >> np.uint64(11)).astype(np.float64) + 0.5) * 2.0 ** -53
+    ctr[:, :, 2] = np.arange(nb, dtype=np.uint64)[None, :]
+    ctr[:, :, 3] = np.uint64(2)
+    w = philox4x64_10(ctr.reshape(-1, 4), (seed, 0)).reshape(R, nb, 4)
+    halves = np.empty((R, nb, 8), np.uint64)
+    halves[:, :, :4] = w >> np.uint64(32)                   # tokens 8j .. 8j+3
+    halves[:, :, 4:] = w & np.uint64(0xFFFFFFFF)            # tokens 8j+4 .. 8j+7
+    lo = halves.reshape(R, nb * 8)[:, :V] >> np.uint64(11)
+    m = (hi << np.uint64(21)) | lo
+    return (m.astype(np.float64) + 0.5) * 2.0 ** -53
+
+
+def gumbel_keys(draft_logits, temperature: float, seed: int, offset: int):
+    """float64 [R, V] sampling keys x/T + G, G = -log(-log u) a standard
+    Gumbel draw from ``gumbel_uniforms``; x/T and the sum in float64."""
+    x = np.asarray(draft_logits, dtype=np.float32)
+    R, V = x.shape
+    u = gumbel_uniforms(R, V, seed, offset)
     g = -np.log(-np.log(u))
-    return (x * invT).astype(np.float32) + g.astype(np.float32)
+    with np.errstate(invalid="ignore"):
+        return x.astype(np.float64) / float(temperature) + g
 
 
 def expand_sample(draft_logits, k: int, temperature: float, seed: int, offset: int):
@@ -77,7 +119,8 @@ def expand_sample(draft_logits, k: int, temperature: float, seed: int, offset: i
     row by x/T plus independent Gumbel noise and keeping the k largest is a
     draw of k tokens from q without replacement, largest key first being the
     order of sequential draws (the Gumbel-top-k construction). Keys are
-    those of ``gumbel_keys``; the lower token first among equal keys.
+    those of ``gumbel_keys`` (float64); the lower token first among equal
+    keys.
     Returns (token int32 [R, k], log q float64 [R, k], entropy float64 [R])
     with log q and the entropy as in ``expand_topk``. Raises ValueError as
     ``expand_topk`` does.
@@ -90,7 +133,7 @@ def expand_sample(draft_logits, k: int, temperature: float, seed: int, offset: i
     if np.isnan(x).any() or not np.isfinite(x.max(axis=1)).all():
         bad = int(np.nonzero(np.isnan(x).any(axis=1) | ~np.isfinite(x.max(axis=1)))[0][0])
         raise ValueError(f"oracle expand: non-finite logits (row {bad})")
-    order = np.argsort(-keys.astype(np.float64), axis=1, kind="stable")   # ties: lower token
+    order = np.argsort(-keys, axis=1, kind="stable")   # ties: lower token
     tok = order[:, :k].astype(np.int32)
     q = softmax(x, temperature)
     with np.errstate(divide="ignore"):

@@ -81,3 +81,26 @@ def test_expand_flags_non_finite_rows():
     assert (tok[1:] == -1).all() and np.isnan(ent[1:]).all()
     rt, rl, re = oracle.expand_topk(x[:1], 4, 1.0)
     np.testing.assert_array_equal(tok[:1], rt)
+
+
+def test_topk_large_logits_match_oracle():
+    """Blocks of equal large logits at T != 1: the sums rebase every term to
+    the wave's maximum with products rounded on their own, so the maximum's
+    term is exactly 1 (a fused product would leave its rounding error there
+    and bend log q by it)."""
+    say("expand topk: large equal logits, T = 0.9")
+    rng = np.random.default_rng(41)
+    dev = device()
+    for big in (1e30, 1e10, 1e4, 100.0):
+        x = rng.standard_normal((3, 9000)).astype(np.float32)
+        x[0, 100:400] = big
+        x[1, 5000:5100] = big
+        x[2, ::7] = big
+        flags = tav.new_flags(dev)
+        tok, lq, ent = tav.tree_expand_topk(torch.from_numpy(x).to(dev), 6, 0.9, dev_flags=flags)
+        torch.cuda.synchronize()
+        assert int(flags.item()) == 0
+        rt, rl, re = oracle.expand_topk(x, 6, 0.9)
+        np.testing.assert_array_equal(to_numpy(tok), rt)
+        np.testing.assert_allclose(to_numpy(lq), rl, rtol=0, atol=1e-5)
+        np.testing.assert_allclose(to_numpy(ent), re, rtol=0, atol=1e-5)

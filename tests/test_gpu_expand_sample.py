@@ -2,12 +2,13 @@
 Gumbel top-k) against the oracle, and the sampled tree verified by the
 without-replacement walk on the GPU.
 
-The sampling keys are fl32(fl32(x/T) + fl32(G)) on both sides; G is an fp64
--log(-log u) on the same Philox draw, computed with each side's own fp64 log
-(within an ulp of each other), so a key may differ by one fp32 ulp where G
-sits at an fp32 rounding boundary. A row's tokens may therefore differ only
-where two of its k + 1 best oracle keys are within two ulps; such rows are
-counted and must be rare. log q and the entropy are as for tree_expand_topk.
+Both sides form every key the same way in float64 (x/T + G, G = -log(-log u)
+on the same 53-bit uniform); they differ only in their log routines, each
+within an ulp, so two keys can be ordered differently only if they agree to
+about 1e-15 relative. A row may therefore differ from the oracle only if two
+of its k + 1 best oracle keys are within 1e-12 relative of each other, and
+such rows must be under 1e-4 of all rows (none at these sizes). log q and the
+entropy are as for tree_expand_topk.
 """
 
 import numpy as np
@@ -23,6 +24,8 @@ from gpu_helpers import compare_walk, device, say, walk_arrays
 
 pytestmark = pytest.mark.gpu
 EXPAND_TOL = 1e-5
+TIE_REL = 1e-12          # keys closer than this may be ordered either way
+EXCUSE_RATE = 1e-4       # rows
 
 
 def run_sample(x, k, T, seed, offset):
@@ -35,10 +38,30 @@ def run_sample(x, k, T, seed, offset):
 
 
 def _near_tie(keys_row, k):
-    top = np.sort(keys_row.astype(np.float32))[::-1][:k + 1]
+    top = np.sort(keys_row)[::-1][:k + 1]
     top = top[np.isfinite(top)]
     gaps = top[:-1] - top[1:]
-    return bool((gaps <= 2 * np.spacing(np.abs(top[:-1]))).any())
+    return bool((gaps <= TIE_REL * np.abs(top[:-1])).any())
+
+
+def _compare(x, k, T, seed, offset):
+    tok, lq, ent, flags = run_sample(x, k, T, seed, offset)
+    assert flags == 0
+    rt, rl, re = oracle.expand_sample(x, k, T, seed, offset)
+    keys = oracle.gumbel_keys(x, T, seed, offset)
+    R = x.shape[0]
+    excused = 0
+    for r in range(R):
+        if (tok[r] == rt[r]).all():
+            ok = np.isfinite(rl[r])
+            np.testing.assert_allclose(lq[r][ok], rl[r][ok], rtol=0, atol=EXPAND_TOL)
+            assert (lq[r][~ok] == rl[r][~ok]).all()
+            continue
+        assert _near_tie(keys[r], k), f"row {r}: gpu {tok[r]} oracle {rt[r]}"
+        excused += 1
+    assert excused <= EXCUSE_RATE * R, (excused, R)
+    assert float(np.abs(ent - re).max()) <= EXPAND_TOL
+    return tok
 
 
 @pytest.mark.parametrize("R,V,k,T,scale,seed,offset", [
@@ -48,26 +71,39 @@ def _near_tie(keys_row, k):
     (33, 1000, 5, 1.0, 2.0, 4, 1),
     (9, 4097, 16, 1.0, 0.5, 5, 2),
     (5, 8, 8, 1.0, 1.0, 6, 3),
+    (7, 2049, 3, 1.0, 12.0, 7, 4),
 ])
 def test_sample_matches_oracle(R, V, k, T, scale, seed, offset):
-    say(f"expand sample: R={R} V={V} k={k} T={T}")
+    say(f"expand sample: R={R} V={V} k={k} T={T} scale={scale}")
     rng = np.random.default_rng(V + 7 * k)
     x = (rng.standard_normal((R, V)) * scale).astype(np.float32)
-    tok, lq, ent, flags = run_sample(x, k, T, seed, offset)
-    assert flags == 0
-    rt, rl, re = oracle.expand_sample(x, k, T, seed, offset)
-    keys = oracle.gumbel_keys(x, T, seed, offset)
-    excused = 0
-    for r in range(R):
-        if (tok[r] == rt[r]).all():
-            np.testing.assert_allclose(lq[r], rl[r], rtol=0, atol=EXPAND_TOL)
-            continue
-        assert _near_tie(keys[r], k), f"row {r}: gpu {tok[r]} oracle {rt[r]}"
-        excused += 1
-    assert excused <= max(1, R // 50)
-    assert float(np.abs(ent - re).max()) <= EXPAND_TOL
+    tok = _compare(x, k, T, seed, offset)
     for r in range(R):
         assert len(set(tok[r].tolist())) == k
+
+
+def test_sample_edge_rows_match_oracle():
+    """Rows that take the rarer paths: a block of equal huge logits (every
+    key ties in float64, so the wave resolves its many contenders exactly
+    and the lowest tokens win), rows masked to -inf except a few tokens
+    (fewer finite tokens than k: the lowest -inf tokens follow), a whole
+    masked share, and a row of equal logits."""
+    say("expand sample: edge rows")
+    rng = np.random.default_rng(31)
+    R, V, k = 6, 9000, 6
+    x = rng.standard_normal((R, V)).astype(np.float32)
+    x[0, 100:400] = 1e30
+    x[1, :] = -np.inf
+    x[1, [7, 4100, 8999]] = (0.5, 2.0, -1.0)
+    x[2, 2048:6144] = -np.inf
+    x[3, :] = 0.25
+    x[4, :] = -np.inf
+    x[4, 3] = 1.0
+    x[5, 5000:5100] = 40.0
+    tok = _compare(x, k, 0.9, 17, 2)
+    assert (tok[0] == np.arange(100, 100 + k)).all()
+    assert sorted(tok[1][:3].tolist()) == [7, 4100, 8999]   # the finite ones first
+    assert tok[1][3:].tolist() == [0, 1, 2]                 # then the lowest -inf tokens
 
 
 def test_one_draw_follows_q_on_gpu():

@@ -10,8 +10,15 @@ What fixes it independently of its code:
     without-replacement rule, emits first tokens that follow p, and the
     i.i.d. rule on the same children fails the same test;
   * log q and the entropy are expand_topk's for the chosen tokens, and the
-    draws depend only on (seed, offset, row, token).
+    draws depend only on (seed, offset, row, token);
+  * the uniforms: SplitMix64 gives the published outputs for seed 0
+    (tests/golden/splitmix64_seed0.txt); the Gumbel noise built from the
+    uniforms follows the standard Gumbel law (Kolmogorov-Smirnov over 10^6
+    tokens); the high words of the two tokens sharing a SplitMix output, and
+    the low bits of the tokens sharing a Philox word, are uncorrelated; the
+    keys are x/T + G in float64.
 """
+import os
 
 import numpy as np
 import pytest
@@ -96,3 +103,49 @@ def test_logq_entropy_and_determinism():
         bad = x.copy()
         bad[2, 7] = np.nan
         oracle.expand_sample(bad, 2, 1.0, 0, 0)
+
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "splitmix64_seed0.txt")
+
+
+def test_splitmix64_published_outputs():
+    from oracle.expand import SPLITMIX_GAMMA, splitmix64
+    want = [int(line.split()[1], 16) for line in open(GOLDEN)
+            if line.strip() and not line.startswith("#")]
+    states = np.array([(SPLITMIX_GAMMA * (i + 1)) % 2**64 for i in range(len(want))], np.uint64)
+    assert [int(z) for z in splitmix64(states)] == want
+
+
+def test_gumbel_noise_follows_the_gumbel_law():
+    import scipy.stats
+    from oracle.expand import gumbel_uniforms
+    u = gumbel_uniforms(8, 125000, seed=7, offset=3).ravel()
+    assert (u > 0).all() and (u < 1).all()
+    g = -np.log(-np.log(u))
+    assert scipy.stats.kstest(g, scipy.stats.gumbel_r.cdf).pvalue > 1e-3
+    # on the 53-bit grid: (u 2^53 - 1/2) is an integer
+    m = u * 2.0 ** 53 - 0.5
+    assert (m[u < 0.5] == np.floor(m[u < 0.5])).all()
+
+
+def test_uniform_words_are_not_shared_or_correlated():
+    from oracle.expand import gumbel_uniforms
+    u = gumbel_uniforms(4, 1 << 16, seed=1, offset=0)
+    # tokens 2i and 2i+1 share a SplitMix output; 8j..8j+7 share a Philox block
+    for a, b in ((0, 1), (0, 4), (1, 5), (3, 7), (0, 8)):
+        x, y = u[:, a::16].ravel(), u[:, b::16].ravel()
+        assert abs(np.corrcoef(x, y)[0, 1]) < 0.02, (a, b)
+        assert (x != y).all()
+    # rows and offsets give different streams
+    assert (gumbel_uniforms(2, 64, 1, 0)[0] != gumbel_uniforms(2, 64, 1, 0)[1]).all()
+    assert (gumbel_uniforms(1, 64, 1, 0) != gumbel_uniforms(1, 64, 1, 1)).all()
+
+
+def test_keys_are_x_over_T_plus_gumbel_in_float64():
+    from oracle.expand import gumbel_uniforms
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((3, 500)) * 2).astype(np.float32)
+    k = oracle.gumbel_keys(x, 0.7, 5, 6)
+    assert k.dtype == np.float64
+    u = gumbel_uniforms(3, 500, 5, 6)
+    np.testing.assert_array_equal(k, x.astype(np.float64) / 0.7 - np.log(-np.log(u)))
