@@ -2,24 +2,29 @@
 
 A step is one pass of the whole path over one batch: tree_mask_build,
 tree_attn_verify (one attention layer), spec_verify_sample and kv_commit_path,
-chained on one stream with no host synchronisation. The workload is the
-Llama-3-70B-shaped layer: batch 8, 64-node trees (depth 6, width 4), 64 query
-/ 8 KV heads, head_dim 128, paged prefixes of 6144..8192 tokens, a 128256-entry
-vocabulary. Inputs are seeded synthetic data already resident in HBM; three
-copies of the paged caches rotate across steps so the 256 MB last-level cache
-cannot hold the step's KV working set.
+chained on one stream with no host synchronisation. Inputs are seeded
+synthetic data already resident in HBM.
 
-Prints one JSON line: verified tree nodes/s (B*N per step time), with the
-attention launch's roofline and the CPU oracle's rate on this host; per-stage
-and per-step percentiles from a second pass with events between the calls;
-and, outside the timed regions, the walk's acceptance over many Philox
-offsets (mean accepted length, emitted tokens, rows visited). The
-attention launch (main kernel + combine) is timed with events on its stream
-inside the timed region; its HBM traffic comes from the rocprofv3 counter
-record under profiles/ while that record matches the kernel source.
+The headline workload is the Llama-3-70B-shaped layer: batch 8, 64-node trees
+(depth 6, width 4), 64 query / 8 KV heads, head_dim 128, paged prefixes of
+6144..8192 tokens, a 128256-entry vocabulary. Three copies of its paged caches
+rotate across steps so the 256 MB last-level cache cannot hold the step's KV
+working set. Its line carries the attention launch's roofline (events on the
+launch stream inside the timed region; HBM traffic from the rocprofv3
+counter record under profiles/ while that record matches the kernel source),
+the CPU oracle's rate on this host, per-stage percentiles, the acceptance over
+many Philox offsets, and timed legs of the other calls.
+
+`configs` reports the other workloads the same way, each step timed on its
+own with a 512 MB write between steps (so the last-level cache starts cold,
+as it would after a model's other layers): the tiny worked example, the
+Llama-3-8B layer at batch 1, the batch sweep (batch 1..128, a 16-node tree
+against a 6-node chain, mean acceptance 0.5 / 0.8 / 0.9) and the 32K-token
+long context. Each has step us, nodes/s, emitted tokens per step, realised
+acceptance, the attention roofline and the oracle's rate on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config llama70b] [--no-cpu]
-                    [--offsets 1000]
+                    [--offsets 1000] [--no-configs] [--config-steps 20]
     python bench.py --copy-calibration     # a plain copy of known size, for the counters
 """
 
@@ -41,22 +46,14 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "tree_attn_llama70b_hbm_traffic.txt")
 COPY_BYTES = 1 << 30           # each of the calibration copy's read and write
+FLUSH_BYTES = 512 << 20        # written between the configs' steps
+SWEEP_BATCHES = (1, 4, 16, 64, 128)
+SWEEP_ACCEPTS = (0.5, 0.8, 0.9)
+STAGES = ["tree_mask_build", "tree_attn_verify", "spec_verify_sample", "kv_commit_path"]
 
 
-def speedup_model(sizes, size_us):
-    """The pages' speedup model fed by this GPU's step times: alpha from the
-    times at tree sizes 1..N, then the best chain length and its model
-    speedup at acceptance 0.8 and 0.9 with no draft cost."""
-    import tree_attention_verification_ancestor_amd as tav
-
-    alpha = tav.fit_alpha(sizes, size_us)
-    rec = {"n": sizes, "step_us": [round(t, 2) for t in size_us], "alpha": round(alpha, 5),
-           "ceiling": round(1.0 / alpha, 2) if alpha > 0 else None, "best_chain": {}}
-    for p in (0.8, 0.9):
-        n, s = tav.best_chain_length(p, 0.0, alpha, 1024)
-        rec["best_chain"][str(p)] = {"n": n, "speedup": round(s, 3)}
-    return rec
-
+# ---------------------------------------------------------------------------
+# algorithmic work
 
 def workload_desc(w) -> str:
     return (f"{w.name}: B={w.B}, N={w.N}-node trees, {w.Hq}/{w.Hkv} heads, D={w.D}, "
@@ -93,78 +90,200 @@ def commit_bytes(w, n_acc):
     return int((n_acc + 1).sum()) * w.Hkv * w.D * 2 * 2 * 2
 
 
-def run_gpu(args, w):
+def roofline(bytes_, flops, seconds):
+    """The binding roofline of a launch of this work taking `seconds`."""
+    t_hbm = bytes_ / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_PEAK_TFLOPS * 1e12)
+    if t_mfma >= t_hbm:
+        ach = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS, 4)}
+    ach = bytes_ / seconds / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4)}
+
+
+def acceptance_stats(w, paths, naccs):
+    """Over Philox offsets: mean accepted per sequence, mean emitted tokens
+    per step (accepted + 1 per sequence), the realised acceptance (children
+    accepted / children tested: a child after its earlier siblings' rejection
+    is one more test), and the mean rows the walk must read."""
+    B, N = w.parent.shape
+    rank = np.zeros((B, N), np.int64)       # position among its parent's children, from 1
+    nkids = np.zeros((B, N), np.int64)
+    for b in range(B):
+        for i in range(1, N):
+            u = int(w.parent[b, i])
+            nkids[b, u] += 1
+            rank[b, i] = nkids[b, u]
+    tests = acc = 0
+    for o in range(len(naccs)):
+        for b in range(B):
+            m = int(naccs[o, b])
+            p = paths[o, b, :m + 1]
+            tests += int(rank[b, p[1:]].sum()) + int(nkids[b, p[-1]])
+            acc += m
+    samp = float(np.mean([sampler_bytes(w, paths[o], naccs[o]) for o in range(len(naccs))]))
+    comm = float(np.mean([commit_bytes(w, naccs[o]) for o in range(len(naccs))]))
+    return {"offsets": int(len(naccs)),
+            "mean_accepted_per_seq": round(float(naccs.mean()), 4),
+            "mean_emitted_per_step": round(float((naccs + 1).sum(axis=1).mean()), 3),
+            "realised_acceptance": round(acc / tests, 4) if tests else None,
+            "mean_sampler_bytes": round(samp), "mean_commit_bytes": round(comm)}
+
+
+def pct(a):
+    return {"p10": round(float(np.percentile(a, 10)) * 1e3, 2),
+            "p50": round(float(np.percentile(a, 50)) * 1e3, 2),
+            "p90": round(float(np.percentile(a, 90)) * 1e3, 2)}
+
+
+# ---------------------------------------------------------------------------
+# the step on the GPU
+
+class StepRunner:
+    """The four calls of a step over one workload, pre-marshalled, with
+    `copies` copies of the paged caches to rotate through."""
+
+    def __init__(self, w, dev, copies=1):
+        import torch
+
+        import tree_attention_verification_ancestor_amd as tav
+        from synth.device import upload
+
+        self.w, self.dev, self.torch, self.tav = w, dev, torch, tav
+        d = upload(w, dev)
+        self.d = d
+        self.copies = [(d["k_cache"], d["v_cache"])]
+        for _ in range(copies - 1):
+            self.copies.append((d["k_cache"].clone(), d["v_cache"].clone()))
+        B, N, V = w.B, w.N, w.V
+        self.flags = tav.new_flags(dev)
+        self.mask = torch.empty((B, N, (N + 63) // 64), dtype=torch.int64, device=dev)
+        self.depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, N, w.Hq, w.D), dtype=torch.float32, device=dev)
+        self.ws_a = torch.empty(max(1, tav.tree_attn_workspace_bytes(B, N, w.Hq, w.Hkv, w.D,
+                                                                     w.max_prefix_len)),
+                                dtype=torch.uint8, device=dev)
+        self.ws_s = tav.new_sampler_workspace(B, N, V, dev)
+        self.path = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.n_acc = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.toks = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.slots = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.new_len = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.stream = torch.cuda.current_stream()
+        s = self.stream
+        # one checked call of each entry point, then pre-marshalled calls
+        tav.tree_mask_build(d["parent"], self.mask, self.depth, self.flags, s)
+        tav.tree_attn_verify(d["q"], d["k_tree"], d["v_tree"], self.copies[0][0],
+                             self.copies[0][1], d["block_table"], d["prefix_len"],
+                             w.max_prefix_len, self.mask, w.scale, self.out, self.ws_a,
+                             self.flags, s)
+        tav.spec_verify_sample(d["target_logits"], d["draft_logits"], d["parent"], d["token"],
+                               w.temperature, w.philox_seed, w.philox_offset, self.path,
+                               self.n_acc, self.toks, self.ws_s, self.flags, s)
+        tav.kv_commit_path(d["k_tree"], d["v_tree"], self.path, self.n_acc, d["block_table"],
+                           d["prefix_len"], self.copies[0][0], self.copies[0][1], self.slots,
+                           self.new_len, self.flags, s)
+        torch.cuda.synchronize()
+        nblk, maxb = int(w.k_cache.shape[0]), int(w.block_table.shape[1])
+        self.calls = []
+        for kc, vc in self.copies:
+            self.calls.append((
+                tav.prepare("tree_mask_build", d["parent"], B, N, self.mask, self.depth,
+                            self.flags, s),
+                tav.prepare("tree_attn_verify", d["q"], d["k_tree"], d["v_tree"], kc, vc, nblk,
+                            d["block_table"], maxb, d["prefix_len"], w.max_prefix_len,
+                            self.mask, B, N, w.Hq, w.Hkv, w.D, w.block, w.scale, self.out,
+                            self.ws_a, self.ws_a.numel(), self.flags, s),
+                tav.prepare("spec_verify_sample", d["target_logits"], d["draft_logits"],
+                            d["parent"], d["token"], B, N, V, w.temperature, w.philox_seed,
+                            w.philox_offset, self.path, self.n_acc, self.toks, self.ws_s,
+                            self.ws_s.numel(), self.flags, s),
+                tav.prepare("kv_commit_path", d["k_tree"], d["v_tree"], self.path, self.n_acc,
+                            nblk, d["block_table"], maxb, d["prefix_len"], kc, vc, B, N, w.Hkv,
+                            w.D, w.block, self.slots, self.new_len, self.flags, s),
+            ))
+        self.i = 0
+
+    def step(self, ev=None, attn_ev=None):
+        c = self.calls[self.i % len(self.calls)]
+        self.i += 1
+        if ev:
+            ev[0].record(self.stream)
+        for k in range(4):
+            if attn_ev and k == 1:
+                attn_ev[0].record(self.stream)
+            c[k]()
+            if attn_ev and k == 1:
+                attn_ev[1].record(self.stream)
+            if ev:
+                ev[k + 1].record(self.stream)
+
+    def ramp(self, seconds=0.3):
+        """Steps until `seconds` have passed: the device reaches its working
+        clock before anything is timed."""
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(10):
+                self.step()
+            self.torch.cuda.synchronize()
+
+    def events(self, n):
+        E = self.torch.cuda.Event
+        return [[E(enable_timing=True) for _ in range(n)]]
+
+    def check(self):
+        self.torch.cuda.synchronize()
+        f = int(self.flags.item())
+        assert f == 0, f"device flags {f:#x}"
+
+    def offsets(self, n):
+        """The walk at Philox offsets 0..n-1 (outside every timed region)."""
+        torch, tav, d, w = self.torch, self.tav, self.d, self.w
+        paths = torch.empty((n, w.B, w.N), dtype=torch.int32, device=self.dev)
+        naccs = torch.empty((n, w.B), dtype=torch.int32, device=self.dev)
+        toks = torch.empty((n, w.B, w.N), dtype=torch.int32, device=self.dev)
+        for o in range(n):
+            tav.spec_verify_sample(d["target_logits"], d["draft_logits"], d["parent"], d["token"],
+                                   w.temperature, w.philox_seed, o, paths[o], naccs[o], toks[o],
+                                   self.ws_s, self.flags, self.stream)
+        self.check()
+        from synth.device import to_numpy
+        return to_numpy(paths), to_numpy(naccs)
+
+    def cold_steps(self, n, warmup, flush):
+        """n steps, each after a write of `flush` (the last-level cache cold),
+        with events between the calls: per-step and per-stage ms."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n)]
+        for e in evs:
+            flush.fill_(1)
+            self.step(ev=e)
+        self.check()
+        stage = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in evs])
+        step = np.array([e[0].elapsed_time(e[4]) for e in evs])
+        return step, stage
+
+
+def run_headline(args, w):
+    """The headline workload: timed region, stage pass, acceptance and the
+    other calls' legs."""
     import torch
 
     import tree_attention_verification_ancestor_amd as tav
-    from synth.device import to_numpy, upload
+    from synth.device import to_numpy
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    d = upload(w, dev)
-    copies = [(d["k_cache"], d["v_cache"])]
-    for _ in range(args.cache_copies - 1):
-        copies.append((d["k_cache"].clone(), d["v_cache"].clone()))
+    r = StepRunner(w, dev, copies=args.cache_copies)
     B, N, V = w.B, w.N, w.V
-    flags = tav.new_flags(dev)
-    mask = torch.empty((B, N, (N + 63) // 64), dtype=torch.int64, device=dev)
-    depth = torch.empty((B, N), dtype=torch.int32, device=dev)
-    out = torch.empty((B, N, w.Hq, w.D), dtype=torch.float32, device=dev)
-    ws_a = torch.empty(max(1, tav.tree_attn_workspace_bytes(B, N, w.Hq, w.Hkv, w.D,
-                                                            w.max_prefix_len)),
-                       dtype=torch.uint8, device=dev)
-    ws_s = tav.new_sampler_workspace(B, N, V, dev)
-    path = torch.empty((B, N), dtype=torch.int32, device=dev)
-    n_acc = torch.empty((B,), dtype=torch.int32, device=dev)
-    toks = torch.empty((B, N), dtype=torch.int32, device=dev)
-    slots = torch.empty((B, N), dtype=torch.int32, device=dev)
-    new_len = torch.empty((B,), dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream()
-    nblk, maxb = int(w.k_cache.shape[0]), int(w.block_table.shape[1])
-    ws_a_n = ws_a.numel()
-    ws_s_n = ws_s.numel()
-
-    # one checked call of each entry point, then pre-marshalled calls for the loop
-    tav.tree_mask_build(d["parent"], mask, depth, flags, stream)
-    tav.tree_attn_verify(d["q"], d["k_tree"], d["v_tree"], copies[0][0], copies[0][1],
-                         d["block_table"], d["prefix_len"], w.max_prefix_len, mask, w.scale, out,
-                         ws_a, flags, stream)
-    tav.spec_verify_sample(d["target_logits"], d["draft_logits"], d["parent"], d["token"],
-                           w.temperature, w.philox_seed, w.philox_offset, path, n_acc, toks, ws_s,
-                           flags, stream)
-    tav.kv_commit_path(d["k_tree"], d["v_tree"], path, n_acc, d["block_table"], d["prefix_len"],
-                       copies[0][0], copies[0][1], slots, new_len, flags, stream)
-    torch.cuda.synchronize()
-    calls = []
-    for kc, vc in copies:
-        calls.append((
-            tav.prepare("tree_mask_build", d["parent"], B, N, mask, depth, flags, stream),
-            tav.prepare("tree_attn_verify", d["q"], d["k_tree"], d["v_tree"], kc, vc, nblk,
-                        d["block_table"], maxb, d["prefix_len"], w.max_prefix_len, mask, B, N,
-                        w.Hq, w.Hkv, w.D, w.block, w.scale, out, ws_a, ws_a_n, flags, stream),
-            tav.prepare("spec_verify_sample", d["target_logits"], d["draft_logits"], d["parent"],
-                        d["token"], B, N, V, w.temperature, w.philox_seed, w.philox_offset, path,
-                        n_acc, toks, ws_s, ws_s_n, flags, stream),
-            tav.prepare("kv_commit_path", d["k_tree"], d["v_tree"], path, n_acc, nblk,
-                        d["block_table"], maxb, d["prefix_len"], kc, vc, B, N, w.Hkv, w.D,
-                        w.block, slots, new_len, flags, stream),
-        ))
-
-    def step(i, ev=None, attn_ev=None):
-        c = calls[i % len(calls)]
-        if ev:
-            ev[0].record(stream)
-        for k in range(4):
-            if attn_ev and k == 1:
-                attn_ev[0].record(stream)
-            c[k]()
-            if attn_ev and k == 1:
-                attn_ev[1].record(stream)
-            if ev:
-                ev[k + 1].record(stream)
-
-    for i in range(args.warmup):
-        step(i)
+    d, stream, flags = r.d, r.stream, r.flags
+    r.ramp()
+    for _ in range(args.warmup):
+        r.step()
     torch.cuda.synchronize()
 
     # the timed region: exactly `steps` steps between two synchronised events;
@@ -174,25 +293,23 @@ def run_gpu(args, w):
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, attn_ev=attn_evs[i])
+        r.step(attn_ev=attn_evs[i])
     stop.record(stream)
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(stop) / args.steps
-    ms_attn = float(np.mean([e[0].elapsed_time(e[1]) for e in attn_evs]))
+    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in attn_evs])
 
     # per-stage times with events on the launch stream (a second pass)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
-        step(args.warmup + args.steps + i, evs[i])
-    torch.cuda.synchronize()
+        r.step(ev=evs[i])
+    r.check()
     stage = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in evs])
-    stage_ms = stage.mean(axis=0)
-    step_ms = np.array([e[0].elapsed_time(e[4]) for e in evs])
-    assert int(flags.item()) == 0, f"device flags {int(flags.item()):#x}"
-    out = dict(ms_step=ms_step, ms_attn=ms_attn, stage_ms=stage_ms, stage_all=stage,
-               step_all=step_ms, depth=to_numpy(depth), path=to_numpy(path), n_acc=to_numpy(n_acc))
-
+    out = dict(ms_step=ms_step, ms_attn=float(attn_ms.mean()), attn_all=attn_ms,
+               stage_ms=stage.mean(axis=0), stage_all=stage,
+               step_all=np.array([e[0].elapsed_time(e[4]) for e in evs]),
+               depth=to_numpy(r.depth), path=to_numpy(r.path), n_acc=to_numpy(r.n_acc))
     if args.step_only:
         out["offset_paths"] = np.zeros((0, B, N), np.int32)
         out["offset_naccs"] = np.zeros((0, B), np.int32)
@@ -215,6 +332,7 @@ def run_gpu(args, w):
     g_path = torch.empty((B, N), dtype=torch.int32, device=dev)
     g_nacc = torch.empty((B,), dtype=torch.int32, device=dev)
     g_toks = torch.empty((B, N), dtype=torch.int32, device=dev)
+    ws_s, ws_s_n = r.ws_s, r.ws_s.numel()
     out["greedy_ms"] = time_leg(tav.prepare(
         "spec_verify_sample", d["target_logits"], None, d["parent"], d["token"], B, N, V, 0.0, 0,
         0, g_path, g_nacc, g_toks, ws_s, ws_s_n, flags, stream))
@@ -231,9 +349,11 @@ def run_gpu(args, w):
     # the zero-copy rollback on the same paths, timed on its own: it moves
     # rows only inside each sequence's tree positions L..L+N-1, which the
     # attention never reads
+    nblk, maxb = int(w.k_cache.shape[0]), int(w.block_table.shape[1])
     out["inplace_ms"] = time_leg(tav.prepare(
-        "kv_commit_inplace", path, n_acc, nblk, d["block_table"], maxb, d["prefix_len"],
-        copies[0][0], copies[0][1], B, N, w.Hkv, w.D, w.block, slots, new_len, flags, stream))
+        "kv_commit_inplace", r.path, r.n_acc, nblk, d["block_table"], maxb, d["prefix_len"],
+        r.copies[0][0], r.copies[0][1], B, N, w.Hkv, w.D, w.block, r.slots, r.new_len, flags,
+        stream))
 
     # tree expansion over every node's draft row (top-4 tokens, log q,
     # entropy): one read of B*N vocabulary rows
@@ -287,6 +407,7 @@ def run_gpu(args, w):
     # (a best-first tree's first n nodes are its budget-n tree), timed alone
     sizes = [n for n in (1, 2, 4, 8, 16, 32, 64, 128, 256) if n <= N]
     size_us = []
+    kc, vc = r.copies[0]
     for n in sizes:
         sl = {k: d[k][:, :n].contiguous() for k in ("parent", "token", "q", "k_tree", "v_tree",
                                                      "target_logits", "draft_logits")}
@@ -302,7 +423,6 @@ def run_gpu(args, w):
         tk = torch.empty((B, n), dtype=torch.int32, device=dev)
         sl_slots = torch.empty((B, n), dtype=torch.int32, device=dev)
         nl = torch.empty((B,), dtype=torch.int32, device=dev)
-        kc, vc = copies[0]
         seq = (
             tav.prepare("tree_mask_build", sl["parent"], B, n, m_n, dep_n, flags, stream),
             tav.prepare("tree_attn_verify", sl["q"], sl["k_tree"], sl["v_tree"], kc, vc, nblk,
@@ -327,18 +447,41 @@ def run_gpu(args, w):
     # acceptance over many Philox offsets (outside the timed regions): the
     # mean accepted length and the rows the walk visits, for the byte count
     n_off = max(0, args.offsets)
-    paths = torch.empty((n_off, B, N), dtype=torch.int32, device=dev)
-    naccs = torch.empty((n_off, B), dtype=torch.int32, device=dev)
-    toks_o = torch.empty((n_off, B, N), dtype=torch.int32, device=dev)
-    for o in range(n_off):
-        tav.spec_verify_sample(d["target_logits"], d["draft_logits"], d["parent"], d["token"],
-                               w.temperature, w.philox_seed, o, paths[o], naccs[o], toks_o[o],
-                               ws_s, flags, stream)
-    torch.cuda.synchronize()
-    assert int(flags.item()) == 0, f"device flags {int(flags.item()):#x}"
-    out["offset_paths"] = to_numpy(paths)
-    out["offset_naccs"] = to_numpy(naccs)
+    paths, naccs = r.offsets(n_off) if n_off else (np.zeros((0, B, N), np.int32),
+                                                  np.zeros((0, B), np.int32))
+    out["offset_paths"] = paths
+    out["offset_naccs"] = naccs
     return out
+
+
+def run_config(w, steps, warmup, n_offsets, flush, dev):
+    """One workload's step timed cold: step and stage times, attention
+    roofline, acceptance, and the step's roofline at the mean visited rows."""
+    from synth.device import to_numpy
+
+    r = StepRunner(w, dev, copies=1)
+    r.ramp(0.1)
+    step, stage = r.cold_steps(steps, warmup, flush)
+    depth = to_numpy(r.depth)
+    paths, naccs = r.offsets(n_offsets)
+    acc = acceptance_stats(w, paths, naccs)
+    a_bytes, a_flops = attention_work(w, depth)
+    t_attn = float(np.median(stage[:, 1])) * 1e-3
+    t_step = float(np.median(step)) * 1e-3
+    floor = max((a_bytes + acc["mean_sampler_bytes"] + acc["mean_commit_bytes"]) / (HBM_PEAK_GBS * 1e9),
+                a_flops / (MFMA_PEAK_TFLOPS * 1e12))
+    res = {"workload": workload_desc(w), "step_us": round(t_step * 1e6, 2),
+           "step_us_pctl": pct(step), "nodes_per_s": round(w.B * w.N / t_step, 1),
+           "emitted_tokens_per_s": round(acc["mean_emitted_per_step"] / t_step, 1),
+           "stages_us": {k: round(float(np.median(stage[:, i])) * 1e3, 2)
+                         for i, k in enumerate(STAGES)},
+           "tree_attn_roofline": roofline(a_bytes, a_flops, t_attn),
+           "step_roofline": {"floor_us": round(floor * 1e6, 2), "frac": round(floor / t_step, 4)},
+           "acceptance": acc}
+    del r
+    import torch
+    torch.cuda.empty_cache()
+    return res
 
 
 def measured_copy_gbs(reps=5):
@@ -374,25 +517,103 @@ def copy_calibration(reps=5):
     print(json.dumps({"copy_bytes": COPY_BYTES, "reps": reps}), flush=True)
 
 
-def cpu_baseline(w, min_seconds=10.0):
+def cpu_baseline(w, min_seconds=10.0, threads=None, sample=None):
+    """The oracle's whole step (oracle.verify_step_ref) on the host, repeated
+    for at least `min_seconds`, as verified tree nodes/s; `threads` caps the
+    BLAS threads (None: all)."""
     import threadpoolctl
 
     import oracle
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.verify_step_ref(w)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds:
-            break
+    with threadpoolctl.threadpool_limits(limits=threads):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.verify_step_ref(w)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds:
+                break
+        info = threadpoolctl.threadpool_info()
+        blas = max([i.get("num_threads", 1) for i in info] or [1])
     per_step = el / reps
-    info = threadpoolctl.threadpool_info()
-    blas = max([i.get("num_threads", 1) for i in info] or [1])
-    return {"value": w.B * w.N / per_step, "unit": "nodes/s", "cores": int(blas),
+    what = sample or f"the whole step ({w.B} sequences x {w.N} nodes)"
+    return {"value": round(w.B * w.N / per_step, 2), "unit": "nodes/s", "cores": int(blas),
             "kind": "oracle",
-            "sample": (f"the whole step ({w.B} sequences x {w.N} nodes) repeated {reps} times in "
-                       f"{el:.1f} s; fp64 numpy attention on {blas} BLAS threads, "
-                       f"single-threaded C walk; {len(os.sched_getaffinity(0))} cores visible")}
+            "sample": (f"{what} repeated {reps} times in {el:.1f} s; fp64 numpy attention on "
+                       f"{blas} BLAS threads, single-threaded C walk; "
+                       f"{len(os.sched_getaffinity(0))} cores visible")}
+
+
+def run_configs(args, dev):
+    """The tiny, 8B, sweep and long-context workloads."""
+    import torch
+
+    from synth import make_workload
+    from synth.workloads import slice_batch, with_acceptance
+
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    steps, warm, offs = args.config_steps, args.warmup, args.config_offsets
+    cpu = not args.no_cpu
+    res = {}
+
+    def log(msg):
+        print(f"[configs] {msg}", file=sys.stderr, flush=True)
+
+    for name in ("tiny", "llama8b", "long"):
+        w = make_workload(name)
+        log(f"{name}: generated")
+        rec = run_config(w, steps, warm, offs, flush, dev)
+        if cpu:
+            if name == "long":
+                one = slice_batch(w, 1)
+                rec["cpu_baseline"] = cpu_baseline(
+                    one, min_seconds=3.0, sample="one sequence of the batch (128 nodes, 32K prefix)")
+            else:
+                rec["cpu_baseline"] = cpu_baseline(w, min_seconds=3.0)
+                rec["cpu_baseline_1thread"] = cpu_baseline(w, min_seconds=2.0, threads=1)
+        res[name] = rec
+        log(f"{name}: step {rec['step_us']} us")
+        del w
+
+    sweep = []
+    for tname in ("sweep_tree16", "sweep_chain6"):
+        base = make_workload(tname, B=max(SWEEP_BATCHES), accept=SWEEP_ACCEPTS[0],
+                             keep_noise=True)
+        log(f"{tname}: generated")
+        for acc in SWEEP_ACCEPTS:
+            wa = base if acc == SWEEP_ACCEPTS[0] else with_acceptance(base, acc)
+            for B in SWEEP_BATCHES:
+                w = slice_batch(wa, B)
+                rec = run_config(w, steps, warm, offs, flush, dev)
+                rec.update({"tree": tname.split("_")[1], "B": B, "target_acceptance": acc})
+                if cpu and B == 1:
+                    rec["cpu_baseline"] = cpu_baseline(w, min_seconds=1.0,
+                                                       sample="the whole step at batch 1")
+                    rec["cpu_baseline_1thread"] = cpu_baseline(
+                        w, min_seconds=1.0, threads=1, sample="the whole step at batch 1")
+                sweep.append(rec)
+                log(f"{tname} accept {acc} B={B}: step {rec['step_us']} us, "
+                    f"emitted/step {rec['acceptance']['mean_emitted_per_step']}")
+            del wa
+        del base
+    res["sweep"] = sweep
+    del flush
+    torch.cuda.empty_cache()
+    return res
+
+
+def speedup_model(sizes, size_us):
+    """The pages' speedup model fed by this GPU's step times: alpha from the
+    times at tree sizes 1..N, then the best chain length and its model
+    speedup at acceptance 0.8 and 0.9 with no draft cost."""
+    import tree_attention_verification_ancestor_amd as tav
+
+    alpha = tav.fit_alpha(sizes, size_us)
+    rec = {"n": sizes, "step_us": [round(t, 2) for t in size_us], "alpha": round(alpha, 5),
+           "ceiling": round(1.0 / alpha, 2) if alpha > 0 else None, "best_chain": {}}
+    for p in (0.8, 0.9):
+        n, s = tav.best_chain_length(p, 0.0, alpha, 1024)
+        rec["best_chain"][str(p)] = {"n": n, "speedup": round(s, 3)}
+    return rec
 
 
 def main():
@@ -404,10 +625,15 @@ def main():
     ap.add_argument("--cache-copies", type=int, default=3)
     ap.add_argument("--offsets", type=int, default=1000,
                     help="Philox offsets of the acceptance statistics run")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time the headline workload only (no tiny/8B/sweep/long)")
+    ap.add_argument("--config-steps", type=int, default=20, help="timed steps per config")
+    ap.add_argument("--config-offsets", type=int, default=100,
+                    help="Philox offsets of each config's acceptance run")
     ap.add_argument("--step-only", action="store_true",
-                    help="time the step alone: no timed legs for the other calls and no "
-                         "tree-size sweep (for counter passes)")
+                    help="time the step alone: no timed legs for the other calls, no "
+                         "tree-size sweep and no configs (for counter passes)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain copy of known size (for the HBM counters)")
     args = ap.parse_args()
@@ -420,10 +646,12 @@ def main():
         copy_calibration()
         return
 
+    import torch
+
     from synth import make_workload
     from tree_attention_verification_ancestor_amd.profiling import current_traffic
     w = make_workload(args.config)
-    g = run_gpu(args, w)
+    g = run_headline(args, w)
     copy_gbs = measured_copy_gbs()
 
     attn_bytes, attn_flops = attention_work(w, g["depth"])
@@ -432,33 +660,19 @@ def main():
     gbs = attn_bytes / t_attn / 1e9
     t_hbm = attn_bytes / (HBM_PEAK_GBS * 1e9)
     t_mfma = attn_flops / (MFMA_PEAK_TFLOPS * 1e12)
-    bound = "mfma" if t_mfma >= t_hbm else "hbm"
     traffic = current_traffic(TRAFFIC_RECORD) if args.config == "llama70b" else None
-    if bound == "mfma":
-        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": traffic}
-    else:
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    roof = roofline(attn_bytes, attn_flops, t_attn)
+    roof["traffic"] = traffic
 
     step_bytes = attn_bytes + sampler_bytes(w, g["path"], g["n_acc"]) + commit_bytes(w, g["n_acc"])
-    pct = lambda a: {"p10": round(float(np.percentile(a, 10)) * 1e3, 2),
-                     "p50": round(float(np.percentile(a, 50)) * 1e3, 2),
-                     "p90": round(float(np.percentile(a, 90)) * 1e3, 2)}
     offp, offn = g["offset_paths"], g["offset_naccs"]
     acceptance = None
     if len(offn) > 0:
-        samp_mean = float(np.mean([sampler_bytes(w, offp[o], offn[o]) for o in range(len(offn))]))
-        acceptance = {
-            "offsets": int(len(offn)),
-            "mean_accepted_per_seq": round(float(offn.mean()), 4),
-            "mean_emitted_per_step": round(float((offn + 1).sum(axis=1).mean()), 3),
-            "mean_sampler_bytes": round(samp_mean),
-            "step_floor_us_at_mean": round(max((attn_bytes + samp_mean + float(np.mean(
-                [commit_bytes(w, offn[o]) for o in range(len(offn))]))) / (HBM_PEAK_GBS * 1e9),
-                attn_flops / (MFMA_PEAK_TFLOPS * 1e12)) * 1e6, 2),
-        }
-    t_floor = max(step_bytes / (HBM_PEAK_GBS * 1e9), attn_flops / (MFMA_PEAK_TFLOPS * 1e12))
+        acceptance = acceptance_stats(w, offp, offn)
+        acceptance["step_floor_us_at_mean"] = round(max(
+            (attn_bytes + acceptance["mean_sampler_bytes"] + acceptance["mean_commit_bytes"])
+            / (HBM_PEAK_GBS * 1e9), t_mfma) * 1e6, 2)
+    t_floor = max(step_bytes / (HBM_PEAK_GBS * 1e9), t_mfma)
     ms = g["ms_step"]
     rec = {
         "metric": "verified tree nodes/s",
@@ -478,14 +692,10 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof,
         "verify_step_us": round(ms * 1e3, 2),
-        "stages_us": {k: round(v * 1e3, 2) for k, v in
-                      zip(["tree_mask_build", "tree_attn_verify", "spec_verify_sample",
-                           "kv_commit_path"], g["stage_ms"])},
-        "stages_us_pctl": {k: pct(g["stage_all"][:, i]) for i, k in
-                           enumerate(["tree_mask_build", "tree_attn_verify",
-                                      "spec_verify_sample", "kv_commit_path"])},
+        "stages_us": {k: round(v * 1e3, 2) for k, v in zip(STAGES, g["stage_ms"])},
+        "stages_us_pctl": {k: pct(g["stage_all"][:, i]) for i, k in enumerate(STAGES)},
         "step_us_pctl": pct(g["step_all"]),
-        "tree_attn": {"us": round(t_attn * 1e6, 2),
+        "tree_attn": {"us": round(t_attn * 1e6, 2), "us_pctl": pct(g["attn_all"]),
                       "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                       "measured_copy_gbs": round(copy_gbs, 1),
                       "hbm_frac_of_copy": round(gbs / copy_gbs, 4),
@@ -518,6 +728,10 @@ def main():
         })
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w)
+    del w, g
+    torch.cuda.empty_cache()
+    if not (args.no_configs or args.step_only):
+        rec["configs"] = run_configs(args, torch.device("cuda:0"))
     print(json.dumps(rec), flush=True)
 
 

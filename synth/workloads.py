@@ -205,6 +205,8 @@ class Workload:
     draft_logits: Optional[np.ndarray]   # float32 [B, N, V]
     k_prefix: Optional[list] = None      # dense bf16 prefixes, [L_b, Hkv, D] each
     v_prefix: Optional[list] = None
+    draft_noise: Optional[np.ndarray] = None   # the N(0, 1) draws behind draft - target
+    widths: Optional[Sequence[int]] = None     # best-first widths per depth, if best-first
 
     @property
     def max_prefix_len(self) -> int:
@@ -261,7 +263,8 @@ CONFIGS = {
 
 
 def make_workload(name: str, *, seed: Optional[int] = None, with_logits: bool = True,
-                  keep_dense: bool = False, poison: bool = True, **over) -> Workload:
+                  keep_dense: bool = False, poison: bool = True, keep_noise: bool = False,
+                  **over) -> Workload:
     """Build a preset, optionally overriding any of its fields.
 
     Overrides: B, N, Hq, Hkv, D, V, L=(lo, hi) inclusive prefix-length range,
@@ -286,6 +289,7 @@ def make_workload(name: str, *, seed: Optional[int] = None, with_logits: bool = 
         tl = rng.standard_normal((B, N, V), dtype=np.float32)
         tl *= np.float32(cfg["sigma_t"])
         dl = rng.standard_normal((B, N, V), dtype=np.float32)
+        noise = dl.copy() if keep_noise else None
         dl *= np.float32(cfg["sigma_d"])
         dl += tl
 
@@ -333,4 +337,44 @@ def make_workload(name: str, *, seed: Optional[int] = None, with_logits: bool = 
         prefix_len=prefix_len, k_cache=k_cache, v_cache=v_cache, block_table=table,
         target_logits=tl if with_logits else None, draft_logits=dl if with_logits else None,
         k_prefix=k_prefix if keep_dense else None, v_prefix=v_prefix if keep_dense else None,
+        draft_noise=noise if (keep_noise and with_logits) else None,
+        widths=tuple(cfg["widths"]) if tree == "best_first" else None,
     )
+
+
+def with_acceptance(w: Workload, accept: float) -> Workload:
+    """The same workload with the draft noise rescaled to the sweep sigma of
+    ``accept`` (draft = target + sigma * the same N(0, 1) draws), and the tree
+    and tokens rebuilt from the new draft rows as ``make_workload`` builds
+    them: equal, bit for bit, to ``make_workload`` of that acceptance. Needs
+    a workload made with ``keep_noise=True``."""
+    if w.draft_noise is None:
+        raise ValueError("workload was made without keep_noise")
+    dl = w.draft_noise.copy()
+    dl *= np.float32(sweep_sigma(accept))
+    dl += w.target_logits
+    parent = np.empty_like(w.parent)
+    token = np.empty_like(w.token)
+    for b in range(w.B):
+        root_tok = int(w.token[b, 0])
+        if w.widths is not None:
+            p, t = best_first_tree(dl[b], w.widths, w.N, root_tok)
+            if p.shape[0] != w.N:
+                raise ValueError(f"tree saturated at {p.shape[0]} < {w.N} nodes")
+            parent[b], token[b] = p, t
+        else:
+            parent[b] = w.parent[b]
+            token[b] = tokens_topk_for_parent(w.parent[b], dl[b], root_tok)
+    return dataclasses.replace(w, parent=parent, token=token, draft_logits=dl)
+
+
+def slice_batch(w: Workload, B: int) -> Workload:
+    """The first B sequences of a workload (the paged caches are shared)."""
+    cut = lambda a: None if a is None else a[:B]
+    return dataclasses.replace(
+        w, B=B, parent=w.parent[:B], token=w.token[:B], q=w.q[:B], k_tree=w.k_tree[:B],
+        v_tree=w.v_tree[:B], prefix_len=w.prefix_len[:B], block_table=w.block_table[:B],
+        target_logits=cut(w.target_logits), draft_logits=cut(w.draft_logits),
+        draft_noise=cut(w.draft_noise),
+        k_prefix=None if w.k_prefix is None else w.k_prefix[:B],
+        v_prefix=None if w.v_prefix is None else w.v_prefix[:B])
