@@ -36,6 +36,10 @@ inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s);
 // Compute units of the current device (0 if there is no usable device).
 int device_cu_count();
 
+// Workgroups of `kernel` with `threads` threads one CU of the current device
+// holds at once (0 on failure).
+int kernel_occupancy(const void *kernel, int threads);
+
 // The launch behind spec_verify_sample and its variants: host checks, plan,
 // workspace check, one kernel launch. wor: the without-replacement sibling
 // rule; p_rows/q_rows/child_pq non-NULL: the probe variant.

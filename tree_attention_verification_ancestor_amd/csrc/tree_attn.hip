@@ -932,10 +932,9 @@ bool attn_plan(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D, int32_t
     if (cus <= 0)
         return false;
     const int NW = waves_for(N, Hq, Hkv);
-    int per_cu = 0;
     const void *fn = D == 128 ? kernel_for<128>(NW) : kernel_for<64>(NW);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NW * 64, 0) != hipSuccess ||
-        per_cu <= 0)
+    const int per_cu = kernel_occupancy(fn, NW * 64);
+    if (per_cu <= 0)
         return false;
     attn_plan_for(B, N, Hq, Hkv, D, max_prefix_len, cus, per_cu, p);
     return true;

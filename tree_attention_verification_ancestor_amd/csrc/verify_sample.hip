@@ -62,6 +62,7 @@
 // a table-free fp64 routine within one ulp, serves tav_target_probs.
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "philox.h"
@@ -346,9 +347,19 @@ __device__ __forceinline__ double bits_f64(uint32_t hi, uint32_t lo)
 // visited node, the normalised p and q the walk holds in registers and the
 // p, q of its children's tokens that the child tests read; nothing else
 // changes.
-template <bool kWor, bool kProbe = false>
+//
+// E is the number of vocabulary entries each thread holds (a workgroup holds
+// 512 E), so a sequence's group has ceil(V / 512 E) members: fewer, larger
+// members let more sequences walk at once when the batch is large. Each entry
+// keeps only its two fp32 exponentials (target and draft, relative to its
+// wave's maximum); the fp64 values the walk decides with (p, q and the
+// residual after k rejections at the current node) are formed from them
+// when needed, by the same operations in the same order every time, so they
+// are the same bits whenever they are formed.
+template <int E, bool kWor, bool kProbe = false>
 __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
 {
+    static_assert(E % 4 == 0, "whole 16-byte runs");
     __shared__ int32_t s_par[kMaxNodes];
     __shared__ int32_t s_first[kMaxNodes];
     __shared__ int32_t s_next[kMaxNodes];
@@ -372,7 +383,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
     // removed tokens (s_qs[0] = 1 is implied); s_rtok[j] = token rejected at step j
     __shared__ double s_qs[kWor ? kMaxNodes + 1 : 1];
     __shared__ int32_t s_rtok[kWor ? kMaxNodes : 1];
-    __shared__ double s_slot[kSvEpt * kSvWaves];
+    __shared__ double s_slot[E * kSvWaves];
     __shared__ double s_hit_off;
     __shared__ int s_bad;
     __shared__ int s_found;
@@ -391,12 +402,14 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
     // base + h * 4 * 512 + 4 tid + j, j < 4, read as one 16-byte load where
     // the row allows it (the chunk is a multiple of 4 tokens).
     constexpr int kRun = 4 * kSvThreads;
+    // (token ids fit 32 bits: V <= 2^21)
+    const int32_t base32 = (int32_t)base;
     auto tok = [&](int e) __attribute__((always_inline)) {
-        return base + (int64_t)(e >> 2) * kRun + 4 * tid + (e & 3);
+        return base32 + (e >> 2) * kRun + 4 * tid + (e & 3);
     };
-    auto load_row = [&](const float *row, float (&v)[kSvEpt]) __attribute__((always_inline)) {
+    auto load_row = [&](const float *row, float (&v)[E]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int h = 0; h < kSvEpt / 4; ++h) {
+        for (int h = 0; h < E / 4; ++h) {
             const int64_t i0 = base + (int64_t)h * kRun + 4 * tid;
             if (a.vec4 && i0 + 3 < lim) {
                 const f32x4 x = *reinterpret_cast<const f32x4 *>(row + i0);
@@ -411,9 +424,9 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             }
         }
     };
-    auto no_row = [&](float (&v)[kSvEpt]) __attribute__((always_inline)) {
+    auto no_row = [&](float (&v)[E]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int e = 0; e < kSvEpt; ++e)
+        for (int e = 0; e < E; ++e)
             v[e] = -INFINITY;
     };
     uint64_t *box = a.box + (size_t)g * 2 * wpg * kSlotWords;
@@ -429,11 +442,19 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
     for (int b = g; b < a.B && alive; b += a.ngroups) {
         const int64_t rowbase = (int64_t)b * N;
         // ---- the root's rows first: the walk starts there --------------------
-        int pf_node = 0;   // rows of the likeliest next node, fetched a level ahead
-        float pf_t[kSvEpt], pf_d[kSvEpt];
+        // Rows of the likeliest next node, fetched a level ahead into
+        // registers (while the current node is decided) when they fit: with
+        // up to 16 entries per thread. Larger E reads each node's rows when
+        // it reaches it.
+        constexpr bool kPrefetch = E <= 16;
+        constexpr int PE = kPrefetch ? E : 4;
+        int pf_node = kPrefetch ? 0 : -1;
+        float pf_t[PE], pf_d[PE];
         float pf_tx = 0.f, pf_dx = 0.f;   // logits of child `tid` of pf_node, if any
-        load_row(a.tl + rowbase * a.V, pf_t);
-        load_row(a.dl + rowbase * a.V, pf_d);
+        if constexpr (kPrefetch) {
+            load_row(a.tl + rowbase * a.V, pf_t);
+            load_row(a.dl + rowbase * a.V, pf_d);
+        }
         // ---- tree structure in LDS, validated ------------------------------
         // Each node's children as a bitmask (bit c of word c / 64), so first
         // child and next sibling are find-first-set operations; meanwhile the
@@ -455,7 +476,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
 #pragma unroll
             for (int w = 0; w < kKidWords; ++w)
                 s_kids[tid][w] = 0ull;
-            if (tid >= 1 && my_par == 0 && my_tok >= 0 && my_tok < a.V) {
+            if (kPrefetch && tid >= 1 && my_par == 0 && my_tok >= 0 && my_tok < a.V) {
                 pf_tx = a.tl[rowbase * a.V + my_tok];
                 pf_dx = a.dl[rowbase * a.V + my_tok];
             }
@@ -513,12 +534,12 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             const bool has_kids = s_first[u] >= 0;
 
             // ---- 1. local (max, sum exp) of target and draft rows ------------
-            float tf[kSvEpt], df[kSvEpt];
+            float tf[E], df[E];
             if (pf_node == u) {
 #pragma unroll
-                for (int e = 0; e < kSvEpt; ++e) {
-                    tf[e] = pf_t[e];
-                    df[e] = has_kids ? pf_d[e] : -INFINITY;
+                for (int e = 0; e < E; ++e) {
+                    tf[e] = pf_t[e % PE];
+                    df[e] = has_kids ? pf_d[e % PE] : -INFINITY;
                 }
                 if (my_par == u) {
                     s_tx[tid] = my_tx = pf_tx;
@@ -543,7 +564,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             bool nan_seen = false;
             float mt_l = -INFINITY, mq_l = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < kSvEpt; ++e) {
+            for (int e = 0; e < E; ++e) {
                 nan_seen |= __builtin_isnan(tf[e]) || __builtin_isnan(df[e]);
                 mt_l = fmaxf(mt_l, tf[e]);
                 mq_l = fmaxf(mq_l, df[e]);
@@ -555,16 +576,16 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             // v_exp_f32 (under one ulp); summed in fp64. An entry's relative
             // error is about |y| 2^-24, so the entries that carry the sum
             // (|y| of a few units) are within a few 1e-7.
-            double pr[kSvEpt], qv[kSvEpt];
+            float ep[E], eq[E];
             double zt = 0.0, zq = 0.0;
 #pragma unroll
-            for (int e = 0; e < kSvEpt; ++e) {
-                pr[e] = (wmt == -INFINITY) ? 0.0
-                                           : (double)__builtin_amdgcn_exp2f(fmaf(tf[e], invT32, -wts32) * kLog2eF);
-                qv[e] = (wmq == -INFINITY) ? 0.0
-                                           : (double)__builtin_amdgcn_exp2f(fmaf(df[e], invT32, -wqs32) * kLog2eF);
-                zt += pr[e];
-                zq += qv[e];
+            for (int e = 0; e < E; ++e) {
+                ep[e] = (wmt == -INFINITY) ? 0.0f
+                                           : __builtin_amdgcn_exp2f(fmaf(tf[e], invT32, -wts32) * kLog2eF);
+                eq[e] = (wmq == -INFINITY) ? 0.0f
+                                           : __builtin_amdgcn_exp2f(fmaf(df[e], invT32, -wqs32) * kLog2eF);
+                zt += (double)ep[e];
+                zq += (double)eq[e];
             }
             if (nan_seen)
                 zt = NAN;
@@ -578,17 +599,19 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             }
 
             // the first child's rows and its children's logits, for the next level
-            if (has_kids) {
+            if (kPrefetch && has_kids) {
                 const int c1 = s_first[u];
                 pf_node = c1;
                 const float *t1 = a.tl + (rowbase + c1) * a.V;
                 const float *d1 = a.dl + (rowbase + c1) * a.V;
                 const bool c1_kids = s_first[c1] >= 0;
-                load_row(t1, pf_t);
-                if (c1_kids)
-                    load_row(d1, pf_d);
-                else
-                    no_row(pf_d);
+                if constexpr (kPrefetch) {
+                    load_row(t1, pf_t);
+                    if (c1_kids)
+                        load_row(d1, pf_d);
+                    else
+                        no_row(pf_d);
+                }
                 if (tid < N && s_par[tid] == c1) {
                     const int x = s_tok[tid];
                     pf_tx = t1[x];
@@ -719,12 +742,12 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 double *prow = a.p_rows + (rowbase + u) * a.V;
                 double *qrow = a.q_rows + (rowbase + u) * a.V;
 #pragma unroll
-                for (int e = 0; e < kSvEpt; ++e) {
+                for (int e = 0; e < E; ++e) {
                     const int64_t t = tok(e);
                     if (t < lim) {
-                        prow[t] = pr[e] * sp;
+                        prow[t] = (double)ep[e] * sp;
                         if (has_kids)
-                            qrow[t] = qv[e] * sq;
+                            qrow[t] = (double)eq[e] * sq;
                     }
                 }
                 if (rank == 0 && tid < N && s_par[tid] == u) {
@@ -777,22 +800,78 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 accept(c);
                 continue;   // the first child needs only the normalisers
             }
-            // A rejection or the final draw follows: p and q of this chunk in
-            // registers, rebased from the wave's max.
-            {
-                const double sp = (wmt == -INFINITY) ? 0.0 : exp_bulk(wts - Mp) * (1.0 / Zp);
-                const double sq = (wmq == -INFINITY) ? 0.0 : exp_bulk(wqs - Mq) * (1.0 / Zq);
+            // A rejection or the final draw follows. This chunk's p and q are
+            // its exponentials rebased from the wave's max and normalised:
+            // p(e) = ep[e] sp, q(e) = eq[e] sq. After k rejections at u the
+            // target is the residual chain res_k(e): res_0 = p(e) and, for
+            // j < k, res_{j+1} = max(0, res_j - q_j(e)) / Z_j when Z_j > 0
+            // (else unchanged), Z_j the residual mass of round j; q_j = q
+            // (independent siblings) or, without replacement, q(e) s_j off
+            // the tokens removed before round j (s_0 = 1).
+            const double sp = (wmt == -INFINITY) ? 0.0 : exp_bulk(wts - Mp) * (1.0 / Zp);
+            const double sq = (wmq == -INFINITY) ? 0.0 : exp_bulk(wqs - Mq) * (1.0 / Zq);
+            // round at which entry e's token left the draft (without
+            // replacement), kMaxNodes if it has not
+            auto removed_at = [&](int e, int k_now) __attribute__((always_inline)) {
+                int at = kMaxNodes;
+                if constexpr (kWor) {
+                    const int64_t t = tok(e);
+                    for (int j = 0; j < k_now; ++j)
+                        if (s_rtok[j] == t && at == kMaxNodes)
+                            at = j;
+                }
+                return at;
+            };
+            // With E > 8 the fp32 exponentials pass through an empty asm
+            // statement at each use so that the compiler forms the fp64
+            // products there instead of hoisting all E of them out of the
+            // loops (which would hold them in 4E registers); with E = 8 they
+            // fit, and are hoisted.
+            auto fresh = [](float v) __attribute__((always_inline)) {
+                if constexpr (E > 8)
+                    asm volatile("" : "+v"(v));
+                return v;
+            };
+            auto q_at = [&](int e, int j, int gone) __attribute__((always_inline)) {
+                const double q = (double)fresh(eq[e]) * sq;
+                if constexpr (kWor)
+                    return j > gone ? 0.0 : q * (j == 0 ? 1.0 : s_qs[j]);
+                else
+                    return q;
+            };
+            auto residual = [&](int e, int k_now) __attribute__((always_inline)) {
+                double r = (double)fresh(ep[e]) * sp;
+                const int gone = removed_at(e, k_now);
+                for (int j = 0; j < k_now; ++j) {
+                    const double zj = s_zhist[j];
+                    if (zj > 0.0) {
+                        const double d = r - q_at(e, j, gone);
+                        r = (d > 0.0 ? d : 0.0) * (1.0 / zj);
+                    }
+                }
+                return r;
+            };
+            // With E = 8, p and q (then the residual) are held in fp64 registers
+            // and updated in place after each rejection, the same operations
+            // on the same values as the chain above, without re-forming it.
+            constexpr bool kHold = E == 8;
+            double pr_h[kHold ? E : 1], qv_h[kHold ? E : 1];
+            double sk = 1.0;   // held, without replacement: q_k = qv_h sk
+            if constexpr (kHold) {
 #pragma unroll
-                for (int e = 0; e < kSvEpt; ++e) {
-                    pr[e] *= sp;
-                    qv[e] *= sq;
+                for (int e = 0; e < E; ++e) {
+                    pr_h[e] = (double)ep[e] * sp;
+                    qv_h[e] = (double)eq[e] * sq;
                 }
             }
+            auto cur_res = [&](int e, int k_now) __attribute__((always_inline)) {
+                if constexpr (kHold)
+                    return pr_h[e];
+                else
+                    return residual(e, k_now);
+            };
             int k = 0;
             bool accepted = false;
-            // without replacement: q_k = qv * sk, where qv holds q with the
-            // removed tokens' entries zeroed
-            double sk = 1.0;
             while (c >= 0) {
                 // rejected: the chunk's residual mass, per wave, then in wave
                 // 0 exchanged with the group and summed in member order
@@ -807,11 +886,19 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                         ex = (int)((off / kRun) * 4 + (off & 3));
                 }
 #pragma unroll
-                for (int e = 0; e < kSvEpt; ++e) {
-                    const double d = pr[e] - (kWor ? qv[e] * sk : qv[e]);
-                    rsum += d > 0.0 ? d : 0.0;
-                    if constexpr (kWor)
-                        qrem += e == ex ? 0.0 : qv[e];
+                for (int e = 0; e < E; ++e) {
+                    if constexpr (kHold) {
+                        const double d = pr_h[e] - (kWor ? qv_h[e] * sk : qv_h[e]);
+                        rsum += d > 0.0 ? d : 0.0;
+                        if constexpr (kWor)
+                            qrem += e == ex ? 0.0 : qv_h[e];
+                    } else {
+                        const int gone = removed_at(e, k);
+                        const double d = residual(e, k) - q_at(e, k, gone);
+                        rsum += d > 0.0 ? d : 0.0;
+                        if constexpr (kWor)
+                            qrem += (e == ex || gone < k) ? 0.0 : (double)fresh(eq[e]) * sq;
+                    }
                 }
                 rsum = wave_sum(rsum);
                 if constexpr (kWor)
@@ -877,21 +964,23 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     alive = false;
                     break;
                 }
-                const double Z = s_zhist[k];
-                if (Z > 0.0) {
-                    const double inv = 1.0 / Z;
+                if constexpr (kHold) {
+                    const double Z = s_zhist[k];
+                    if (Z > 0.0) {
+                        const double inv = 1.0 / Z;
 #pragma unroll
-                    for (int e = 0; e < kSvEpt; ++e) {
-                        const double d = pr[e] - (kWor ? qv[e] * sk : qv[e]);
-                        pr[e] = (d > 0.0 ? d : 0.0) * inv;
+                        for (int e = 0; e < E; ++e) {
+                            const double d = pr_h[e] - (kWor ? qv_h[e] * sk : qv_h[e]);
+                            pr_h[e] = (d > 0.0 ? d : 0.0) * inv;
+                        }
                     }
-                }
-                if constexpr (kWor) {
+                    if constexpr (kWor) {
 #pragma unroll
-                    for (int e = 0; e < kSvEpt; ++e)
-                        if (e == ex)
-                            qv[e] = 0.0;
-                    sk = s_qs[k + 1];
+                        for (int e = 0; e < E; ++e)
+                            if (e == ex)
+                                qv_h[e] = 0.0;
+                        sk = s_qs[k + 1];
+                    }
                 }
                 ++k;
                 c = s_next[c];
@@ -940,10 +1029,11 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 // entries.
                 const int lane = tid & 63, wave = tid >> 6;
                 auto run_sum = [&](int h) __attribute__((always_inline)) {
-                    return ((pr[4 * h] + pr[4 * h + 1]) + pr[4 * h + 2]) + pr[4 * h + 3];
+                    return ((cur_res(4 * h, k) + cur_res(4 * h + 1, k)) + cur_res(4 * h + 2, k)) +
+                           cur_res(4 * h + 3, k);
                 };
 #pragma unroll
-                for (int h = 0; h < kSvEpt / 4; ++h) {
+                for (int h = 0; h < E / 4; ++h) {
                     const double t = wave_sum_ordered(run_sum(h));
                     if (lane == 0)
                         s_slot[h * kSvWaves + wave] = t;
@@ -951,7 +1041,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 __syncthreads();
                 if (tid == 0) {
                     double run = before;
-                    for (int k2 = 0; k2 < (kSvEpt / 4) * kSvWaves; ++k2) {
+                    for (int k2 = 0; k2 < (E / 4) * kSvWaves; ++k2) {
                         const double nxt = run + s_slot[k2];
                         if (s_slot[k2] > 0.0 && run <= target && target < nxt) {
                             s_hit = k2;
@@ -967,12 +1057,12 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     const int h_hit = hit / kSvWaves;
                     double v = 0.0, pe[4];
 #pragma unroll
-                    for (int h = 0; h < kSvEpt / 4; ++h)
+                    for (int h = 0; h < E / 4; ++h)
                         if (h == h_hit) {
                             v = run_sum(h);
 #pragma unroll
                             for (int j = 0; j < 4; ++j)
-                                pe[j] = pr[4 * h + j];
+                                pe[j] = cur_res(4 * h + j, k);
                         }
                     double incl = v;
 #pragma unroll
@@ -1011,8 +1101,8 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 // chunk's last live token takes it
                 if (hit < 0) {
 #pragma unroll
-                    for (int e = 0; e < kSvEpt; ++e)
-                        if (pr[e] > 0.0)
+                    for (int e = 0; e < E; ++e)
+                        if (cur_res(e, k) > 0.0)
                             atomicMax(&s_last_live, (int)tok(e));
                 }
                 __syncthreads();
@@ -1369,39 +1459,75 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_greedy_kernel(SvArgs a
 }
 
 struct SvPlan {
+    int E;                // vocabulary entries per thread
     int wpg, ngroups, chunk;
     size_t box_bytes;
 };
 
-bool sv_plan(int32_t B, int32_t V, SvPlan &p)
+// Workgroups of the sampling kernels with E entries per thread the device
+// holds at once (every variant that may run with that E: the group syncs
+// wait on each other, so a grid must be resident); 0 on failure.
+template <int E>
+int64_t sampling_resident(int cus)
+{
+    const int a = kernel_occupancy(reinterpret_cast<const void *>(spec_verify_kernel<E, false>),
+                                   kSvThreads);
+    const int b = kernel_occupancy(reinterpret_cast<const void *>(spec_verify_kernel<E, true>),
+                                   kSvThreads);
+    const int c = kernel_occupancy(
+        reinterpret_cast<const void *>(spec_verify_kernel<E, false, true>), kSvThreads);
+    return (int64_t)std::min(std::min(a, b), c) * cus;
+}
+
+// A group of ceil(V / 512 E) workgroups per sequence, as many groups as the
+// device holds at once (at most B), each walking its sequences in turn. The
+// sampling walk takes the E of 8 and 16 that needs the fewer sequences per
+// group, the smaller among equals (more members share each row); greedy
+// verification keeps E = 8. (E = 32 would need more registers than a
+// resident 512-thread workgroup has.)
+bool sv_plan(int32_t B, int32_t V, bool greedy, SvPlan &p)
 {
     const int cus = device_cu_count();
     if (cus <= 0)
         return false;
-    // the grid must be resident at once for either kernel (the group syncs
-    // wait on each other), so the smaller of their occupancies counts
-    int per_cu = 0, per_cu_g = 0;
-    int per_cu_w = 0, per_cu_p = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, spec_verify_kernel<false>,
-                                                     kSvThreads, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_w, spec_verify_kernel<true>,
-                                                     kSvThreads, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_p, spec_verify_kernel<false, true>,
-                                                     kSvThreads, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_g, spec_verify_greedy_kernel,
-                                                     kSvThreads, 0) != hipSuccess)
-        return false;
-    per_cu = std::min(std::min(std::min(per_cu, per_cu_w), per_cu_g), per_cu_p);
-    if (per_cu <= 0)
-        return false;
-    const int64_t resident = (int64_t)per_cu * cus;
-    p.wpg = (int)ceil_div(V, kSvChunk);
-    if (p.wpg > resident || p.wpg > kMaxWpg)
-        return false;
-    p.chunk = (int)(ceil_div(ceil_div(V, p.wpg), 4) * 4);   // whole 16-byte runs
-    p.ngroups = (int)std::min<int64_t>(B, resident / p.wpg);
-    p.box_bytes = (size_t)p.ngroups * 2 * p.wpg * kSlotWords * sizeof(uint64_t);
-    return true;
+    auto fit = [&](int E, int64_t resident, SvPlan &q) {
+        q.E = E;
+        q.wpg = (int)ceil_div(V, (int64_t)kSvThreads * E);
+        if (resident <= 0 || q.wpg > resident || q.wpg > kMaxWpg)
+            return false;
+        q.chunk = (int)(ceil_div(ceil_div(V, q.wpg), 4) * 4);   // whole 16-byte runs
+        q.ngroups = (int)std::min<int64_t>(B, resident / q.wpg);
+        q.box_bytes = (size_t)q.ngroups * 2 * q.wpg * kSlotWords * sizeof(uint64_t);
+        return true;
+    };
+    if (greedy) {
+        const int g = kernel_occupancy(reinterpret_cast<const void *>(spec_verify_greedy_kernel),
+                                       kSvThreads);
+        return fit(kSvEpt, (int64_t)g * cus, p);
+    }
+    const int64_t res[2] = {sampling_resident<8>(cus), sampling_resident<16>(cus)};
+    const int Es[2] = {8, 16};
+    bool found = false;
+    for (int i = 0; i < 2; ++i) {
+        SvPlan q;
+        if (!fit(Es[i], res[i], q))
+            continue;
+        const int64_t rounds = ceil_div(B, q.ngroups);
+        if (!found || rounds < ceil_div(B, p.ngroups)) {
+            p = q;
+            found = true;
+        }
+    }
+    return found;
+}
+
+// Workspace for either mode of spec_verify_sample (0 if neither plan fits).
+size_t sv_workspace(int32_t B, int32_t V)
+{
+    SvPlan s, g;
+    if (!sv_plan(B, V, false, s) || !sv_plan(B, V, true, g))
+        return 0;
+    return kHeaderBytes + std::max(s.box_bytes, g.box_bytes);
 }
 
 // ---------------------------------------------------------------------------
@@ -1456,10 +1582,7 @@ extern "C" size_t spec_verify_workspace_bytes(int32_t B, int32_t N, int32_t V)
     using namespace tav;
     if (B < 1 || N < 1 || N > kMaxNodes || V < 1 || V > kMaxVocab)
         return 0;
-    SvPlan p;
-    if (!sv_plan(B, V, p))
-        return 0;
-    return kHeaderBytes + p.box_bytes;
+    return sv_workspace(B, V);
 }
 
 namespace tav {
@@ -1484,7 +1607,7 @@ tav_status sv_launch(const float *target_logits, const float *draft_logits,
     if (!aligned(target_logits, 4) || (!greedy && !aligned(draft_logits, 4)))
         return TAV_ERR_ARG;
     SvPlan p;
-    if (!sv_plan(B, V, p))
+    if (!sv_plan(B, V, greedy, p))
         return TAV_ERR_LAUNCH;
     const size_t need = kHeaderBytes + p.box_bytes;
     if (!workspace || ws_bytes < need || !aligned(workspace, 256))
@@ -1515,18 +1638,23 @@ tav_status sv_launch(const float *target_logits, const float *draft_logits,
     a.q_rows = q_rows;
     a.child_pq = child_pq;
     const bool probe = p_rows != nullptr;
-    if (probe)
-        hipLaunchKernelGGL((spec_verify_kernel<false, true>), dim3(p.wpg * p.ngroups),
-                           dim3(kSvThreads), 0, as_stream(stream), a);
-    else if (greedy)
-        hipLaunchKernelGGL(spec_verify_greedy_kernel, dim3(p.wpg * p.ngroups), dim3(kSvThreads), 0,
-                           as_stream(stream), a);
-    else if (wor)
-        hipLaunchKernelGGL(spec_verify_kernel<true>, dim3(p.wpg * p.ngroups), dim3(kSvThreads),
-                           0, as_stream(stream), a);
+    const dim3 grid(p.wpg * p.ngroups), block(kSvThreads);
+    hipStream_t st = as_stream(stream);
+    auto sampling = [&](auto e_c) {
+        constexpr int E = decltype(e_c)::value;
+        if (probe)
+            hipLaunchKernelGGL((spec_verify_kernel<E, false, true>), grid, block, 0, st, a);
+        else if (wor)
+            hipLaunchKernelGGL((spec_verify_kernel<E, true>), grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL((spec_verify_kernel<E, false>), grid, block, 0, st, a);
+    };
+    if (greedy)
+        hipLaunchKernelGGL(spec_verify_greedy_kernel, grid, block, 0, st, a);
+    else if (p.E == 8)
+        sampling(std::integral_constant<int, 8>{});
     else
-        hipLaunchKernelGGL(spec_verify_kernel<false>, dim3(p.wpg * p.ngroups), dim3(kSvThreads),
-                           0, as_stream(stream), a);
+        sampling(std::integral_constant<int, 16>{});
     return hipGetLastError() == hipSuccess ? TAV_OK : TAV_ERR_LAUNCH;
 }
 
