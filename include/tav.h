@@ -14,6 +14,7 @@
  *   tree_expand_sample  the same with the k tokens drawn without replacement
  *   tree_select_topm    the budget's best M-node subtree of a candidate tree
  *   tree_widths_by_entropy  branching widths from the frontier's entropy ranks
+ *   tree_topology_dp    the budget's best topology under acceptance by sibling rank
  *   tav_model_speedup, tav_best_chain_length, tav_fit_alpha
  *                       the speedup model, on the host, fed by measured times
  *
@@ -478,6 +479,46 @@ tav_status tree_select_topm(const int32_t *parent, const int32_t *token, const d
                             int32_t B, int32_t Nc, int32_t M, int32_t *out_parent,
                             int32_t *out_token, int32_t *out_src, uint32_t *dev_flags,
                             void *stream);
+
+/*
+ * tree_topology_workspace_bytes — device workspace tree_topology_dp needs
+ * (0 for unsupported sizes).
+ */
+size_t tree_topology_workspace_bytes(int32_t K, int32_t n, int32_t depth);
+
+/*
+ * tree_topology_dp — the budget-constrained tree topology by dynamic
+ * programming: the node count is capped at n and branches are allotted to
+ * maximise the expected number of accepted tokens (jisaku.com glossary,
+ * tree-topology strategies, budget-constrained optimisation; the Sequoia
+ * paragraph: a topology chosen for the hardware and the draft's behaviour).
+ * Acceptance model by sibling rank: the k-th child of a node, once reached,
+ * is accepted with probability p_rank[k-1] at any depth, so the expected
+ * accepted count of a tree is the sum over non-root nodes of the product of
+ * p over the ranks along the node's path. Among all trees of n nodes, depth
+ * at most `depth` and at most K children per node, the one of largest
+ * expected count, from
+ *   F(1, r) = 0, F(m, 0) = -inf (m > 1), F(m, r) = C(m - 1, r - 1, 1),
+ *   C(0, r, j) = 0, C(s, r, j) = -inf for j > K,
+ *   C(s, r, j) = max_{t=1..s} p_j (1 + F(t, r)) + C(s - t, r, j + 1)
+ * in fp64, each value formed as (1 + F), times p_j, plus C, the smallest t
+ * among equal maxima (C places s nodes in the subtrees of children j, j+1,
+ * ...). The tree is written breadth-first: node 0 the root, each node's
+ * children in rank order as nodes are reached (topological; siblings in the
+ * order the walk tries them).
+ *
+ *   p_rank  host array of K probabilities in [0, 1]
+ *   parent  int32 [n] out (device): parent of each node, -1 for node 0
+ *   rank    int32 [n] out (device): 1-based position among its siblings (0 for the root)
+ *   value   fp64 [1] out (device): the expected accepted count
+ *   workspace  device buffer of >= tree_topology_workspace_bytes(K, n, depth)
+ *   Supported: 1 <= K <= 16, 1 <= n <= 256, 0 <= depth <= 64.
+ *   TAV_ERR_ARG for a p outside [0, 1] or NaN; TAV_ERR_UNSUPPORTED when no
+ *   n-node tree fits within the depth and K children per node.
+ */
+tav_status tree_topology_dp(const double *p_rank, int32_t K, int32_t n, int32_t depth,
+                            int32_t *parent, int32_t *rank, double *value, void *workspace,
+                            size_t ws_bytes, void *stream);
 
 /*
  * tree_widths_by_entropy — entropy-based branching: a frontier node whose

@@ -11,6 +11,8 @@ computes, in float64:
                     log-probabilities and entropy per row;
   * ``select``    - the budget-constrained top-M subtree by cumulative log q,
                     and entropy-ranked branching widths;
+  * ``topology``  - the budget's best tree topology by dynamic programming
+                    under acceptance by sibling rank;
   * ``cost``      - the speedup model and the per-position overhead fit;
   * ``step``      - the four composed.
 
@@ -29,5 +31,6 @@ from .sampling import (softmax, philox4x64_10, node_uniforms,  # noqa: F401
 from .commit import kv_commit, kv_commit_inplace  # noqa: F401
 from .expand import expand_topk, expand_sample, gumbel_keys  # noqa: F401
 from .select import select_topm, widths_by_entropy  # noqa: F401
+from .topology import topology, tree_value  # noqa: F401
 from . import cost  # noqa: F401
 from .step import verify_step_ref  # noqa: F401

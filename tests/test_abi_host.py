@@ -239,3 +239,17 @@ def test_noalloc_sampler_rejects_bad_arguments_before_any_device_work():
         args = dict(base)
         args.update(kw)
         assert fn(*args.values()) == code, kw
+
+
+def test_topology_rejects_bad_arguments_on_the_host():
+    lib = tav.lib()
+    bad = (ctypes.c_double * 2)(0.5, 1.5)
+    ok = (ctypes.c_double * 2)(0.5, 0.5)
+    cast = lambda a: ctypes.cast(a, P)
+    assert lib.tree_topology_dp(cast(bad), 2, 4, 3, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == tav.ERR_ARG
+    assert lib.tree_topology_dp(None, 2, 4, 3, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == tav.ERR_ARG
+    # no 8-node tree of depth 2 with 2 children per node (at most 1 + 2 + 4)
+    assert lib.tree_topology_dp(cast(ok), 2, 8, 2, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == tav.ERR_UNSUPPORTED
+    assert lib.tree_topology_dp(cast(ok), 17, 8, 2, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == tav.ERR_UNSUPPORTED
+    assert lib.tree_topology_dp(cast(ok), 2, 7, 2, FAKE, FAKE, FAKE, None, 0, None) == tav.ERR_WORKSPACE
+    assert lib.tree_topology_workspace_bytes(4, 64, 6) == 6 * 6 * 64 * 2

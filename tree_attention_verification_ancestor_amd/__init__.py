@@ -82,6 +82,8 @@ _SIGNATURES = {
     "tree_expand_sample": (_I32, [_P, _I64, _I32, _I32, _F64, _U64, _U64, _P, _P, _P, _P, _SZ, _P, _P]),
     "tree_select_topm": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "tree_widths_by_entropy": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    "tree_topology_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "tree_topology_dp": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]),
     "tav_model_speedup": (ctypes.c_double, [_F64, _F64, _F64, _I32]),
     "tav_best_chain_length": (_I32, [_F64, _F64, _F64, _I32, _P]),
     "tav_fit_alpha": (ctypes.c_double, [_P, _P, _I32]),
@@ -556,6 +558,24 @@ def tree_widths_by_entropy(entropy, w_min: int, w_max: int, width=None, dev_flag
         _ptr(entropy), B, F, int(w_min), int(w_max), _ptr(width), _ptr(dev_flags),
         _stream(stream)))
     return width
+
+
+def tree_topology_dp(p_rank, n: int, depth: int, device=None, stream=None):
+    """The n-node topology of largest expected accepted count under
+    acceptance by sibling rank (p_rank: K floats, host). Returns (parent
+    int32 [n], rank int32 [n], value fp64 [1]) on the device."""
+    K = len(p_rank)
+    dev = device or torch.device("cuda")
+    p = (ctypes.c_double * K)(*[float(x) for x in p_rank])
+    parent = torch.empty((n,), dtype=torch.int32, device=dev)
+    rank = torch.empty((n,), dtype=torch.int32, device=dev)
+    value = torch.empty((1,), dtype=torch.float64, device=dev)
+    need = int(lib().tree_topology_workspace_bytes(K, n, depth))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check("tree_topology_dp", lib().tree_topology_dp(
+        ctypes.cast(p, ctypes.c_void_p), K, n, depth, _ptr(parent), _ptr(rank), _ptr(value),
+        _ptr(ws), need, _stream(stream)))
+    return parent, rank, value
 
 
 def model_speedup(expected_emitted: float, draft_ratio: float, alpha: float, n: int) -> float:
