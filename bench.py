@@ -49,6 +49,12 @@ COPY_BYTES = 1 << 30           # each of the calibration copy's read and write
 FLUSH_BYTES = 512 << 20        # written between the configs' steps
 SWEEP_BATCHES = (1, 4, 16, 64, 128)
 SWEEP_ACCEPTS = (0.5, 0.8, 0.9)
+# Llama-3-8B, the sweep's shape: 32 layers of 4096-wide projections (q, k,
+# v, o: 4096 x (4096 + 1024 + 1024 + 4096); MLP 3 x 4096 x 14336) and a
+# 128256 x 4096 vocabulary head
+LAYERS_8B = 32
+LAYER_PARAMS_8B = 4096 * (4096 + 1024 + 1024 + 4096) + 3 * 4096 * 14336
+HEAD_PARAMS_8B = 128256 * 4096
 STAGES = ["tree_mask_build", "tree_attn_verify", "spec_verify_sample", "kv_commit_path"]
 
 
@@ -130,6 +136,36 @@ def acceptance_stats(w, paths, naccs):
             "mean_emitted_per_step": round(float((naccs + 1).sum(axis=1).mean()), 3),
             "realised_acceptance": round(acc / tests, 4) if tests else None,
             "mean_sampler_bytes": round(samp), "mean_commit_bytes": round(comm)}
+
+
+def rank_acceptance(w, paths, naccs, K=16):
+    """Acceptance rate of the k-th child by rank (k = 1..K): of the times the
+    walk tried a node's k-th child, the share it accepted."""
+    B, N = w.parent.shape
+    rank = np.zeros((B, N), np.int64)
+    kids = [[[] for _ in range(N)] for _ in range(B)]
+    for b in range(B):
+        for i in range(1, N):
+            u = int(w.parent[b, i])
+            kids[b][u].append(i)
+            rank[b, i] = len(kids[b][u])
+    tried = np.zeros(K + 1)
+    took = np.zeros(K + 1)
+    for o in range(len(naccs)):
+        for b in range(B):
+            m = int(naccs[o, b])
+            p = paths[o, b, :m + 1]
+            for t in range(m + 1):
+                u = int(p[t])
+                ch = kids[b][u]
+                if not ch:
+                    continue
+                r_acc = int(rank[b, p[t + 1]]) if t < m else 0
+                n_try = r_acc if r_acc else len(ch)
+                for r in range(1, min(n_try, K) + 1):
+                    tried[r] += 1
+                    took[r] += 1 if r == r_acc else 0
+    return [float(took[r] / tried[r]) if tried[r] else 0.0 for r in range(1, K + 1)], tried[1:]
 
 
 def pct(a):
@@ -396,6 +432,19 @@ def run_headline(args, w):
         stream))
     out["select_shape"] = (B, Nc, sel_M)
 
+    # the budget's best topology by dynamic programming (acceptance by sibling
+    # rank, the rates read off the walk over Philox offsets below): timed here
+    # for a 64-node, depth-6, width-4 budget with placeholder rates
+    p_guess = [0.5, 0.25, 0.15, 0.1]
+    topo = tav.tree_topology_dp(p_guess, 64, 6, device=dev)
+    topo_need = int(tav.lib().tree_topology_workspace_bytes(4, 64, 6))
+    topo_ws = torch.empty(max(topo_need, 1), dtype=torch.uint8, device=dev)
+    import ctypes
+    topo_p = (ctypes.c_double * 4)(*p_guess)
+    out["topology_ms"] = time_leg(tav.prepare(
+        "tree_topology_dp", ctypes.cast(topo_p, ctypes.c_void_p), 4, 64, 6, topo[0], topo[1],
+        topo[2], topo_ws, topo_need, stream))
+
     # entropy-ranked widths (1..4) for a 64-node frontier per sequence
     wid_h = (torch.rand((B, 64), generator=gen, dtype=torch.float64) * 5).to(dev)
     wid_out = torch.empty((B, 64), dtype=torch.int32, device=dev)
@@ -543,12 +592,53 @@ def cpu_baseline(w, min_seconds=10.0, threads=None, sample=None):
                        f"{len(os.sched_getaffinity(0))} cores visible")}
 
 
-def run_configs(args, dev):
+def sweep_model(sweep, decode, copy_gbs):
+    """For each batch size and acceptance: the speedup model of a whole
+    8B-shaped decoding step for the 16-node tree and the 6-node chain from
+    their measured attention and walk times against a decode step's (the same
+    workload cut to its root), the better of the two, and the best chain
+    length for the chain's realised acceptance and overhead."""
+    import tree_attention_verification_ancestor_amd as tav
+
+    def times(rec):
+        st = rec["stages_us"]
+        return st["tree_attn_verify"], st["spec_verify_sample"] + st["tree_mask_build"] + \
+            st["kv_commit_path"]
+
+    out = []
+    for acc in SWEEP_ACCEPTS:
+        for B in SWEEP_BATCHES:
+            dec = decode[B]
+            ad, sd = dec["stages_us"]["tree_attn_verify"], \
+                dec["stages_us"]["spec_verify_sample"] + dec["stages_us"]["kv_commit_path"]
+            row = {"B": B, "target_acceptance": acc}
+            for rec in sweep:
+                if rec["B"] != B or rec["target_acceptance"] != acc:
+                    continue
+                n = 16 if rec["tree"] == "tree16" else 6
+                av, sv = times(rec)
+                E = rec["acceptance"]["mean_emitted_per_step"] / B
+                sp, alpha, td, tv = tav.verify_speedup(
+                    E, 0.0, LAYERS_8B, LAYER_PARAMS_8B, HEAD_PARAMS_8B, B, n, av, sv, ad, sd,
+                    copy_gbs, MFMA_PEAK_TFLOPS)
+                row[rec["tree"]] = {"emitted_per_seq": round(E, 3), "speedup": round(sp, 3),
+                                    "alpha": round(alpha, 4), "t_decode_us": round(td, 1),
+                                    "t_verify_us": round(tv, 1)}
+                if rec["tree"] == "chain6":
+                    p = rec["acceptance"]["realised_acceptance"] or 0.0
+                    nb, sb = tav.best_chain_length(p, 0.0, max(alpha, 0.0), 64)
+                    row["best_chain"] = {"n": nb, "speedup": round(sb, 3), "acceptance": p}
+            row["choice"] = max(("tree16", "chain6"), key=lambda k: row[k]["speedup"])
+            out.append(row)
+    return out
+
+
+def run_configs(args, dev, copy_gbs):
     """The tiny, 8B, sweep and long-context workloads."""
     import torch
 
     from synth import make_workload
-    from synth.workloads import slice_batch, with_acceptance
+    from synth.workloads import slice_batch, slice_nodes, with_acceptance
 
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     steps, warm, offs = args.config_steps, args.warmup, args.config_offsets
@@ -575,6 +665,7 @@ def run_configs(args, dev):
         del w
 
     sweep = []
+    decode = {}
     for tname in ("sweep_tree16", "sweep_chain6"):
         base = make_workload(tname, B=max(SWEEP_BATCHES), accept=SWEEP_ACCEPTS[0],
                              keep_noise=True)
@@ -593,9 +684,17 @@ def run_configs(args, dev):
                 sweep.append(rec)
                 log(f"{tname} accept {acc} B={B}: step {rec['step_us']} us, "
                     f"emitted/step {rec['acceptance']['mean_emitted_per_step']}")
+                if tname == "sweep_chain6" and acc == 0.8:
+                    # the decode step of this batch: the workload cut to its root
+                    dec = run_config(slice_nodes(w, 1), steps, warm, offs, flush, dev)
+                    decode[B] = dec
+                    log(f"decode B={B}: step {dec['step_us']} us")
             del wa
         del base
     res["sweep"] = sweep
+    res["sweep_decode"] = [{"B": B, "step_us": decode[B]["step_us"],
+                            "stages_us": decode[B]["stages_us"]} for B in SWEEP_BATCHES]
+    res["sweep_model"] = sweep_model(sweep, decode, copy_gbs)
     del flush
     torch.cuda.empty_cache()
     return res
@@ -672,6 +771,22 @@ def main():
         acceptance["step_floor_us_at_mean"] = round(max(
             (attn_bytes + acceptance["mean_sampler_bytes"] + acceptance["mean_commit_bytes"])
             / (HBM_PEAK_GBS * 1e9), t_mfma) * 1e6, 2)
+    topology = None
+    if len(offn) > 0 and "topology_ms" in g:
+        import tree_attention_verification_ancestor_amd as tav
+        rates, tried = rank_acceptance(w, offp, offn, K=4)
+        parent, rank, value = tav.tree_topology_dp(rates, w.N, 6)
+        parent = parent.cpu().numpy()
+        depth = np.zeros(w.N, np.int64)
+        for i in range(1, w.N):
+            depth[i] = depth[parent[i]] + 1
+        topology = {"rank_acceptance": [round(r, 4) for r in rates],
+                    "rank_tries": [int(t) for t in tried],
+                    "n": w.N, "depth_limit": 6,
+                    "expected_accepted": round(float(value.cpu().numpy()[0]), 4),
+                    "nodes_per_depth": np.bincount(depth).tolist(),
+                    "best_first_tree_mean_accepted": acceptance["mean_accepted_per_seq"],
+                    "us": pct(g["topology_ms"])}
     t_floor = max(step_bytes / (HBM_PEAK_GBS * 1e9), t_mfma)
     ms = g["ms_step"]
     rec = {
@@ -716,6 +831,7 @@ def main():
             "kv_commit_inplace_us": pct(g["inplace_ms"]),
             "speedup_model": speedup_model(g["size_n"], g["size_us"]),
             "tree_widths_by_entropy": {"B": w.B, "F": 64, "us": pct(g["widths_ms"])},
+            "tree_topology_dp": topology,
             "tree_expand_sample": {"rows": g["expand_rows"], "k": 4, "us": pct(g["expand_sample_ms"])},
             "tree_select_topm": {"B": g["select_shape"][0], "Nc": g["select_shape"][1],
                                  "M": g["select_shape"][2], "us": pct(g["select_ms"])},
@@ -731,7 +847,7 @@ def main():
     del w, g
     torch.cuda.empty_cache()
     if not (args.no_configs or args.step_only):
-        rec["configs"] = run_configs(args, torch.device("cuda:0"))
+        rec["configs"] = run_configs(args, torch.device("cuda:0"), copy_gbs)
     print(json.dumps(rec), flush=True)
 
 

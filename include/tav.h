@@ -558,6 +558,27 @@ tav_status tree_widths_by_entropy(const double *entropy, int32_t B, int32_t F, i
  * t(N)/t(1) - 1 against N - 1, through the origin. NaN on bad input.
  */
 double tav_model_speedup(double expected_emitted, double draft_ratio, double alpha, int32_t n);
+
+/*
+ * tav_verify_speedup — the same model at batch B with a whole decode step as
+ * the baseline of alpha (LLM Primer ch. 9, §9.3; the yuuk.io wiki notes the
+ * speedup falls as the batch grows). With lin(T) = max(2 params / HBM,
+ * 2 params T / MFMA) the roofline time of a bf16 product over T tokens:
+ *   T_decode = layers (lin_layer(B) + attn_decode) + lin_head(B) + sampler_decode
+ *   T_verify = layers (lin_layer(B n) + attn_verify) + lin_head(B n) + sampler_verify
+ *   alpha = (T_verify / T_decode - 1) / n,
+ *   speedup = expected_emitted / (draft_ratio + 1 + alpha n).
+ * attn_* are one layer's attention times and sampler_* the walk's, in us (as
+ * measured); params counts of a layer's projections and of the vocabulary
+ * head; hbm_gbs in GB/s, mfma_tflops in TFLOP/s. Writes alpha, T_decode and
+ * T_verify (us) to out[0..2] if out is not NULL. NaN for a negative or
+ * non-finite argument, layers, batch or n below 1, or a non-positive rate.
+ */
+double tav_verify_speedup(double expected_emitted, double draft_ratio, int32_t layers,
+                          double layer_params, double head_params, int32_t batch, int32_t n,
+                          double attn_verify_us, double sampler_verify_us, double attn_decode_us,
+                          double sampler_decode_us, double hbm_gbs, double mfma_tflops,
+                          double *out);
 int32_t tav_best_chain_length(double p, double draft_ratio, double alpha, int32_t n_max,
                               double *speedup_out);
 double tav_fit_alpha(const int32_t *n, const double *t_us, int32_t count);

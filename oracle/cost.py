@@ -74,3 +74,34 @@ def alpha_from_times(n_values, step_us) -> float:
     x = n - 1.0
     y = t / t[0] - 1.0
     return float((x * y).sum() / (x * x).sum())
+
+
+def linear_us(params: float, tokens: int, hbm_gbs: float, mfma_tflops: float) -> float:
+    """Roofline time of a bf16 weight matrix product: its weights read once
+    (2 bytes each) or 2 FLOP per weight per token, whichever takes longer."""
+    return max(2.0 * params / (hbm_gbs * 1e3), 2.0 * params * tokens / (mfma_tflops * 1e6))
+
+
+def verify_speedup(expected_emitted: float, draft_ratio: float, layers: int,
+                   layer_params: float, head_params: float, batch: int, n: int,
+                   attn_verify_us: float, sampler_verify_us: float, attn_decode_us: float,
+                   sampler_decode_us: float, hbm_gbs: float, mfma_tflops: float):
+    """The speedup model of LLM Primer ch. 9 section 9.3 with a whole decode
+    step as the baseline, at batch B (the yuuk.io wiki notes the speedup
+    falls as the batch grows; this is why):
+
+      T_decode = layers (lin(B) + attn_decode) + head(B) + sampler_decode
+      T_verify = layers (lin(B n) + attn_verify) + head(B n) + sampler_verify
+      alpha    = (T_verify / T_decode - 1) / n
+      speedup  = E / (T_draft/T_decode + 1 + alpha n)
+
+    lin and head are ``linear_us`` of a layer's projections and of the
+    vocabulary head; attn and sampler are measured times of one layer's
+    attention and of the walk. Returns (speedup, alpha, T_decode, T_verify),
+    times in us."""
+    t_dec = layers * (linear_us(layer_params, batch, hbm_gbs, mfma_tflops) + attn_decode_us) \
+        + linear_us(head_params, batch, hbm_gbs, mfma_tflops) + sampler_decode_us
+    t_ver = layers * (linear_us(layer_params, batch * n, hbm_gbs, mfma_tflops) + attn_verify_us) \
+        + linear_us(head_params, batch * n, hbm_gbs, mfma_tflops) + sampler_verify_us
+    alpha = (t_ver / t_dec - 1.0) / n
+    return speedup(expected_emitted, draft_ratio, alpha, n), alpha, t_dec, t_ver

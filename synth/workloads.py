@@ -378,3 +378,14 @@ def slice_batch(w: Workload, B: int) -> Workload:
         draft_noise=cut(w.draft_noise),
         k_prefix=None if w.k_prefix is None else w.k_prefix[:B],
         v_prefix=None if w.v_prefix is None else w.v_prefix[:B])
+
+
+def slice_nodes(w: Workload, n: int) -> Workload:
+    """The first n nodes of every tree (a subtree: nodes are numbered
+    topologically), with their rows; n = 1 leaves the root alone, a decode
+    step's shape."""
+    cut = lambda a: None if a is None else np.ascontiguousarray(a[:, :n])
+    return dataclasses.replace(
+        w, N=n, parent=cut(w.parent), token=cut(w.token), q=cut(w.q), k_tree=cut(w.k_tree),
+        v_tree=cut(w.v_tree), target_logits=cut(w.target_logits),
+        draft_logits=cut(w.draft_logits), draft_noise=cut(w.draft_noise))

@@ -43,3 +43,21 @@ def test_bad_input():
     assert math.isnan(tav.fit_alpha([2, 4], [1.0, 2.0]))
     assert math.isnan(tav.fit_alpha([1], [1.0]))
     assert math.isnan(tav.fit_alpha([1, 2], [1.0, -2.0]))
+
+
+def test_verify_speedup_matches_the_oracle_and_rejects_bad_input():
+    import math
+    from oracle.cost import verify_speedup
+    cases = [(3.0, 0.0, 32, 218e6, 525e6, 1, 16, 26.5, 36.6, 20.0, 30.0, 8000.0, 2500.0),
+             (2.6, 0.1, 32, 218e6, 525e6, 128, 6, 341.0, 326.0, 300.0, 200.0, 6200.0, 2500.0),
+             (4.4, 0.0, 80, 855e6, 1050e6, 8, 64, 153.0, 50.0, 100.0, 20.0, 8000.0, 2500.0)]
+    for c in cases:
+        got = tav.verify_speedup(*c)
+        want = verify_speedup(*c)
+        for g, w in zip(got, want):
+            assert math.isclose(g, w, rel_tol=1e-12), (c, got, want)
+    bad = list(cases[0])
+    for i, v in ((0, -1.0), (2, 0), (5, 0), (6, 0), (7, float("nan")), (11, 0.0)):
+        b = list(bad)
+        b[i] = v
+        assert math.isnan(tav.verify_speedup(*b)[0]), i

@@ -91,3 +91,39 @@ def test_alpha_fit_recovers_the_model():
 def test_speedup_falls_with_overheads():
     e = cost.chain_expected_emitted(0.8, 6)
     assert cost.speedup(e, 0.0, 0.1, 6) > cost.speedup(e, 0.2, 0.1, 6) > cost.speedup(e, 0.2, 0.15, 6)
+
+
+# --- the batch-aware model (a whole decode step as alpha's baseline) -------
+
+def _vs(E=3.0, B=1, n=16, av=0.0, sv=0.0, ad=0.0, sd=0.0, draft=0.0):
+    from oracle.cost import verify_speedup
+    return verify_speedup(E, draft, 32, 218e6, 525e6, B, n, av, sv, ad, sd, 8000.0, 2500.0)
+
+
+def test_verify_model_is_the_plain_model_when_verification_costs_a_decode_step():
+    # n = 1 with the decode step's own times: T_verify = T_decode, alpha = 0
+    s, alpha, td, tv = _vs(E=1.7, n=1, av=20.0, sv=30.0, ad=20.0, sd=30.0)
+    assert alpha == 0.0 and td == tv and s == 1.7
+
+
+def test_weight_bound_batch_has_no_overhead_from_the_linear_layers():
+    # B n tokens still read the weights in less time than their FLOPs take
+    # (2 params B n / MFMA < 2 params / HBM while B n < 312): alpha = 0
+    s, alpha, td, tv = _vs(E=2.5, B=4, n=16)
+    assert alpha == 0.0 and s == 2.5
+
+
+def test_compute_bound_batch_costs_n_decode_steps():
+    # at B = 4096 both passes are MFMA-bound: T_verify / T_decode = n exactly
+    s, alpha, td, tv = _vs(E=2.0, B=4096, n=8)
+    assert abs(tv / td - 8.0) < 1e-12
+    assert abs(s - 2.0 / 8.0) < 1e-12
+
+
+def test_speedup_falls_as_the_batch_grows():
+    prev = None
+    for B in (1, 4, 16, 64, 128, 256, 1024):
+        s = _vs(E=3.0, B=B, n=16, av=30.0 + B, sv=40.0 + B, ad=20.0 + B / 4, sd=30.0 + B / 4)[0]
+        if prev is not None:
+            assert s <= prev + 1e-12
+        prev = s

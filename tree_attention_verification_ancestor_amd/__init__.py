@@ -85,6 +85,8 @@ _SIGNATURES = {
     "tree_topology_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "tree_topology_dp": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]),
     "tav_model_speedup": (ctypes.c_double, [_F64, _F64, _F64, _I32]),
+    "tav_verify_speedup": (ctypes.c_double, [_F64, _F64, _I32, _F64, _F64, _I32, _I32, _F64,
+                                             _F64, _F64, _F64, _F64, _F64, _P]),
     "tav_best_chain_length": (_I32, [_F64, _F64, _F64, _I32, _P]),
     "tav_fit_alpha": (ctypes.c_double, [_P, _P, _I32]),
     "tav_philox_uniforms": (_I32, [_U64, _U64, _I32, _I32, _P, _P]),
@@ -576,6 +578,19 @@ def tree_topology_dp(p_rank, n: int, depth: int, device=None, stream=None):
         ctypes.cast(p, ctypes.c_void_p), K, n, depth, _ptr(parent), _ptr(rank), _ptr(value),
         _ptr(ws), need, _stream(stream)))
     return parent, rank, value
+
+
+def verify_speedup(expected_emitted, draft_ratio, layers, layer_params, head_params, batch, n,
+                   attn_verify_us, sampler_verify_us, attn_decode_us, sampler_decode_us,
+                   hbm_gbs, mfma_tflops):
+    """tav_verify_speedup (host): (speedup, alpha, T_decode us, T_verify us)."""
+    out = (ctypes.c_double * 3)()
+    s = lib().tav_verify_speedup(float(expected_emitted), float(draft_ratio), int(layers),
+                                 float(layer_params), float(head_params), int(batch), int(n),
+                                 float(attn_verify_us), float(sampler_verify_us),
+                                 float(attn_decode_us), float(sampler_decode_us), float(hbm_gbs),
+                                 float(mfma_tflops), ctypes.cast(out, ctypes.c_void_p))
+    return float(s), out[0], out[1], out[2]
 
 
 def model_speedup(expected_emitted: float, draft_ratio: float, alpha: float, n: int) -> float:

@@ -60,3 +60,52 @@ extern "C" double tav_fit_alpha(const int32_t *n, const double *t_us, int32_t co
     }
     return sxx > 0.0 ? sxy / sxx : NAN;
 }
+
+// The same model with a whole decode step as its baseline, at batch B: a
+// layer's linear projections and the vocabulary head by their roofline
+// (bf16 weights read once, or 2 FLOP per weight per token), one layer's
+// attention and the walk as measured. The verification pass scores B*n
+// tokens where a decode step scores B, which is why the speedup falls as the
+// batch grows (the yuuk.io wiki's observation).
+namespace {
+
+double linear_us(double params, double tokens, double hbm_gbs, double mfma_tflops)
+{
+    const double t_mem = 2.0 * params / (hbm_gbs * 1e3);
+    const double t_mac = 2.0 * params * tokens / (mfma_tflops * 1e6);
+    return t_mem > t_mac ? t_mem : t_mac;
+}
+
+} // namespace
+
+extern "C" double tav_verify_speedup(double expected_emitted, double draft_ratio, int32_t layers,
+                                     double layer_params, double head_params, int32_t batch,
+                                     int32_t n, double attn_verify_us, double sampler_verify_us,
+                                     double attn_decode_us, double sampler_decode_us,
+                                     double hbm_gbs, double mfma_tflops, double *out)
+{
+    const double args[] = {expected_emitted, draft_ratio, layer_params, head_params,
+                           attn_verify_us, sampler_verify_us, attn_decode_us, sampler_decode_us};
+    for (double v : args)
+        if (!(v >= 0.0) || !std::isfinite(v))
+            return NAN;
+    if (layers < 1 || batch < 1 || n < 1 || !(hbm_gbs > 0.0) || !(mfma_tflops > 0.0))
+        return NAN;
+    const double t_dec = layers * (linear_us(layer_params, batch, hbm_gbs, mfma_tflops) +
+                                   attn_decode_us) +
+                         linear_us(head_params, batch, hbm_gbs, mfma_tflops) + sampler_decode_us;
+    const double t_ver = layers * (linear_us(layer_params, (double)batch * n, hbm_gbs,
+                                             mfma_tflops) +
+                                   attn_verify_us) +
+                         linear_us(head_params, (double)batch * n, hbm_gbs, mfma_tflops) +
+                         sampler_verify_us;
+    if (!(t_dec > 0.0))
+        return NAN;
+    const double alpha = (t_ver / t_dec - 1.0) / n;
+    if (out) {
+        out[0] = alpha;
+        out[1] = t_dec;
+        out[2] = t_ver;
+    }
+    return expected_emitted / (draft_ratio + 1.0 + alpha * n);
+}
