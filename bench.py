@@ -1,9 +1,13 @@
 """Benchmark of the tree-verification step on one MI355X.
 
-A step is one pass of the whole path over one batch: tree_mask_build,
-tree_attn_verify (one attention layer), spec_verify_sample and kv_commit_path,
-chained on one stream with no host synchronisation. Inputs are seeded
-synthetic data already resident in HBM.
+A step is one pass of the whole path over one batch, chained on one stream
+with no host synchronisation: tree_attn_verify_tree (one attention layer, the
+ancestor mask built from parent[] in the same launch and written out) and
+spec_verify_sample_commit (the rejection-sampling walk, each sequence's
+accepted path committed to the paged cache by the walk's own workgroups).
+The same step as four calls (tree_mask_build, tree_attn_verify,
+spec_verify_sample, kv_commit_path) is timed beside it for the per-call
+breakdown. Inputs are seeded synthetic data already resident in HBM.
 
 The headline workload is the Llama-3-70B-shaped layer: batch 8, 64-node trees
 (depth 6, width 4), 64 query / 8 KV heads, head_dim 128, paged prefixes of
@@ -55,7 +59,8 @@ SWEEP_ACCEPTS = (0.5, 0.8, 0.9)
 LAYERS_8B = 32
 LAYER_PARAMS_8B = 4096 * (4096 + 1024 + 1024 + 4096) + 3 * 4096 * 14336
 HEAD_PARAMS_8B = 128256 * 4096
-STAGES = ["tree_mask_build", "tree_attn_verify", "spec_verify_sample", "kv_commit_path"]
+STAGES_UNFUSED = ["tree_mask_build", "tree_attn_verify", "spec_verify_sample", "kv_commit_path"]
+STAGES = ["tree_attn_verify_tree", "spec_verify_sample_commit"]
 
 
 # ---------------------------------------------------------------------------
@@ -178,8 +183,9 @@ def pct(a):
 # the step on the GPU
 
 class StepRunner:
-    """The four calls of a step over one workload, pre-marshalled, with
-    `copies` copies of the paged caches to rotate through."""
+    """A step over one workload as two fused calls (the default) or as the
+    four separate calls, pre-marshalled, with `copies` copies of the paged
+    caches to rotate through."""
 
     def __init__(self, w, dev, copies=1):
         import torch
@@ -223,9 +229,22 @@ class StepRunner:
                            self.new_len, self.flags, s)
         torch.cuda.synchronize()
         nblk, maxb = int(w.k_cache.shape[0]), int(w.block_table.shape[1])
+        self.calls_unfused = []
         self.calls = []
         for kc, vc in self.copies:
             self.calls.append((
+                tav.prepare("tree_attn_verify_tree", d["q"], d["k_tree"], d["v_tree"], kc, vc,
+                            nblk, d["block_table"], maxb, d["prefix_len"], w.max_prefix_len,
+                            d["parent"], self.mask, self.depth, B, N, w.Hq, w.Hkv, w.D, w.block,
+                            w.scale, self.out, self.ws_a, self.ws_a.numel(), self.flags, s),
+                tav.prepare("spec_verify_sample_commit", d["target_logits"], d["draft_logits"],
+                            d["parent"], d["token"], B, N, V, w.temperature, w.philox_seed,
+                            w.philox_offset, 0, self.path, self.n_acc, self.toks, d["k_tree"],
+                            d["v_tree"], nblk, d["block_table"], maxb, d["prefix_len"], kc, vc,
+                            w.Hkv, w.D, w.block, self.slots, self.new_len, self.ws_s,
+                            self.ws_s.numel(), self.flags, s),
+            ))
+            self.calls_unfused.append((
                 tav.prepare("tree_mask_build", d["parent"], B, N, self.mask, self.depth,
                             self.flags, s),
                 tav.prepare("tree_attn_verify", d["q"], d["k_tree"], d["v_tree"], kc, vc, nblk,
@@ -242,16 +261,20 @@ class StepRunner:
             ))
         self.i = 0
 
-    def step(self, ev=None, attn_ev=None):
-        c = self.calls[self.i % len(self.calls)]
+    def step(self, ev=None, attn_ev=None, unfused=False):
+        """One step; ev: events before and after each call; attn_ev: events
+        around the attention launch."""
+        calls = self.calls_unfused if unfused else self.calls
+        c = calls[self.i % len(calls)]
         self.i += 1
+        attn = 1 if unfused else 0
         if ev:
             ev[0].record(self.stream)
-        for k in range(4):
-            if attn_ev and k == 1:
+        for k in range(len(c)):
+            if attn_ev and k == attn:
                 attn_ev[0].record(self.stream)
             c[k]()
-            if attn_ev and k == 1:
+            if attn_ev and k == attn:
                 attn_ev[1].record(self.stream)
             if ev:
                 ev[k + 1].record(self.stream)
@@ -288,19 +311,20 @@ class StepRunner:
         from synth.device import to_numpy
         return to_numpy(paths), to_numpy(naccs)
 
-    def cold_steps(self, n, warmup, flush):
+    def cold_steps(self, n, warmup, flush, unfused=False):
         """n steps, each after a write of `flush` (the last-level cache cold),
-        with events between the calls: per-step and per-stage ms."""
+        with events between the calls: per-step and per-call ms."""
         torch = self.torch
+        k = 4 if unfused else 2
         for _ in range(warmup):
-            self.step()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n)]
+            self.step(unfused=unfused)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(k + 1)] for _ in range(n)]
         for e in evs:
             flush.fill_(1)
-            self.step(ev=e)
+            self.step(ev=e, unfused=unfused)
         self.check()
-        stage = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in evs])
-        step = np.array([e[0].elapsed_time(e[4]) for e in evs])
+        stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(k)] for e in evs])
+        step = np.array([e[0].elapsed_time(e[k]) for e in evs])
         return step, stage
 
 
@@ -335,17 +359,28 @@ def run_headline(args, w):
     ms_step = start.elapsed_time(stop) / args.steps
     attn_ms = np.array([e[0].elapsed_time(e[1]) for e in attn_evs])
 
-    # per-stage times with events on the launch stream (a second pass)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # per-call times with events on the launch stream (a second pass), and
+    # the same step as four separate calls
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         r.step(ev=evs[i])
     r.check()
-    stage = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in evs])
+    stage = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(2)] for e in evs])
     out = dict(ms_step=ms_step, ms_attn=float(attn_ms.mean()), attn_all=attn_ms,
                stage_ms=stage.mean(axis=0), stage_all=stage,
-               step_all=np.array([e[0].elapsed_time(e[4]) for e in evs]),
+               step_all=np.array([e[0].elapsed_time(e[2]) for e in evs]),
                depth=to_numpy(r.depth), path=to_numpy(r.path), n_acc=to_numpy(r.n_acc))
+    for _ in range(args.warmup):
+        r.step(unfused=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        r.step(ev=evs[i], unfused=True)
+    r.check()
+    stage_u = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in evs])
+    out["unfused_stage_ms"] = stage_u.mean(axis=0)
+    out["unfused_step_all"] = np.array([e[0].elapsed_time(e[4]) for e in evs])
     if args.step_only:
         out["offset_paths"] = np.zeros((0, B, N), np.int32)
         out["offset_naccs"] = np.zeros((0, B), np.int32)
@@ -473,16 +508,15 @@ def run_headline(args, w):
         sl_slots = torch.empty((B, n), dtype=torch.int32, device=dev)
         nl = torch.empty((B,), dtype=torch.int32, device=dev)
         seq = (
-            tav.prepare("tree_mask_build", sl["parent"], B, n, m_n, dep_n, flags, stream),
-            tav.prepare("tree_attn_verify", sl["q"], sl["k_tree"], sl["v_tree"], kc, vc, nblk,
-                        d["block_table"], maxb, d["prefix_len"], w.max_prefix_len, m_n, B, n,
-                        w.Hq, w.Hkv, w.D, w.block, w.scale, o_n, wa, wa.numel(), flags, stream),
-            tav.prepare("spec_verify_sample", sl["target_logits"], sl["draft_logits"],
+            tav.prepare("tree_attn_verify_tree", sl["q"], sl["k_tree"], sl["v_tree"], kc, vc,
+                        nblk, d["block_table"], maxb, d["prefix_len"], w.max_prefix_len,
+                        sl["parent"], m_n, dep_n, B, n, w.Hq, w.Hkv, w.D, w.block, w.scale, o_n,
+                        wa, wa.numel(), flags, stream),
+            tav.prepare("spec_verify_sample_commit", sl["target_logits"], sl["draft_logits"],
                         sl["parent"], sl["token"], B, n, V, w.temperature, w.philox_seed,
-                        w.philox_offset, pa, na, tk, ws, ws.numel(), flags, stream),
-            tav.prepare("kv_commit_path", sl["k_tree"], sl["v_tree"], pa, na, nblk,
-                        d["block_table"], maxb, d["prefix_len"], kc, vc, B, n, w.Hkv, w.D,
-                        w.block, sl_slots, nl, flags, stream),
+                        w.philox_offset, 0, pa, na, tk, sl["k_tree"], sl["v_tree"], nblk,
+                        d["block_table"], maxb, d["prefix_len"], kc, vc, w.Hkv, w.D, w.block,
+                        sl_slots, nl, ws, ws.numel(), flags, stream),
         )
 
         def step_n(seq=seq):
@@ -515,7 +549,7 @@ def run_config(w, steps, warmup, n_offsets, flush, dev):
     paths, naccs = r.offsets(n_offsets)
     acc = acceptance_stats(w, paths, naccs)
     a_bytes, a_flops = attention_work(w, depth)
-    t_attn = float(np.median(stage[:, 1])) * 1e-3
+    t_attn = float(np.median(stage[:, 0])) * 1e-3
     t_step = float(np.median(step)) * 1e-3
     floor = max((a_bytes + acc["mean_sampler_bytes"] + acc["mean_commit_bytes"]) / (HBM_PEAK_GBS * 1e9),
                 a_flops / (MFMA_PEAK_TFLOPS * 1e12))
@@ -602,15 +636,14 @@ def sweep_model(sweep, decode, copy_gbs):
 
     def times(rec):
         st = rec["stages_us"]
-        return st["tree_attn_verify"], st["spec_verify_sample"] + st["tree_mask_build"] + \
-            st["kv_commit_path"]
+        return st["tree_attn_verify_tree"], st["spec_verify_sample_commit"]
 
     out = []
     for acc in SWEEP_ACCEPTS:
         for B in SWEEP_BATCHES:
             dec = decode[B]
-            ad, sd = dec["stages_us"]["tree_attn_verify"], \
-                dec["stages_us"]["spec_verify_sample"] + dec["stages_us"]["kv_commit_path"]
+            ad, sd = dec["stages_us"]["tree_attn_verify_tree"], \
+                dec["stages_us"]["spec_verify_sample_commit"]
             row = {"B": B, "target_acceptance": acc}
             for rec in sweep:
                 if rec["B"] != B or rec["target_acceptance"] != acc:
@@ -810,6 +843,9 @@ def main():
         "stages_us": {k: round(v * 1e3, 2) for k, v in zip(STAGES, g["stage_ms"])},
         "stages_us_pctl": {k: pct(g["stage_all"][:, i]) for i, k in enumerate(STAGES)},
         "step_us_pctl": pct(g["step_all"]),
+        "unfused_step": {"us_pctl": pct(g["unfused_step_all"]),
+                         "stages_us": {k: round(v * 1e3, 2)
+                                       for k, v in zip(STAGES_UNFUSED, g["unfused_stage_ms"])}},
         "tree_attn": {"us": round(t_attn * 1e6, 2), "us_pctl": pct(g["attn_all"]),
                       "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                       "measured_copy_gbs": round(copy_gbs, 1),

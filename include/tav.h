@@ -4,10 +4,12 @@
  * C ABI of the verification step of tree-based speculative decoding:
  *   tree_mask_build     parent[] -> packed ancestor-or-self bitmasks
  *   tree_attn_verify    tree attention over a paged KV prefix plus ancestors
+ *   tree_attn_verify_tree  the same from parent[] (mask built in the launch)
  *   spec_verify_sample  target/draft softmax and the rejection-sampling walk
  *   spec_verify_sample_wor  the same walk for siblings drawn without replacement
  *   spec_verify_sample_probe  the walk, also writing the p and q it decides with
  *   spec_verify_sample_noalloc  the walk on the library's fixed scratch (no workspace)
+ *   spec_verify_sample_commit  the walk and kv_commit_path in one launch
  *   kv_commit_path      copy the accepted path's K/V into the paged cache
  *   kv_commit_inplace   the same when the tree's K/V already sit in the cache
  *   tree_expand_topk    top-k draft tokens, log q and entropy per frontier row
@@ -158,6 +160,33 @@ tav_status tree_attn_verify(const uint16_t *q, const uint16_t *k_tree, const uin
                             const uint64_t *mask, int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
                             int32_t D, int32_t block_size, float scale, float *out,
                             void *workspace, size_t ws_bytes, uint32_t *dev_flags, void *stream);
+
+/*
+ * tree_attn_verify_tree — tree_attn_verify with the tree given as parent[]
+ * instead of a mask: the attention launch builds the ancestor-or-self bits
+ * itself (the rule of tree_mask_build: node j is visible to node i exactly
+ * when j is i or one of its ancestors; jisaku.com glossary, tree-attention
+ * section), so a step needs no separate mask launch. Outputs and every
+ * other argument are those of tree_attn_verify; out is bit-identical to
+ * tree_attn_verify's with the mask tree_mask_build makes from the same
+ * parent[].
+ *   parent     int32 [B][N], topological (parent[0] = -1, parent[i] < i)
+ *   mask_out   optional uint64 [B][N][ceil(N/64)]: the mask, as tree_mask_build
+ *              writes it (NULL: not written)
+ *   depth_out  optional int32 [B][N]: node depths, as tree_mask_build
+ * Flags: those of tree_attn_verify, and TAV_FLAG_BAD_PARENT for a parent
+ * entry that breaks the numbering (as tree_mask_build; the bits of such a
+ * node stop where its climb stops).
+ */
+tav_status tree_attn_verify_tree(const uint16_t *q, const uint16_t *k_tree,
+                                 const uint16_t *v_tree, const uint16_t *k_cache,
+                                 const uint16_t *v_cache, int32_t num_blocks,
+                                 const int32_t *block_table, int32_t max_blocks,
+                                 const int32_t *prefix_len, int32_t max_prefix_len,
+                                 const int32_t *parent, uint64_t *mask_out, int32_t *depth_out,
+                                 int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                 int32_t block_size, float scale, float *out, void *workspace,
+                                 size_t ws_bytes, uint32_t *dev_flags, void *stream);
 
 /*
  * spec_verify_workspace_bytes — device workspace spec_verify_sample needs
@@ -329,6 +358,32 @@ tav_status kv_commit_path(const uint16_t *k_tree, const uint16_t *v_tree, const 
                           int32_t B, int32_t N, int32_t Hkv, int32_t D, int32_t block_size,
                           int32_t *commit_slots, int32_t *new_prefix_len, uint32_t *dev_flags,
                           void *stream);
+
+/*
+ * spec_verify_sample_commit — spec_verify_sample (or spec_verify_sample_wor
+ * with without_replacement = 1; greedy at temperature 0) followed by
+ * kv_commit_path, in one launch: the walk's workgroups copy each sequence's
+ * accepted path into the paged cache as soon as that sequence is decided
+ * (radar-34b blog §5 and jisaku.com glossary, KV-cache section: only the
+ * accepted root-to-node path is kept, at the sequence's next positions).
+ * Every output is the bytes the two separate calls write for the same
+ * arguments: path, n_accepted, out_tokens as spec_verify_sample; the caches,
+ * commit_slots and new_prefix_len as kv_commit_path given that path (a
+ * sequence whose walk raised a flag commits its root row, as there).
+ * Arguments are the union of the two calls' and mean the same; the commit's
+ * are checked first (kv_commit_path's rules: D 64 or 128, block_size 16,
+ * 16-byte aligned k_tree, v_tree, k_cache), then the walk's. The workspace is
+ * spec_verify_workspace_bytes(B, N, V) bytes, as for spec_verify_sample.
+ * Flags: the union of the two calls' flags.
+ */
+tav_status spec_verify_sample_commit(
+    const float *target_logits, const float *draft_logits, const int32_t *parent,
+    const int32_t *token, int32_t B, int32_t N, int32_t V, double temperature, uint64_t seed,
+    uint64_t offset, int32_t without_replacement, int32_t *path, int32_t *n_accepted,
+    int32_t *out_tokens, const uint16_t *k_tree, const uint16_t *v_tree, int32_t num_blocks,
+    const int32_t *block_table, int32_t max_blocks, const int32_t *prefix_len, uint16_t *k_cache,
+    uint16_t *v_cache, int32_t Hkv, int32_t D, int32_t block_size, int32_t *commit_slots,
+    int32_t *new_prefix_len, void *workspace, size_t ws_bytes, uint32_t *dev_flags, void *stream);
 
 /*
  * kv_commit_inplace — zero-copy rollback: the tree's K/V already sit in the

@@ -85,6 +85,51 @@ def test_sampler_rejects_bad_arguments(fn, kw, code):
     assert _sample(fn, **kw) == code
 
 
+def _attn_tree(**kw):
+    args = dict(q=FAKE, k_tree=FAKE, v_tree=FAKE, k_cache=FAKE, v_cache=FAKE, num_blocks=10,
+                block_table=FAKE, max_blocks=4, prefix_len=FAKE, max_prefix_len=64, parent=FAKE,
+                mask_out=None, depth_out=None, B=1, N=5, Hq=8, Hkv=2, D=128, block_size=16,
+                scale=0.088, out=FAKE, workspace=None, ws_bytes=0, dev_flags=None, stream=None)
+    args.update(kw)
+    return tav.lib().tree_attn_verify_tree(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(parent=None), tav.ERR_ARG), (dict(q=None), tav.ERR_ARG), (dict(B=0), tav.ERR_ARG),
+    (dict(scale=0.0), tav.ERR_ARG), (dict(D=96), tav.ERR_UNSUPPORTED),
+    (dict(N=300), tav.ERR_UNSUPPORTED), (dict(parent=ctypes.c_void_p(0x10002)), tav.ERR_ARG),
+    (dict(mask_out=ctypes.c_void_p(0x10004)), tav.ERR_ARG),
+    (dict(depth_out=ctypes.c_void_p(0x10002)), tav.ERR_ARG),
+])
+def test_attention_from_parents_rejects_bad_arguments(kw, code):
+    assert _attn_tree(**kw) == code
+
+
+def _sample_commit(**kw):
+    args = dict(tl=FAKE, dl=FAKE, parent=FAKE, token=FAKE, B=2, N=5, V=1000, T=1.0, seed=0,
+                offset=0, wor=0, path=FAKE, n_acc=FAKE, out_tok=FAKE, k_tree=FAKE, v_tree=FAKE,
+                num_blocks=10, block_table=FAKE, max_blocks=4, prefix_len=FAKE, k_cache=FAKE,
+                v_cache=FAKE, Hkv=2, D=128, block_size=16, slots=FAKE, new_len=FAKE, ws=FAKE,
+                ws_bytes=1 << 20, flags=None, stream=None)
+    args.update(kw)
+    return tav.lib().spec_verify_sample_commit(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    # the commit's checks
+    (dict(k_cache=None), tav.ERR_ARG), (dict(slots=None), tav.ERR_ARG),
+    (dict(num_blocks=0), tav.ERR_ARG), (dict(wor=2), tav.ERR_ARG),
+    (dict(D=80), tav.ERR_UNSUPPORTED), (dict(block_size=8), tav.ERR_UNSUPPORTED),
+    (dict(k_tree=ctypes.c_void_p(0x10008)), tav.ERR_ARG),
+    # then the walk's
+    (dict(tl=None), tav.ERR_ARG), (dict(path=None), tav.ERR_ARG), (dict(V=0), tav.ERR_ARG),
+    (dict(T=-1.0), tav.ERR_ARG), (dict(dl=None), tav.ERR_ARG),
+    (dict(V=(1 << 21) + 1), tav.ERR_UNSUPPORTED),
+])
+def test_sample_commit_rejects_bad_arguments(kw, code):
+    assert _sample_commit(**kw) == code
+
+
 def _commit(**kw):
     args = dict(k_tree=FAKE, v_tree=FAKE, path=FAKE, n_acc=FAKE, num_blocks=10,
                 block_table=FAKE, max_blocks=4, prefix_len=FAKE, k_cache=FAKE, v_cache=FAKE,

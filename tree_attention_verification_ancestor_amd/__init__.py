@@ -64,6 +64,9 @@ _SIGNATURES = {
     "tav_attn_plan": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
     "tree_attn_verify": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _P, _I32, _I32,
                                 _I32, _I32, _I32, _I32, _F32, _P, _P, _SZ, _P, _P]),
+    "tree_attn_verify_tree": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _P, _P, _P,
+                                     _I32, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _SZ, _P,
+                                     _P]),
     "spec_verify_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "spec_verify_sample": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _F64, _U64, _U64, _P, _P,
                                   _P, _P, _SZ, _P, _P]),
@@ -73,6 +76,9 @@ _SIGNATURES = {
                                         _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
     "spec_verify_sample_noalloc": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _F64, _U64, _U64,
                                           _P, _P, _P, _P, _P]),
+    "spec_verify_sample_commit": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _F64, _U64, _U64,
+                                         _I32, _P, _P, _P, _P, _P, _I32, _P, _I32, _P, _P, _P,
+                                         _I32, _I32, _I32, _P, _P, _P, _SZ, _P, _P]),
     "kv_commit_path": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _P, _I32, _I32, _I32,
                               _I32, _I32, _P, _P, _P, _P]),
     "kv_commit_inplace": (_I32, [_P, _P, _I32, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
@@ -266,6 +272,48 @@ def tree_attn_verify(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_le
     return out
 
 
+def tree_attn_verify_tree(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len,
+                          max_prefix_len: int, parent, scale: Optional[float] = None,
+                          out: Optional[torch.Tensor] = None, mask_out=None, depth_out=None,
+                          workspace: Optional[torch.Tensor] = None,
+                          dev_flags: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Tree attention with the mask built in the launch from parent [B, N];
+    optionally also writes the mask and depths into mask_out, depth_out."""
+    _need(q, "q", _BF16)
+    B, N, Hq, D = q.shape
+    dev = q.device
+    Hkv = k_tree.shape[2]
+    _need(k_tree, "k_tree", _BF16, (B, N, Hkv, D), dev)
+    _need(v_tree, "v_tree", _BF16, (B, N, Hkv, D), dev)
+    nblk = k_cache.shape[0]
+    _need(k_cache, "k_cache", _BF16, (nblk, Hkv, BLOCK, D), dev)
+    _need(v_cache, "v_cache", _BF16, (nblk, Hkv, D, BLOCK), dev)
+    _need(block_table, "block_table", _I32T, None, dev)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    _need(prefix_len, "prefix_len", _I32T, (B,), dev)
+    _need(parent, "parent", _I32T, (B, N), dev)
+    if mask_out is not None:
+        _need(mask_out, "mask_out", _MASKT, (B, N, (N + 63) // 64), dev)
+    if depth_out is not None:
+        _need(depth_out, "depth_out", _I32T, (B, N), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, N, Hq, D), dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,), (B, N, Hq, D), dev)
+    need = tree_attn_workspace_bytes(B, N, Hq, Hkv, D, max_prefix_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("tree_attn_verify_tree", lib().tree_attn_verify_tree(
+        _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), nblk,
+        _ptr(block_table), block_table.shape[1], _ptr(prefix_len), int(max_prefix_len),
+        _ptr(parent), _ptr(mask_out), _ptr(depth_out), B, N, Hq, Hkv, D, BLOCK, float(scale),
+        _ptr(out), _ptr(workspace), ws_bytes, _ptr(dev_flags), _stream(stream)))
+    return out
+
+
 def spec_verify_workspace_bytes(B, N, V) -> int:
     return int(lib().spec_verify_workspace_bytes(B, N, V))
 
@@ -413,6 +461,52 @@ def kv_commit_path(k_tree, v_tree, path, n_accepted, block_table, prefix_len, k_
         block_table.shape[1], _ptr(prefix_len), _ptr(k_cache), _ptr(v_cache), B, N, Hkv, D,
         BLOCK, _ptr(commit_slots), _ptr(new_prefix_len), _ptr(dev_flags), _stream(stream)))
     return commit_slots, new_prefix_len
+
+
+def spec_verify_sample_commit(target_logits, draft_logits, parent, token, k_tree, v_tree,
+                              block_table, prefix_len, k_cache, v_cache,
+                              temperature: float = 1.0, seed: int = 0, offset: int = 0,
+                              without_replacement: bool = False, path=None, n_accepted=None,
+                              out_tokens=None, commit_slots=None, new_prefix_len=None,
+                              workspace=None, dev_flags=None, stream=None):
+    """The walk and the KV commit of its accepted paths in one launch; returns
+    (path, n_accepted, out_tokens, commit_slots, new_prefix_len), the outputs
+    of spec_verify_sample (or its without-replacement form) followed by
+    kv_commit_path."""
+    _need(target_logits, "target_logits", (torch.float32,))
+    B, N, V = target_logits.shape
+    dev = target_logits.device
+    if draft_logits is not None or temperature != 0:
+        _need(draft_logits, "draft_logits", (torch.float32,), (B, N, V), dev)
+    _need(parent, "parent", _I32T, (B, N), dev)
+    _need(token, "token", _I32T, (B, N), dev)
+    _need(k_tree, "k_tree", _BF16)
+    _, _, Hkv, D = k_tree.shape
+    _need(k_tree, "k_tree", _BF16, (B, N, Hkv, D), dev)
+    _need(v_tree, "v_tree", _BF16, (B, N, Hkv, D), dev)
+    _need(block_table, "block_table", _I32T, None, dev)
+    _need(prefix_len, "prefix_len", _I32T, (B,), dev)
+    nblk = k_cache.shape[0]
+    _need(k_cache, "k_cache", _BF16, (nblk, Hkv, BLOCK, D), dev)
+    _need(v_cache, "v_cache", _BF16, (nblk, Hkv, D, BLOCK), dev)
+    outs = []
+    for t, shape in ((path, (B, N)), (n_accepted, (B,)), (out_tokens, (B, N)),
+                     (commit_slots, (B, N)), (new_prefix_len, (B,))):
+        if t is None:
+            t = torch.empty(shape, dtype=torch.int32, device=dev)
+        _need(t, "output", _I32T, shape, dev)
+        outs.append(t)
+    if workspace is None:
+        workspace = new_sampler_workspace(B, N, V, dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("spec_verify_sample_commit", lib().spec_verify_sample_commit(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(parent), _ptr(token), B, N, V,
+        float(temperature), int(seed), int(offset), int(bool(without_replacement)),
+        _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _ptr(k_tree), _ptr(v_tree), nblk,
+        _ptr(block_table), block_table.shape[1], _ptr(prefix_len), _ptr(k_cache), _ptr(v_cache),
+        Hkv, D, BLOCK, _ptr(outs[3]), _ptr(outs[4]), _ptr(workspace), ws_bytes,
+        _ptr(dev_flags), _stream(stream)))
+    return tuple(outs)
 
 
 def kv_commit_inplace(path, n_accepted, block_table, prefix_len, k_cache, v_cache,

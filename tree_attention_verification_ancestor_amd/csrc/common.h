@@ -40,14 +40,26 @@ int device_cu_count();
 // holds at once (0 on failure).
 int kernel_occupancy(const void *kernel, int threads);
 
+// The KV commit that the walk's workgroups can do themselves right after each
+// sequence is decided (null k_tree: none): path row t of sequence b to token
+// position prefix_len[b] + t, as kv_commit_path does.
+struct CommitArgs {
+    const uint16_t *k_tree, *v_tree;
+    const int32_t *block_table, *prefix_len;
+    uint16_t *k_cache, *v_cache;
+    int32_t *commit_slots, *new_prefix_len;
+    int32_t num_blocks, max_blocks, Hkv, D;
+};
+
 // The launch behind spec_verify_sample and its variants: host checks, plan,
 // workspace check, one kernel launch. wor: the without-replacement sibling
-// rule; p_rows/q_rows/child_pq non-NULL: the probe variant.
+// rule; p_rows/q_rows/child_pq non-NULL: the probe variant; commit non-NULL:
+// the walk also commits the accepted path (its arguments already checked).
 tav_status sv_launch(const float *target_logits, const float *draft_logits,
                      const int32_t *parent, const int32_t *token, int32_t B, int32_t N, int32_t V,
                      double temperature, uint64_t seed, uint64_t offset, int32_t *path,
                      int32_t *n_accepted, int32_t *out_tokens, void *workspace, size_t ws_bytes,
                      uint32_t *dev_flags, void *stream, bool wor, double *p_rows,
-                     double *q_rows, double *child_pq);
+                     double *q_rows, double *child_pq, const CommitArgs *commit = nullptr);
 
 } // namespace tav

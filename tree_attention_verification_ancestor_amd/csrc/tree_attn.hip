@@ -85,7 +85,10 @@ struct Cfg {
 struct AttnArgs {
     const uint16_t *q, *k_tree, *v_tree, *k_cache, *v_cache;
     const int32_t *block_table, *prefix_len;
-    const uint64_t *mask;
+    const uint64_t *mask;    // [B][N][W] ancestor bits, or NULL: built from parent
+    const int32_t *parent;   // [B][N] when mask is NULL
+    uint64_t *mask_out;      // optional copies of the built mask and depths
+    int32_t *depth_out;
     float *out, *part_o, *part_ml;
     uint32_t *flags;
     int32_t num_blocks, max_blocks, max_prefix_len;
@@ -200,6 +203,10 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(16))) char s_v[kVSlots * VTB];
     // this split's cache blocks as head-block indices (block * Hkv + kvh)
     __shared__ __attribute__((aligned(16))) uint32_t s_bt[kMaxSplitBlocks];
+    // ancestor bits of this workgroup's nodes built from parent[] (when no
+    // mask is passed in), and the parent row they are built from
+    __shared__ uint64_t s_mask[C::kRows][kMaxNodes / 64];
+    __shared__ int32_t s_par[kMaxNodes];
 
     // ---- which (sequence, kv head, split, row block) ------------------------
     const int bid = blockIdx.x;
@@ -281,7 +288,16 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
             qf[k] = __builtin_bit_cast(bf16x8, v);
         }
     }
-    const uint64_t mrow0 = (n_tree > 0 && row_ok) ? a.mask[((int64_t)b * a.N + node) * a.W + tt0] : 1;
+    const bool built = a.mask == nullptr;
+    // The workgroup of (sequence, KV head 0, split 0, row block 0) also
+    // checks the tree and writes the built mask out, if asked to.
+    const bool lead_mask = built && kvh == 0 && s == 0 && rb == 0;
+    const bool need_mask = built && (n_tree > 0 || lead_mask);
+    const uint64_t mrow0 =
+        (!built && n_tree > 0 && row_ok) ? a.mask[((int64_t)b * a.N + node) * a.W + tt0] : 1;
+    if (need_mask)
+        for (int i = tid; i < a.N; i += C::kThreads)
+            s_par[i] = a.parent[(int64_t)b * a.N + i];
     // Wait for these loads here, before any tile load is in flight. The
     // compiler does not see the direct tile loads (inline assembly), so a
     // register load it still counts as outstanding inside the tile loop would
@@ -480,7 +496,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
             const int tt = it - n_pre + tt0;
             mw = 1;    // a padding row sees key 0 only
             if (row_ok)
-                mw = tt == tt0 ? mrow0 : a.mask[((int64_t)b * a.N + node) * a.W + tt];
+                mw = built ? s_mask[node - rb * C::kRows / a.G][tt]
+                           : tt == tt0 ? mrow0 : a.mask[((int64_t)b * a.N + node) * a.W + tt];
             lim = a.N - tt * kKT;
         } else {
             mw = ~0ull;
@@ -637,7 +654,46 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     // times zero V
     for (int q = tid; q < 2 * VTB / 16; q += C::kThreads)
         *lds_at<u32x4>(v_lds + 3 * VTB + q * 16) = u32x4{0, 0, 0, 0};
-    __syncthreads();   // s_bt written by all threads before any wave reads it
+    __syncthreads();   // s_bt (and s_par) written by all threads before any wave reads it
+    if (need_mask) {
+        // Node i's bits: climb from i to the root setting one bit per node
+        // met (parent[i] < i, so each climb ends); the same rule and flag as
+        // tree_mask_build. Read only at the tree tiles, several barriers on.
+        // this workgroup's nodes: those of rows [rb R, rb R + R), R = kRows
+        const int node_lo = rb * C::kRows / a.G;
+        const int node_hi = std::min(a.N, (rb * C::kRows + C::kRows - 1) / a.G + 1);
+        for (int i = lead_mask ? tid : node_lo + tid; i < (lead_mask ? a.N : node_hi);
+             i += C::kThreads) {
+            uint64_t words[kMaxNodes / 64] = {0, 0, 0, 0};
+            bool bad = (i == 0) ? (s_par[0] != -1) : (s_par[i] < 0 || s_par[i] >= i);
+            int dep = 0, j = i;
+            while (!bad) {
+                words[j >> 6] |= 1ull << (j & 63);
+                if (j == 0)
+                    break;
+                const int pj = s_par[j];
+                if (pj < 0 || pj >= j) {
+                    bad = true;
+                    break;
+                }
+                j = pj;
+                ++dep;
+            }
+            if (i >= node_lo && i < node_hi)
+#pragma unroll
+                for (int w = 0; w < kMaxNodes / 64; ++w)
+                    s_mask[i - node_lo][w] = words[w];
+            if (lead_mask) {
+                if (bad)
+                    raise_flag(a.flags, TAV_FLAG_BAD_PARENT);
+                if (a.mask_out)
+                    for (int w = 0; w < a.W; ++w)
+                        a.mask_out[((int64_t)b * a.N + i) * a.W + w] = words[w];
+                if (a.depth_out)
+                    a.depth_out[(int64_t)b * a.N + i] = dep;
+            }
+        }
+    }
     fill(0, read_ids(0));
     fill(1, read_ids(1));
 
@@ -1012,19 +1068,21 @@ extern "C" size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, in
     return p.ws_bytes;
 }
 
-extern "C" tav_status tree_attn_verify(const uint16_t *q, const uint16_t *k_tree,
-                                       const uint16_t *v_tree, const uint16_t *k_cache,
-                                       const uint16_t *v_cache, int32_t num_blocks,
-                                       const int32_t *block_table, int32_t max_blocks,
-                                       const int32_t *prefix_len, int32_t max_prefix_len,
-                                       const uint64_t *mask, int32_t B, int32_t N, int32_t Hq,
-                                       int32_t Hkv, int32_t D, int32_t block_size, float scale,
-                                       float *out, void *workspace, size_t ws_bytes,
-                                       uint32_t *dev_flags, void *stream)
+namespace tav {
+namespace {
+
+// The launch behind tree_attn_verify and tree_attn_verify_tree: exactly one
+// of mask and parent is non-NULL.
+tav_status attn_launch(const uint16_t *q, const uint16_t *k_tree, const uint16_t *v_tree,
+                       const uint16_t *k_cache, const uint16_t *v_cache, int32_t num_blocks,
+                       const int32_t *block_table, int32_t max_blocks, const int32_t *prefix_len,
+                       int32_t max_prefix_len, const uint64_t *mask, const int32_t *parent,
+                       uint64_t *mask_out, int32_t *depth_out, int32_t B, int32_t N, int32_t Hq,
+                       int32_t Hkv, int32_t D, int32_t block_size, float scale, float *out,
+                       void *workspace, size_t ws_bytes, uint32_t *dev_flags, void *stream)
 {
-    using namespace tav;
     if (!q || !k_tree || !v_tree || !k_cache || !v_cache || !block_table || !prefix_len ||
-        !mask || !out)
+        (!mask && !parent) || !out)
         return TAV_ERR_ARG;
     if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || num_blocks < 1 || max_blocks < 1 ||
         max_prefix_len < 0 || !(scale > 0.0f) || !(scale < INFINITY))
@@ -1033,8 +1091,9 @@ extern "C" tav_status tree_attn_verify(const uint16_t *q, const uint16_t *k_tree
         (int64_t)num_blocks * Hkv > (int64_t)UINT32_MAX)
         return TAV_ERR_UNSUPPORTED;
     if (!aligned(q, 16) || !aligned(k_tree, 16) || !aligned(v_tree, 16) || !aligned(k_cache, 16) ||
-        !aligned(v_cache, 16) || !aligned(mask, 8) || !aligned(out, 16) || !aligned(block_table, 4) ||
-        !aligned(prefix_len, 4))
+        !aligned(v_cache, 16) || (mask && !aligned(mask, 8)) || (parent && !aligned(parent, 4)) ||
+        (mask_out && !aligned(mask_out, 8)) || (depth_out && !aligned(depth_out, 4)) ||
+        !aligned(out, 16) || !aligned(block_table, 4) || !aligned(prefix_len, 4))
         return TAV_ERR_ARG;
     AttnPlan p;
     if (!attn_plan(B, N, Hq, Hkv, D, max_prefix_len, p))
@@ -1051,6 +1110,9 @@ extern "C" tav_status tree_attn_verify(const uint16_t *q, const uint16_t *k_tree
     a.block_table = block_table;
     a.prefix_len = prefix_len;
     a.mask = mask;
+    a.parent = parent;
+    a.mask_out = mask_out;
+    a.depth_out = depth_out;
     a.out = out;
     a.part_o = p.S > 1 ? static_cast<float *>(workspace) : nullptr;
     a.part_ml = p.S > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) +
@@ -1088,4 +1150,45 @@ extern "C" tav_status tree_attn_verify(const uint16_t *q, const uint16_t *k_tree
             return TAV_ERR_LAUNCH;
     }
     return TAV_OK;
+}
+
+} // namespace
+} // namespace tav
+
+extern "C" tav_status tree_attn_verify(const uint16_t *q, const uint16_t *k_tree,
+                                       const uint16_t *v_tree, const uint16_t *k_cache,
+                                       const uint16_t *v_cache, int32_t num_blocks,
+                                       const int32_t *block_table, int32_t max_blocks,
+                                       const int32_t *prefix_len, int32_t max_prefix_len,
+                                       const uint64_t *mask, int32_t B, int32_t N, int32_t Hq,
+                                       int32_t Hkv, int32_t D, int32_t block_size, float scale,
+                                       float *out, void *workspace, size_t ws_bytes,
+                                       uint32_t *dev_flags, void *stream)
+{
+    if (!mask)
+        return TAV_ERR_ARG;
+    return tav::attn_launch(q, k_tree, v_tree, k_cache, v_cache, num_blocks, block_table,
+                            max_blocks, prefix_len, max_prefix_len, mask, nullptr, nullptr,
+                            nullptr, B, N, Hq, Hkv, D, block_size, scale, out, workspace,
+                            ws_bytes, dev_flags, stream);
+}
+
+extern "C" tav_status tree_attn_verify_tree(const uint16_t *q, const uint16_t *k_tree,
+                                            const uint16_t *v_tree, const uint16_t *k_cache,
+                                            const uint16_t *v_cache, int32_t num_blocks,
+                                            const int32_t *block_table, int32_t max_blocks,
+                                            const int32_t *prefix_len, int32_t max_prefix_len,
+                                            const int32_t *parent, uint64_t *mask_out,
+                                            int32_t *depth_out, int32_t B, int32_t N,
+                                            int32_t Hq, int32_t Hkv, int32_t D,
+                                            int32_t block_size, float scale, float *out,
+                                            void *workspace, size_t ws_bytes,
+                                            uint32_t *dev_flags, void *stream)
+{
+    if (!parent)
+        return TAV_ERR_ARG;
+    return tav::attn_launch(q, k_tree, v_tree, k_cache, v_cache, num_blocks, block_table,
+                            max_blocks, prefix_len, max_prefix_len, nullptr, parent, mask_out,
+                            depth_out, B, N, Hq, Hkv, D, block_size, scale, out, workspace,
+                            ws_bytes, dev_flags, stream);
 }

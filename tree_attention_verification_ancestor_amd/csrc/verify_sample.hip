@@ -104,6 +104,7 @@ struct SvArgs {
     double *p_rows;   // [B][N][V]
     double *q_rows;   // [B][N][V]
     double *child_pq; // [B][N][2]
+    CommitArgs cm;
 };
 
 // ---------------------------------------------------------------------------
@@ -340,6 +341,65 @@ __device__ __forceinline__ double bits_f64(uint32_t hi, uint32_t lo)
 
 // ---------------------------------------------------------------------------
 
+// The group's share of sequence b's KV commit: path rows 0..m (s_path, in
+// LDS) to positions prefix_len[b] + t, work items (row, KV head, 16-byte
+// chunk) spread over the group's members; member 0 writes the slots and the
+// new length. Bad entries raise the flags kv_commit_path raises.
+__device__ void commit_path_rows(const CommitArgs &c, int b, int N, int m, const int32_t *s_path,
+                                 int rank, int wpg, int tid, uint32_t *flags)
+{
+    const int32_t L = c.prefix_len[b];
+    const int64_t rowbase = (int64_t)b * N;
+    if (rank == 0) {
+        for (int t = tid; t < N; t += kSvThreads) {
+            int32_t slot = -1;
+            if (t <= m) {
+                const int64_t pos = (int64_t)L + t;
+                const int64_t lb = pos / kBlock;
+                if (L >= 0 && lb < c.max_blocks) {
+                    const int32_t blk = c.block_table[(int64_t)b * c.max_blocks + lb];
+                    if (blk >= 0 && blk < c.num_blocks)
+                        slot = blk * kBlock + (int32_t)(pos % kBlock);
+                }
+            }
+            c.commit_slots[rowbase + t] = slot;
+        }
+        if (tid == 0)
+            c.new_prefix_len[b] = L + m + 1;
+    }
+    if (L < 0)
+        return;
+    const int cpr = c.D / 8;
+    const int64_t items = (int64_t)(m + 1) * c.Hkv * cpr;
+    for (int64_t it = (int64_t)rank * kSvThreads + tid; it < items; it += (int64_t)wpg * kSvThreads) {
+        const int ch = (int)(it % cpr);
+        const int h = (int)((it / cpr) % c.Hkv);
+        const int t = (int)(it / ((int64_t)cpr * c.Hkv));
+        const int32_t node = s_path[t];
+        const int64_t pos = (int64_t)L + t;
+        const int64_t lb = pos / kBlock;
+        if (lb >= c.max_blocks) {
+            raise_flag(flags, TAV_FLAG_CAPACITY);
+            continue;
+        }
+        const int32_t blk = c.block_table[(int64_t)b * c.max_blocks + lb];
+        if (blk < 0 || blk >= c.num_blocks) {
+            raise_flag(flags, TAV_FLAG_BAD_BLOCK);
+            continue;
+        }
+        const int sl = (int)(pos % kBlock);
+        const int64_t src = ((rowbase + node) * c.Hkv + h) * c.D + ch * 8;
+        const u32x4 kv = *reinterpret_cast<const u32x4 *>(c.k_tree + src);
+        *reinterpret_cast<u32x4 *>(c.k_cache + (((int64_t)blk * c.Hkv + h) * kBlock + sl) * c.D + ch * 8) = kv;
+        const u32x4 vv = *reinterpret_cast<const u32x4 *>(c.v_tree + src);
+        uint16_t *vdst = c.v_cache + (((int64_t)blk * c.Hkv + h) * c.D + ch * 8) * kBlock + sl;
+        const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            vdst[e * kBlock] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+    }
+}
+
 // kWor selects the sibling rule: false, every child of u is tested with q_u
 // (siblings drawn independently from q_u); true, a rejected child's token
 // leaves q_u, the rest renormalised, before the next sibling is tried
@@ -361,6 +421,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
 {
     static_assert(E % 4 == 0, "whole 16-byte runs");
     __shared__ int32_t s_par[kMaxNodes];
+    __shared__ int32_t s_path[kMaxNodes];   // accepted path, for the fused commit
     __shared__ int32_t s_first[kMaxNodes];
     __shared__ int32_t s_next[kMaxNodes];
     constexpr int kKidWords = kMaxNodes / 64;
@@ -466,8 +527,10 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
         // from these registers for nodes below 64)
         int my_par = -2, my_tok = 0;
         float my_tx = 0.f, my_dx = 0.f;
-        if (tid == 0)
+        if (tid == 0) {
             s_bad = 0;
+            s_path[0] = 0;
+        }
         if (tid < N) {
             my_par = a.parent[rowbase + tid];
             my_tok = a.token[rowbase + tid];
@@ -792,6 +855,8 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     a.out_tok[rowbase + nacc] = s_tok[c];
                     a.path[rowbase + nacc + 1] = c;
                 }
+                if (tid == 0)
+                    s_path[nacc + 1] = c;
                 ++nacc;
                 u = c;
             };
@@ -1132,6 +1197,11 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 a.n_acc[b] = nacc;
             }
         }
+        if (a.cm.k_tree) {
+            __syncthreads();   // s_path complete
+            commit_path_rows(a.cm, b, N, (failed || !alive) ? 0 : nacc, s_path, rank, wpg, tid,
+                             a.flags);
+        }
     }
 
     // ---- exit: the last workgroup out clears every mailbox word -------------
@@ -1214,6 +1284,7 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t v)
 __global__ __launch_bounds__(kSvThreads) void spec_verify_greedy_kernel(SvArgs a)
 {
     __shared__ int32_t s_par[kMaxNodes];
+    __shared__ int32_t s_path[kMaxNodes];   // accepted path, for the fused commit
     __shared__ int32_t s_first[kMaxNodes];
     __shared__ int32_t s_next[kMaxNodes];
     __shared__ int32_t s_tok[kMaxNodes];
@@ -1269,8 +1340,10 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_greedy_kernel(SvArgs a
         // ---- tree structure in LDS, validated (children as bitmasks) --------
         __syncthreads();
         int my_par = -2, my_tok = 0;
-        if (tid == 0)
+        if (tid == 0) {
             s_bad = 0;
+            s_path[0] = 0;
+        }
         if (tid < N) {
             my_par = a.parent[rowbase + tid];
             my_tok = a.token[rowbase + tid];
@@ -1416,6 +1489,8 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_greedy_kernel(SvArgs a
                 break;   // the target's choice is emitted; the walk stops
             if (lead)
                 a.path[rowbase + nacc + 1] = c;
+            if (tid == 0)
+                s_path[nacc + 1] = c;
             ++nacc;
             u = c;
         }
@@ -1438,6 +1513,11 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_greedy_kernel(SvArgs a
                 a.path[rowbase] = 0;
                 a.n_acc[b] = nacc;
             }
+        }
+        if (a.cm.k_tree) {
+            __syncthreads();   // s_path complete
+            commit_path_rows(a.cm, b, N, (failed || !alive) ? 0 : nacc, s_path, rank, wpg, tid,
+                             a.flags);
         }
     }
 
@@ -1592,7 +1672,7 @@ tav_status sv_launch(const float *target_logits, const float *draft_logits,
                      double temperature, uint64_t seed, uint64_t offset, int32_t *path,
                      int32_t *n_accepted, int32_t *out_tokens, void *workspace, size_t ws_bytes,
                      uint32_t *dev_flags, void *stream, bool wor, double *p_rows,
-                     double *q_rows, double *child_pq)
+                     double *q_rows, double *child_pq, const CommitArgs *commit)
 {
     using namespace tav;
     // temperature 0 selects greedy verification, which reads no draft row
@@ -1637,6 +1717,7 @@ tav_status sv_launch(const float *target_logits, const float *draft_logits,
     a.p_rows = p_rows;
     a.q_rows = q_rows;
     a.child_pq = child_pq;
+    a.cm = commit ? *commit : CommitArgs{};
     const bool probe = p_rows != nullptr;
     const dim3 grid(p.wpg * p.ngroups), block(kSvThreads);
     hipStream_t st = as_stream(stream);
@@ -1683,6 +1764,46 @@ extern "C" tav_status spec_verify_sample_wor(const float *target_logits,
     return tav::sv_launch(target_logits, draft_logits, parent, token, B, N, V, temperature, seed,
                      offset, path, n_accepted, out_tokens, workspace, ws_bytes, dev_flags, stream,
                      true, nullptr, nullptr, nullptr);
+}
+
+extern "C" tav_status spec_verify_sample_commit(
+    const float *target_logits, const float *draft_logits, const int32_t *parent,
+    const int32_t *token, int32_t B, int32_t N, int32_t V, double temperature, uint64_t seed,
+    uint64_t offset, int32_t without_replacement, int32_t *path, int32_t *n_accepted,
+    int32_t *out_tokens, const uint16_t *k_tree, const uint16_t *v_tree, int32_t num_blocks,
+    const int32_t *block_table, int32_t max_blocks, const int32_t *prefix_len, uint16_t *k_cache,
+    uint16_t *v_cache, int32_t Hkv, int32_t D, int32_t block_size, int32_t *commit_slots,
+    int32_t *new_prefix_len, void *workspace, size_t ws_bytes, uint32_t *dev_flags, void *stream)
+{
+    using namespace tav;
+    // kv_commit_path's checks, then the walk's (in sv_launch)
+    if (!k_tree || !v_tree || !block_table || !prefix_len || !k_cache || !v_cache ||
+        !commit_slots || !new_prefix_len)
+        return TAV_ERR_ARG;
+    if (B < 1 || N < 1 || Hkv < 1 || num_blocks < 1 || max_blocks < 1 ||
+        (without_replacement != 0 && without_replacement != 1))
+        return TAV_ERR_ARG;
+    if (block_size != kBlock || (D != 64 && D != 128) || N > kMaxNodes)
+        return TAV_ERR_UNSUPPORTED;
+    if (!aligned(k_tree, 16) || !aligned(v_tree, 16) || !aligned(k_cache, 16) ||
+        !aligned(v_cache, 2))
+        return TAV_ERR_ARG;
+    CommitArgs c;
+    c.k_tree = k_tree;
+    c.v_tree = v_tree;
+    c.block_table = block_table;
+    c.prefix_len = prefix_len;
+    c.k_cache = k_cache;
+    c.v_cache = v_cache;
+    c.commit_slots = commit_slots;
+    c.new_prefix_len = new_prefix_len;
+    c.num_blocks = num_blocks;
+    c.max_blocks = max_blocks;
+    c.Hkv = Hkv;
+    c.D = D;
+    return sv_launch(target_logits, draft_logits, parent, token, B, N, V, temperature, seed,
+                     offset, path, n_accepted, out_tokens, workspace, ws_bytes, dev_flags, stream,
+                     without_replacement != 0, nullptr, nullptr, nullptr, &c);
 }
 
 extern "C" tav_status spec_verify_sample_probe(
