@@ -754,6 +754,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="llama70b")
+    ap.add_argument("--batch", type=int, default=None, help="override the workload's batch")
+    ap.add_argument("--accept", type=float, default=None,
+                    help="mean acceptance of a sweep workload (0.5, 0.8 or 0.9)")
     ap.add_argument("--cache-copies", type=int, default=3)
     ap.add_argument("--offsets", type=int, default=1000,
                     help="Philox offsets of the acceptance statistics run")
@@ -782,7 +785,12 @@ def main():
 
     from synth import make_workload
     from tree_attention_verification_ancestor_amd.profiling import current_traffic
-    w = make_workload(args.config)
+    over = {}
+    if args.batch is not None:
+        over["B"] = args.batch
+    if args.accept is not None:
+        over["accept"] = args.accept
+    w = make_workload(args.config, **over)
     g = run_headline(args, w)
     copy_gbs = measured_copy_gbs()
 
@@ -792,7 +800,7 @@ def main():
     gbs = attn_bytes / t_attn / 1e9
     t_hbm = attn_bytes / (HBM_PEAK_GBS * 1e9)
     t_mfma = attn_flops / (MFMA_PEAK_TFLOPS * 1e12)
-    traffic = current_traffic(TRAFFIC_RECORD) if args.config == "llama70b" else None
+    traffic = current_traffic(TRAFFIC_RECORD) if args.config == "llama70b" and not over else None
     roof = roofline(attn_bytes, attn_flops, t_attn)
     roof["traffic"] = traffic
 

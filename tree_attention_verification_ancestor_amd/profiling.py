@@ -16,6 +16,12 @@ different source treats the figure as stale.
 The second form writes per-kernel counter means over several counter passes
 (each pass within the hardware's per-block counter limits) and the ratios
 derived from them.
+
+    python -m tree_attention_verification_ancestor_amd.profiling \
+        --trace DIR --title "..." --out profiles/FILE.md --command "..."
+
+The third form writes a kernel-trace summary: dispatches and durations per
+kernel and grid, with the SHA-256 of every library source.
 """
 
 from __future__ import annotations
@@ -68,7 +74,8 @@ def write_record(out: str, fetch: dict, write: dict, copy_fetch: dict, copy_writ
     cf = copy_fetch["copy"]["FETCH_SIZE"] * 1024.0 / copy_bytes
     cw = copy_write["copy"]["WRITE_SIZE"] * 1024.0 / copy_bytes
     lines = [
-        "# HBM traffic of one tree_attn_verify launch (main kernel + combine), from",
+        "# HBM traffic of one attention launch (main kernel + combine; tree_attn_verify",
+        "# and tree_attn_verify_tree run the same kernels), from",
         "# rocprofv3 counter passes; KiB per dispatch as the counters read them, then",
         "# bytes after dividing by the copy-kernel factors (counter bytes per true byte).",
         "# commands (from the repository root):",
@@ -117,6 +124,54 @@ def current_traffic(path: str):
 
 
 MOPS_FLOPS = 512   # FLOPs per unit of the SQ_INSTS_VALU_MFMA_MOPS_* counters
+
+
+def trace_rows(run_dir: str) -> list:
+    """[(kernel, grid, workgroup, [durations us])] from the kernel_trace CSV(s)
+    under a rocprofv3 output directory, in order of first dispatch."""
+    files = glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no kernel_trace.csv under {run_dir}")
+    rows = {}
+    for path in files:
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                name = name[5:] if name.startswith("void ") else name
+                name = name.replace("tav::(anonymous namespace)::", "").split("(")[0]
+                wg = int(r.get("Workgroup_Size", r.get("Workgroup_Size_X", 0)) or 0)
+                grid = int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0)
+                key = (name, grid // max(wg, 1), wg)
+                dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                rows.setdefault(key, []).append(dur)
+    return [(k[0], k[1], k[2], v) for k, v in rows.items()]
+
+
+def write_trace_summary(out: str, run_dir: str, title: str, command: str, note: str = "") -> list:
+    """Markdown table of a kernel trace: per library kernel and grid, the
+    dispatch count and mean / min / max duration; the other kernels (torch's
+    fills and copies) summed in one line."""
+    rows = trace_rows(run_dir)
+    ours = [r for r in rows if not r[0].startswith(("at::", "__amd", "void at::"))]
+    other = [d for r in rows if r not in ours for d in r[3]]
+    total = sum(sum(r[3]) for r in rows)
+    lines = [f"# {title}", ""] + ([note, ""] if note else []) + [
+        "Command (from the repository root; `cd /tmp && export TMPDIR=/tmp` first):", ""]
+    lines += [f"    {c}" for c in command.split(" ;; ")]
+    lines += ["", "| kernel | workgroups × threads | dispatches | mean µs | min µs | max µs | share of kernel time |",
+              "|---|---|---|---|---|---|---|"]
+    for name, wgs, wg, d in sorted(ours, key=lambda r: -sum(r[3])):
+        lines.append(f"| {name} | {wgs} × {wg} | {len(d)} | {sum(d) / len(d):.2f} | {min(d):.2f} | "
+                     f"{max(d):.2f} | {100 * sum(d) / total:.1f} % |")
+    if other:
+        lines.append(f"| (torch fills and copies, all) | | {len(other)} | {sum(other) / len(other):.2f} | "
+                     f"{min(other):.2f} | {max(other):.2f} | {100 * sum(other) / total:.1f} % |")
+    lines += ["", "Library sources at the time of the trace (SHA-256):", ""]
+    for path in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
+        lines.append(f"- {os.path.basename(path)} {source_sha256(path)}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return ours
 
 
 def derived_counters(c: dict, xcds: int, simds: int) -> dict:
@@ -176,10 +231,17 @@ def main():
     ap.add_argument("--copy-write")
     ap.add_argument("--copy-bytes", type=int)
     ap.add_argument("--counters", nargs="+", help="counter-pass directories: write a counter summary")
+    ap.add_argument("--trace", help="a kernel-trace directory: write a trace summary")
+    ap.add_argument("--title", default="Kernel trace")
+    ap.add_argument("--note", default="", help="a paragraph under the title (the workload)")
     ap.add_argument("--kernels", nargs="+", default=list(ATTN_KERNELS) + ["spec_verify_kernel"])
     ap.add_argument("--xcds", type=int, default=8)
     ap.add_argument("--simds", type=int, default=1024)
     a = ap.parse_args()
+    if a.trace:
+        for r in write_trace_summary(a.out, a.trace, a.title, a.command, a.note):
+            print(r[0], r[1], r[2], len(r[3]), round(sum(r[3]) / len(r[3]), 2))
+        return
     if a.counters:
         print(write_counter_summary(a.out, [counter_means(d) for d in a.counters], a.kernels, a.xcds,
                                     a.simds, a.command))
