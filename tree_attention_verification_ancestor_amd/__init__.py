@@ -19,7 +19,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtav.so")
+# TAV_LIBRARY names another build of the library (a sanitized host build, say)
+LIB_PATH = os.environ.get("TAV_LIBRARY") or os.path.join(_HERE, "libtav.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tav.h")
 
 OK = 0

@@ -63,5 +63,45 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# The host side of every source built with AddressSanitizer and
+# UndefinedBehaviorSanitizer (the device code as usual): the argument checks,
+# plans and host arithmetic behind the C ABI, checked by running the host
+# tests against this build (TAV_LIBRARY=<path>, the sanitizer runtime
+# preloaded). Not for GPU runs.
+SAN_DIR = os.path.join(HERE, "_build_san")
+SAN_LIB = os.path.join(SAN_DIR, "libtav_san.so")
+SAN_FLAGS = [f"--offload-arch={ARCH}", "-O1", "-g", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def sanitizer_runtime():
+    """The compiler's shared AddressSanitizer runtime, or None."""
+    found = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib",
+                                          "clang", "*", "lib", "linux",
+                                          "libclang_rt.asan-x86_64.so")))
+    found += sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return found[0] if found else None
+
+
+def build_sanitized() -> str:
+    os.makedirs(SAN_DIR, exist_ok=True)
+
+    def one(src):
+        obj = os.path.join(SAN_DIR, os.path.basename(src) + ".o")
+        res = subprocess.run([HIPCC, *SAN_FLAGS, "-c", src, "-o", obj], capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr[-4000:]}")
+        return obj
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(sources()))) as ex:
+        objs = list(ex.map(one, sources()))
+    subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host",
+                    "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libasan",
+                    "-o", SAN_LIB, *objs], check=True)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
