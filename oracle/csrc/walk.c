@@ -155,9 +155,22 @@ static void log_draw(draw_log *lg, double margin, double eps, int32_t n_acc)
  * (accepted nodes from the root, -1 padded), out_tokens[N] (emitted tokens,
  * -1 padded) and returns the accepted count through *n_acc_out.
  */
+/* Node i's two uniforms: from the caller's table utab[i][0..1] when it gives
+ * one, else from Philox. */
+static void node_uniforms_or_table(const double *utab, uint64_t seed, uint64_t offset, int64_t b,
+                                   int32_t i, double ur[2])
+{
+    if (utab) {
+        ur[0] = utab[2 * (size_t)i];
+        ur[1] = utab[2 * (size_t)i + 1];
+    } else {
+        oracle_node_uniforms(seed, offset, b, i, ur);
+    }
+}
+
 static int walk_one(const float *target, const float *draft, const int32_t *parent,
                     const int32_t *token, int32_t N, int32_t V, double T, int32_t rule,
-                    uint64_t seed, uint64_t offset, int64_t b, double eps,
+                    uint64_t seed, uint64_t offset, int64_t b, double eps, const double *utab,
                     int32_t *path, int32_t *out_tokens, int32_t *n_acc_out,
                     draw_log *lg, double *p, double *q, double *pr)
 {
@@ -197,7 +210,7 @@ static int walk_one(const float *target, const float *draft, const int32_t *pare
                     continue;
                 int32_t x = token[c];
                 double ur[2];
-                oracle_node_uniforms(seed, offset, b, c, ur);
+                node_uniforms_or_table(utab, seed, offset, b, c, ur);
                 double r = ur[0];
                 double margin = q[x] > 0.0 ? fabs(r - pr[x] / q[x]) : INFINITY;
                 log_draw(lg, margin, eps, n_acc);
@@ -237,7 +250,7 @@ static int walk_one(const float *target, const float *draft, const int32_t *pare
 
         /* Inverse-CDF draw from the final distribution at u. */
         double ur[2];
-        oracle_node_uniforms(seed, offset, b, u, ur);
+        node_uniforms_or_table(utab, seed, offset, b, u, ur);
         double total = 0.0;
         for (int32_t y = 0; y < V; ++y)
             total += final_dist[y];
@@ -269,17 +282,19 @@ static int walk_one(const float *target, const float *draft, const int32_t *pare
 
 /*
  * Batch entry.  target/draft: float32 [B][N][V]; parent/token: int32 [B][N];
- * rule: ORACLE_RULE_IID or ORACLE_RULE_WITHOUT_REPLACEMENT.
+ * rule: ORACLE_RULE_IID or ORACLE_RULE_WITHOUT_REPLACEMENT; uniforms: NULL
+ * (Philox from seed and offset) or the uniforms to use, double [B][N][2]
+ * (acceptance, resampling), so a test can integrate over them exactly.
  * Outputs: path, out_tokens int32 [B][N]; n_accepted int32 [B]; per sequence
  * draws/near/first_near int32 [B] and min_margin double [B].  Returns 0 or the
  * first error code met (then *bad_seq names the sequence).
  */
-int oracle_verify_walk(const float *target, const float *draft, const int32_t *parent,
-                       const int32_t *token, int64_t B, int32_t N, int32_t V, double T,
-                       uint64_t seed, uint64_t offset, double eps, int32_t rule,
-                       int32_t *path, int32_t *n_accepted, int32_t *out_tokens,
-                       int32_t *draws, int32_t *near, int32_t *first_near,
-                       double *min_margin, int64_t *bad_seq)
+int oracle_verify_walk_u(const float *target, const float *draft, const int32_t *parent,
+                         const int32_t *token, int64_t B, int32_t N, int32_t V, double T,
+                         uint64_t seed, uint64_t offset, double eps, int32_t rule,
+                         const double *uniforms, int32_t *path, int32_t *n_accepted,
+                         int32_t *out_tokens, int32_t *draws, int32_t *near,
+                         int32_t *first_near, double *min_margin, int64_t *bad_seq)
 {
     if (B < 0 || N < 1 || V < 1 || !(T > 0.0) ||
         (rule != ORACLE_RULE_IID && rule != ORACLE_RULE_WITHOUT_REPLACEMENT))
@@ -292,8 +307,9 @@ int oracle_verify_walk(const float *target, const float *draft, const int32_t *p
         draw_log lg = {0, 0, -1, INFINITY};
         size_t row0 = (size_t)b * (size_t)N;
         rc = walk_one(target + row0 * V, draft + row0 * V, parent + row0, token + row0,
-                      N, V, T, rule, seed, offset, b, eps, path + row0, out_tokens + row0,
-                      n_accepted + b, &lg, buf, buf + V, buf + 2 * (size_t)V);
+                      N, V, T, rule, seed, offset, b, eps, uniforms ? uniforms + row0 * 2 : NULL,
+                      path + row0, out_tokens + row0, n_accepted + b, &lg, buf, buf + V,
+                      buf + 2 * (size_t)V);
         if (rc) {
             *bad_seq = b;
             break;
@@ -305,6 +321,18 @@ int oracle_verify_walk(const float *target, const float *draft, const int32_t *p
     }
     free(buf);
     return rc;
+}
+
+int oracle_verify_walk(const float *target, const float *draft, const int32_t *parent,
+                       const int32_t *token, int64_t B, int32_t N, int32_t V, double T,
+                       uint64_t seed, uint64_t offset, double eps, int32_t rule,
+                       int32_t *path, int32_t *n_accepted, int32_t *out_tokens,
+                       int32_t *draws, int32_t *near, int32_t *first_near,
+                       double *min_margin, int64_t *bad_seq)
+{
+    return oracle_verify_walk_u(target, draft, parent, token, B, N, V, T, seed, offset, eps,
+                                rule, NULL, path, n_accepted, out_tokens, draws, near,
+                                first_near, min_margin, bad_seq);
 }
 
 /* u[b][i][0..1] for a whole batch (used by tests to cross-check the device). */

@@ -39,6 +39,11 @@ def _load():
                                            ctypes.c_int32, ctypes.c_double, ctypes.c_uint64,
                                            ctypes.c_uint64, ctypes.c_double, ctypes.c_int32,
                                            P, P, P, P, P, P, P, P]
+        lib.oracle_verify_walk_u.restype = ctypes.c_int
+        lib.oracle_verify_walk_u.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_double, ctypes.c_uint64,
+                                             ctypes.c_uint64, ctypes.c_double, ctypes.c_int32,
+                                             P, P, P, P, P, P, P, P, P]
         lib.oracle_uniform_table.restype = None
         lib.oracle_uniform_table.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
                                              ctypes.c_int32, P]
@@ -96,7 +101,7 @@ _ERRORS = {1: "bad parent array", 2: "token out of range", 3: "non-finite logits
 
 def verify_walk(target_logits, draft_logits, parent, token, temperature: float = 1.0,
                 seed: int = 0, offset: int = 0, near_eps: float = NEAR_EPS,
-                without_replacement: bool = False) -> WalkResult:
+                without_replacement: bool = False, uniforms=None) -> WalkResult:
     """Root-down rejection-sampling walk for a batch of trees.
 
     target_logits, draft_logits: float32 [B, N, V]; row u of the draft is the
@@ -110,6 +115,9 @@ def verify_walk(target_logits, draft_logits, parent, token, temperature: float =
     replacement. The rejection step itself (radar-34b blog section 2) is the
     same under both: the residual is the normalised positive part of the
     current p minus the current q.
+    uniforms: None (Philox from seed and offset, the default) or float64
+    [B, N, 2], node i's (acceptance, resampling) uniforms, for tests that
+    integrate over them.
     Raises ValueError on an invalid tree, token or logit row.
     """
     tl = np.ascontiguousarray(target_logits, dtype=np.float32)
@@ -127,11 +135,17 @@ def verify_walk(target_logits, draft_logits, parent, token, temperature: float =
     first_near = np.full(B, -1, np.int32)
     min_margin = np.full(B, np.inf)
     bad = np.zeros(1, np.int64)
-    rc = _load().oracle_verify_walk(_ptr(tl), _ptr(dl), _ptr(par), _ptr(tok), B, N, V,
-                                    float(temperature), int(seed), int(offset), float(near_eps),
-                                    1 if without_replacement else 0, _ptr(path), _ptr(n_acc),
-                                    _ptr(out_tok), _ptr(draws), _ptr(near), _ptr(first_near),
-                                    _ptr(min_margin), _ptr(bad))
+    utab = None
+    if uniforms is not None:
+        utab = np.ascontiguousarray(uniforms, dtype=np.float64)
+        if utab.shape != (B, N, 2):
+            raise ValueError("uniforms must be [B, N, 2]")
+    rc = _load().oracle_verify_walk_u(_ptr(tl), _ptr(dl), _ptr(par), _ptr(tok), B, N, V,
+                                      float(temperature), int(seed), int(offset),
+                                      float(near_eps), 1 if without_replacement else 0,
+                                      None if utab is None else _ptr(utab), _ptr(path),
+                                      _ptr(n_acc), _ptr(out_tok), _ptr(draws), _ptr(near),
+                                      _ptr(first_near), _ptr(min_margin), _ptr(bad))
     if rc:
         raise ValueError(f"oracle walk: {_ERRORS.get(rc, rc)} (sequence {int(bad[0])})")
     return WalkResult(path, n_acc, out_tok, draws, near, first_near, min_margin)
