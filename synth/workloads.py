@@ -380,6 +380,22 @@ def slice_batch(w: Workload, B: int) -> Workload:
         v_prefix=None if w.v_prefix is None else w.v_prefix[:B])
 
 
+def gather_nodes(w: Workload, parent, token, src) -> Workload:
+    """A workload whose trees are given (parent, token int [B, M]) and whose
+    node j of sequence b takes the rows of node src[b, j] of `w` (Q, the
+    tree's K/V, both logits). For trees built elsewhere over w's rows; the
+    prefix, caches and block table are w's."""
+    src = np.asarray(src, dtype=np.int64)
+    B, M = src.shape
+    take = lambda a: None if a is None else np.ascontiguousarray(
+        np.take_along_axis(a, src.reshape((B, M) + (1,) * (a.ndim - 2)), axis=1))
+    return dataclasses.replace(
+        w, N=M, parent=np.ascontiguousarray(parent, dtype=np.int32),
+        token=np.ascontiguousarray(token, dtype=np.int32), q=take(w.q), k_tree=take(w.k_tree),
+        v_tree=take(w.v_tree), target_logits=take(w.target_logits),
+        draft_logits=take(w.draft_logits), draft_noise=take(w.draft_noise), widths=None)
+
+
 def slice_nodes(w: Workload, n: int) -> Workload:
     """The first n nodes of every tree (a subtree: nodes are numbered
     topologically), with their rows; n = 1 leaves the root alone, a decode
