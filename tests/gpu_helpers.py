@@ -34,7 +34,7 @@ def run_mask(w, dev):
     return to_numpy(mask, np.uint64), to_numpy(depth), int(flags.item())
 
 
-def run_attention(w, dev, mask=None):
+def run_attention(w, dev, mask=None, max_prefix_len=None):
     d = upload(w, dev, logits=False)
     flags = tav.new_flags(dev)
     if mask is None:
@@ -42,8 +42,9 @@ def run_attention(w, dev, mask=None):
     else:
         mask = torch.from_numpy(mask.view(np.int64)).to(dev)
     out = tav.tree_attn_verify(d["q"], d["k_tree"], d["v_tree"], d["k_cache"], d["v_cache"],
-                               d["block_table"], d["prefix_len"], w.max_prefix_len, mask,
-                               scale=w.scale, dev_flags=flags)
+                               d["block_table"], d["prefix_len"],
+                               w.max_prefix_len if max_prefix_len is None else max_prefix_len,
+                               mask, scale=w.scale, dev_flags=flags)
     torch.cuda.synchronize()
     return to_numpy(out), int(flags.item())
 

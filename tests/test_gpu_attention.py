@@ -60,6 +60,35 @@ def test_attention_matches_oracle(cfg):
     say(f"  max abs err {err:.2e}")
 
 
+# Prefix lengths far apart within one batch under a split plan: splits of
+# one sequence range from many tiles to none (a sequence with fewer tiles
+# than splits leaves some empty), and the partials of long and short
+# sequences are merged side by side.
+SPLIT_CASES = [
+    # (B, N, Hq, Hkv, D, max prefix, prefix lengths)
+    (5, 9, 8, 2, 128, 3000, [0, 3000, 5, 64, 2000]),
+    (6, 16, 64, 8, 128, 3000, [3000, 0, 0, 0, 10, 3000]),
+    (4, 7, 8, 2, 64, 4096, [0, 0, 1, 0]),                 # more ranges than tiles
+    (3, 70, 8, 4, 128, 5000, [4999, 63, 1500]),           # two tree tiles
+    (8, 64, 64, 8, 128, 2000, [2000, 1, 640, 1999, 65, 700, 1300, 128]),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: f"B{c[0]}-N{c[1]}-D{c[4]}")
+def test_attention_splits_with_prefix_lengths_far_apart(case):
+    B, N, Hq, Hkv, D, Lmax, lens = case
+    plan = tav.attn_plan(B, N, Hq, Hkv, D, Lmax, torch.cuda.get_device_properties(0).multi_processor_count, 1)
+    say(f"attention, split ranges: {case} plan {plan}")
+    assert plan["splits"] >= 2
+    w = make_workload("tiny", with_logits=False, seed=B * 100 + N, B=B, N=N, Hq=Hq, Hkv=Hkv, D=D,
+                      L=(Lmax, Lmax), tree="random")
+    # shorter prefixes than the cache holds: the slots past them must not count
+    w.prefix_len[:] = lens
+    out, flags = run_attention(w, device(), max_prefix_len=Lmax)
+    err = _check(w, out, flags)
+    say(f"  max abs err {err:.2e}")
+
+
 def test_attention_70b_full_size_sampled():
     say("attention: llama70b full size, sampled heads")
     w = make_workload("llama70b", with_logits=False)

@@ -159,6 +159,33 @@ def test_attention_from_parents_is_the_mask_path(cfg):
     np.testing.assert_array_equal(to_numpy(depth2), to_numpy(depth))
 
 
+def test_attention_from_parents_with_prefix_lengths_far_apart():
+    """Prefix lengths far apart under a split plan (some splits hold no
+    tile): the built masks and depths are written once per sequence, and the
+    output is the mask path's."""
+    w = make_workload("tiny", with_logits=False, seed=12, B=6, N=70, Hq=16, Hkv=4, D=128,
+                      L=(3000, 3000), tree="random")
+    w.prefix_len[:] = [0, 3000, 7, 0, 1200, 64]
+    dev = device()
+    d = upload(w, dev, logits=False)
+    say("attention from parents: prefix lengths far apart, split plan")
+    f1, f2 = tav.new_flags(dev), tav.new_flags(dev)
+    mask, depth = tav.tree_mask_build(d["parent"], dev_flags=f1)
+    ref = tav.tree_attn_verify(d["q"], d["k_tree"], d["v_tree"], d["k_cache"], d["v_cache"],
+                               d["block_table"], d["prefix_len"], 3000, mask, scale=w.scale,
+                               dev_flags=f1)
+    mask2 = torch.zeros_like(mask)
+    depth2 = torch.full_like(depth, -7)
+    out = tav.tree_attn_verify_tree(d["q"], d["k_tree"], d["v_tree"], d["k_cache"], d["v_cache"],
+                                    d["block_table"], d["prefix_len"], 3000, d["parent"],
+                                    scale=w.scale, mask_out=mask2, depth_out=depth2, dev_flags=f2)
+    torch.cuda.synchronize()
+    assert int(f1.item()) == int(f2.item()) == 0
+    np.testing.assert_array_equal(to_numpy(out).view(np.uint32), to_numpy(ref).view(np.uint32))
+    np.testing.assert_array_equal(to_numpy(mask2, np.uint64), to_numpy(mask, np.uint64))
+    np.testing.assert_array_equal(to_numpy(depth2), to_numpy(depth))
+
+
 def test_attention_from_parents_flags_a_bad_tree_like_the_mask_builder():
     w = make_workload("tiny", with_logits=False, N=30, B=3, Hq=8, Hkv=2, D=128, L=(40, 90),
                       tree="random", seed=3)

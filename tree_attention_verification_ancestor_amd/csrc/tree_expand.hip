@@ -614,6 +614,9 @@ __device__ __forceinline__ int wave_excl_scan(int v, int lane, int &total)
 // One wave's share of a sampled expansion. Entries past the row were loaded
 // as NaN, so "live" (a finite or +inf logit: not NaN, not -inf) needs no
 // range test; only the NaN flag looks at the range.
+// kClean: every entry of the wave is in the row and none is NaN (as
+// load_share found), so the maxima need no range or NaN test.
+template <bool kClean>
 __device__ __forceinline__ void sample_wave(const ExArgs &a, const float (&v)[kExEpt], int64_t r,
                                             int32_t wbase, int lane, ExSPart *out, SpBatch *lds)
 {
@@ -633,11 +636,16 @@ __device__ __forceinline__ void sample_wave(const ExArgs &a, const float (&v)[kE
     float lmax = -INFINITY, amax = 0.0f;
 #pragma unroll
     for (int e = 0; e < kExEpt; ++e) {
-        nan_seen |= tok(e) < lim && __builtin_isnan(v[e]);
-        if (!__builtin_isnan(v[e])) {
+        if constexpr (kClean) {
             lmax = fmaxf(lmax, v[e]);
-            if (v[e] != -INFINITY)
-                amax = fmaxf(amax, fabsf(v[e]));
+            amax = fmaxf(amax, v[e] != -INFINITY ? fabsf(v[e]) : 0.0f);
+        } else {
+            nan_seen |= tok(e) < lim && __builtin_isnan(v[e]);
+            if (!__builtin_isnan(v[e])) {
+                lmax = fmaxf(lmax, v[e]);
+                if (v[e] != -INFINITY)
+                    amax = fmaxf(amax, fabsf(v[e]));
+            }
         }
     }
     const uint64_t mkey = wave_max_key(lmax == -INFINITY ? 0ull : (uint64_t)ordered_bits(lmax) << 32);
@@ -653,17 +661,19 @@ __device__ __forceinline__ void sample_wave(const ExArgs &a, const float (&v)[kE
     //   sc = e^y / (c - 1)  for u >= 1/2 (hi >= 2^31; c = 2^32 - hi), +inf if
     //                       c = 1 (u may reach 1);
     //   sc = -1             for u < 1/2;
-    //   sc = NaN            for a token that is not live (past the row, NaN
+    //   sc = -1/2           for a token that is not live (past the row, NaN
     //                       or -inf logit).
     // e^y / (1 - u) is about e^(key - ms) for u near 1, so each lane's
     // largest sc also picks its likeliest token (a choice only: any token's
-    // lower bound serves below).
+    // lower bound serves below). The pick is one integer maximum per token
+    // over sc's bits as a signed integer (ordered like sc for sc >= 0, then
+    // -1, then -1/2) with the low five bits replaced by 31 - e: the first
+    // entry among (nearly) equal values.
     const float ms = mul_rn(m, a.invT32);
     double s0 = 0.0, s1 = 0.0;
     float sc[kExEpt];
-    float pbest = -1.5f;
-    int ebest = -1;
-    int finite = 0;
+    int32_t pick = INT32_MIN;
+    int finite = 0;   // live tokens of the wave (wave-uniform)
 #pragma unroll
     for (int h = 0; h < kExEpt / 8; ++h) {
         const uint64_t sbase = rbase + kSmGamma * (uint64_t)(tok(8 * h) >> 1);
@@ -683,18 +693,16 @@ __device__ __forceinline__ void sample_wave(const ExArgs &a, const float (&v)[kE
                 const float x = v[e];
                 const float y = mul_rn(x, a.invT32) - ms;
                 const float ev = __builtin_amdgcn_exp2f(y * 0x1.715476p+0f);
-                const bool live = !__builtin_isnan(x) && x != -INFINITY;
+                const bool live = x > -INFINITY;   // not NaN, not -inf
                 r0 += live ? ev : 0.f;
                 r1 = live ? fmaf(y, ev, r1) : r1;
                 const uint32_t hi = hw[4 * q4 + j];
                 const uint32_t cm1 = ~hi;
                 const float ratio = cm1 == 0u ? INFINITY : ev * __builtin_amdgcn_rcpf((float)cm1);
-                const float t = live ? (hi >= 0x80000000u ? ratio : -1.0f) : NAN;
+                const float t = live ? (hi >= 0x80000000u ? ratio : -1.0f) : -0.5f;
                 sc[e] = t;
-                const bool better = t > pbest;
-                pbest = better ? t : pbest;
-                ebest = better ? e : ebest;
-                finite += live ? 1 : 0;
+                pick = max(pick, (int32_t)((__builtin_bit_cast(uint32_t, t) & ~31u) | (uint32_t)(31 - e)));
+                finite += __builtin_popcountll(__ballot(live));
             }
             if (m != -INFINITY) {
                 s0 += (double)r0;
@@ -708,7 +716,10 @@ __device__ __forceinline__ void sample_wave(const ExArgs &a, const float (&v)[kE
     auto entry_token = [&](int e) __attribute__((always_inline)) {
         return wbase + (e >> 3) * 512 + 8 * lane + (e & 7);
     };
-    // the lane's chosen token's lower bound
+    // the lane's chosen token's lower bound (none if all its tokens are dead)
+    static_assert(kExEpt <= 32, "entry index in five bits");
+    const int ebest =
+        ((uint32_t)pick >> 5) == (__builtin_bit_cast(uint32_t, -0.5f) >> 5) ? -1 : 31 - (pick & 31);
     float lbest = -INFINITY;
     if (ebest >= 0) {
         const int32_t t = entry_token(ebest);
@@ -716,7 +727,7 @@ __device__ __forceinline__ void sample_wave(const ExArgs &a, const float (&v)[kE
         key_bounds(row[t] * a.invT32, high_word(t), lo, u);
         lbest = lo;
     }
-    const int nfin = (int)wave_sum((double)finite);
+    const int nfin = finite;
     // tau: the k-th largest of the lanes' lower bounds (k rounds of a wave
     // maximum; one lane holding the maximum drops out each round), at most
     // the wave's k-th key
@@ -890,7 +901,10 @@ __global__ __launch_bounds__(kExThreads) __attribute__((amdgpu_waves_per_eu(4)))
     bool clean;
     load_share<8>(a, row, wbase, lane, v, clean);
     ExSPart *out = a.spart + (r * a.wpr + w) * kExWaves + wave;
-    sample_wave(a, v, r, wbase, lane, out, &s_batch[wave]);
+    if (clean)
+        sample_wave<true>(a, v, r, wbase, lane, out, &s_batch[wave]);
+    else
+        sample_wave<false>(a, v, r, wbase, lane, out, &s_batch[wave]);
 }
 
 __global__ __launch_bounds__(kMergeThreads) void expand_sample_merge_kernel(ExArgs a)
@@ -902,18 +916,48 @@ __global__ __launch_bounds__(kMergeThreads) void expand_sample_merge_kernel(ExAr
     const int lane = threadIdx.x;
     const int np = a.wpr * kExWaves;
     const ExSPart *p = a.spart + r * np;
+    // The first kMergeRegs contenders of partial `lane` (token, interval) are
+    // read once into registers; the selection rounds below scan them there.
+    // Contenders past those, and partials lane + 64, ..., are read where
+    // they are used.
+    constexpr int kMergeRegs = 8;
+    int32_t rtok[kMergeRegs];
+    float rlo[kMergeRegs], rup[kMergeRegs];
+    const int n0 = lane < np ? p[lane].n : 0;
+#pragma unroll
+    for (int i = 0; i < kMergeRegs; ++i) {
+        rtok[i] = 0;
+        rlo[i] = rup[i] = -INFINITY;
+        if (i < n0) {
+            const SpCand &c = p[lane].c[i];
+            rtok[i] = c.tok;
+            rlo[i] = c.lo;
+            rup[i] = c.up;
+        }
+    }
     double Ms, logS0, ratio;
     if (!row_stats(a, p, np, r, lane, Ms, logS0, ratio))
         return;
-    // the row's k-th largest lower bound: k rounds of "each lane offers its
-    // best not yet taken", over the contenders of partials lane, lane + 64, ...
+    // fn(w, i, lo, up, tok) for every contender i of partials lane, lane + 64, ...
     auto for_each = [&](auto &&fn) __attribute__((always_inline)) {
-        for (int w = lane; w < np; w += kMergeThreads) {
+#pragma unroll
+        for (int i = 0; i < kMergeRegs; ++i)
+            if (i < n0)
+                fn(lane, i, rlo[i], rup[i], rtok[i]);
+        for (int i = kMergeRegs; i < n0; ++i) {
+            const SpCand &c = p[lane].c[i];
+            fn(lane, i, c.lo, c.up, c.tok);
+        }
+        for (int w = lane + kMergeThreads; w < np; w += kMergeThreads) {
             const int n = p[w].n;
-            for (int i = 0; i < n; ++i)
-                fn(w, i, p[w].c[i]);
+            for (int i = 0; i < n; ++i) {
+                const SpCand &c = p[w].c[i];
+                fn(w, i, c.lo, c.up, c.tok);
+            }
         }
     };
+    // the row's k-th largest lower bound: k rounds of "each lane offers its
+    // best not yet taken"
     float tau = -INFINITY;
     {
         float prev_v = INFINITY;
@@ -923,11 +967,11 @@ __global__ __launch_bounds__(kMergeThreads) void expand_sample_merge_kernel(ExAr
             float bv = -INFINITY;
             int32_t bt = 0x7FFFFFFF;
             bool any = false;
-            for_each([&](int, int, const SpCand &c) __attribute__((always_inline)) {
-                const bool below = c.lo < prev_v || (c.lo == prev_v && c.tok > prev_t);
-                if (below && (!any || c.lo > bv || (c.lo == bv && c.tok < bt))) {
-                    bv = c.lo;
-                    bt = c.tok;
+            for_each([&](int, int, float lo, float, int32_t tok) __attribute__((always_inline)) {
+                const bool below = lo < prev_v || (lo == prev_v && tok > prev_t);
+                if (below && (!any || lo > bv || (lo == bv && tok < bt))) {
+                    bv = lo;
+                    bt = tok;
                     any = true;
                 }
             });
@@ -945,18 +989,19 @@ __global__ __launch_bounds__(kMergeThreads) void expand_sample_merge_kernel(ExAr
     }
     // survivors: up >= tau; exact keys 64 at a time, k best kept
     int cnt = 0;
-    for_each([&](int, int, const SpCand &c) __attribute__((always_inline)) {
-        cnt += c.up >= tau ? 1 : 0;
+    for_each([&](int, int, float, float up, int32_t) __attribute__((always_inline)) {
+        cnt += up >= tau ? 1 : 0;
     });
     int total;
     const int base = wave_excl_scan(cnt, lane, total);
     TopRun run;
     for (int b0 = 0; b0 < total; b0 += 64) {
         int idx = base;
-        for_each([&](int, int, const SpCand &c) __attribute__((always_inline)) {
-            if (c.up >= tau) {
+        for_each([&](int w, int i, float, float up, int32_t tok) __attribute__((always_inline)) {
+            if (up >= tau) {
                 if (idx >= b0 && idx < b0 + 64) {
-                    s_batch.tok[idx - b0] = c.tok;
+                    const SpCand &c = p[w].c[i];
+                    s_batch.tok[idx - b0] = tok;
                     s_batch.hi[idx - b0] = c.hi;
                     s_key[idx - b0] = c.key;
                     s_exact[idx - b0] = c.exact;
