@@ -31,8 +31,11 @@
 //                 keeps 8, which the output tolerance needs when attention
 //                 falls on a few keys. Weights carry a 2^7 bias so small ones
 //                 stay clear of fp16 subnormals; the bias cancels in O/l.
-// Staging. K tiles sit in a ring of three LDS slots and V tiles in a ring of
-// five, filled two tiles ahead. Prefix tiles move from HBM straight into LDS
+// Staging. V tiles sit in a ring of five LDS slots and K tiles in a ring of
+// one slot more than the tiles in flight: an 8-wave workgroup fills two tiles
+// ahead (three K slots; its lagging waves read V up to two tiles behind),
+// smaller D = 128 workgroups, which wait on memory more than on arithmetic,
+// three (four K slots; their V is read one tile behind). Prefix tiles move from HBM straight into LDS
 // (global_load_lds_dwordx4: 16 bytes per lane, no staging registers), with
 // the block table resolved once per split into head-block indices in LDS;
 // in an 8-wave workgroup the four waves with the shorter chain of work per
@@ -195,10 +198,16 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     constexpr int LPW = C::kChunks / 64 / kIssuers;   // loads per issuing wave per K (or V) tile
     static_assert(LPW * 64 * kIssuers == C::kChunks, "direct loads must split evenly");
     constexpr int KTB = C::kKTileBytes, VTB = C::kVTileBytes;
-    // K tiles live in a ring of 3 slots and V tiles in a ring of 5: tile t's
-    // K is read in step t only, its V in step t+1 or t+2 (P.V runs one or
-    // two tiles behind), and tile t+2 streams in during step t.
-    constexpr int kKSlots = 3, kVSlots = 5;
+    // Tiles in flight: tile t + kAhead streams in during step t. Tile t's K
+    // is read in step t only, its V in step t+1 (or t+2 for the lagging
+    // waves of an 8-wave workgroup), so K needs kAhead + 1 slots and V
+    // kAhead + 2 (+ 1 with lagging waves): 3 and 5 at depth 2 with lagging
+    // waves, 4 and 5 at depth 3 without. Depth 3 fits the LDS for D = 128
+    // below 8 waves (157 KB); for D = 64 it would cost the second workgroup
+    // per CU.
+    constexpr int kAhead = (D == 128 && NW < 8) ? 3 : 2;
+    constexpr int kKSlots = kAhead + 1, kVSlots = 5;
+    static_assert(kVSlots >= kAhead + (NW == 8 ? 3 : 2), "V ring too short for the pipeline");
     __shared__ __attribute__((aligned(16))) char s_k[kKSlots * KTB];
     __shared__ __attribute__((aligned(16))) char s_v[kVSlots * VTB];
     // this split's cache blocks as head-block indices (block * Hkv + kvh)
@@ -625,12 +634,13 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     };
 
     // ---- the tile pipeline ---------------------------------------------------
-    // Tile t's K sits in K slot t % 3 and its V in V slot t % 5; both are
-    // filled two steps ahead, by direct loads (prefix tiles) or through
-    // registers (tree tiles). Every step starts by waiting for tile t (tile
-    // t+1's loads may stay in flight) and passing the step's only barrier,
-    // after which every wave is done with tile t-1's K and tile t-3's V; it
-    // then fills tile t+2 into those slots. Per tile a wave has an MFMA phase
+    // Tile t's K sits in K slot t % kKSlots and its V in V slot t % 5; both
+    // are filled kAhead steps ahead, by direct loads (prefix tiles) or
+    // through registers (tree tiles). Every step starts by waiting for tile t
+    // (the later tiles' loads may stay in flight) and passing the step's only
+    // barrier, after which every wave is done with tile t-1's K and tile
+    // t-3's V (t-2's without lagging waves); it then fills tile t + kAhead
+    // into those slots. Per tile a wave has an MFMA phase
     //   Q(t): S = K Q^T (and tile t's V turned into fp16 meanwhile)
     // and a phase that is mostly vector ALU work:
     //   R(t): the softmax of tile t, with P.V of the tile before on the
@@ -694,8 +704,9 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
             }
         }
     }
-    fill(0, read_ids(0));
-    fill(1, read_ids(1));
+#pragma unroll
+    for (int t = 0; t < kAhead; ++t)
+        fill(t, read_ids(t));
 
     f16x8 pb_prev[2][2];
 #pragma unroll
@@ -775,14 +786,19 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
         };
         for (int it = 0; it < n_tiles; ++it) {
             TileIds ids{};
-            if (issuer && it + 2 < n_pre)
-                ids = read_ids(it + 2);
-            if (it + 1 < n_pre)
-                wait_vmem<(2 * LPW < 64 ? 2 * LPW : 63)>();   // beyond the counter's range: waits longer
+            if (issuer && it + kAhead < n_pre)
+                ids = read_ids(it + kAhead);
+            // tile it's loads done; those of the prefix tiles after it (up to
+            // kAhead - 1, issued later) may stay in flight. Counts beyond the
+            // counter's range wait longer.
+            if (kAhead == 3 && it + 2 < n_pre)
+                wait_vmem<(4 * LPW < 64 ? 4 * LPW : 63)>();
+            else if (it + 1 < n_pre)
+                wait_vmem<(2 * LPW < 64 ? 2 * LPW : 63)>();
             else
                 wait_vmem<0>();
             __syncthreads();
-            fill(it + 2, ids);
+            fill(it + kAhead, ids);
 
             const uint32_t kcur = k_lds + kslot * KTB;
             const uint32_t vcur = v_lds + vslot * VTB;
