@@ -17,6 +17,7 @@
  *   tree_select_topm    the budget's best M-node subtree of a candidate tree
  *   tree_widths_by_entropy  branching widths from the frontier's entropy ranks
  *   tree_topology_dp    the budget's best topology under acceptance by sibling rank
+ *   tav_sampler_plan    how the walk lays out a batch on the device
  *   tav_model_speedup, tav_best_chain_length, tav_fit_alpha
  *                       the speedup model, on the host, fed by measured times
  *
@@ -118,6 +119,22 @@ size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, 
  */
 tav_status tav_attn_plan(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
                          int32_t max_prefix_len, int32_t cus, int32_t per_cu, int32_t *plan);
+
+/*
+ * tav_sampler_plan — how spec_verify_sample and its variants lay out B
+ * sequences of vocabulary V on the current device (a host call that reads
+ * the device's CU count and the kernels' occupancy; nothing launched).
+ * greedy: 0 the sampling walks (temperature > 0), 1 greedy verification.
+ *   plan[0] vocabulary entries per thread (held in registers);
+ *   plan[1] workgroups per sequence (a group), ceil(V / (512 plan[0]));
+ *   plan[2] groups walking at once, each taking sequences g, g + plan[2],
+ *           ... in turn (ceil(B / plan[2]) of them);
+ *   plan[3] vocabulary entries per workgroup.
+ * TAV_ERR_ARG for a NULL plan, B < 1, V < 1 or greedy outside {0, 1};
+ * TAV_ERR_UNSUPPORTED for V > 2^21; TAV_ERR_LAUNCH if no plan fits the
+ * device (or there is none).
+ */
+tav_status tav_sampler_plan(int32_t B, int32_t V, int32_t greedy, int32_t *plan);
 
 /*
  * tree_attn_verify — one attention layer of the verification forward pass.

@@ -273,6 +273,16 @@ def test_attention_plan_rejects_bad_arguments():
     assert lib.tav_attn_plan(1, 5, 8, 2, 96, 64, 256, 1, ctypes.cast(plan, P)) == tav.ERR_UNSUPPORTED
 
 
+def test_sampler_plan_rejects_bad_arguments():
+    lib = tav.lib()
+    plan = (ctypes.c_int32 * 4)()
+    assert lib.tav_sampler_plan(8, 1000, 0, None) == tav.ERR_ARG
+    assert lib.tav_sampler_plan(0, 1000, 0, ctypes.cast(plan, P)) == tav.ERR_ARG
+    assert lib.tav_sampler_plan(8, 0, 0, ctypes.cast(plan, P)) == tav.ERR_ARG
+    assert lib.tav_sampler_plan(8, 1000, 2, ctypes.cast(plan, P)) == tav.ERR_ARG
+    assert lib.tav_sampler_plan(8, (1 << 21) + 1, 0, ctypes.cast(plan, P)) == tav.ERR_UNSUPPORTED
+
+
 def test_noalloc_sampler_rejects_bad_arguments_before_any_device_work():
     lib = tav.lib()
     fn = lib.spec_verify_sample_noalloc

@@ -63,6 +63,7 @@ _SIGNATURES = {
     "tree_mask_build": (_I32, [_P, _I32, _I32, _P, _P, _P, _P]),
     "tree_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "tav_attn_plan": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
+    "tav_sampler_plan": (_I32, [_I32, _I32, _I32, _P]),
     "tree_attn_verify": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _P, _I32, _I32,
                                 _I32, _I32, _I32, _I32, _F32, _P, _P, _SZ, _P, _P]),
     "tree_attn_verify_tree": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _P, _P, _P,
@@ -231,6 +232,18 @@ def attn_plan(B, N, Hq, Hkv, D, max_prefix_len, cus, per_cu):
                                                 ctypes.cast(plan, ctypes.c_void_p)))
     return {"waves": plan[0], "row_blocks": plan[1], "splits": plan[2],
             "max_split_blocks": plan[3], "capacity": plan[4]}
+
+
+def sampler_plan(B, V, greedy=False):
+    """spec_verify_sample's layout for B sequences of vocabulary V on the
+    current device (needs one): entries per thread, workgroups per sequence,
+    groups walking at once, vocabulary entries per workgroup, and the
+    sequences each group walks in turn."""
+    plan = (ctypes.c_int32 * 4)()
+    _check("tav_sampler_plan", lib().tav_sampler_plan(B, V, int(bool(greedy)),
+                                                      ctypes.cast(plan, ctypes.c_void_p)))
+    return {"entries_per_thread": plan[0], "workgroups_per_sequence": plan[1], "groups": plan[2],
+            "chunk": plan[3], "sequences_per_group": -(-B // plan[2])}
 
 
 def tree_attn_workspace_bytes(B, N, Hq, Hkv, D, max_prefix_len) -> int:

@@ -1657,6 +1657,23 @@ __global__ __launch_bounds__(kSvThreads) void target_probs_kernel(const float *l
 } // namespace
 } // namespace tav
 
+extern "C" tav_status tav_sampler_plan(int32_t B, int32_t V, int32_t greedy, int32_t *plan)
+{
+    using namespace tav;
+    if (!plan || B < 1 || V < 1 || greedy < 0 || greedy > 1)
+        return TAV_ERR_ARG;
+    if (V > kMaxVocab)
+        return TAV_ERR_UNSUPPORTED;
+    SvPlan p;
+    if (!sv_plan(B, V, greedy == 1, p))
+        return TAV_ERR_LAUNCH;
+    plan[0] = p.E;
+    plan[1] = p.wpg;
+    plan[2] = p.ngroups;
+    plan[3] = p.chunk;
+    return TAV_OK;
+}
+
 extern "C" size_t spec_verify_workspace_bytes(int32_t B, int32_t N, int32_t V)
 {
     using namespace tav;
