@@ -204,9 +204,7 @@ class StepRunner:
         self.mask = torch.empty((B, N, (N + 63) // 64), dtype=torch.int64, device=dev)
         self.depth = torch.empty((B, N), dtype=torch.int32, device=dev)
         self.out = torch.empty((B, N, w.Hq, w.D), dtype=torch.float32, device=dev)
-        self.ws_a = torch.empty(max(1, tav.tree_attn_workspace_bytes(B, N, w.Hq, w.Hkv, w.D,
-                                                                     w.max_prefix_len)),
-                                dtype=torch.uint8, device=dev)
+        self.ws_a = tav.new_attn_workspace(B, N, w.Hq, w.Hkv, w.D, w.max_prefix_len, dev)
         self.ws_s = tav.new_sampler_workspace(B, N, V, dev)
         self.path = torch.empty((B, N), dtype=torch.int32, device=dev)
         self.n_acc = torch.empty((B,), dtype=torch.int32, device=dev)
@@ -498,9 +496,7 @@ def run_headline(args, w):
         m_n = torch.empty((B, n, (n + 63) // 64), dtype=torch.int64, device=dev)
         dep_n = torch.empty((B, n), dtype=torch.int32, device=dev)
         o_n = torch.empty((B, n, w.Hq, w.D), dtype=torch.float32, device=dev)
-        wa = torch.empty(max(1, tav.tree_attn_workspace_bytes(B, n, w.Hq, w.Hkv, w.D,
-                                                              w.max_prefix_len)),
-                         dtype=torch.uint8, device=dev)
+        wa = tav.new_attn_workspace(B, n, w.Hq, w.Hkv, w.D, w.max_prefix_len, dev)
         ws = tav.new_sampler_workspace(B, n, V, dev)
         pa = torch.empty((B, n), dtype=torch.int32, device=dev)
         na = torch.empty((B,), dtype=torch.int32, device=dev)

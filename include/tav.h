@@ -158,8 +158,12 @@ tav_status tav_sampler_plan(int32_t B, int32_t V, int32_t greedy, int32_t *plan)
  *   prefix_len     int32 [B], each in [0, max_prefix_len]
  *   mask           uint64 [B][N][ceil(N/64)] from tree_mask_build
  *   out            fp32 [B][N][Hq][D]
- *   workspace      device buffer of >= tree_attn_workspace_bytes(...) bytes
- *                  (256-byte aligned; NULL allowed when that is 0)
+ *   workspace      device buffer of >= tree_attn_workspace_bytes(...) bytes,
+ *                  256-byte aligned, zero-filled before its first use; every
+ *                  call leaves it zero-filled again (NULL allowed when the size
+ *                  is 0). It holds the split partials and the counters the
+ *                  splits of a (sequence, KV head) merge by, so calls that
+ *                  share a workspace must not overlap.
  *   Supported: D in {64, 128}, block_size == 16, Hq % Hkv == 0,
  *   1 <= N <= 256, Hq/Hkv * N <= 4096, num_blocks * Hkv < 2^32 (cache
  *   block-heads are indexed with 32 bits). bf16 tensors 16-byte aligned.
@@ -168,7 +172,8 @@ tav_status tav_sampler_plan(int32_t B, int32_t V, int32_t greedy, int32_t *plan)
  *   |v| < 65520), accumulating in fp32.
  *   Flags: TAV_FLAG_BAD_BLOCK for a needed block outside [0, num_blocks);
  *   TAV_FLAG_CAPACITY for prefix_len beyond max_prefix_len or the table;
- *   TAV_FLAG_ATTN_RANGE for a non-finite output.
+ *   TAV_FLAG_ATTN_RANGE for a non-finite output; TAV_FLAG_SYNC_TIMEOUT if a
+ *   split's bounded wait for the other splits' partials ran out.
  */
 tav_status tree_attn_verify(const uint16_t *q, const uint16_t *k_tree, const uint16_t *v_tree,
                             const uint16_t *k_cache, const uint16_t *v_cache, int32_t num_blocks,

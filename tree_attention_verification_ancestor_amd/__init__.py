@@ -250,6 +250,12 @@ def tree_attn_workspace_bytes(B, N, Hq, Hkv, D, max_prefix_len) -> int:
     return int(lib().tree_attn_workspace_bytes(B, N, Hq, Hkv, D, max_prefix_len))
 
 
+def new_attn_workspace(B, N, Hq, Hkv, D, max_prefix_len, device=None) -> torch.Tensor:
+    """A zero-filled workspace for ``tree_attn_verify`` (each call leaves it zeroed)."""
+    n = tree_attn_workspace_bytes(B, N, Hq, Hkv, D, max_prefix_len)
+    return torch.zeros(max(1, n), dtype=torch.uint8, device=device or "cuda")
+
+
 def tree_attn_verify(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len,
                      max_prefix_len: int, mask, scale: Optional[float] = None,
                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
@@ -276,7 +282,7 @@ def tree_attn_verify(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_le
     _need(out, "out", (torch.float32,), (B, N, Hq, D), dev)
     need = tree_attn_workspace_bytes(B, N, Hq, Hkv, D, max_prefix_len)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = new_attn_workspace(B, N, Hq, Hkv, D, max_prefix_len, dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("tree_attn_verify", lib().tree_attn_verify(
         _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), nblk,
@@ -318,7 +324,7 @@ def tree_attn_verify_tree(q, k_tree, v_tree, k_cache, v_cache, block_table, pref
     _need(out, "out", (torch.float32,), (B, N, Hq, D), dev)
     need = tree_attn_workspace_bytes(B, N, Hq, Hkv, D, max_prefix_len)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = new_attn_workspace(B, N, Hq, Hkv, D, max_prefix_len, dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("tree_attn_verify_tree", lib().tree_attn_verify_tree(
         _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), nblk,

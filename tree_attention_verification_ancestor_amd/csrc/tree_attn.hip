@@ -52,9 +52,12 @@
 // P.V MFMAs of the tile before. In an 8-wave workgroup the two waves that
 // share a SIMD run these in opposite order, one a tile behind the other.
 // The key tiles of a (sequence, KV head) are its prefix tiles and then its
-// tree tiles (keys masked by the ancestor bitmask), split evenly; splits
-// write unnormalised partials (O, max, sum) that a combine kernel merges
-// with log-sum-exp.
+// tree tiles (keys masked by the ancestor bitmask), split evenly. The splits
+// of a (sequence, KV head, row block) count their arrival on a counter in
+// the workspace; every split but the last writes its unnormalised partial
+// (O, max, sum) with coherent stores and counts itself done, and the last
+// one waits for those, merges them with its own registers in split order
+// (log-sum-exp) and writes the result, then clears the counters.
 
 #include <algorithm>
 #include <type_traits>
@@ -65,6 +68,7 @@ namespace tav {
 namespace {
 
 constexpr int kKT = 64;              // keys per tile
+constexpr uint32_t kMergeSpinLimit = 1u << 20;   // polls before the merge's wait gives up
 constexpr int kMaxSplitBlocks = 2048; // block-table entries one split stages in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kWeightBias = 7.0f;  // log2 of the bias on the fp16 weights
@@ -93,6 +97,7 @@ struct AttnArgs {
     uint64_t *mask_out;      // optional copies of the built mask and depths
     int32_t *depth_out;
     float *out, *part_o, *part_ml;
+    uint32_t *counters;      // [B * Hkv * RB][2]: arrived, done (zero between calls)
     uint32_t *flags;
     int32_t num_blocks, max_blocks, max_prefix_len;
     int32_t B, N, Hq, Hkv, G, NG, W;
@@ -216,6 +221,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     // mask is passed in), and the parent row they are built from
     __shared__ uint64_t s_mask[C::kRows][kMaxNodes / 64];
     __shared__ int32_t s_par[kMaxNodes];
+    __shared__ int s_last;   // this split arrived last at its unit
 
     // ---- which (sequence, kv head, split, row block) ------------------------
     const int bid = blockIdx.x;
@@ -250,17 +256,16 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     const int u0 = (int)((int64_t)s * Ub / a.S), u1 = (int)((int64_t)(s + 1) * Ub / a.S);
     const int t_begin = std::min(u0, Tb);
     const int t_end = std::min(u1, Tb);
-    const int n_pre = t_end - t_begin;
-    const int tt0 = std::max(u0, Tb) - Tb;               // first tree tile of the split
-    const int n_tree = std::max(0, u1 - std::max(u0, Tb));
-    const int n_tiles = n_pre + n_tree;
     // The plan keeps every split's slice within its LDS copy; a launch that
-    // broke that rule would index past it, so it computes nothing instead.
-    if (n_pre * (kKT / kBlock) > kMaxSplitBlocks) {
-        if (tid == 0)
-            raise_flag(a.flags, TAV_FLAG_CAPACITY);
-        return;
-    }
+    // broke that rule would index past it, so that split computes nothing
+    // (and still takes its part in the merge).
+    const bool oversize = (t_end - t_begin) * (kKT / kBlock) > kMaxSplitBlocks;
+    if (oversize && tid == 0)
+        raise_flag(a.flags, TAV_FLAG_CAPACITY);
+    const int n_pre = oversize ? 0 : t_end - t_begin;
+    const int tt0 = std::max(u0, Tb) - Tb;               // first tree tile of the split
+    const int n_tree = oversize ? 0 : std::max(0, u1 - std::max(u0, Tb));
+    const int n_tiles = n_pre + n_tree;
     // The split's block-table slice, validated once. Entries past the prefix
     // (and bad ones, which also raise a flag) name block 0 of this head, a
     // valid address whose keys are masked and whose V entries are zeroed.
@@ -824,116 +829,152 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     else
         run(std::false_type{});
 
-    // ---- write the result or the split's partial ------------------------------
+    // ---- write the result, or leave a partial, or merge the splits -------------
     const float ltot = lsum + __shfl_xor(lsum, 32);
-    if (!row_ok)
-        return;
-    if (a.S == 1) {
-        const float inv = 1.0f / ltot;
+    const float mrow = (m_used == -INFINITY) ? -INFINITY : m_used * a.c;   // log2 units
+    auto write_out = [&](const f32x16 (&o)[C::kDTiles], float inv) __attribute__((always_inline)) {
         float *orow = a.out + (((int64_t)b * a.N + node) * a.Hq + head) * D;
         bool finite = true;
 #pragma unroll
         for (int m = 0; m < C::kDTiles; ++m)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const f32x4 v = {oacc[m][4 * i] * inv, oacc[m][4 * i + 1] * inv,
-                                 oacc[m][4 * i + 2] * inv, oacc[m][4 * i + 3] * inv};
+                const f32x4 v = {o[m][4 * i] * inv, o[m][4 * i + 1] * inv, o[m][4 * i + 2] * inv,
+                                 o[m][4 * i + 3] * inv};
                 finite &= __builtin_isfinite(v.x) && __builtin_isfinite(v.y) &&
                           __builtin_isfinite(v.z) && __builtin_isfinite(v.w);
                 *reinterpret_cast<f32x4 *>(orow + 32 * m + 8 * i + 4 * hh) = v;
             }
         if (!finite)
             raise_flag(a.flags, TAV_FLAG_ATTN_RANGE);
-    } else {
-        const int64_t P = ((int64_t)bh * a.RB + rb) * a.S + s;
-        const int rloc = wave * 32 + col;
-        float *po = a.part_o + (P * C::kRows + rloc) * D;
+    };
+    if (a.S == 1) {
+        if (row_ok)
+            write_out(oacc, 1.0f / ltot);
+        return;
+    }
+    const int64_t unit = (int64_t)bh * a.RB + rb;
+    uint32_t *arrived = a.counters + 2 * unit, *done = arrived + 1;
+    const int rloc = wave * 32 + col;
+    const int64_t P0 = unit * a.S;
+    if (tid == 0)
+        s_last = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 (uint32_t)(a.S - 1);
+    __syncthreads();
+    // A split leaves its partial with ordinary stores and one write-back of
+    // its XCD's L2 before it counts itself done; the merging split reads the
+    // partials with agent-scope atomic loads (64 bits each), which are
+    // coherent across XCDs at the memory side, so its L2 is not invalidated
+    // (that would also drop the K/V tiles the other row block of its XCD is
+    // reading).
+    auto pack = [](float x, float y) __attribute__((always_inline)) {
+        return ((uint64_t)__builtin_bit_cast(uint32_t, y) << 32) | __builtin_bit_cast(uint32_t, x);
+    };
+    auto unpack = [](uint64_t w) __attribute__((always_inline)) {
+        return f32x2{__builtin_bit_cast(float, (uint32_t)w), __builtin_bit_cast(float, (uint32_t)(w >> 32))};
+    };
+    if (!s_last) {
+        if (row_ok) {
+            float *po = a.part_o + ((P0 + s) * C::kRows + rloc) * D;
+#pragma unroll
+            for (int m = 0; m < C::kDTiles; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4 v = {oacc[m][4 * i], oacc[m][4 * i + 1], oacc[m][4 * i + 2],
+                                     oacc[m][4 * i + 3]};
+                    *reinterpret_cast<f32x4 *>(po + 32 * m + 8 * i + 4 * hh) = v;
+                }
+            if (hh == 0)
+                *reinterpret_cast<f32x2 *>(a.part_ml + ((P0 + s) * C::kRows + rloc) * 2) = f32x2{mrow, ltot};
+        }
+        wait_vmem<0>();   // this wave's stores are in the L2
+        __syncthreads();
+        if (tid == 0) {
+            // the L2's dirty lines, the partial among them, written back to
+            // memory before the count
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return;
+    }
+    // The last split: the others arrived before it and are past their tile
+    // loops, so they finish their partials without waiting on anything; the
+    // wait is bounded all the same.
+    if (tid == 0) {
+        uint32_t polls = 0;
+        while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+               (uint32_t)(a.S - 1)) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++polls > kMergeSpinLimit) {
+                raise_flag(a.flags, TAV_FLAG_SYNC_TIMEOUT);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    if (row_ok) {
+        // out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s in split order
+        // (a split that saw no key has m_s = -inf and is skipped)
+        auto ml_of = [&](int s2) __attribute__((always_inline)) {
+            return s2 == s ? f32x2{mrow, ltot}
+                           : unpack(__hip_atomic_load(reinterpret_cast<const uint64_t *>(a.part_ml) +
+                                                          (P0 + s2) * C::kRows + rloc,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        };
+        float M = -INFINITY;
+        for (int s2 = 0; s2 < a.S; ++s2)
+            M = fmaxf(M, ml_of(s2).x);
+        f32x16 acc[C::kDTiles];
 #pragma unroll
         for (int m = 0; m < C::kDTiles; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x4 v = {oacc[m][4 * i], oacc[m][4 * i + 1], oacc[m][4 * i + 2],
-                                 oacc[m][4 * i + 3]};
-                *reinterpret_cast<f32x4 *>(po + 32 * m + 8 * i + 4 * hh) = v;
+            for (int e = 0; e < 16; ++e)
+                acc[m][e] = 0.f;
+        float lw = 0.f;
+        for (int s2 = 0; s2 < a.S; ++s2) {
+            const f32x2 ml = ml_of(s2);
+            if (ml.x == -INFINITY)
+                continue;
+            const float w = __builtin_amdgcn_exp2f(ml.x - M);
+            lw += w * ml.y;
+            if (s2 == s) {
+#pragma unroll
+                for (int m = 0; m < C::kDTiles; ++m)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        acc[m][e] += w * oacc[m][e];
+            } else {
+                const uint64_t *po =
+                    reinterpret_cast<const uint64_t *>(a.part_o + ((P0 + s2) * C::kRows + rloc) * D);
+#pragma unroll
+                for (int m = 0; m < C::kDTiles; ++m)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int f = 32 * m + 8 * i + 4 * hh;
+                        const f32x2 v0 = unpack(__hip_atomic_load(po + f / 2, __ATOMIC_RELAXED,
+                                                                  __HIP_MEMORY_SCOPE_AGENT));
+                        const f32x2 v1 = unpack(__hip_atomic_load(po + f / 2 + 1, __ATOMIC_RELAXED,
+                                                                  __HIP_MEMORY_SCOPE_AGENT));
+                        acc[m][4 * i] += w * v0.x;
+                        acc[m][4 * i + 1] += w * v0.y;
+                        acc[m][4 * i + 2] += w * v1.x;
+                        acc[m][4 * i + 3] += w * v1.y;
+                    }
             }
-        if (hh == 0) {
-            float *pml = a.part_ml + (P * C::kRows + rloc) * 2;
-            pml[0] = (m_used == -INFINITY) ? -INFINITY : m_used * a.c;
-            pml[1] = ltot;
         }
+        write_out(acc, 1.0f / lw);
     }
-}
-
-// Merge split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-template <int D>
-__global__ __launch_bounds__(256) void tree_attn_combine_kernel(AttnArgs a, int rows_per_block)
-{
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int dq = (int)(idx % (D / 4));
-    const int64_t rr = idx / (D / 4);              // (bh, rb, rloc)
-    const int rloc = (int)(rr % rows_per_block);
-    const int64_t brb = rr / rows_per_block;
-    const int rb = (int)(brb % a.RB);
-    const int64_t bh = brb / a.RB;
-    if (bh >= (int64_t)a.B * a.Hkv)
-        return;
-    const int row = rb * rows_per_block + rloc;
-    if (row >= a.NG)
-        return;
-    const int b = (int)(bh / a.Hkv), kvh = (int)(bh % a.Hkv);
-    const int node = row / a.G, head = kvh * a.G + row % a.G;
-    const int64_t P0 = ((int64_t)bh * a.RB + rb) * a.S;
-    // The (max, sum) pair and O chunk of up to kCombineBatch splits are
-    // requested before any is used, so the loads overlap instead of waiting
-    // on one another (the common split counts fit one batch). A split that
-    // saw no key has max -inf, O = 0 and sum 0; it is skipped.
-    constexpr int kCombineBatch = 4;
-    f32x2 ml[kCombineBatch];
-    f32x4 v[kCombineBatch];
-    auto load_batch = [&](int s0) __attribute__((always_inline)) {
-#pragma unroll
-        for (int k = 0; k < kCombineBatch; ++k) {
-            if (s0 + k < a.S) {
-                const int64_t pr = (P0 + s0 + k) * rows_per_block + rloc;
-                ml[k] = *reinterpret_cast<const f32x2 *>(a.part_ml + pr * 2);
-                v[k] = *reinterpret_cast<const f32x4 *>(a.part_o + pr * D + dq * 4);
-            }
-        }
-    };
-    load_batch(0);
-    float M = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < kCombineBatch; ++k)
-        if (k < a.S)
-            M = fmaxf(M, ml[k].x);
-    for (int s = kCombineBatch; s < a.S; ++s)
-        M = fmaxf(M, a.part_ml[((P0 + s) * rows_per_block + rloc) * 2]);
-    float lsum = 0.f;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < a.S; s0 += kCombineBatch) {
-        if (s0 > 0)
-            load_batch(s0);
-#pragma unroll
-        for (int k = 0; k < kCombineBatch; ++k) {
-            if (s0 + k < a.S && ml[k].x != -INFINITY) {
-                const float w = __builtin_amdgcn_exp2f(ml[k].x - M);
-                lsum += w * ml[k].y;
-                o += w * v[k];
-            }
-        }
+    // leave the counters as the call found them
+    if (tid == 0) {
+        __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    const float inv = 1.0f / lsum;
-    const f32x4 r = o * inv;
-    if (!(__builtin_isfinite(r.x) && __builtin_isfinite(r.y) && __builtin_isfinite(r.z) &&
-          __builtin_isfinite(r.w)))
-        raise_flag(a.flags, TAV_FLAG_ATTN_RANGE);
-    *reinterpret_cast<f32x4 *>(a.out + (((int64_t)b * a.N + node) * a.Hq + head) * D + dq * 4) = r;
 }
 
 struct AttnPlan {
     int NW, rows, RB, S, KS;
     int64_t grid;
-    size_t part_o_bytes, part_ml_bytes, ws_bytes;
+    size_t counter_bytes, part_o_bytes, part_ml_bytes, ws_bytes;
 };
 
 size_t round_up(size_t v, size_t al) { return (v + al - 1) / al * al; }
@@ -988,12 +1029,15 @@ void attn_plan_for(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
     p.KS = (int)((int64_t)B * Hkv * p.S);
     p.grid = ceil_div(p.KS, 8) * 8 * p.RB;
     if (p.S > 1) {
+        p.counter_bytes = (size_t)B * Hkv * p.RB * 2 * sizeof(uint32_t);
         p.part_o_bytes = (size_t)B * Hkv * p.RB * p.S * p.rows * D * sizeof(float);
         p.part_ml_bytes = (size_t)B * Hkv * p.RB * p.S * p.rows * 2 * sizeof(float);
     } else {
-        p.part_o_bytes = p.part_ml_bytes = 0;
+        p.counter_bytes = p.part_o_bytes = p.part_ml_bytes = 0;
     }
-    p.ws_bytes = p.S > 1 ? round_up(p.part_o_bytes, 256) + round_up(p.part_ml_bytes, 256) : 0;
+    p.ws_bytes = p.S > 1 ? round_up(p.counter_bytes, 256) + round_up(p.part_o_bytes, 256) +
+                               round_up(p.part_ml_bytes, 256)
+                         : 0;
 }
 
 // The same for the current device.
@@ -1130,8 +1174,11 @@ tav_status attn_launch(const uint16_t *q, const uint16_t *k_tree, const uint16_t
     a.mask_out = mask_out;
     a.depth_out = depth_out;
     a.out = out;
-    a.part_o = p.S > 1 ? static_cast<float *>(workspace) : nullptr;
-    a.part_ml = p.S > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) +
+    // workspace: the merge counters, then the partials O and (max, sum)
+    char *ws = static_cast<char *>(workspace);
+    a.counters = p.S > 1 ? reinterpret_cast<uint32_t *>(ws) : nullptr;
+    a.part_o = p.S > 1 ? reinterpret_cast<float *>(ws + round_up(p.counter_bytes, 256)) : nullptr;
+    a.part_ml = p.S > 1 ? reinterpret_cast<float *>(ws + round_up(p.counter_bytes, 256) +
                                                      round_up(p.part_o_bytes, 256))
                         : nullptr;
     a.flags = dev_flags;
@@ -1155,16 +1202,6 @@ tav_status attn_launch(const uint16_t *q, const uint16_t *k_tree, const uint16_t
     hipError_t err = D == 128 ? launch_main_d<128>(p, a, s) : launch_main_d<64>(p, a, s);
     if (err != hipSuccess)
         return TAV_ERR_LAUNCH;
-    if (p.S > 1) {
-        const int64_t threads = (int64_t)B * Hkv * p.RB * p.rows * (D / 4);
-        const unsigned blocks = (unsigned)ceil_div(threads, 256);
-        if (D == 128)
-            hipLaunchKernelGGL(tree_attn_combine_kernel<128>, dim3(blocks), dim3(256), 0, s, a, p.rows);
-        else
-            hipLaunchKernelGGL(tree_attn_combine_kernel<64>, dim3(blocks), dim3(256), 0, s, a, p.rows);
-        if (hipGetLastError() != hipSuccess)
-            return TAV_ERR_LAUNCH;
-    }
     return TAV_OK;
 }
 
