@@ -52,12 +52,14 @@
 // P.V MFMAs of the tile before. In an 8-wave workgroup the two waves that
 // share a SIMD run these in opposite order, one a tile behind the other.
 // The key tiles of a (sequence, KV head) are its prefix tiles and then its
-// tree tiles (keys masked by the ancestor bitmask), split evenly. The splits
-// of a (sequence, KV head, row block) count their arrival on a counter in
-// the workspace; every split but the last writes its unnormalised partial
-// (O, max, sum) with coherent stores and counts itself done, and the last
-// one waits for those, merges them with its own registers in split order
-// (log-sum-exp) and writes the result, then clears the counters.
+// tree tiles (keys masked by the ancestor bitmask), split evenly. Two splits
+// of a (sequence, KV head, row block) merge inside the launch: each counts
+// its arrival on a counter in the workspace, the first writes its
+// unnormalised partial (O, max, sum) and counts itself done, and the second
+// waits for that, merges it with its own registers in split order
+// (log-sum-exp), writes the result and clears the counters. With more
+// splits every split writes its partial and a combine kernel merges them
+// (the last split's serial reads of many partials cost more than a kernel).
 
 #include <algorithm>
 #include <type_traits>
@@ -98,6 +100,7 @@ struct AttnArgs {
     int32_t *depth_out;
     float *out, *part_o, *part_ml;
     uint32_t *counters;      // [B * Hkv * RB][2]: arrived, done (zero between calls)
+    int32_t merge;           // S == 2: the splits merge inside the launch
     uint32_t *flags;
     int32_t num_blocks, max_blocks, max_prefix_len;
     int32_t B, N, Hq, Hkv, G, NG, W;
@@ -854,9 +857,29 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
         return;
     }
     const int64_t unit = (int64_t)bh * a.RB + rb;
-    uint32_t *arrived = a.counters + 2 * unit, *done = arrived + 1;
     const int rloc = wave * 32 + col;
     const int64_t P0 = unit * a.S;
+    auto write_partial = [&]() __attribute__((always_inline)) {
+        float *po = a.part_o + ((P0 + s) * C::kRows + rloc) * D;
+#pragma unroll
+        for (int m = 0; m < C::kDTiles; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 v = {oacc[m][4 * i], oacc[m][4 * i + 1], oacc[m][4 * i + 2],
+                                 oacc[m][4 * i + 3]};
+                *reinterpret_cast<f32x4 *>(po + 32 * m + 8 * i + 4 * hh) = v;
+            }
+        if (hh == 0)
+            *reinterpret_cast<f32x2 *>(a.part_ml + ((P0 + s) * C::kRows + rloc) * 2) = f32x2{mrow, ltot};
+    };
+    if (!a.merge) {
+        // more than two splits: every split leaves its partial for the
+        // combine kernel
+        if (row_ok)
+            write_partial();
+        return;
+    }
+    uint32_t *arrived = a.counters + 2 * unit, *done = arrived + 1;
     if (tid == 0)
         s_last = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                  (uint32_t)(a.S - 1);
@@ -874,19 +897,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
         return f32x2{__builtin_bit_cast(float, (uint32_t)w), __builtin_bit_cast(float, (uint32_t)(w >> 32))};
     };
     if (!s_last) {
-        if (row_ok) {
-            float *po = a.part_o + ((P0 + s) * C::kRows + rloc) * D;
-#pragma unroll
-            for (int m = 0; m < C::kDTiles; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const f32x4 v = {oacc[m][4 * i], oacc[m][4 * i + 1], oacc[m][4 * i + 2],
-                                     oacc[m][4 * i + 3]};
-                    *reinterpret_cast<f32x4 *>(po + 32 * m + 8 * i + 4 * hh) = v;
-                }
-            if (hh == 0)
-                *reinterpret_cast<f32x2 *>(a.part_ml + ((P0 + s) * C::kRows + rloc) * 2) = f32x2{mrow, ltot};
-        }
+        if (row_ok)
+            write_partial();
         wait_vmem<0>();   // this wave's stores are in the L2
         __syncthreads();
         if (tid == 0) {
@@ -971,8 +983,75 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     }
 }
 
+// Merge split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+template <int D>
+__global__ __launch_bounds__(256) void tree_attn_combine_kernel(AttnArgs a, int rows_per_block)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int dq = (int)(idx % (D / 4));
+    const int64_t rr = idx / (D / 4);              // (bh, rb, rloc)
+    const int rloc = (int)(rr % rows_per_block);
+    const int64_t brb = rr / rows_per_block;
+    const int rb = (int)(brb % a.RB);
+    const int64_t bh = brb / a.RB;
+    if (bh >= (int64_t)a.B * a.Hkv)
+        return;
+    const int row = rb * rows_per_block + rloc;
+    if (row >= a.NG)
+        return;
+    const int b = (int)(bh / a.Hkv), kvh = (int)(bh % a.Hkv);
+    const int node = row / a.G, head = kvh * a.G + row % a.G;
+    const int64_t P0 = ((int64_t)bh * a.RB + rb) * a.S;
+    // The (max, sum) pair and O chunk of up to kCombineBatch splits are
+    // requested before any is used, so the loads overlap instead of waiting
+    // on one another (the common split counts fit one batch). A split that
+    // saw no key has max -inf, O = 0 and sum 0; it is skipped.
+    constexpr int kCombineBatch = 4;
+    f32x2 ml[kCombineBatch];
+    f32x4 v[kCombineBatch];
+    auto load_batch = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < kCombineBatch; ++k) {
+            if (s0 + k < a.S) {
+                const int64_t pr = (P0 + s0 + k) * rows_per_block + rloc;
+                ml[k] = *reinterpret_cast<const f32x2 *>(a.part_ml + pr * 2);
+                v[k] = *reinterpret_cast<const f32x4 *>(a.part_o + pr * D + dq * 4);
+            }
+        }
+    };
+    load_batch(0);
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k)
+        if (k < a.S)
+            M = fmaxf(M, ml[k].x);
+    for (int s = kCombineBatch; s < a.S; ++s)
+        M = fmaxf(M, a.part_ml[((P0 + s) * rows_per_block + rloc) * 2]);
+    float lsum = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < a.S; s0 += kCombineBatch) {
+        if (s0 > 0)
+            load_batch(s0);
+#pragma unroll
+        for (int k = 0; k < kCombineBatch; ++k) {
+            if (s0 + k < a.S && ml[k].x != -INFINITY) {
+                const float w = __builtin_amdgcn_exp2f(ml[k].x - M);
+                lsum += w * ml[k].y;
+                o += w * v[k];
+            }
+        }
+    }
+    const float inv = 1.0f / lsum;
+    const f32x4 r = o * inv;
+    if (!(__builtin_isfinite(r.x) && __builtin_isfinite(r.y) && __builtin_isfinite(r.z) &&
+          __builtin_isfinite(r.w)))
+        raise_flag(a.flags, TAV_FLAG_ATTN_RANGE);
+    *reinterpret_cast<f32x4 *>(a.out + (((int64_t)b * a.N + node) * a.Hq + head) * D + dq * 4) = r;
+}
+
 struct AttnPlan {
     int NW, rows, RB, S, KS;
+    bool merge;   // the two splits merge inside the launch
     int64_t grid;
     size_t counter_bytes, part_o_bytes, part_ml_bytes, ws_bytes;
 };
@@ -1028,8 +1107,9 @@ void attn_plan_for(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
     p.S = (int)S;
     p.KS = (int)((int64_t)B * Hkv * p.S);
     p.grid = ceil_div(p.KS, 8) * 8 * p.RB;
+    p.merge = p.S == 2;
     if (p.S > 1) {
-        p.counter_bytes = (size_t)B * Hkv * p.RB * 2 * sizeof(uint32_t);
+        p.counter_bytes = p.merge ? (size_t)B * Hkv * p.RB * 2 * sizeof(uint32_t) : 0;
         p.part_o_bytes = (size_t)B * Hkv * p.RB * p.S * p.rows * D * sizeof(float);
         p.part_ml_bytes = (size_t)B * Hkv * p.RB * p.S * p.rows * 2 * sizeof(float);
     } else {
@@ -1176,7 +1256,8 @@ tav_status attn_launch(const uint16_t *q, const uint16_t *k_tree, const uint16_t
     a.out = out;
     // workspace: the merge counters, then the partials O and (max, sum)
     char *ws = static_cast<char *>(workspace);
-    a.counters = p.S > 1 ? reinterpret_cast<uint32_t *>(ws) : nullptr;
+    a.counters = p.merge ? reinterpret_cast<uint32_t *>(ws) : nullptr;
+    a.merge = p.merge ? 1 : 0;
     a.part_o = p.S > 1 ? reinterpret_cast<float *>(ws + round_up(p.counter_bytes, 256)) : nullptr;
     a.part_ml = p.S > 1 ? reinterpret_cast<float *>(ws + round_up(p.counter_bytes, 256) +
                                                      round_up(p.part_o_bytes, 256))
@@ -1202,6 +1283,16 @@ tav_status attn_launch(const uint16_t *q, const uint16_t *k_tree, const uint16_t
     hipError_t err = D == 128 ? launch_main_d<128>(p, a, s) : launch_main_d<64>(p, a, s);
     if (err != hipSuccess)
         return TAV_ERR_LAUNCH;
+    if (p.S > 1 && !p.merge) {
+        const int64_t threads = (int64_t)B * Hkv * p.RB * p.rows * (D / 4);
+        const unsigned blocks = (unsigned)ceil_div(threads, 256);
+        if (D == 128)
+            hipLaunchKernelGGL(tree_attn_combine_kernel<128>, dim3(blocks), dim3(256), 0, s, a, p.rows);
+        else
+            hipLaunchKernelGGL(tree_attn_combine_kernel<64>, dim3(blocks), dim3(256), 0, s, a, p.rows);
+        if (hipGetLastError() != hipSuccess)
+            return TAV_ERR_LAUNCH;
+    }
     return TAV_OK;
 }
 

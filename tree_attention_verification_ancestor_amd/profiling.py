@@ -35,7 +35,7 @@ from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ATTN_SOURCE = os.path.join(PKG, "csrc", "tree_attn.hip")
-ATTN_KERNELS = ("tree_attn_kernel",)
+ATTN_KERNELS = ("tree_attn_kernel", "tree_attn_combine_kernel")
 
 
 def source_sha256(path: str = ATTN_SOURCE) -> str:
@@ -74,8 +74,9 @@ def write_record(out: str, fetch: dict, write: dict, copy_fetch: dict, copy_writ
     cf = copy_fetch["copy"]["FETCH_SIZE"] * 1024.0 / copy_bytes
     cw = copy_write["copy"]["WRITE_SIZE"] * 1024.0 / copy_bytes
     lines = [
-        "# HBM traffic of one attention launch (one kernel, the splits merged inside",
-        "# it; tree_attn_verify and tree_attn_verify_tree run the same kernel), from",
+        "# HBM traffic of one attention launch (the main kernel, and the combine kernel",
+        "# when more than two splits are merged; tree_attn_verify and",
+        "# tree_attn_verify_tree run the same kernels), from",
         "# rocprofv3 counter passes; KiB per dispatch as the counters read them, then",
         "# bytes after dividing by the copy-kernel factors (counter bytes per true byte).",
         "# commands (from the repository root):",
