@@ -90,6 +90,8 @@ def write_record(out: str, fetch: dict, write: dict, copy_fetch: dict, copy_writ
     ]
     total = 0.0
     for k in ATTN_KERNELS:
+        if k not in fetch and k not in write:
+            continue   # not launched in this workload (the combine kernel at two splits)
         fk = fetch.get(k, {}).get("FETCH_SIZE", 0.0)
         wk = write.get(k, {}).get("WRITE_SIZE", 0.0)
         b = fk * 1024.0 / cf + wk * 1024.0 / cw
