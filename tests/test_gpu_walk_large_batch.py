@@ -4,7 +4,9 @@ several sequences in turn, so these cases cover a group's second and later
 sequences (state reset between them, the mailbox generations carried on,
 the fused commit after each) under both sibling rules, with one and several
 workgroups per sequence, many rejections, ragged chunks, determinism and the
-input flags."""
+input flags. Most take the layout with 28 entries per thread (16 held in
+registers, 12 in LDS, fetched ahead by direct loads; rows that are not
+16-byte aligned go through registers instead); one takes 16 per thread."""
 
 import dataclasses
 
@@ -20,32 +22,38 @@ from synth.device import to_numpy, upload
 pytestmark = pytest.mark.gpu
 
 
-def _in_turn(B, V, least=3):
+def _in_turn(B, V, least=3, entries=None):
     plan = tav.sampler_plan(B, V)
     say(f"  plan {plan}")
     assert plan["sequences_per_group"] >= least
+    if entries is not None:
+        assert plan["entries_per_thread"] == entries
     return plan
 
 
 # Vocabularies above 8192 entries take several workgroups per sequence, so
-# these batches leave three or more sequences per group.
+# these batches leave two or more sequences per group. (Layouts as a
+# 256-CU device plans them.)
 CASES = [
-    # (workload, overrides, workgroups per sequence at least)
-    ("tiny", dict(N=8, B=300, V=20000, tree="random", seed=31), 1),             # ragged last step
-    ("tiny", dict(N=8, B=128, V=50000, tree="random", seed=32), 2),             # two members
-    ("tiny", dict(N=8, B=128, V=50000, tree="chain", seed=33, sigma_d=3.0), 2),   # many rejections
-    ("tiny", dict(N=16, B=200, V=20001, tree="random", temperature=0.6, seed=34), 1),   # odd V: no 16-byte loads
-    ("sweep_tree16", dict(B=64, accept=0.5), 4),
-    ("sweep_chain6", dict(B=128, accept=0.9), 2),
+    # (workload, overrides, workgroups per sequence at least, sequences per
+    #  group at least, entries per thread)
+    ("tiny", dict(N=8, B=300, V=28000, tree="random", seed=31), 2, 3, 28),   # ragged last step and chunk
+    ("tiny", dict(N=8, B=200, V=43000, tree="random", seed=32), 3, 3, 28),
+    ("tiny", dict(N=8, B=200, V=43000, tree="chain", seed=33, sigma_d=3.0), 3, 3, 28),   # many rejections
+    ("tiny", dict(N=16, B=300, V=28001, tree="random", temperature=0.6, seed=34), 2, 3, 28),   # odd V: no 16-byte loads
+    ("tiny", dict(N=8, B=70, V=50000, tree="random", seed=36), 7, 2, 16),   # registers only
+    ("sweep_tree16", dict(B=64, accept=0.5), 16, 4, 16),
+    ("sweep_chain6", dict(B=128, accept=0.9), 9, 5, 28),
 ]
 
 
 @pytest.mark.parametrize("wor", [False, True], ids=["iid", "wor"])
-@pytest.mark.parametrize("name,over,members", CASES, ids=lambda c: str(c)[:40] if isinstance(c, dict) else None)
-def test_walk_in_turn_matches_oracle(name, over, members, wor):
+@pytest.mark.parametrize("name,over,members,least,entries", CASES,
+                         ids=lambda c: str(c)[:40] if isinstance(c, dict) else None)
+def test_walk_in_turn_matches_oracle(name, over, members, least, entries, wor):
     say(f"walk, sequences in turn: {name} {over} wor={wor}")
     w = make_workload(name, **over)
-    plan = _in_turn(w.B, w.V)
+    plan = _in_turn(w.B, w.V, least, entries)
     assert plan["workgroups_per_sequence"] >= members
     path, n_acc, toks, flags = run_walk(w, device(), wor=wor)
     assert flags == 0
@@ -56,16 +64,18 @@ def test_walk_in_turn_matches_oracle(name, over, members, wor):
 
 
 def test_walk_in_turn_many_offsets():
-    """300 sequences of 6-node random trees over a 9000-token vocabulary
-    (two workgroups per sequence, a ragged second chunk), five Philox
-    offsets."""
+    """300 sequences of 6-node random trees over a 28004-token vocabulary
+    (two workgroups per sequence, chunks of 14004 and 14000 entries that end
+    inside the last run of their LDS entries), five Philox offsets. (The
+    oracle's draws here stay 3e-8 or more from their boundaries.)"""
     rng = np.random.default_rng(41)
-    B, N, V = 300, 6, 9000
+    B, N, V = 300, 6, 28004
     parent = np.stack([random_parent(rng, N) for _ in range(B)])
     tl = (rng.standard_normal((B, N, V)) * 2.0).astype(np.float32)
     dl = (tl + rng.standard_normal((B, N, V)) * 1.0).astype(np.float32)
     token = rng.integers(0, V, (B, N)).astype(np.int32)
-    _in_turn(B, V, least=2)
+    plan = _in_turn(B, V, least=2, entries=28)
+    assert plan["workgroups_per_sequence"] == 2
     total_excused = total_draws = 0
     for offset in range(5):
         say(f"walk in turn: offset {offset}")
@@ -80,7 +90,7 @@ def test_walk_in_turn_many_offsets():
 
 def test_walk_in_turn_is_deterministic():
     w = make_workload("tiny", N=8, B=128, V=50000, tree="random", seed=35)
-    _in_turn(w.B, w.V)
+    _in_turn(w.B, w.V, least=2)
     say("walk in turn: determinism")
     a = run_walk(w, device())
     b = run_walk(w, device())
@@ -89,18 +99,23 @@ def test_walk_in_turn_is_deterministic():
 
 
 def test_walk_in_turn_flags_bad_inputs():
-    """A NaN logit, a row of -inf, a bad parent and a bad token, in
-    sequences a group walks after others, each raise their flag and fail
-    only their own sequence."""
+    """A NaN logit (in a register entry, and in an LDS entry), a row of
+    -inf, a bad parent and a bad token, in sequences a group walks after
+    others, each raise their flag and fail only their own sequence."""
     rng = np.random.default_rng(42)
-    B, N, V = 300, 4, 9000
+    B, N, V = 520, 4, 9000
     tl = (rng.standard_normal((B, N, V))).astype(np.float32)
     parent = np.tile(np.array([-1, 0, 1, 0], np.int32), (B, 1))
     token = rng.integers(0, V, (B, N)).astype(np.int32)
-    _in_turn(B, V, least=2)
+    _in_turn(B, V, least=2, entries=28)
     say("walk in turn: bad-input flags")
     t1 = tl.copy()
     t1[1, 0, 4097] = np.nan
+    path, n_acc, toks, flags = walk_arrays(t1, tl, parent, token, 1.0, 0, 0, device())
+    assert flags == tav.FLAG_NONFINITE_LOGITS
+    assert n_acc[1] == 0 and (path[1, 1:] == -1).all() and (toks[1] == -1).all()
+    t1 = tl.copy()
+    t1[1, 0, 8500] = np.nan   # past the 8192 register entries of the one workgroup
     path, n_acc, toks, flags = walk_arrays(t1, tl, parent, token, 1.0, 0, 0, device())
     assert flags == tav.FLAG_NONFINITE_LOGITS
     assert n_acc[1] == 0 and (path[1, 1:] == -1).all() and (toks[1] == -1).all()

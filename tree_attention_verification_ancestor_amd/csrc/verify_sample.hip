@@ -13,8 +13,9 @@
 //
 // Layout of the work. A "group" of wpg workgroups owns one sequence at a
 // time; workgroup r of the group owns vocabulary entries
-// [r*chunk, (r+1)*chunk) and keeps them in registers (8 per thread, 512
-// threads), so every pass over a row after the first is register-resident.
+// [r*chunk, (r+1)*chunk) and keeps them in registers (8 or 16 per thread,
+// 512 threads; at large batches 16 in registers and 12 more in LDS), so
+// every pass over a row after the first stays on the CU.
 // The walk is serial; for each visited node u the group
 //   1. takes its chunk of target row u (and draft row u if u has children)
 //      and the logits of u's children's tokens; each wave reduces a local
@@ -416,10 +417,56 @@ __device__ void commit_path_rows(const CommitArgs &c, int b, int N, int m, const
 // residual after k rejections at the current node) are formed from them
 // when needed, by the same operations in the same order every time, so they
 // are the same bits whenever they are formed.
+// One direct HBM -> LDS load: lane l's 16 bytes at base + voff land at LDS
+// byte address lds_addr + 16 l (base and lds_addr the same for the whole
+// wave). Inline assembly, so the compiler neither makes later LDS accesses
+// wait for it nor reasons about what it writes: a reader of the destination
+// first waits with sv_wait_loads.
+__device__ __forceinline__ void sv_load_lds16(const void *base, uint32_t voff, uint32_t lds_addr)
+{
+    // (both are the same in every lane; the compiler cannot always tell)
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint64_t bs = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint32_t ls = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(bs), "s"(ls)
+                 : "memory", "m0");
+}
+
+// Every vector memory load of the wave complete (its LDS writes included).
+__device__ __forceinline__ void sv_wait_loads()
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// This wave's LDS accesses complete.
+__device__ __forceinline__ void sv_wait_lds()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// LDS byte address of a __shared__ object.
+template <typename T>
+__device__ __forceinline__ uint32_t sv_lds_addr(T *p)
+{
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)p;
+}
+
 template <int E, bool kWor, bool kProbe = false>
 __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
 {
     static_assert(E % 4 == 0, "whole 16-byte runs");
+    // Entries e < ER are held in registers. With E > 16 the other EL per
+    // thread keep their exponentials in LDS, in two buffers: one holds the
+    // current node's, the other takes the logits of the node fetched ahead
+    // (direct HBM -> LDS loads) while the current node is decided. Thread
+    // tid only ever touches its own slots, so no barrier guards them.
+    constexpr int ER = E > 16 ? 16 : E;
+    constexpr int EL = E - ER;
+    constexpr int kLRuns = EL / 4;
+    __shared__ f32x4 s_lx[EL ? 2 : 1][EL ? kLRuns : 1][2][EL ? kSvThreads : 1];
     __shared__ int32_t s_par[kMaxNodes];
     __shared__ int32_t s_path[kMaxNodes];   // accepted path, for the fused commit
     __shared__ int32_t s_first[kMaxNodes];
@@ -468,9 +515,9 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
     auto tok = [&](int e) __attribute__((always_inline)) {
         return base32 + (e >> 2) * kRun + 4 * tid + (e & 3);
     };
-    auto load_row = [&](const float *row, float (&v)[E]) __attribute__((always_inline)) {
+    auto load_row = [&](const float *row, float (&v)[ER]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int h = 0; h < E / 4; ++h) {
+        for (int h = 0; h < ER / 4; ++h) {
             const int64_t i0 = base + (int64_t)h * kRun + 4 * tid;
             if (a.vec4 && i0 + 3 < lim) {
                 const f32x4 x = *reinterpret_cast<const f32x4 *>(row + i0);
@@ -485,10 +532,49 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             }
         }
     };
-    auto no_row = [&](float (&v)[E]) __attribute__((always_inline)) {
+    auto no_row = [&](float (&v)[ER]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int e = 0; e < E; ++e)
+        for (int e = 0; e < ER; ++e)
             v[e] = -INFINITY;
+    };
+    // The LDS entries' runs of a node's target row (and draft row, if the
+    // node has children) into buffer `buf`: run hl holds tokens
+    // base + (ER / 4 + hl) * kRun + 4 tid + j. Tokens past the chunk are
+    // masked where they are read; a run past the row reads the row's first
+    // run instead, so no address leaves the row. Rows that are not 16-byte
+    // aligned go through registers.
+    const int wave_s = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int32_t lim32 = (int32_t)lim;
+    // how many of run h's four tokens lie in the chunk (32-bit arithmetic)
+    auto run_valid = [&](int h) __attribute__((always_inline)) {
+        return std::min(4, std::max(0, lim32 - (base32 + h * kRun + 4 * tid)));
+    };
+    auto stage_rows = [&](int buf, const float *trow, const float *drow,
+                          bool kids) __attribute__((always_inline)) {
+        if constexpr (EL > 0) {
+            sv_wait_lds();   // this thread's earlier accesses of the buffer are done
+#pragma unroll
+            for (int hl = 0; hl < kLRuns; ++hl) {
+                const int32_t i0 = base32 + (ER / 4 + hl) * kRun + 4 * tid;
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    if (r == 1 && !kids)
+                        break;
+                    const float *row = r ? drow : trow;
+                    if (a.vec4) {
+                        const uint32_t voff = i0 < a.V ? (uint32_t)(4 * i0) : 0u;
+                        sv_load_lds16(row, voff, sv_lds_addr(&s_lx[buf][hl][r][64 * wave_s]));
+                    } else {
+                        const int nv = run_valid(ER / 4 + hl);
+                        f32x4 x;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            x[j] = j < nv ? row[i0 + j] : -INFINITY;
+                        s_lx[buf][hl][r][tid] = x;
+                    }
+                }
+            }
+        }
     };
     uint64_t *box = a.box + (size_t)g * 2 * wpg * kSlotWords;
     const double invT = 1.0 / a.T;
@@ -499,6 +585,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
     constexpr float kLog2eF = 0x1.715476p+0f;
     uint32_t gen = 0;
     bool alive = true;
+    int lb = 0;   // the LDS buffer of the current node's entries
 
     for (int b = g; b < a.B && alive; b += a.ngroups) {
         const int64_t rowbase = (int64_t)b * N;
@@ -507,12 +594,16 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
         // registers (while the current node is decided) when they fit: with
         // up to 16 entries per thread. Larger E reads each node's rows when
         // it reaches it.
-        constexpr bool kPrefetch = E <= 16;
-        constexpr int PE = kPrefetch ? E : 4;
+        constexpr bool kPrefetch = ER <= 16;
+        constexpr int PE = kPrefetch ? ER : 4;
         int pf_node = kPrefetch ? 0 : -1;
         float pf_t[PE], pf_d[PE];
         float pf_tx = 0.f, pf_dx = 0.f;   // logits of child `tid` of pf_node, if any
         if constexpr (kPrefetch) {
+            if constexpr (EL > 0) {
+                sv_wait_loads();   // no fetch-ahead of the last sequence still lands there
+                stage_rows(lb ^ 1, a.tl + rowbase * a.V, a.dl + rowbase * a.V, true);
+            }
             load_row(a.tl + rowbase * a.V, pf_t);
             load_row(a.dl + rowbase * a.V, pf_d);
         }
@@ -597,10 +688,10 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             const bool has_kids = s_first[u] >= 0;
 
             // ---- 1. local (max, sum exp) of target and draft rows ------------
-            float tf[E], df[E];
+            float tf[ER], df[ER];
             if (pf_node == u) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
+                for (int e = 0; e < ER; ++e) {
                     tf[e] = pf_t[e % PE];
                     df[e] = has_kids ? pf_d[e % PE] : -INFINITY;
                 }
@@ -608,7 +699,10 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     s_tx[tid] = my_tx = pf_tx;
                     s_dx[tid] = my_dx = pf_dx;
                 }
+                lb ^= 1;   // its LDS entries were fetched into the other buffer
             } else {
+                // (the current buffer's entries belong to a node left behind)
+                stage_rows(lb, trow, drow, has_kids);
                 load_row(trow, tf);
                 if (has_kids)
                     load_row(drow, df);
@@ -620,6 +714,8 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     s_dx[tid] = my_dx = drow[x];
                 }
             }
+            if constexpr (EL > 0)
+                sv_wait_loads();
             // Maxima of the raw fp32 logits (exact; x -> x/T is monotone) and
             // sums of exp relative to them, per wave (DPP, no barrier). A NaN
             // logit makes the sum NaN.
@@ -627,10 +723,27 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             bool nan_seen = false;
             float mt_l = -INFINITY, mq_l = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
+            for (int e = 0; e < ER; ++e) {
                 nan_seen |= __builtin_isnan(tf[e]) || __builtin_isnan(df[e]);
                 mt_l = fmaxf(mt_l, tf[e]);
                 mq_l = fmaxf(mq_l, df[e]);
+            }
+            // an LDS entry's logit, -inf past the chunk (and for the draft
+            // row of a node without children)
+            auto lds_logit = [&](const f32x4 &x, int hl, int j, bool row_ok)
+                __attribute__((always_inline)) {
+                return row_ok && j < run_valid(ER / 4 + hl) ? x[j] : -INFINITY;
+            };
+#pragma unroll
+            for (int hl = 0; hl < kLRuns; ++hl) {
+                const f32x4 xt = s_lx[lb][hl][0][tid], xd = s_lx[lb][hl][1][tid];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float t = lds_logit(xt, hl, j, true), d = lds_logit(xd, hl, j, has_kids);
+                    nan_seen |= __builtin_isnan(t) || __builtin_isnan(d);
+                    mt_l = fmaxf(mt_l, t);
+                    mq_l = fmaxf(mq_l, d);
+                }
             }
             const float wmt = wave_max_f32(mt_l), wmq = wave_max_f32(mq_l);
             const float wts32 = wmt * invT32, wqs32 = wmq * invT32;
@@ -639,10 +752,10 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             // v_exp_f32 (under one ulp); summed in fp64. An entry's relative
             // error is about |y| 2^-24, so the entries that carry the sum
             // (|y| of a few units) are within a few 1e-7.
-            float ep[E], eq[E];
+            float ep[ER], eq[ER];
             double zt = 0.0, zq = 0.0;
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
+            for (int e = 0; e < ER; ++e) {
                 ep[e] = (wmt == -INFINITY) ? 0.0f
                                            : __builtin_amdgcn_exp2f(fmaf(tf[e], invT32, -wts32) * kLog2eF);
                 eq[e] = (wmq == -INFINITY) ? 0.0f
@@ -650,6 +763,44 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 zt += (double)ep[e];
                 zq += (double)eq[e];
             }
+            // the LDS entries' exponentials replace their logits in place
+#pragma unroll
+            for (int hl = 0; hl < kLRuns; ++hl) {
+                const f32x4 xt = s_lx[lb][hl][0][tid], xd = s_lx[lb][hl][1][tid];
+                f32x4 et, eqv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float t = lds_logit(xt, hl, j, true), d = lds_logit(xd, hl, j, has_kids);
+                    et[j] = (wmt == -INFINITY) ? 0.0f
+                                               : __builtin_amdgcn_exp2f(fmaf(t, invT32, -wts32) * kLog2eF);
+                    eqv[j] = (wmq == -INFINITY) ? 0.0f
+                                                : __builtin_amdgcn_exp2f(fmaf(d, invT32, -wqs32) * kLog2eF);
+                    zt += (double)et[j];
+                    zq += (double)eqv[j];
+                }
+                s_lx[lb][hl][0][tid] = et;
+                s_lx[lb][hl][1][tid] = eqv;
+            }
+            // Entry e's exponentials. With E > 8 a register entry passes
+            // through an empty asm statement at each use so that the compiler
+            // forms the fp64 products there instead of hoisting all of them
+            // out of the loops (which would hold them in 4E registers); with
+            // E = 8 they fit, and are hoisted.
+            auto fresh = [](float v) __attribute__((always_inline)) {
+                if constexpr (E > 8)
+                    asm volatile("" : "+v"(v));
+                return v;
+            };
+            auto ep_of = [&](int e) __attribute__((always_inline)) -> float {
+                if (e < ER)
+                    return fresh(ep[e < ER ? e : 0]);
+                return s_lx[lb][(e - ER) >> 2][0][tid][e & 3];
+            };
+            auto eq_of = [&](int e) __attribute__((always_inline)) -> float {
+                if (e < ER)
+                    return fresh(eq[e < ER ? e : 0]);
+                return s_lx[lb][(e - ER) >> 2][1][tid][e & 3];
+            };
             if (nan_seen)
                 zt = NAN;
             zt = wave_sum(zt);
@@ -669,6 +820,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 const float *d1 = a.dl + (rowbase + c1) * a.V;
                 const bool c1_kids = s_first[c1] >= 0;
                 if constexpr (kPrefetch) {
+                    stage_rows(lb ^ 1, t1, d1, c1_kids);
                     load_row(t1, pf_t);
                     if (c1_kids)
                         load_row(d1, pf_d);
@@ -808,9 +960,9 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 for (int e = 0; e < E; ++e) {
                     const int64_t t = tok(e);
                     if (t < lim) {
-                        prow[t] = (double)ep[e] * sp;
+                        prow[t] = (double)ep_of(e) * sp;
                         if (has_kids)
-                            qrow[t] = (double)eq[e] * sq;
+                            qrow[t] = (double)eq_of(e) * sq;
                     }
                 }
                 if (rank == 0 && tid < N && s_par[tid] == u) {
@@ -887,25 +1039,15 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 }
                 return at;
             };
-            // With E > 8 the fp32 exponentials pass through an empty asm
-            // statement at each use so that the compiler forms the fp64
-            // products there instead of hoisting all E of them out of the
-            // loops (which would hold them in 4E registers); with E = 8 they
-            // fit, and are hoisted.
-            auto fresh = [](float v) __attribute__((always_inline)) {
-                if constexpr (E > 8)
-                    asm volatile("" : "+v"(v));
-                return v;
-            };
             auto q_at = [&](int e, int j, int gone) __attribute__((always_inline)) {
-                const double q = (double)fresh(eq[e]) * sq;
+                const double q = (double)eq_of(e) * sq;
                 if constexpr (kWor)
                     return j > gone ? 0.0 : q * (j == 0 ? 1.0 : s_qs[j]);
                 else
                     return q;
             };
             auto residual = [&](int e, int k_now) __attribute__((always_inline)) {
-                double r = (double)fresh(ep[e]) * sp;
+                double r = (double)ep_of(e) * sp;
                 const int gone = removed_at(e, k_now);
                 for (int j = 0; j < k_now; ++j) {
                     const double zj = s_zhist[j];
@@ -962,7 +1104,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                         const double d = residual(e, k) - q_at(e, k, gone);
                         rsum += d > 0.0 ? d : 0.0;
                         if constexpr (kWor)
-                            qrem += (e == ex || gone < k) ? 0.0 : (double)fresh(eq[e]) * sq;
+                            qrem += (e == ex || gone < k) ? 0.0 : (double)eq_of(e) * sq;
                     }
                 }
                 rsum = wave_sum(rsum);
@@ -1206,7 +1348,10 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
 
     // ---- exit: the last workgroup out clears every mailbox word -------------
     // Each workgroup counts itself out only after its last poll, so the last
-    // one knows no slot is still being read.
+    // one knows no slot is still being read. (No fetch-ahead into LDS may
+    // outlive the workgroup.)
+    if constexpr (EL > 0)
+        sv_wait_loads();
     __syncthreads();
     if (tid == 0) {
         const uint32_t out =
@@ -1561,10 +1706,16 @@ int64_t sampling_resident(int cus)
 
 // A group of ceil(V / 512 E) workgroups per sequence, as many groups as the
 // device holds at once (at most B), each walking its sequences in turn. The
-// sampling walk takes the E of 8 and 16 that needs the fewer sequences per
-// group, the smaller among equals (more members share each row); greedy
-// verification keeps E = 8. (E = 32 would need more registers than a
-// resident 512-thread workgroup has.)
+// sampling walk takes the E of 8, 16 and 28 (16 in registers and 12 in LDS)
+// with the least cost, sequences per group times a weight per E, the
+// smallest E among equals (more members share each row); greedy
+// verification keeps E = 8. A sequence costs about the same with 8 or 16
+// entries per thread (the group syncs set a level's time) and about 1.5
+// times that with 28 (measured at batches 64 and 128 over a 128256-token
+// vocabulary: 42-45 against 63-65 us per sequence), so 28 pays only where
+// it cuts the sequences per group by more than a third. (More than 16 in
+// registers would need more than a resident 512-thread workgroup has; the
+// two LDS buffers of 12 entries take 96 KB.)
 bool sv_plan(int32_t B, int32_t V, bool greedy, SvPlan &p)
 {
     const int cus = device_cu_count();
@@ -1585,16 +1736,20 @@ bool sv_plan(int32_t B, int32_t V, bool greedy, SvPlan &p)
                                        kSvThreads);
         return fit(kSvEpt, (int64_t)g * cus, p);
     }
-    const int64_t res[2] = {sampling_resident<8>(cus), sampling_resident<16>(cus)};
-    const int Es[2] = {8, 16};
+    const int64_t res[3] = {sampling_resident<8>(cus), sampling_resident<16>(cus),
+                            sampling_resident<28>(cus)};
+    const int Es[3] = {8, 16, 28};
+    const int64_t weight[3] = {2, 2, 3};
     bool found = false;
-    for (int i = 0; i < 2; ++i) {
+    int64_t best = 0;
+    for (int i = 0; i < 3; ++i) {
         SvPlan q;
         if (!fit(Es[i], res[i], q))
             continue;
-        const int64_t rounds = ceil_div(B, q.ngroups);
-        if (!found || rounds < ceil_div(B, p.ngroups)) {
+        const int64_t cost = ceil_div(B, q.ngroups) * weight[i];
+        if (!found || cost < best) {
             p = q;
+            best = cost;
             found = true;
         }
     }
@@ -1751,8 +1906,10 @@ tav_status sv_launch(const float *target_logits, const float *draft_logits,
         hipLaunchKernelGGL(spec_verify_greedy_kernel, grid, block, 0, st, a);
     else if (p.E == 8)
         sampling(std::integral_constant<int, 8>{});
-    else
+    else if (p.E == 16)
         sampling(std::integral_constant<int, 16>{});
+    else
+        sampling(std::integral_constant<int, 28>{});
     return hipGetLastError() == hipSuccess ? TAV_OK : TAV_ERR_LAUNCH;
 }
 
