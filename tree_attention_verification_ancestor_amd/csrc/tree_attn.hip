@@ -1004,9 +1004,10 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(AttnArgs a, int 
     const int64_t P0 = ((int64_t)bh * a.RB + rb) * a.S;
     // The (max, sum) pair and O chunk of up to kCombineBatch splits are
     // requested before any is used, so the loads overlap instead of waiting
-    // on one another (the common split counts fit one batch). A split that
-    // saw no key has max -inf, O = 0 and sum 0; it is skipped.
-    constexpr int kCombineBatch = 4;
+    // on one another: every split count the planner makes for a batch of one
+    // (up to 16) is a single round trip to memory. A split that saw no key
+    // has max -inf, O = 0 and sum 0; it is skipped.
+    constexpr int kCombineBatch = 16;
     f32x2 ml[kCombineBatch];
     f32x4 v[kCombineBatch];
     auto load_batch = [&](int s0) __attribute__((always_inline)) {
