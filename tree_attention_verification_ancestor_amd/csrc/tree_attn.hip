@@ -1059,7 +1059,13 @@ struct AttnPlan {
 
 size_t round_up(size_t v, size_t al) { return (v + al - 1) / al * al; }
 
-constexpr int kMinTilesPerSplit = 4;   // below this, partials cost more than the split gains
+// Splits of a prefix: at least kMinTilesPerSplit tiles each and at most
+// kMaxSplits of them (where the block-table bound below allows). Measured at
+// batch one (8B-shaped 64-node trees over 4096 tokens, 16-node trees over
+// 2048): 16 splits beat both 8 and 32, each split's fixed cost (Q, the
+// first tiles' latency, its partial) against the tiles it shares out.
+constexpr int kMinTilesPerSplit = 2;
+constexpr int kMaxSplits = 16;
 
 template <int D>
 const void *kernel_for(int NW)
@@ -1098,7 +1104,7 @@ void attn_plan_for(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
     const int64_t target = (int64_t)cus * per_cu;
     const int64_t tiles = std::max<int64_t>(1, ceil_div(max_prefix_len, kKT));
     int64_t S = ceil_div(target, base);
-    S = std::max<int64_t>(1, std::min<int64_t>(S, tiles / kMinTilesPerSplit));
+    S = std::max<int64_t>(1, std::min<int64_t>({S, tiles / kMinTilesPerSplit, (int64_t)kMaxSplits}));
     // A split's block-table slice must fit its LDS copy. Split s takes units
     // [s U / S, (s + 1) U / S) of the U = prefix tiles + tree tiles, so it
     // can hold up to ceil(U / S) prefix tiles: the bound counts every unit.
