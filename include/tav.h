@@ -125,7 +125,7 @@ tav_status tav_attn_plan(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t 
  * sequences of vocabulary V on the current device (a host call that reads
  * the device's CU count and the kernels' occupancy; nothing launched).
  * greedy: 0 the sampling walks (temperature > 0), 1 greedy verification.
- *   plan[0] vocabulary entries per thread: 8 or 16 (held in registers) or
+ *   plan[0] vocabulary entries per thread: 4, 8 or 16 (held in registers) or
  *           28 (16 in registers, 12 in LDS); 28 only where it cuts the
  *           sequences per group by more than a third (a sequence costs about
  *           1.5 times as much with it), else the fewest sequences per group,

@@ -1058,10 +1058,10 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 }
                 return r;
             };
-            // With E = 8, p and q (then the residual) are held in fp64 registers
+            // With E <= 8, p and q (then the residual) are held in fp64 registers
             // and updated in place after each rejection, the same operations
             // on the same values as the chain above, without re-forming it.
-            constexpr bool kHold = E == 8;
+            constexpr bool kHold = E <= 8;
             double pr_h[kHold ? E : 1], qv_h[kHold ? E : 1];
             double sk = 1.0;   // held, without replacement: q_k = qv_h sk
             if constexpr (kHold) {
@@ -1706,10 +1706,12 @@ int64_t sampling_resident(int cus)
 
 // A group of ceil(V / 512 E) workgroups per sequence, as many groups as the
 // device holds at once (at most B), each walking its sequences in turn. The
-// sampling walk takes the E of 8, 16 and 28 (16 in registers and 12 in LDS)
-// with the least cost, sequences per group times a weight per E, the
-// smallest E among equals (more members share each row); greedy
-// verification keeps E = 8. A sequence costs about the same with 8 or 16
+// sampling walk takes the E of 4, 8, 16 and 28 (16 in registers and 12 in
+// LDS) with the least cost, sequences per group times a weight per E, the
+// smallest E among equals (more members share each row: at batches up to 4
+// over a 128256-token vocabulary, 63 workgroups of 4 entries per thread,
+// 2-5 % faster than 32 of 8 at batch one); greedy verification keeps E = 8.
+// A sequence costs about the same with 4, 8 or 16
 // entries per thread (the group syncs set a level's time) and about 1.5
 // times that with 28 (measured at batches 64 and 128 over a 128256-token
 // vocabulary: 42-45 against 63-65 us per sequence), so 28 pays only where
@@ -1736,13 +1738,13 @@ bool sv_plan(int32_t B, int32_t V, bool greedy, SvPlan &p)
                                        kSvThreads);
         return fit(kSvEpt, (int64_t)g * cus, p);
     }
-    const int64_t res[3] = {sampling_resident<8>(cus), sampling_resident<16>(cus),
-                            sampling_resident<28>(cus)};
-    const int Es[3] = {8, 16, 28};
-    const int64_t weight[3] = {2, 2, 3};
+    const int64_t res[4] = {sampling_resident<4>(cus), sampling_resident<8>(cus),
+                            sampling_resident<16>(cus), sampling_resident<28>(cus)};
+    const int Es[4] = {4, 8, 16, 28};
+    const int64_t weight[4] = {2, 2, 2, 3};
     bool found = false;
     int64_t best = 0;
-    for (int i = 0; i < 3; ++i) {
+    for (int i = 0; i < 4; ++i) {
         SvPlan q;
         if (!fit(Es[i], res[i], q))
             continue;
@@ -1904,6 +1906,8 @@ tav_status sv_launch(const float *target_logits, const float *draft_logits,
     };
     if (greedy)
         hipLaunchKernelGGL(spec_verify_greedy_kernel, grid, block, 0, st, a);
+    else if (p.E == 4)
+        sampling(std::integral_constant<int, 4>{});
     else if (p.E == 8)
         sampling(std::integral_constant<int, 8>{});
     else if (p.E == 16)
