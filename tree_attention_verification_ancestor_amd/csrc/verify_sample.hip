@@ -219,16 +219,27 @@ __device__ __forceinline__ float wave_max_f32(float v)
                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 48))));
 }
 
-// Sum over the wave in lane order (an inclusive scan's last value).
-__device__ __forceinline__ double wave_sum_ordered(double v)
+// Inclusive prefix sums over the wave in a fixed order: a Hillis-Steele
+// scan inside each 16-lane row (DPP row shifts), then the rows' totals
+// carried across in row order. Every caller with the same inputs gets the
+// same bits, and lane 63 holds the total.
+__device__ __forceinline__ double wave_scan_incl(double v)
 {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const double y = __shfl_up(v, o);
-        if ((threadIdx.x & 63) >= o)
-            v += y;
-    }
-    return __shfl(v, 63);
+    v += dpp_f64<0x111>(v);   // row_shr:1 (0 where the row has no lane below)
+    v += dpp_f64<0x112>(v);   // row_shr:2
+    v += dpp_f64<0x114>(v);   // row_shr:4
+    v += dpp_f64<0x118>(v);   // row_shr:8
+    const double c1 = lane_f64(v, 15);
+    const double c2 = c1 + lane_f64(v, 31);
+    const double c3 = c2 + lane_f64(v, 47);
+    const int row = (int)(threadIdx.x & 63) >> 4;
+    return row == 0 ? v : v + (row == 1 ? c1 : row == 2 ? c2 : c3);
+}
+
+// The value of the lane below (0 in lane 0): DPP wave_shr:1.
+__device__ __forceinline__ double wave_shift_up1(double v)
+{
+    return dpp_f64<0x138>(v);
 }
 
 // Workgroup-wide reductions of two values at once; every thread gets the
@@ -1203,23 +1214,30 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 continue;
 
             // ---- 4. inverse-CDF draw from the final distribution at u ---------
-            // Member w's interval is [before_w, before_w + mass_w) with the
-            // masses summed in member order, identically in every workgroup.
-            if (tid == 0) {
-                double run = 0.0, before = 0.0;
-                for (int w = 0; w < wpg; ++w) {
-                    if (w == rank)
-                        before = run;
-                    run += s_mass[w];
+            // Member w's interval is [end_{w-1}, end_w): end_w the inclusive
+            // prefix sums of the members' masses in member order (a wave scan
+            // per 64 members, carried across), the same bits in every
+            // workgroup, so the intervals tile [0, total) exactly.
+            if (wave == 0) {
+                double carry = 0.0;
+                for (int w0 = 0; w0 < wpg; w0 += 64) {
+                    const double inc = wave_scan_incl(w0 + lane < wpg ? s_mass[w0 + lane] : 0.0);
+                    const double exc = wave_shift_up1(inc);
+                    if (w0 + lane == rank) {
+                        s_red[0] = carry + exc;   // this member's interval
+                        s_red[2] = carry + inc;
+                    }
+                    carry = carry + lane_f64(inc, 63);
                 }
-                s_red[0] = before;
-                s_red[1] = run;
-                s_found = -1;
-                s_last_live = -1;
-                s_hit = -1;
+                if (lane == 0) {
+                    s_red[1] = carry;
+                    s_found = -1;
+                    s_last_live = -1;
+                    s_hit = -1;
+                }
             }
             __syncthreads();
-            const double before = s_red[0], total = s_red[1];
+            const double before = s_red[0], total = s_red[1], end = s_red[2];
             const double mass = s_mass[rank];
             const double target = s_ures[u] * total;
             __syncthreads();
@@ -1229,11 +1247,12 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 failed = true;
                 break;
             }
-            if (mass > 0.0 && before <= target && target < before + mass) {
+            if (mass > 0.0 && before <= target && target < end) {
                 // Token order is (run h, wave, lane, entry j). Totals of every
-                // (run, wave) slot first, in that order; then the wave holding
-                // the target scans its lanes' run sums, and the lane its four
-                // entries.
+                // (run, wave) slot first (a wave scan's last value); then the
+                // slots scanned in that order, the wave holding the target
+                // scans its lanes' run sums the same way, and the lane its
+                // four entries.
                 const int lane = tid & 63, wave = tid >> 6;
                 auto run_sum = [&](int h) __attribute__((always_inline)) {
                     return ((cur_res(4 * h, k) + cur_res(4 * h + 1, k)) + cur_res(4 * h + 2, k)) +
@@ -1241,22 +1260,23 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 };
 #pragma unroll
                 for (int h = 0; h < E / 4; ++h) {
-                    const double t = wave_sum_ordered(run_sum(h));
+                    const double t = lane_f64(wave_scan_incl(run_sum(h)), 63);
                     if (lane == 0)
                         s_slot[h * kSvWaves + wave] = t;
                 }
                 __syncthreads();
-                if (tid == 0) {
-                    double run = before;
-                    for (int k2 = 0; k2 < (E / 4) * kSvWaves; ++k2) {
-                        const double nxt = run + s_slot[k2];
-                        if (s_slot[k2] > 0.0 && run <= target && target < nxt) {
-                            s_hit = k2;
-                            s_hit_off = run;
-                            break;
-                        }
-                        run = nxt;
-                    }
+                if (wave == 0) {
+                    constexpr int kSlots = (E / 4) * kSvWaves;
+                    static_assert(kSlots <= 64, "one lane per slot");
+                    const double sl = lane < kSlots ? s_slot[lane] : 0.0;
+                    const double inc = wave_scan_incl(sl);
+                    const double lo = before + wave_shift_up1(inc), hi = before + inc;
+                    const uint64_t hits = __ballot(sl > 0.0 && lo <= target && target < hi);
+                    const int first = hits ? (int)__builtin_ctzll(hits) : -1;
+                    if (lane == 0)
+                        s_hit = first;
+                    if (lane == first)
+                        s_hit_off = lo;
                 }
                 __syncthreads();
                 const int hit = s_hit;
@@ -1271,17 +1291,8 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                             for (int j = 0; j < 4; ++j)
                                 pe[j] = cur_res(4 * h + j, k);
                         }
-                    double incl = v;
-#pragma unroll
-                    for (int o = 1; o < 64; o <<= 1) {
-                        const double y = __shfl_up(incl, o);
-                        if (lane >= o)
-                            incl += y;
-                    }
-                    double excl = __shfl_up(incl, 1);
-                    if (lane == 0)
-                        excl = 0.0;
-                    const double lo = s_hit_off + excl, hi = s_hit_off + incl;
+                    const double incl = wave_scan_incl(v);
+                    const double lo = s_hit_off + wave_shift_up1(incl), hi = s_hit_off + incl;
                     const int64_t i0 = base + (int64_t)h_hit * kRun + 4 * tid;
                     if (v > 0.0) {
                         int last = -1, found = -1;
