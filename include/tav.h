@@ -18,6 +18,7 @@
  *   tree_widths_by_entropy  branching widths from the frontier's entropy ranks
  *   tree_topology_dp    the budget's best topology under acceptance by sibling rank
  *   tav_sampler_plan    how the walk lays out a batch on the device
+ *   tav_sampler_plan_for  the same rule for a given device shape (host only)
  *   tav_model_speedup, tav_best_chain_length, tav_fit_alpha
  *                       the speedup model, on the host, fed by measured times
  *
@@ -139,6 +140,19 @@ tav_status tav_attn_plan(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t 
  * device (or there is none).
  */
 tav_status tav_sampler_plan(int32_t B, int32_t V, int32_t greedy, int32_t *plan);
+
+/*
+ * tav_sampler_plan_for — the same layout rule on a device of `cus` compute
+ * units holding per_cu[i] workgroups of each walk kernel at once (per_cu[0..3]
+ * the sampling walk with 4, 8, 16 and 28 entries per thread, per_cu[4] greedy
+ * verification; host arithmetic only, nothing queried or launched), so the
+ * rule can be checked without a device. plan as for tav_sampler_plan.
+ * TAV_ERR_ARG for a NULL pointer, B < 1, V < 1, cus < 1, a negative per_cu
+ * entry or greedy outside {0, 1}; TAV_ERR_UNSUPPORTED for V > 2^21;
+ * TAV_ERR_LAUNCH if no layout fits.
+ */
+tav_status tav_sampler_plan_for(int32_t B, int32_t V, int32_t greedy, int32_t cus,
+                                const int32_t *per_cu, int32_t *plan);
 
 /*
  * tree_attn_verify — one attention layer of the verification forward pass.

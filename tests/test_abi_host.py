@@ -283,6 +283,64 @@ def test_sampler_plan_rejects_bad_arguments():
     assert lib.tav_sampler_plan(8, (1 << 21) + 1, 0, ctypes.cast(plan, P)) == tav.ERR_UNSUPPORTED
 
 
+def test_sampler_plan_for_rejects_bad_arguments():
+    lib = tav.lib()
+    plan = (ctypes.c_int32 * 4)()
+    occ = (ctypes.c_int32 * 5)(1, 1, 1, 1, 1)
+    bad = (ctypes.c_int32 * 5)(1, -1, 1, 1, 1)
+    pp, po, pb = (ctypes.cast(x, P) for x in (plan, occ, bad))
+    assert lib.tav_sampler_plan_for(8, 1000, 0, 256, po, None) == tav.ERR_ARG
+    assert lib.tav_sampler_plan_for(8, 1000, 0, 256, None, pp) == tav.ERR_ARG
+    assert lib.tav_sampler_plan_for(8, 1000, 0, 0, po, pp) == tav.ERR_ARG
+    assert lib.tav_sampler_plan_for(8, 1000, 0, 256, pb, pp) == tav.ERR_ARG
+    assert lib.tav_sampler_plan_for(0, 1000, 0, 256, po, pp) == tav.ERR_ARG
+    assert lib.tav_sampler_plan_for(8, 1000, 3, 256, po, pp) == tav.ERR_ARG
+    assert lib.tav_sampler_plan_for(8, (1 << 21) + 1, 0, 256, po, pp) == tav.ERR_UNSUPPORTED
+    # nothing resident: no layout fits
+    zero = (ctypes.c_int32 * 5)(0, 0, 0, 0, 0)
+    assert lib.tav_sampler_plan_for(8, 1000, 0, 256, ctypes.cast(zero, P), pp) == tav.ERR_LAUNCH
+
+
+@pytest.mark.parametrize("B,entries,groups", [
+    (1, 4, 1), (4, 4, 4), (8, 8, 8), (16, 16, 16), (32, 16, 16), (64, 16, 16),
+    (96, 16, 16), (128, 28, 28), (256, 28, 28)])
+def test_sampler_plan_for_the_70b_vocabulary(B, entries, groups):
+    """The layout rule on a 256-CU device holding one walk workgroup per CU,
+    over a 128256-token vocabulary: 4 entries per thread up to batch 4, 8 at
+    batch 8, 16 up to batch 96, and 28 (16 in registers, 12 in LDS) where it
+    cuts the sequences per group by more than a third."""
+    p = tav.sampler_plan_for(B, 128256, 256, (1, 1, 1, 1, 1))
+    assert (p["entries_per_thread"], p["groups"]) == (entries, groups), p
+    assert p["workgroups_per_sequence"] == -(-128256 // (512 * entries))
+    g = tav.sampler_plan_for(B, 128256, 256, (1, 1, 1, 1, 1), greedy=True)
+    assert g["entries_per_thread"] == 8
+
+
+def test_sampler_plan_for_covers_the_vocabulary():
+    """Over a sweep of batches, vocabularies and device shapes: the chunks
+    are whole 16-byte runs that cover the vocabulary with no workgroup past
+    its capacity, no more groups than sequences, and no more workgroups
+    than the device holds at once."""
+    for cus in (1, 8, 80, 256):
+        for occ in ((1, 1, 1, 1, 1), (2, 2, 1, 1, 2), (2, 1, 1, 0, 1)):
+            for B in (1, 2, 3, 5, 8, 17, 64, 100, 128, 300):
+                for V in (1, 3, 1000, 4097, 20001, 32000, 128256, 151936, 1 << 21):
+                    for greedy in (False, True):
+                        try:
+                            p = tav.sampler_plan_for(B, V, cus, occ, greedy=greedy)
+                        except tav.TavError as e:
+                            assert e.status == tav.ERR_LAUNCH
+                            continue
+                        E, wpg, ng, chunk = (p["entries_per_thread"], p["workgroups_per_sequence"],
+                                             p["groups"], p["chunk"])
+                        assert E in ((8,) if greedy else (4, 8, 16, 28))
+                        assert chunk % 4 == 0 and chunk <= 512 * E
+                        assert wpg * chunk >= V and (wpg - 1) * chunk < V
+                        assert 1 <= ng <= B
+                        i = 4 if greedy else (4, 8, 16, 28).index(E)
+                        assert ng * wpg <= occ[i] * cus
+
+
 def test_noalloc_sampler_rejects_bad_arguments_before_any_device_work():
     lib = tav.lib()
     fn = lib.spec_verify_sample_noalloc

@@ -64,6 +64,7 @@ _SIGNATURES = {
     "tree_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "tav_attn_plan": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
     "tav_sampler_plan": (_I32, [_I32, _I32, _I32, _P]),
+    "tav_sampler_plan_for": (_I32, [_I32, _I32, _I32, _I32, _P, _P]),
     "tree_attn_verify": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _P, _I32, _I32,
                                 _I32, _I32, _I32, _I32, _F32, _P, _P, _SZ, _P, _P]),
     "tree_attn_verify_tree": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _P, _P, _P,
@@ -242,6 +243,19 @@ def sampler_plan(B, V, greedy=False):
     plan = (ctypes.c_int32 * 4)()
     _check("tav_sampler_plan", lib().tav_sampler_plan(B, V, int(bool(greedy)),
                                                       ctypes.cast(plan, ctypes.c_void_p)))
+    return {"entries_per_thread": plan[0], "workgroups_per_sequence": plan[1], "groups": plan[2],
+            "chunk": plan[3], "sequences_per_group": -(-B // plan[2])}
+
+
+def sampler_plan_for(B, V, cus, per_cu, greedy=False):
+    """``sampler_plan``'s rule on a device of ``cus`` compute units holding
+    ``per_cu`` workgroups at once of each walk kernel (4, 8, 16 and 28
+    entries per thread, then greedy verification); host only."""
+    occ = (ctypes.c_int32 * 5)(*per_cu)
+    plan = (ctypes.c_int32 * 4)()
+    _check("tav_sampler_plan_for", lib().tav_sampler_plan_for(
+        B, V, int(bool(greedy)), cus, ctypes.cast(occ, ctypes.c_void_p),
+        ctypes.cast(plan, ctypes.c_void_p)))
     return {"entries_per_thread": plan[0], "workgroups_per_sequence": plan[1], "groups": plan[2],
             "chunk": plan[3], "sequences_per_group": -(-B // plan[2])}
 

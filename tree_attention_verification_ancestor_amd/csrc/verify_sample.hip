@@ -1729,35 +1729,30 @@ int64_t sampling_resident(int cus)
 // it cuts the sequences per group by more than a third. (More than 16 in
 // registers would need more than a resident 512-thread workgroup has; the
 // two LDS buffers of 12 entries take 96 KB.)
-bool sv_plan(int32_t B, int32_t V, bool greedy, SvPlan &p)
+// The same from the workgroups a device holds at once for each layout
+// (resident[i] for E = 4, 8, 16, 28, then greedy verification): pure
+// arithmetic, so it can be checked on the host.
+bool sv_plan_for(int32_t B, int32_t V, bool greedy, const int64_t (&resident)[5], SvPlan &p)
 {
-    const int cus = device_cu_count();
-    if (cus <= 0)
-        return false;
-    auto fit = [&](int E, int64_t resident, SvPlan &q) {
+    auto fit = [&](int E, int64_t res, SvPlan &q) {
         q.E = E;
         q.wpg = (int)ceil_div(V, (int64_t)kSvThreads * E);
-        if (resident <= 0 || q.wpg > resident || q.wpg > kMaxWpg)
+        if (res <= 0 || q.wpg > res || q.wpg > kMaxWpg)
             return false;
         q.chunk = (int)(ceil_div(ceil_div(V, q.wpg), 4) * 4);   // whole 16-byte runs
-        q.ngroups = (int)std::min<int64_t>(B, resident / q.wpg);
+        q.ngroups = (int)std::min<int64_t>(B, res / q.wpg);
         q.box_bytes = (size_t)q.ngroups * 2 * q.wpg * kSlotWords * sizeof(uint64_t);
         return true;
     };
-    if (greedy) {
-        const int g = kernel_occupancy(reinterpret_cast<const void *>(spec_verify_greedy_kernel),
-                                       kSvThreads);
-        return fit(kSvEpt, (int64_t)g * cus, p);
-    }
-    const int64_t res[4] = {sampling_resident<4>(cus), sampling_resident<8>(cus),
-                            sampling_resident<16>(cus), sampling_resident<28>(cus)};
+    if (greedy)
+        return fit(kSvEpt, resident[4], p);
     const int Es[4] = {4, 8, 16, 28};
     const int64_t weight[4] = {2, 2, 2, 3};
     bool found = false;
     int64_t best = 0;
     for (int i = 0; i < 4; ++i) {
         SvPlan q;
-        if (!fit(Es[i], res[i], q))
+        if (!fit(Es[i], resident[i], q))
             continue;
         const int64_t cost = ceil_div(B, q.ngroups) * weight[i];
         if (!found || cost < best) {
@@ -1767,6 +1762,24 @@ bool sv_plan(int32_t B, int32_t V, bool greedy, SvPlan &p)
         }
     }
     return found;
+}
+
+bool sv_plan(int32_t B, int32_t V, bool greedy, SvPlan &p)
+{
+    const int cus = device_cu_count();
+    if (cus <= 0)
+        return false;
+    int64_t res[5] = {0, 0, 0, 0, 0};
+    if (greedy) {
+        res[4] = (int64_t)kernel_occupancy(reinterpret_cast<const void *>(spec_verify_greedy_kernel),
+                                           kSvThreads) * cus;
+    } else {
+        res[0] = sampling_resident<4>(cus);
+        res[1] = sampling_resident<8>(cus);
+        res[2] = sampling_resident<16>(cus);
+        res[3] = sampling_resident<28>(cus);
+    }
+    return sv_plan_for(B, V, greedy, res, p);
 }
 
 // Workspace for either mode of spec_verify_sample (0 if neither plan fits).
@@ -1834,6 +1847,30 @@ extern "C" tav_status tav_sampler_plan(int32_t B, int32_t V, int32_t greedy, int
         return TAV_ERR_UNSUPPORTED;
     SvPlan p;
     if (!sv_plan(B, V, greedy == 1, p))
+        return TAV_ERR_LAUNCH;
+    plan[0] = p.E;
+    plan[1] = p.wpg;
+    plan[2] = p.ngroups;
+    plan[3] = p.chunk;
+    return TAV_OK;
+}
+
+extern "C" tav_status tav_sampler_plan_for(int32_t B, int32_t V, int32_t greedy, int32_t cus,
+                                           const int32_t *per_cu, int32_t *plan)
+{
+    using namespace tav;
+    if (!plan || !per_cu || B < 1 || V < 1 || greedy < 0 || greedy > 1 || cus < 1)
+        return TAV_ERR_ARG;
+    for (int i = 0; i < 5; ++i)
+        if (per_cu[i] < 0)
+            return TAV_ERR_ARG;
+    if (V > kMaxVocab)
+        return TAV_ERR_UNSUPPORTED;
+    int64_t res[5];
+    for (int i = 0; i < 5; ++i)
+        res[i] = (int64_t)per_cu[i] * cus;
+    SvPlan p;
+    if (!sv_plan_for(B, V, greedy == 1, res, p))
         return TAV_ERR_LAUNCH;
     plan[0] = p.E;
     plan[1] = p.wpg;
