@@ -205,18 +205,25 @@ __device__ __forceinline__ double wave_max(double v)
     return fmax(fmax(lane_f64(v, 0), lane_f64(v, 16)), fmax(lane_f64(v, 32), lane_f64(v, 48)));
 }
 
-// The same for fp32 values (32-bit DPP: half the moves of the fp64 form).
+// The same for fp32 values (32-bit DPP: half the moves of the fp64 form),
+// with the IEEE maximum, which propagates NaN: a NaN anywhere in the wave is
+// the result.
+__device__ __forceinline__ float fmax_nan(float a, float b)
+{
+    return __builtin_elementwise_maximum(a, b);
+}
+
 __device__ __forceinline__ float wave_max_f32(float v)
 {
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kQuadSwap1, 0xF, 0xF, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kQuadSwap2, 0xF, 0xF, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kRowHalfMirror, 0xF, 0xF, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kRowMirror, 0xF, 0xF, false)));
+    v = fmax_nan(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kQuadSwap1, 0xF, 0xF, false)));
+    v = fmax_nan(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kQuadSwap2, 0xF, 0xF, false)));
+    v = fmax_nan(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kRowHalfMirror, 0xF, 0xF, false)));
+    v = fmax_nan(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kRowMirror, 0xF, 0xF, false)));
     const int u = __builtin_bit_cast(int, v);
-    return fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 0)),
-                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 16))),
-                 fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 32)),
-                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 48))));
+    return fmax_nan(fmax_nan(__builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 0)),
+                             __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 16))),
+                    fmax_nan(__builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 32)),
+                             __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 48))));
 }
 
 // Inclusive prefix sums over the wave in a fixed order: a Hillis-Steele
@@ -728,16 +735,15 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
             if constexpr (EL > 0)
                 sv_wait_loads();
             // Maxima of the raw fp32 logits (exact; x -> x/T is monotone) and
-            // sums of exp relative to them, per wave (DPP, no barrier). A NaN
-            // logit makes the sum NaN.
+            // sums of exp relative to them, per wave (DPP, no barrier). The
+            // maxima propagate NaN, so a NaN logit makes the wave's maximum,
+            // every exponential against it and the row's sum NaN.
             const int lane = tid & 63, wave = tid >> 6;
-            bool nan_seen = false;
             float mt_l = -INFINITY, mq_l = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < ER; ++e) {
-                nan_seen |= __builtin_isnan(tf[e]) || __builtin_isnan(df[e]);
-                mt_l = fmaxf(mt_l, tf[e]);
-                mq_l = fmaxf(mq_l, df[e]);
+            for (int e = 0; e < ER; e += 2) {
+                mt_l = fmax_nan(mt_l, fmax_nan(tf[e], tf[e + 1]));
+                mq_l = fmax_nan(mq_l, fmax_nan(df[e], df[e + 1]));
             }
             // an LDS entry's logit, -inf past the chunk (and for the draft
             // row of a node without children)
@@ -750,10 +756,8 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 const f32x4 xt = s_lx[lb][hl][0][tid], xd = s_lx[lb][hl][1][tid];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float t = lds_logit(xt, hl, j, true), d = lds_logit(xd, hl, j, has_kids);
-                    nan_seen |= __builtin_isnan(t) || __builtin_isnan(d);
-                    mt_l = fmaxf(mt_l, t);
-                    mq_l = fmaxf(mq_l, d);
+                    mt_l = fmax_nan(mt_l, lds_logit(xt, hl, j, true));
+                    mq_l = fmax_nan(mq_l, lds_logit(xd, hl, j, has_kids));
                 }
             }
             const float wmt = wave_max_f32(mt_l), wmq = wave_max_f32(mq_l);
@@ -812,8 +816,6 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                     return fresh(eq[e < ER ? e : 0]);
                 return s_lx[lb][(e - ER) >> 2][1][tid][e & 3];
             };
-            if (nan_seen)
-                zt = NAN;
             zt = wave_sum(zt);
             zq = wave_sum(zq);
             if (lane == 0) {
