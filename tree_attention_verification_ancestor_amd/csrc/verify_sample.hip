@@ -515,6 +515,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
     __shared__ int s_found;
     __shared__ int s_last_live;
     __shared__ int s_hit;
+    __shared__ int s_owner;   // the member whose interval holds the draw
     __shared__ int s_is_last;
 
     const int g = blockIdx.x % a.ngroups;
@@ -1216,32 +1217,58 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 continue;
 
             // ---- 4. inverse-CDF draw from the final distribution at u ---------
-            // Member w's interval is [end_{w-1}, end_w): end_w the inclusive
-            // prefix sums of the members' masses in member order (a wave scan
-            // per 64 members, carried across), the same bits in every
-            // workgroup, so the intervals tile [0, total) exactly.
+            // Member w's interval starts at lo_w, the exclusive prefix sum of
+            // the members' masses in member order (a wave scan per 64
+            // members, carried across; the same bits in every workgroup),
+            // and the draw belongs to the last member with mass whose
+            // interval starts at or before it. A member without mass owns
+            // nothing, not even the ulp-wide interval the scan's differently
+            // associated sums can leave it.
             if (wave == 0) {
-                double carry = 0.0;
-                for (int w0 = 0; w0 < wpg; w0 += 64) {
-                    const double inc = wave_scan_incl(w0 + lane < wpg ? s_mass[w0 + lane] : 0.0);
-                    const double exc = wave_shift_up1(inc);
-                    if (w0 + lane == rank) {
-                        s_red[0] = carry + exc;   // this member's interval
-                        s_red[2] = carry + inc;
+                int owner = -1;
+                double total = 0.0, target = 0.0;
+                if (wpg <= 64) {
+                    const double m = lane < wpg ? s_mass[lane] : 0.0;
+                    const double inc = wave_scan_incl(m);
+                    total = lane_f64(inc, 63);
+                    target = s_ures[u] * total;
+                    const double lo = wave_shift_up1(inc);
+                    const uint64_t at = __ballot(m > 0.0 && lo <= target);
+                    if (at) {
+                        owner = 63 - (int)__builtin_clzll(at);
+                        if (lane == owner)
+                            s_red[0] = lo;
                     }
-                    carry = carry + lane_f64(inc, 63);
+                } else {
+                    for (int w0 = 0; w0 < wpg; w0 += 64)
+                        total = total + lane_f64(wave_scan_incl(w0 + lane < wpg ? s_mass[w0 + lane] : 0.0), 63);
+                    target = s_ures[u] * total;
+                    double carry = 0.0;
+                    for (int w0 = 0; w0 < wpg; w0 += 64) {
+                        const double m = w0 + lane < wpg ? s_mass[w0 + lane] : 0.0;
+                        const double inc = wave_scan_incl(m);
+                        const double lo = carry + wave_shift_up1(inc);
+                        const uint64_t at = __ballot(m > 0.0 && lo <= target);
+                        if (at) {
+                            owner = w0 + 63 - (int)__builtin_clzll(at);
+                            if (w0 + lane == owner)
+                                s_red[0] = lo;
+                        }
+                        carry = carry + lane_f64(inc, 63);
+                    }
                 }
                 if (lane == 0) {
-                    s_red[1] = carry;
+                    s_red[1] = total;
+                    s_red[2] = target;
+                    s_owner = owner;
                     s_found = -1;
                     s_last_live = -1;
                     s_hit = -1;
                 }
             }
             __syncthreads();
-            const double before = s_red[0], total = s_red[1], end = s_red[2];
-            const double mass = s_mass[rank];
-            const double target = s_ures[u] * total;
+            const double before = s_red[0], total = s_red[1], target = s_red[2];
+            const int owner = s_owner;
             __syncthreads();
             if (!(total > 0.0)) {
                 if (lead)
@@ -1249,7 +1276,7 @@ __global__ __launch_bounds__(kSvThreads) void spec_verify_kernel(SvArgs a)
                 failed = true;
                 break;
             }
-            if (mass > 0.0 && before <= target && target < end) {
+            if (rank == owner) {
                 // Token order is (run h, wave, lane, entry j). Totals of every
                 // (run, wave) slot first (a wave scan's last value); then the
                 // slots scanned in that order, the wave holding the target
