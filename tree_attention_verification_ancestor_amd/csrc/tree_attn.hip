@@ -890,9 +890,6 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     // coherent across XCDs at the memory side, so its L2 is not invalidated
     // (that would also drop the K/V tiles the other row block of its XCD is
     // reading).
-    auto pack = [](float x, float y) __attribute__((always_inline)) {
-        return ((uint64_t)__builtin_bit_cast(uint32_t, y) << 32) | __builtin_bit_cast(uint32_t, x);
-    };
     auto unpack = [](uint64_t w) __attribute__((always_inline)) {
         return f32x2{__builtin_bit_cast(float, (uint32_t)w), __builtin_bit_cast(float, (uint32_t)(w >> 32))};
     };
