@@ -111,7 +111,9 @@ size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, 
  * tav_attn_plan — how tree_attn_verify divides the work for these sizes on a
  * device of `cus` compute units holding `per_cu` of its workgroups each. A
  * host function (nothing launched, no device needed), for checking the plan:
- *   plan[0] waves per workgroup, plan[1] row blocks, plan[2] prefix splits,
+ *   plan[0] waves per workgroup (32 query rows per wave; with one or two
+ *   such row waves, twice that: two wave sets split each tile's keys),
+ *   plan[1] row blocks, plan[2] prefix splits,
  *   plan[3] the most block-table entries any split stages, over every prefix
  *   length up to max_prefix_len, plan[4] the capacity of that staging copy
  *   (plan[3] <= plan[4] for every supported shape).

@@ -47,6 +47,12 @@
 // Operand reads. The S and P.V MFMAs take their LDS operands from reads
 // issued four MFMAs ahead into separate registers, held in that order by a
 // scheduling fence after each MFMA.
+// Small row counts. With one or two row waves (32 or 64 query rows) a
+// workgroup has two wave sets over the same rows: set h takes keys
+// [32h, 32h + 32) of every tile (half the S and P.V MFMAs and half the
+// softmax each), and at the end the upper set's (O, max, sum) merge into
+// the lower set's through LDS, as two splits would. A tile's chain of work
+// per wave is then half as long and twice the SIMDs work on it.
 // Overlap. A wave's work per tile is an MFMA phase (S) and a phase that
 // mixes vector ALU work and MFMAs: the softmax of the tile spread between the
 // P.V MFMAs of the tile before. In an 8-wave workgroup the two waves that
@@ -75,10 +81,10 @@ constexpr int kMaxSplitBlocks = 2048; // block-table entries one split stages in
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kWeightBias = 7.0f;  // log2 of the bias on the fp16 weights
 
-template <int D, int NW>
+template <int D, int NW, int KSP = 1>
 struct Cfg {
-    static constexpr int kThreads = NW * 64;
-    static constexpr int kRows = NW * 32;                // query rows per workgroup (32 per wave)
+    static constexpr int kThreads = NW * KSP * 64;
+    static constexpr int kRows = NW * 32;                // query rows per workgroup (32 per row wave)
     static constexpr int kKSteps = D / 16;
     static constexpr int kDTiles = D / 32;
     static constexpr int kCpr = D / 8;                   // 16-byte chunks per row
@@ -194,15 +200,16 @@ __device__ __forceinline__ void wait_vmem()
 // sched_group_barrier instruction classes
 constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100;
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
+template <int D, int NW, int KSP = 1>
+__global__ __launch_bounds__(NW * KSP * 64) void tree_attn_kernel(AttnArgs a)
 {
-    using C = Cfg<D, NW>;
+    using C = Cfg<D, NW, KSP>;
+    static_assert(KSP == 1 || (KSP == 2 && NW <= 4), "keys split between two wave sets");
     // Which waves issue the direct tile loads. A wave stalls at each one until
     // the CU's load path takes it (about 14 cycles per kilobyte, every wave of
     // the CU in one queue), so with 8 waves the four whose work per tile is
     // the shorter chain (see "Overlap") issue them all and the other four none.
-    constexpr int kIssuers = NW == 8 ? NW / 2 : NW;
+    constexpr int kIssuers = NW == 8 ? NW / 2 : NW * KSP;
     constexpr int LPW = C::kChunks / 64 / kIssuers;   // loads per issuing wave per K (or V) tile
     static_assert(LPW * 64 * kIssuers == C::kChunks, "direct loads must split evenly");
     constexpr int KTB = C::kKTileBytes, VTB = C::kVTileBytes;
@@ -242,6 +249,11 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: SGPR arithmetic
+    // With KSP = 2 the workgroup's waves form two sets over the same query
+    // rows (row wave rw), set `half` taking keys [32 half, 32 half + 32) of
+    // every tile; the two online softmaxes merge at the end.
+    const int rw = wave % NW;
+    const int half = wave / NW;
     const int col = lane & 31;      // query column of this lane
     const int hh = lane >> 5;       // which half of the K dimension this lane feeds
 
@@ -290,7 +302,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     }
 
     // ---- this lane's query row, and the first word of its ancestor mask ------
-    const int row = rb * C::kRows + wave * 32 + col;
+    const int row = rb * C::kRows + rw * 32 + col;
     const bool row_ok = row < a.NG;
     const int node = row_ok ? row / a.G : 0;
     const int head = kvh * a.G + (row_ok ? row % a.G : 0);
@@ -465,25 +477,39 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     for (int k = 0; k < C::kKSteps; ++k)
         kfrag[k] = (uint32_t)(col * (2 * D) + (((2 * k) ^ hh ^ k_swz<D>(col)) << 4));
     constexpr int kDepth = 4;
-    constexpr int kQkN = 2 * C::kKSteps;
+    // halves of a tile's keys per wave: both, or (KSP = 2) the wave's own,
+    // kept in sacc[0] / pb[0]
+    constexpr int kT = 2 / KSP;
+    constexpr int kQkN = kT * C::kKSteps;
     static_assert(kQkN >= kDepth, "read pipeline deeper than the MFMA sequence");
+    // MFMA j of a tile: key half t = j & 1 (or the wave's), K step j >> 1 (or j)
+    auto kfrag_of = [&](int j) __attribute__((always_inline)) {
+        if constexpr (KSP == 1)
+            return kfrag[j >> 1] + (uint32_t)((j & 1) * (64 * D));
+        else
+            return kfrag[j];
+    };
     auto qk = [&](uint32_t kaddr, f32x16 (&sacc)[2], auto &&between) __attribute__((always_inline)) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < kT; ++t)
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 sacc[t][e] = 0.f;
+        if constexpr (KSP == 2)
+            kaddr += (uint32_t)(half * (64 * D));
         bf16x8 kb[kDepth];
 #pragma unroll
         for (int j = 0; j < kDepth; ++j)
-            kb[j] = *lds_at<bf16x8>(kaddr + kfrag[j >> 1] + (j & 1) * (64 * D));
+            kb[j] = *lds_at<bf16x8>(kaddr + kfrag_of(j));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < kQkN; ++j) {
-            sacc[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[j % kDepth], qf[j >> 1], sacc[j & 1], 0, 0, 0);
+            constexpr int kTShift = KSP == 1 ? 1 : 0;
+            const int t = KSP == 1 ? (j & 1) : 0;
+            sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[j % kDepth], qf[j >> kTShift], sacc[t], 0, 0, 0);
             if (j + kDepth < kQkN) {
                 const int n = j + kDepth;
-                kb[j % kDepth] = *lds_at<bf16x8>(kaddr + kfrag[n >> 1] + (n & 1) * (64 * D));
+                kb[j % kDepth] = *lds_at<bf16x8>(kaddr + kfrag_of(n));
             }
             between(j);
             __builtin_amdgcn_sched_barrier(0);
@@ -524,14 +550,15 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
         lim -= 8 * hh;
         const uint32_t mlo = (uint32_t)mw, mhi = (uint32_t)(mw >> 32);
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < kT; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int kr = 16 * (i >> 1) + 4 * (i & 1) + j;   // < 32
-                    const uint32_t word = t ? mhi : mlo;
-                    const bool ok = (32 * t + kr < lim) && ((word >> kr) & 1u);
+                    const int th = KSP == 1 ? t : half;                  // the key half
+                    const uint32_t word = th ? mhi : mlo;
+                    const bool ok = (32 * th + kr < lim) && ((word >> kr) & 1u);
                     if (!ok)
                         sacc[t][4 * i + j] = -INFINITY;
                 }
@@ -546,7 +573,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
         // NaN score leaves the max alone and surfaces in the output check)
         float mt = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < kT; ++t)
 #pragma unroll
             for (int e = 0; e < 16; e += 2)
                 mt = __builtin_elementwise_maximum(mt, __builtin_elementwise_maximum(sacc[t][e], sacc[t][e + 1]));
@@ -564,8 +591,15 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
         m_used = mnew;
         lsum *= alpha;
         const float moff = (m_used == -INFINITY) ? 0.f : m_used * a.c - kWeightBias;
+        if constexpr (KSP == 2) {   // the other half's weights: none
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pb[1][h2][e] = (_Float16)0.0f;
+        }
+#pragma unroll
+        for (int t = 0; t < kT; ++t)
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
@@ -589,7 +623,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     // pb[bi/2][bi%2]) and feature tile m = j % kDTiles. The same read pipeline
     // as the scores; pv_begin issues the first kDepth reads, so a caller can
     // put vector work between them and the MFMAs.
-    constexpr int kPvN = 4 * C::kDTiles;
+    constexpr int kPvN = 2 * kT * C::kDTiles;
     static_assert(kPvN >= kDepth, "read pipeline deeper than the MFMA sequence");
     struct VReads {
         uint32_t base;
@@ -598,6 +632,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     auto pv_begin = [&](uint32_t vaddr) __attribute__((always_inline)) {
         VReads r;
         r.base = vaddr + (uint32_t)v_off<D>(0, col, hh);
+        if constexpr (KSP == 2)   // this wave's key half: 16-key blocks 2 half, 2 half + 1
+            r.base += (uint32_t)(half * 2 * (D * 32));
         asm("" : "+v"(r.base));   // keep the sum in one register
 #pragma unroll
         for (int j = 0; j < kDepth; ++j)
@@ -832,6 +868,44 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     else
         run(std::false_type{});
 
+    // Two wave sets over the same rows: the upper key half's waves leave
+    // their (O, running max, sum share) in LDS (the K ring, no longer read)
+    // and the lower half's merge them into theirs, as two splits merge.
+    if constexpr (KSP == 2) {
+        constexpr int kOW = 16 * C::kDTiles;   // O values per lane
+        static_assert(NW * (kOW + 2) * 64 * 4 <= kKSlots * KTB, "merge area inside the K ring");
+        float *s_po = reinterpret_cast<float *>(s_k);
+        float *s_pml = s_po + NW * kOW * 64;
+        __syncthreads();   // every wave is past its last read of the ring
+        if (half == 1) {
+#pragma unroll
+            for (int m = 0; m < C::kDTiles; ++m)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    s_po[(rw * kOW + 16 * m + e) * 64 + lane] = oacc[m][e];
+            s_pml[(2 * rw) * 64 + lane] = m_used;
+            s_pml[(2 * rw + 1) * 64 + lane] = lsum;
+        }
+        __syncthreads();
+        if (half == 0) {
+            const float m1 = s_pml[(2 * rw) * 64 + lane], l1 = s_pml[(2 * rw + 1) * 64 + lane];
+            const float M = fmaxf(m_used, m1);
+            if (M != -INFINITY) {
+                const float w0 = m_used == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_used - M) * a.c);
+                const float w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - M) * a.c);
+#pragma unroll
+                for (int m = 0; m < C::kDTiles; ++m)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        oacc[m][e] = oacc[m][e] * w0 + s_po[(rw * kOW + 16 * m + e) * 64 + lane] * w1;
+                lsum = lsum * w0 + l1 * w1;
+                m_used = M;
+            }
+        }
+    }
+    // the lower key half's waves (all waves when KSP = 1) own the output
+    const bool out_ok = row_ok && half == 0;
+
     // ---- write the result, or leave a partial, or merge the splits -------------
     const float ltot = lsum + __shfl_xor(lsum, 32);
     const float mrow = (m_used == -INFINITY) ? -INFINITY : m_used * a.c;   // log2 units
@@ -852,12 +926,12 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
             raise_flag(a.flags, TAV_FLAG_ATTN_RANGE);
     };
     if (a.S == 1) {
-        if (row_ok)
+        if (out_ok)
             write_out(oacc, 1.0f / ltot);
         return;
     }
     const int64_t unit = (int64_t)bh * a.RB + rb;
-    const int rloc = wave * 32 + col;
+    const int rloc = rw * 32 + col;
     const int64_t P0 = unit * a.S;
     auto write_partial = [&]() __attribute__((always_inline)) {
         float *po = a.part_o + ((P0 + s) * C::kRows + rloc) * D;
@@ -875,7 +949,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
     if (!a.merge) {
         // more than two splits: every split leaves its partial for the
         // combine kernel
-        if (row_ok)
+        if (out_ok)
             write_partial();
         return;
     }
@@ -894,7 +968,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
         return f32x2{__builtin_bit_cast(float, (uint32_t)w), __builtin_bit_cast(float, (uint32_t)(w >> 32))};
     };
     if (!s_last) {
-        if (row_ok)
+        if (out_ok)
             write_partial();
         wait_vmem<0>();   // this wave's stores are in the L2
         __syncthreads();
@@ -921,7 +995,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_kernel(AttnArgs a)
         }
     }
     __syncthreads();
-    if (row_ok) {
+    if (out_ok) {
         // out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s in split order
         // (a split that saw no key has m_s = -inf and is skipped)
         auto ml_of = [&](int s2) __attribute__((always_inline)) {
@@ -1073,10 +1147,19 @@ const void *kernel_for(int NW)
     case 4:
         return reinterpret_cast<const void *>(tree_attn_kernel<D, 4>);
     case 2:
-        return reinterpret_cast<const void *>(tree_attn_kernel<D, 2>);
+        return reinterpret_cast<const void *>(tree_attn_kernel<D, 2, 2>);
     default:
-        return reinterpret_cast<const void *>(tree_attn_kernel<D, 1>);
+        return reinterpret_cast<const void *>(tree_attn_kernel<D, 1, 2>);
     }
+}
+
+// Wave sets per workgroup: with one or two row waves the keys of every tile
+// are split between two sets of waves over the same rows, so a workgroup
+// keeps two or four SIMDs busy instead of one or two (a tile's chain of work
+// per wave is the same length at any row count).
+constexpr int ksp_for(int NW)
+{
+    return NW <= 2 ? 2 : 1;
 }
 
 int waves_for(int32_t N, int32_t Hq, int32_t Hkv)
@@ -1133,7 +1216,7 @@ bool attn_plan(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D, int32_t
         return false;
     const int NW = waves_for(N, Hq, Hkv);
     const void *fn = D == 128 ? kernel_for<128>(NW) : kernel_for<64>(NW);
-    const int per_cu = kernel_occupancy(fn, NW * 64);
+    const int per_cu = kernel_occupancy(fn, NW * ksp_for(NW) * 64);
     if (per_cu <= 0)
         return false;
     attn_plan_for(B, N, Hq, Hkv, D, max_prefix_len, cus, per_cu, p);
@@ -1150,7 +1233,8 @@ bool attn_shape_ok(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
 template <int D, int NW>
 hipError_t launch_main(const AttnPlan &p, const AttnArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL((tree_attn_kernel<D, NW>), dim3((unsigned)p.grid), dim3(NW * 64), 0, s, a);
+    constexpr int KSP = ksp_for(NW);
+    hipLaunchKernelGGL((tree_attn_kernel<D, NW, KSP>), dim3((unsigned)p.grid), dim3(NW * KSP * 64), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1192,7 +1276,7 @@ extern "C" tav_status tav_attn_plan(int32_t B, int32_t N, int32_t Hq, int32_t Hk
         const int64_t u0 = s * Ub / p.S, u1 = (s + 1) * Ub / p.S;
         most = std::max(most, std::min(u1, Tb) - std::min(u0, Tb));
     }
-    plan[0] = p.NW;
+    plan[0] = p.NW * ksp_for(p.NW);
     plan[1] = p.RB;
     plan[2] = p.S;
     plan[3] = (int32_t)(most * (kKT / kBlock));
