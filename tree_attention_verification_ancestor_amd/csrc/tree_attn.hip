@@ -47,12 +47,13 @@
 // Operand reads. The S and P.V MFMAs take their LDS operands from reads
 // issued four MFMAs ahead into separate registers, held in that order by a
 // scheduling fence after each MFMA.
-// Small row counts. With one or two row waves (32 or 64 query rows) a
-// workgroup has two wave sets over the same rows: set h takes keys
-// [32h, 32h + 32) of every tile (half the S and P.V MFMAs and half the
-// softmax each), and at the end the upper set's (O, max, sum) merge into
-// the lower set's through LDS, as two splits would. A tile's chain of work
-// per wave is then half as long and twice the SIMDs work on it.
+// Small row counts. Up to 128 query rows per (sequence, KV head) a
+// workgroup takes 128 rows (four row waves) in two wave sets over the same
+// rows: set h takes keys [32h, 32h + 32) of every tile (half the S and P.V
+// MFMAs and half the softmax each), and at the end the upper set's
+// (O, max, sum) merge into the lower set's through LDS, as two splits
+// would. A tile's chain of work per wave is then half as long, and eight
+// waves (two per SIMD) work on it.
 // Overlap. A wave's work per tile is an MFMA phase (S) and a phase that
 // mixes vector ALU work and MFMAs: the softmax of the tile spread between the
 // P.V MFMAs of the tile before. In an 8-wave workgroup the two waves that
@@ -873,8 +874,8 @@ __global__ __launch_bounds__(NW * KSP * 64) void tree_attn_kernel(AttnArgs a)
     // and the lower half's merge them into theirs, as two splits merge.
     if constexpr (KSP == 2) {
         constexpr int kOW = 16 * C::kDTiles;   // O values per lane
-        static_assert(NW * (kOW + 2) * 64 * 4 <= kKSlots * KTB, "merge area inside the K ring");
-        float *s_po = reinterpret_cast<float *>(s_k);
+        static_assert(NW * (kOW + 2) * 64 * 4 <= kVSlots * VTB, "merge area inside the V ring");
+        float *s_po = reinterpret_cast<float *>(s_v);
         float *s_pml = s_po + NW * kOW * 64;
         __syncthreads();   // every wave is past its last read of the ring
         if (half == 1) {
@@ -1141,31 +1142,24 @@ constexpr int kMaxSplits = 16;
 template <int D>
 const void *kernel_for(int NW)
 {
-    switch (NW) {
-    case 8:
-        return reinterpret_cast<const void *>(tree_attn_kernel<D, 8>);
-    case 4:
-        return reinterpret_cast<const void *>(tree_attn_kernel<D, 4>);
-    case 2:
-        return reinterpret_cast<const void *>(tree_attn_kernel<D, 2, 2>);
-    default:
-        return reinterpret_cast<const void *>(tree_attn_kernel<D, 1, 2>);
-    }
+    return NW == 8 ? reinterpret_cast<const void *>(tree_attn_kernel<D, 8>)
+                   : reinterpret_cast<const void *>(tree_attn_kernel<D, 4, 2>);
 }
 
-// Wave sets per workgroup: with one or two row waves the keys of every tile
-// are split between two sets of waves over the same rows, so a workgroup
-// keeps two or four SIMDs busy instead of one or two (a tile's chain of work
-// per wave is the same length at any row count).
+// Wave sets per workgroup: up to 128 query rows per (sequence, KV head) a
+// workgroup takes 128 rows (four row waves, padding rows included) and
+// splits the keys of every tile between two sets of them, eight waves, two
+// per SIMD (a tile's chain of work per wave is about the same length at any
+// row count, so more waves per CU is what shortens the launch).
 constexpr int ksp_for(int NW)
 {
-    return NW <= 2 ? 2 : 1;
+    return NW == 8 ? 1 : 2;
 }
 
 int waves_for(int32_t N, int32_t Hq, int32_t Hkv)
 {
     const int NG = N * (Hq / Hkv);
-    return NG > 128 ? 8 : NG > 64 ? 4 : NG > 32 ? 2 : 1;
+    return NG > 128 ? 8 : 4;   // see ksp_for
 }
 
 // Work decomposition for a shape on a device of `cus` compute units holding
@@ -1241,16 +1235,7 @@ hipError_t launch_main(const AttnPlan &p, const AttnArgs &a, hipStream_t s)
 template <int D>
 hipError_t launch_main_d(const AttnPlan &p, const AttnArgs &a, hipStream_t s)
 {
-    switch (p.NW) {
-    case 8:
-        return launch_main<D, 8>(p, a, s);
-    case 4:
-        return launch_main<D, 4>(p, a, s);
-    case 2:
-        return launch_main<D, 2>(p, a, s);
-    default:
-        return launch_main<D, 1>(p, a, s);
-    }
+    return p.NW == 8 ? launch_main<D, 8>(p, a, s) : launch_main<D, 4>(p, a, s);
 }
 
 } // namespace
