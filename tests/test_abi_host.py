@@ -265,6 +265,25 @@ def test_attention_plan_case_that_once_overflowed():
     assert p["splits"] >= 2
 
 
+def test_attention_plan_takes_four_row_waves_only_where_eight_underfill():
+    """64 tree nodes, 32 query heads on 8 KV heads (256 query rows per KV
+    head), 4096-token prefix, a 256-CU device: at batch one the 8-row-wave
+    form makes 128 workgroups (16 splits at most), so the plan takes the
+    4-row-wave form with two key sets (8 waves, 256 workgroups); from batch
+    two on the 8-row-wave form fills the device and is kept."""
+    p = tav.attn_plan(1, 64, 32, 8, 128, 4096, 256, 1)
+    assert (p["waves"], p["row_blocks"], p["splits"]) == (8, 2, 16)
+    for B in (2, 8, 32):
+        p = tav.attn_plan(B, 64, 32, 8, 128, 4096, 256, 1)
+        assert (p["waves"], p["row_blocks"]) == (8, 1), (B, p)
+    # above 256 rows the 8-row-wave form stays, filled or not
+    p = tav.attn_plan(1, 65, 32, 8, 128, 4096, 256, 1)
+    assert (p["waves"], p["row_blocks"]) == (8, 2)
+    # at most 128 rows: the 4-row-wave form, as before
+    p = tav.attn_plan(1, 16, 64, 8, 128, 4096, 256, 1)
+    assert (p["waves"], p["row_blocks"]) == (8, 1)
+
+
 def test_attention_plan_rejects_bad_arguments():
     lib = tav.lib()
     plan = (ctypes.c_int32 * 5)()

@@ -1162,16 +1162,15 @@ int waves_for(int32_t N, int32_t Hq, int32_t Hkv)
     return NG > 128 ? 8 : 4;   // see ksp_for
 }
 
-// Work decomposition for a shape on a device of `cus` compute units holding
-// `per_cu` workgroups each: waves per workgroup (NW, 32 query rows each), row
-// blocks (RB) and prefix splits (S), enough workgroups to fill the device
-// once. Pure arithmetic (no device call), so it can be checked on the host.
-void attn_plan_for(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
-                   int32_t max_prefix_len, int cus, int per_cu, AttnPlan &p)
+// The decomposition with NW row waves per workgroup (32 query rows each): row
+// blocks (RB) and prefix splits (S), enough workgroups to fill a device of
+// `cus` compute units holding `per_cu` workgroups each once.
+void attn_plan_nw(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                  int32_t max_prefix_len, int cus, int per_cu, int NW, AttnPlan &p)
 {
     const int G = Hq / Hkv;
     const int NG = N * G;
-    p.NW = waves_for(N, Hq, Hkv);
+    p.NW = NW;
     p.rows = 32 * p.NW;
     p.RB = (int)ceil_div(NG, p.rows);
     const int64_t base = (int64_t)B * Hkv * p.RB;
@@ -1199,6 +1198,26 @@ void attn_plan_for(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
     p.ws_bytes = p.S > 1 ? round_up(p.counter_bytes, 256) + round_up(p.part_o_bytes, 256) +
                                round_up(p.part_ml_bytes, 256)
                          : 0;
+}
+
+// Work decomposition for a shape. Pure arithmetic (no device call), so it can
+// be checked on the host. Above 128 query rows per (sequence, KV head) the
+// 8-row-wave form; but when it cannot fill the device (the 8B-shaped batch
+// one: 128 workgroups for 256 CUs) and the rows are at most 256, the 4-row-
+// wave form with its two key sets makes twice the row blocks and fills it
+// (measured: 27.7 against 32.9 us there, while at batch 8 and 32 of the same
+// shape, where the 8-row-wave form fills the device, it lost 4 and 23 %).
+void attn_plan_for(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                   int32_t max_prefix_len, int cus, int per_cu, AttnPlan &p)
+{
+    attn_plan_nw(B, N, Hq, Hkv, D, max_prefix_len, cus, per_cu, waves_for(N, Hq, Hkv), p);
+    const int64_t NG = (int64_t)N * (Hq / Hkv);
+    if (p.NW == 8 && NG <= 256 && p.grid < (int64_t)cus * per_cu) {
+        AttnPlan q;
+        attn_plan_nw(B, N, Hq, Hkv, D, max_prefix_len, cus, per_cu, 4, q);
+        if (q.grid > p.grid)
+            p = q;
+    }
 }
 
 // The same for the current device.
