@@ -276,6 +276,9 @@ def test_attention_plan_takes_four_row_waves_only_where_eight_underfill():
     for B in (2, 8, 32):
         p = tav.attn_plan(B, 64, 32, 8, 128, 4096, 256, 1)
         assert (p["waves"], p["row_blocks"]) == (8, 1), (B, p)
+    # the two GPU parity cases of this form (ragged second row block)
+    assert tav.attn_plan(1, 40, 32, 8, 64, 2000, 256, 1)["row_blocks"] == 2
+    assert tav.attn_plan(1, 60, 32, 8, 128, 2600, 256, 1)["row_blocks"] == 2
     # above 256 rows the 8-row-wave form stays, filled or not
     p = tav.attn_plan(1, 65, 32, 8, 128, 4096, 256, 1)
     assert (p["waves"], p["row_blocks"]) == (8, 2)

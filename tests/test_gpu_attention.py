@@ -34,6 +34,11 @@ CASES = [
     dict(N=1, B=2, Hq=64, Hkv=8, D=128, L=(700, 900), tree="chain"),
     dict(N=2, B=2, Hq=64, Hkv=8, D=128, L=(700, 900), tree="chain"),
     dict(N=4, B=2, Hq=64, Hkv=8, D=128, L=(300, 1500), tree="random"),
+    # 129..256 rows at batch one, which eight row waves cannot spread over
+    # the device: four row waves in two key sets, two row blocks (the
+    # second ragged), 16 splits
+    dict(N=40, B=1, Hq=32, Hkv=8, D=64, L=(2000, 2000), tree="random"),
+    dict(N=60, B=1, Hq=32, Hkv=8, D=128, L=(2600, 2600), tree="random"),
 ]
 
 
