@@ -673,7 +673,7 @@ LONG_ROWS, LONG_DEPTH, LONG_ROOT_WIDTH, LONG_W_MIN, LONG_W_MAX, LONG_BUDGET = 25
 
 
 def run_configs(args, dev, copy_gbs):
-    """The tiny, 8B, sweep and long-context workloads."""
+    """The tiny, 8B, 70B TP-8 share, sweep and long-context workloads."""
     import torch
 
     from synth import make_workload
@@ -687,7 +687,7 @@ def run_configs(args, dev, copy_gbs):
     def log(msg):
         print(f"[configs] {msg}", file=sys.stderr, flush=True)
 
-    for name in ("tiny", "llama8b", "long"):
+    for name in ("tiny", "llama8b", "llama70b_tp8", "long"):
         tree_info = None
         if name == "long":
             from synth.workloads import gather_nodes
@@ -793,7 +793,7 @@ def main():
                     help="Philox offsets of the acceptance statistics run")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
     ap.add_argument("--no-configs", action="store_true",
-                    help="time the headline workload only (no tiny/8B/sweep/long)")
+                    help="time the headline workload only (no tiny/8B/TP-8 share/sweep/long)")
     ap.add_argument("--config-steps", type=int, default=20, help="timed steps per config")
     ap.add_argument("--config-offsets", type=int, default=100,
                     help="Philox offsets of each config's acceptance run")

@@ -256,6 +256,11 @@ CONFIGS = {
                          sigma_t=3.0, accept=0.8, tree="best_first", widths=(3, 3, 3, 3)),
     "sweep_chain6": dict(seed=3, B=1, N=6, Hq=32, Hkv=8, D=128, V=128256, L=(2048, 2048),
                          sigma_t=3.0, accept=0.8, tree="chain"),
+    # One GPU's share of the 70B-shaped layer under 8-way tensor parallelism
+    # over KV heads: one KV head and its 8 query heads, the rest as the 70B
+    # layer (seeded as it, not by position).
+    "llama70b_tp8": dict(seed=2, B=8, N=64, Hq=8, Hkv=1, D=128, V=128256, L=(6144, 8192),
+                         sigma_t=3.0, sigma_d=1.0, tree="best_first", widths=(4,) * 6),
     # Long context: 70B-shaped layer, 32K paged prefix, 128-node depth-8 tree.
     "long": dict(seed=4, B=4, N=128, Hq=64, Hkv=8, D=128, V=151936, L=(32768, 32768),
                  sigma_t=3.0, sigma_d=0.7, tree="best_first", widths=(4,) * 8),

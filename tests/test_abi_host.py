@@ -265,26 +265,31 @@ def test_attention_plan_case_that_once_overflowed():
     assert p["splits"] >= 2
 
 
-def test_attention_plan_takes_four_row_waves_only_where_eight_underfill():
-    """64 tree nodes, 32 query heads on 8 KV heads (256 query rows per KV
-    head), 4096-token prefix, a 256-CU device: at batch one the 8-row-wave
-    form makes 128 workgroups (16 splits at most), so the plan takes the
-    4-row-wave form with two key sets (8 waves, 256 workgroups); from batch
-    two on the 8-row-wave form fills the device and is kept."""
-    p = tav.attn_plan(1, 64, 32, 8, 128, 4096, 256, 1)
-    assert (p["waves"], p["row_blocks"], p["splits"]) == (8, 2, 16)
-    for B in (2, 8, 32):
-        p = tav.attn_plan(B, 64, 32, 8, 128, 4096, 256, 1)
-        assert (p["waves"], p["row_blocks"]) == (8, 1), (B, p)
+def test_attention_plan_takes_four_row_waves_where_splits_dominate():
+    """On a 256-CU device: 64 tree nodes, 32 query heads on 8 KV heads (256
+    query rows per KV head), 4096-token prefix. At batch one the 8-row-wave
+    form makes 128 workgroups (16 splits at most) and at batch 2 and 4 it
+    needs 16 and 8 splits, so the plan takes four row waves in two key sets
+    (two row blocks, half the splits); from batch 8 on it fills the device
+    with 4 splits or fewer and keeps eight row waves. Above 256 rows (the
+    70B-shaped layer, 512 rows) only the split cap switches: batch one and
+    one KV head of batch 8 (16 splits) switch, batch 2 (8 splits) does not."""
+    rb = lambda *a: (lambda p: (p["row_blocks"], p["splits"]))(tav.attn_plan(*a, 256, 1))
+    assert rb(1, 64, 32, 8, 128, 4096) == (2, 16)
+    assert rb(2, 64, 32, 8, 128, 4096) == (2, 8)
+    assert rb(4, 64, 32, 8, 128, 4096) == (2, 4)
+    for B in (8, 32):
+        assert rb(B, 64, 32, 8, 128, 4096)[0] == 1, B
+    assert rb(1, 64, 64, 8, 128, 8192) == (4, 8)
+    assert rb(8, 64, 8, 1, 128, 8192) == (4, 8)
+    assert rb(2, 64, 64, 8, 128, 8192) == (2, 8)
+    assert rb(8, 64, 64, 8, 128, 8192) == (2, 2)
     # the two GPU parity cases of this form (ragged second row block)
     assert tav.attn_plan(1, 40, 32, 8, 64, 2000, 256, 1)["row_blocks"] == 2
     assert tav.attn_plan(1, 60, 32, 8, 128, 2600, 256, 1)["row_blocks"] == 2
-    # above 256 rows the 8-row-wave form stays, filled or not
-    p = tav.attn_plan(1, 65, 32, 8, 128, 4096, 256, 1)
-    assert (p["waves"], p["row_blocks"]) == (8, 2)
     # at most 128 rows: the 4-row-wave form, as before
-    p = tav.attn_plan(1, 16, 64, 8, 128, 4096, 256, 1)
-    assert (p["waves"], p["row_blocks"]) == (8, 1)
+    assert tav.attn_plan(1, 16, 64, 8, 128, 4096, 256, 1)["row_blocks"] == 1
+    assert tav.attn_plan(1, 16, 64, 8, 128, 4096, 256, 1)["waves"] == 8
 
 
 def test_attention_plan_rejects_bad_arguments():

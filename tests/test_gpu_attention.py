@@ -102,6 +102,14 @@ def test_attention_70b_full_size_sampled():
     say(f"  max abs err {err:.2e}")
 
 
+def test_attention_70b_tp8_share_sampled():
+    say("attention: one GPU's share of the 70B-shaped layer under 8-way tensor parallelism")
+    w = make_workload("llama70b_tp8", with_logits=False)
+    out, flags = run_attention(w, device())
+    err = _check(w, out, flags, batches=[0, 3, 6])
+    say(f"  max abs err {err:.2e}")
+
+
 def test_attention_long_context_sampled():
     say("attention: long context, sampled heads")
     w = make_workload("long", with_logits=False)

@@ -870,7 +870,7 @@ __global__ __launch_bounds__(NW * KSP * 64) void tree_attn_kernel(AttnArgs a)
         run(std::false_type{});
 
     // Two wave sets over the same rows: the upper key half's waves leave
-    // their (O, running max, sum share) in LDS (the K ring, no longer read)
+    // their (O, running max, sum share) in LDS (the V ring, no longer read)
     // and the lower half's merge them into theirs, as two splits merge.
     if constexpr (KSP == 2) {
         constexpr int kOW = 16 * C::kDTiles;   // O values per lane
@@ -1202,20 +1202,30 @@ void attn_plan_nw(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
 
 // Work decomposition for a shape. Pure arithmetic (no device call), so it can
 // be checked on the host. Above 128 query rows per (sequence, KV head) the
-// 8-row-wave form; but when it cannot fill the device (the 8B-shaped batch
-// one: 128 workgroups for 256 CUs) and the rows are at most 256, the 4-row-
-// wave form with its two key sets makes twice the row blocks and fills it
-// (measured: 27.7 against 32.9 us there, while at batch 8 and 32 of the same
-// shape, where the 8-row-wave form fills the device, it lost 4 and 23 %).
+// 8-row-wave form, unless its plan is dominated by splits, where the 4-row-
+// wave form with its two key sets makes twice the row blocks and so needs
+// half the splits (each split's fp32 partial is written and read back once
+// more): at most 256 rows, when the 8-row-wave form cannot fill the device
+// or needs 8 splits or more; above, only when it reaches the split cap.
+// Measured side by side: the 8B-shaped batch one 32.3 -> 27.4 us, batch 4
+// 48.0 -> 44.8 us; the 70B-shaped batch one 42.0 -> 39.9 us and one KV head
+// of its batch 8 43.3 -> 42.2 us; but the 70B-shaped batch 2 (8 splits, 512
+// rows) 57.3 against 58.7 us, and the 8B-shaped batch 8 and 32, where the
+// 8-row-wave form fills the device with few splits, 66.0 against 68.5 and
+// 156 against 191 us, so these keep it.
 void attn_plan_for(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
                    int32_t max_prefix_len, int cus, int per_cu, AttnPlan &p)
 {
     attn_plan_nw(B, N, Hq, Hkv, D, max_prefix_len, cus, per_cu, waves_for(N, Hq, Hkv), p);
+    if (p.NW != 8)
+        return;
     const int64_t NG = (int64_t)N * (Hq / Hkv);
-    if (p.NW == 8 && NG <= 256 && p.grid < (int64_t)cus * per_cu) {
+    const bool try4 = NG <= 256 ? (p.grid < (int64_t)cus * per_cu || p.S >= 8)
+                                : p.S >= kMaxSplits;
+    if (try4) {
         AttnPlan q;
         attn_plan_nw(B, N, Hq, Hkv, D, max_prefix_len, cus, per_cu, 4, q);
-        if (q.grid > p.grid)
+        if (q.grid > p.grid || q.S < p.S)
             p = q;
     }
 }
