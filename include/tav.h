@@ -111,9 +111,12 @@ size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, 
  * tav_attn_plan — how tree_attn_verify divides the work for these sizes on a
  * device of `cus` compute units holding `per_cu` of its workgroups each. A
  * host function (nothing launched, no device needed), for checking the plan:
- *   plan[0] waves per workgroup (32 query rows per wave; with one or two
- *   such row waves, twice that: two wave sets split each tile's keys),
- *   plan[1] row blocks, plan[2] prefix splits,
+ *   plan[0] waves per workgroup: 8 in both forms, eight row waves of 32
+ *   query rows (row blocks of 256 rows), or four row waves in two sets that
+ *   split each tile's keys (row blocks of 128 rows; taken up to 128 rows per
+ *   KV head, and above that where the first form's plan is dominated by
+ *   prefix splits),
+ *   plan[1] row blocks per (sequence, KV head), plan[2] prefix splits,
  *   plan[3] the most block-table entries any split stages, over every prefix
  *   length up to max_prefix_len, plan[4] the capacity of that staging copy
  *   (plan[3] <= plan[4] for every supported shape).
