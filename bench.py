@@ -805,7 +805,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path is single-GPU; see DESIGN.md for how it would shard)", file=sys.stderr)
+              "(the path runs on one GPU: no collectives or sharding across GPUs are built)", file=sys.stderr)
         sys.exit(2)
 
     if args.copy_calibration:
