@@ -284,6 +284,12 @@ def test_attention_plan_takes_four_row_waves_where_splits_dominate():
     assert rb(8, 64, 8, 1, 128, 8192) == (4, 8)
     assert rb(2, 64, 64, 8, 128, 8192) == (2, 8)
     assert rb(8, 64, 64, 8, 128, 8192) == (2, 2)
+    # splits the block-table bound forces on a full device do not switch:
+    # a 1M-token prefix at batch 4 (70B-shaped) and at batch 32 (8B-shaped)
+    p = tav.attn_plan(4, 64, 64, 8, 128, 1 << 20, 256, 1)
+    assert p["row_blocks"] == 2 and p["splits"] > 16, p
+    p = tav.attn_plan(32, 64, 32, 8, 128, 1 << 20, 256, 1)
+    assert p["row_blocks"] == 1 and p["splits"] > 8, p
     # the two GPU parity cases of this form (ragged second row block)
     assert tav.attn_plan(1, 40, 32, 8, 64, 2000, 256, 1)["row_blocks"] == 2
     assert tav.attn_plan(1, 60, 32, 8, 128, 2600, 256, 1)["row_blocks"] == 2

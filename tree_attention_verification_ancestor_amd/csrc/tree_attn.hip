@@ -1206,7 +1206,8 @@ void attn_plan_nw(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
 // wave form with its two key sets makes twice the row blocks and so needs
 // half the splits (each split's fp32 partial is written and read back once
 // more): at most 256 rows, when the 8-row-wave form cannot fill the device
-// or needs 8 splits or more; above, only when it reaches the split cap.
+// or needs 8 splits or more to fill it; above, only when filling it takes
+// the split cap.
 // Measured side by side: the 8B-shaped batch one 32.3 -> 27.4 us, batch 4
 // 48.0 -> 44.8 us; the 70B-shaped batch one 42.0 -> 39.9 us and one KV head
 // of its batch 8 43.3 -> 42.2 us; but the 70B-shaped batch 2 (8 splits, 512
@@ -1219,9 +1220,12 @@ void attn_plan_for(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
     attn_plan_nw(B, N, Hq, Hkv, D, max_prefix_len, cus, per_cu, waves_for(N, Hq, Hkv), p);
     if (p.NW != 8)
         return;
+    // the splits filling the device would take, before the caps and the
+    // block-table bound (which long prefixes raise on a full device too)
     const int64_t NG = (int64_t)N * (Hq / Hkv);
-    const bool try4 = NG <= 256 ? (p.grid < (int64_t)cus * per_cu || p.S >= 8)
-                                : p.S >= kMaxSplits;
+    const int64_t S_fill = ceil_div((int64_t)cus * per_cu, (int64_t)B * Hkv * p.RB);
+    const bool try4 = NG <= 256 ? (p.grid < (int64_t)cus * per_cu || S_fill >= 8)
+                                : S_fill >= kMaxSplits;
     if (try4) {
         AttnPlan q;
         attn_plan_nw(B, N, Hq, Hkv, D, max_prefix_len, cus, per_cu, 4, q);
